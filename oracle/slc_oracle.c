@@ -1,0 +1,583 @@
+/*
+ * slc_oracle.c -- plain, slow CPU oracle for one compressed sparse attention
+ * layer (DeepSeek-V4 style: compressor, lightning indexer + top-k, sparse MLA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library under sparse_long_context_compressor_amd/) never calls it, and
+ * the two share no source: no headers, helpers, tables or constants.
+ *
+ * Everything here works on *logical* per-sequence arrays in host memory (no
+ * paging); floating point is evaluated in double and rounded once to the
+ * output format.  Where floating point decides an integer (an fp8 code, a
+ * top-k membership) the decision is taken on the fp32 value, the precision
+ * the compressor state and the indexer accumulate in on the pages.
+ *
+ * Sources (the pages' titles; sections named as on each page):
+ *  [P1] "DeepSeek V4 attention in vLLM" (juejin.cn post 7667401749827403791):
+ *       layer-type table; "Compressor: ratio 4 vs 128" (window diagram,
+ *       position rule (pos//r)*r, start-of-sequence masking); "Indexer, C4A
+ *       and C128A top-k branch".
+ *  [P3] "DeepseekV4Attention" (devpress.csdn.net, AMD): DeepseekCompressor
+ *       forward (RoPE conventions), "CSA compressor" (softmax-gated pooling
+ *       formula, boundary table), "Indexer" (I_{t,s} formula), cache block
+ *       layout (fp8 nope + bf16 rope + per-64 scales).
+ *  [P5] "DeepSeek attention evolution: MLA to CSA/HCA": 5.1 CSA (slot j
+ *       covers [4j-4, 4j+3], anchor 4j, causality i >= 4j+3), 5.2 HCA
+ *       ([128j, 128j+127]), 6.1 (fp8 e4m3 + UE8M0 scales), 6.3 (slot
+ *       mapping: valid iff (pos+1) % r == 0, slot = pos // r), Ch.2 MLA
+ *       (absorbed MQA over the 576-wide latent, values = first 512 dims).
+ *
+ * Readings taken where the pages are silent or disagree (each is listed in
+ * the design notes): slots are ceil(L/r) with a trailing partial slot pooled
+ * over the tokens present; softmax is per channel over the window's tokens;
+ * RMSNorm runs over all 576 latent dims; the pow2 scale is the smallest 2^e
+ * with amax <= 448 * 2^e (exact comparison), stored as fp32; fp8 is OCP
+ * E4M3FN with round-to-nearest-even; top-k ties go to the lower slot index.
+ *
+ * Parity pins: every function here is pinned by tests/test_oracle_pins.py
+ * (closed forms, worked examples from the pages, library routines for the
+ * codecs, brute force over the full pool); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_D 576      /* latent row: 512 nope + 64 rope            [P5 Ch.2] */
+#define OR_DN 512     /* value / nope width                        [P5 Ch.2] */
+#define OR_DR 64      /* rope width                                [P3]      */
+#define OR_QB 64      /* fp8 quantisation block                    [P5 6.1]  */
+#define OR_DI 128     /* indexer head dim                          [P3]      */
+#define OR_E4M3_MAX 448.0
+
+/* ------------------------------------------------------------------ codecs */
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; largest finite 448 = 1.75 * 2^8. */
+double oracle_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);          /* m/8 * 2^(1-7) */
+    else
+        v = ldexp(8.0 + m, e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* Round x to the nearest E4M3FN value, ties to even; magnitudes at or above
+ * 448 saturate to 448.  The sign of a value that rounds to zero is kept. */
+uint8_t oracle_e4m3_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x), quantum, v;
+    int ex, lg;
+    if (isnan(x))
+        return 0x7F;
+    if (a >= OR_E4M3_MAX)
+        return sign | 0x7E;
+    if (a == 0.0)
+        return sign;
+    frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+    lg = ex - 1;                   /* floor(log2 a) */
+    if (lg < -6)
+        lg = -6;                   /* subnormal range shares 2^-6's quantum */
+    quantum = ldexp(1.0, lg - 3);  /* 3 mantissa bits */
+    v = nearbyint(a / quantum) * quantum;   /* default mode: ties to even */
+    if (v == 0.0)
+        return sign;
+    frexp(v, &ex);
+    lg = ex - 1;
+    if (lg < -6)
+        return sign | (uint8_t)(v * 512.0);            /* subnormal: v / 2^-9 */
+    return sign | (uint8_t)(((lg + 7) << 3) | ((int)ldexp(v, 3 - lg) - 8));
+}
+
+double oracle_bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round x to the nearest bfloat16 (8 significant bits, fp32 exponent range),
+ * ties to even, overflow to infinity. */
+uint16_t oracle_bf16_encode(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x), quantum, v;
+    int ex, lg;
+    float f;
+    uint32_t u;
+    if (isnan(x))
+        return 0x7FC0;
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7F80;
+    frexp(a, &ex);
+    lg = ex - 1;
+    if (lg < -126)
+        lg = -126;                 /* subnormal quantum is 2^-133 */
+    quantum = ldexp(1.0, lg - 7);
+    v = nearbyint(a / quantum) * quantum;
+    if (v >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    f = (float)v;                  /* exact: v has <= 8 significant bits */
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------ slot algebra */
+
+/* Slots a sequence of L tokens produces: ceil(L / r).  The pages emit a slot
+ * when (pos+1) % r == 0 [P5 6.3], i.e. floor(L/r) complete slots; a trailing
+ * partial window is also pooled (over the tokens present) but no query inside
+ * the sequence can see it (oracle_n_visible). */
+int oracle_n_slots(int L, int r)
+{
+    return L <= 0 ? 0 : (L + r - 1) / r;
+}
+
+/* Slots visible to a query at position p: j with p >= r*j + r - 1 [P5 5.1],
+ * capped by the slots that exist. */
+int oracle_n_visible(int p, int r, int n_slots)
+{
+    int v = (p + 1) / r;
+    if (v > n_slots)
+        v = n_slots;
+    return v < 0 ? 0 : v;
+}
+
+/* Token window of slot j: r=4 gathers 2r tokens with stride r, covering
+ * [4j-4, 4j+3] [P5 5.1; P3 boundary table]; r=128 covers [128j, 128j+127]
+ * [P5 5.2].  Clipped to [0, L) [P1: the first window only uses pos >= 0]. */
+void oracle_window(int j, int r, int L, int *t_lo, int *t_hi)
+{
+    int coff = (r == 4) ? 2 : 1;
+    int lo = r * j - (coff - 1) * r, hi = r * j + r - 1;
+    *t_lo = lo < 0 ? 0 : lo;
+    *t_hi = hi > L - 1 ? L - 1 : hi;
+}
+
+/* --------------------------------------------------------------- compress */
+
+static int pow2_exponent_for(double amax)
+{
+    int ex, e;
+    if (amax == 0.0)
+        return 0;
+    frexp(amax / OR_E4M3_MAX, &ex);
+    e = ex;
+    while (amax <= ldexp(OR_E4M3_MAX, e - 1))
+        e--;
+    while (amax > ldexp(OR_E4M3_MAX, e))
+        e++;
+    return e;
+}
+
+/*
+ * One sequence of L tokens, ratio r in {4, 128}.
+ *   kv    [L, 576] bf16 bits     per-token latent kv
+ *   score [L, 576] fp32          per-token gate logits (post-APE)
+ *   gamma [576] fp32, eps        RMSNorm weight
+ *   cos_sin [max_pos, 64] fp32   row p: 32 cos then 32 sin
+ * Outputs for each of n = ceil(L/r) slots:
+ *   codes [n, 512] e4m3, scales [n, 8] fp32 (powers of two), rope [n, 64] bf16;
+ *   pooled [n, 576] double (nullable) -- the softmax-pooled row;
+ *   prequant [n, 576] fp32 (nullable) -- the row after RMSNorm and RoPE.
+ * Returns 0, or -1 when a slot's anchor position is outside the table.
+ *
+ * Steps, in the pages' order [P3 CSA compressor diagram; P5 6.2]:
+ *  pool:  per channel d, w_t = softmax over t in the window of score[t][d];
+ *         pooled[d] = sum_t w_t kv[t][d]                       [P3; P5 5.1]
+ *  norm:  y = pooled * gamma / sqrt(mean(pooled^2) + eps)       [P3]
+ *  rope:  GPT-J interleaved pairs (512+2i, 513+2i) of the last 64 dims,
+ *         at position (pos // r) * r = r*j, cos/sin from the table [P3, P1]
+ *  quant: nope dims in 8 blocks of 64 -> e4m3 codes + pow2 scale;
+ *         rope dims -> bf16                                    [P3; P5 6.1]
+ */
+int oracle_compress_seq(int r, int L, const uint16_t *kv, const float *score,
+                        const float *gamma, double eps, const float *cos_sin,
+                        int max_pos, uint8_t *codes, float *scales,
+                        uint16_t *rope, double *pooled_out, float *prequant_out)
+{
+    int n = oracle_n_slots(L, r);
+    for (int j = 0; j < n; j++) {
+        double pooled[OR_D], y[OR_D];
+        float y32[OR_D];
+        int t_lo, t_hi, pos;
+        double ms = 0.0, inv;
+
+        oracle_window(j, r, L, &t_lo, &t_hi);
+        for (int d = 0; d < OR_D; d++) {
+            double m = -INFINITY, se = 0.0, acc = 0.0;
+            for (int t = t_lo; t <= t_hi; t++)
+                if ((double)score[(size_t)t * OR_D + d] > m)
+                    m = score[(size_t)t * OR_D + d];
+            for (int t = t_lo; t <= t_hi; t++) {
+                double e = exp((double)score[(size_t)t * OR_D + d] - m);
+                se += e;
+                acc += e * oracle_bf16_value(kv[(size_t)t * OR_D + d]);
+            }
+            pooled[d] = acc / se;
+        }
+        if (pooled_out)
+            memcpy(pooled_out + (size_t)j * OR_D, pooled, sizeof pooled);
+
+        for (int d = 0; d < OR_D; d++)
+            ms += pooled[d] * pooled[d];
+        ms /= OR_D;
+        inv = 1.0 / sqrt(ms + eps);
+        for (int d = 0; d < OR_D; d++)
+            y[d] = pooled[d] * inv * (double)gamma[d];
+
+        pos = r * j;
+        if (pos >= max_pos)
+            return -1;
+        for (int i = 0; i < OR_DR / 2; i++) {
+            double c = cos_sin[(size_t)pos * OR_DR + i];
+            double s = cos_sin[(size_t)pos * OR_DR + OR_DR / 2 + i];
+            double a = y[OR_DN + 2 * i], b = y[OR_DN + 2 * i + 1];
+            y[OR_DN + 2 * i] = a * c - b * s;
+            y[OR_DN + 2 * i + 1] = a * s + b * c;
+        }
+
+        for (int d = 0; d < OR_D; d++)
+            y32[d] = (float)y[d];
+        if (prequant_out)
+            memcpy(prequant_out + (size_t)j * OR_D, y32, sizeof y32);
+
+        for (int blk = 0; blk < OR_DN / OR_QB; blk++) {
+            double amax = 0.0, scale;
+            for (int i = 0; i < OR_QB; i++) {
+                double a = fabs((double)y32[blk * OR_QB + i]);
+                if (a > amax)
+                    amax = a;
+            }
+            scale = ldexp(1.0, pow2_exponent_for(amax));
+            scales[(size_t)j * (OR_DN / OR_QB) + blk] = (float)scale;
+            for (int i = 0; i < OR_QB; i++)
+                codes[(size_t)j * OR_DN + blk * OR_QB + i] =
+                    oracle_e4m3_encode((double)y32[blk * OR_QB + i] / scale);
+        }
+        for (int i = 0; i < OR_DR; i++)
+            rope[(size_t)j * OR_DR + i] = oracle_bf16_encode((double)y32[OR_DN + i]);
+    }
+    return 0;
+}
+
+/* Several sequences packed back to back: cu_seqlens [n_seq+1] token offsets;
+ * slot outputs packed the same way with cu_slots[b] = sum of ceil(L_b'/r)
+ * over earlier sequences.  Returns 0 or the first failing sequence's -1. */
+int oracle_compress_batch(int r, int n_seq, const int32_t *cu_seqlens,
+                          const uint16_t *kv, const float *score,
+                          const float *gamma, double eps, const float *cos_sin,
+                          int max_pos, uint8_t *codes, float *scales,
+                          uint16_t *rope, float *prequant_out)
+{
+    int rc = 0;
+    int64_t slot0 = 0;
+    for (int b = 0; b < n_seq; b++) {
+        int L = cu_seqlens[b + 1] - cu_seqlens[b];
+        size_t t0 = (size_t)cu_seqlens[b];
+        if (oracle_compress_seq(r, L, kv + t0 * OR_D, score + t0 * OR_D, gamma,
+                                eps, cos_sin, max_pos, codes + slot0 * OR_DN,
+                                scales + slot0 * (OR_DN / OR_QB),
+                                rope + slot0 * OR_DR, NULL,
+                                prequant_out ? prequant_out + slot0 * OR_D : NULL))
+            rc = -1;
+        slot0 += oracle_n_slots(L, r);
+    }
+    return rc;
+}
+
+/* ---------------------------------------------------------------- indexer */
+
+/*
+ * Lightning-indexer scores of one query against n keys [P3 Indexer]:
+ *   I_s = sum_j w_j * ReLU(q_j . k_s),  with the fp8 dequantisation scales
+ *   folded in: q_j . k_s = q_scale_j * k_scale_s * sum_d q_j[d] k_s[d].
+ * The fp8 dot is exact in double (each product is an integer multiple of
+ * 2^-18 below 2^18, and 128 of them stay below 2^53).  out64 is the double
+ * value, out32 its fp32 rounding (the value top-k decides on).
+ */
+void oracle_index_scores(int h_idx, int n, const uint8_t *q, const float *q_scale,
+                         const float *w, const uint8_t *keys,
+                         const float *key_scale, float *out32, double *out64)
+{
+    double qv[OR_DI];
+    double *acc = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    for (int j = 0; j < h_idx; j++) {
+        for (int d = 0; d < OR_DI; d++)
+            qv[d] = oracle_e4m3_value(q[(size_t)j * OR_DI + d]);
+        for (int s = 0; s < n; s++) {
+            double dot = 0.0, v;
+            for (int d = 0; d < OR_DI; d++)
+                dot += qv[d] * oracle_e4m3_value(keys[(size_t)s * OR_DI + d]);
+            v = (double)q_scale[j] * (double)key_scale[s] * dot;
+            if (v < 0.0)
+                v = 0.0;
+            acc[s] += (double)w[j] * v;
+        }
+    }
+    for (int s = 0; s < n; s++) {
+        if (out64)
+            out64[s] = acc[s];
+        if (out32)
+            out32[s] = (float)acc[s];
+    }
+    free(acc);
+}
+
+struct or_pair { float v; int32_t i; };
+
+static int cmp_score_desc_index_asc(const void *pa, const void *pb)
+{
+    const struct or_pair *a = (const struct or_pair *)pa, *b = (const struct or_pair *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i > b->i) - (a->i < b->i);
+}
+
+/* Per-query global top-k [P1 C4A branch; P3 SparseAttnIndexer]: the min(k, n)
+ * indices with the largest scores, ties to the lower index, listed in
+ * (score desc, index asc) order and padded with -1 [P2: -1 fill].
+ * Returns the length min(k, n). */
+int oracle_topk(int n, const float *scores, int k, int32_t *idx)
+{
+    struct or_pair *p = (struct or_pair *)malloc(sizeof(struct or_pair) * (size_t)(n > 0 ? n : 1));
+    int len = n < k ? n : k;
+    for (int s = 0; s < n; s++) {
+        p[s].v = scores[s];
+        p[s].i = s;
+    }
+    qsort(p, (size_t)n, sizeof(struct or_pair), cmp_score_desc_index_asc);
+    for (int t = 0; t < k; t++)
+        idx[t] = t < len ? p[t].i : -1;
+    free(p);
+    return len;
+}
+
+/*
+ * Scores + top-k for n_q queries.  Query t belongs to sequence q_seq[t] and
+ * sits at position q_pos[t]; it scores the visible slots
+ * s < n_visible(q_pos, r, n_slots[seq]).  Sequence b's keys start at key row
+ * key_off[b] of keys [*, 128] e4m3 / key_scale [*].
+ *   q [n_q, h_idx, 128] e4m3, q_scale / w [n_q, h_idx] fp32
+ *   idx [n_q, k] int32 out, len [n_q] out
+ *   scores32 [n_q, max_slots] fp32 out (nullable; unscored tail untouched)
+ */
+void oracle_index_topk_batch(int n_q, int h_idx, int k, const uint8_t *q,
+                             const float *q_scale, const float *w,
+                             const int32_t *q_pos, const int32_t *q_seq, int r,
+                             const int64_t *key_off, const int32_t *n_slots,
+                             const uint8_t *keys, const float *key_scale,
+                             int32_t *idx, int32_t *len, float *scores32,
+                             int max_slots)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < n_q; t++) {
+        int b = q_seq[t];
+        int nv = oracle_n_visible(q_pos[t], r, n_slots[b]);
+        float *sc = (float *)malloc(sizeof(float) * (size_t)(nv > 0 ? nv : 1));
+        oracle_index_scores(h_idx, nv, q + (size_t)t * h_idx * OR_DI,
+                            q_scale + (size_t)t * h_idx, w + (size_t)t * h_idx,
+                            keys + (size_t)key_off[b] * OR_DI,
+                            key_scale + key_off[b], sc, NULL);
+        len[t] = oracle_topk(nv, sc, k, idx + (size_t)t * k);
+        if (scores32)
+            memcpy(scores32 + (size_t)t * max_slots, sc, sizeof(float) * (size_t)nv);
+        free(sc);
+    }
+}
+
+/* --------------------------------------------------------------- attention */
+
+/*
+ * Sparse MLA attention of one query in absorbed (MQA) form [P5 Ch.2; P3
+ * forward_mqa / _forward_decode]: h query heads, one shared 576-wide latent
+ * key per attended entry, values = the key's first 512 dims.
+ *
+ * Attended list [P1: SWA indices together with compressed top-k; P4: the
+ * selected history concatenated with the recent window]:
+ *   SWA entries: positions max(0, p-W+1) .. p, rows swa_rows[pos - swa_base];
+ *   compressed entries: idx[0..k) with 0 <= idx < n_slots (others skipped),
+ *   each row = e4m3 code * pow2 scale for the 512 nope dims ++ bf16 rope.
+ * Entries are not deduplicated.
+ *   logit_i = sm_scale * q_h . K_i;  p = softmax(logit);
+ *   out_h = sum_i p_i K_i[0:512] (bf16), lse_h = ln sum_i exp(logit_i) (fp32).
+ * An empty list gives out = 0 and lse = -inf.
+ * Returns 0, or -1 if a window position has no row in swa_rows.
+ */
+int oracle_sparse_mla(int h, const uint16_t *q, int p, int W, int swa_base,
+                      int swa_count, const uint16_t *swa_rows, int n_slots,
+                      const uint8_t *codes, const float *scales,
+                      const uint16_t *rope, int k, const int32_t *idx,
+                      double sm_scale, uint16_t *out, float *lse,
+                      double *out64, double *lse64)
+{
+    int lo = p - W + 1 < 0 ? 0 : p - W + 1;
+    int n_swa = W > 0 ? p - lo + 1 : 0;
+    int cap = n_swa + (k > 0 ? k : 0);
+    double *K = (double *)malloc(sizeof(double) * OR_D * (size_t)(cap > 0 ? cap : 1));
+    double *logit = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    int n = 0;
+
+    for (int pos = lo; n_swa > 0 && pos <= p; pos++) {
+        if (pos < swa_base || pos >= swa_base + swa_count) {
+            free(K);
+            free(logit);
+            return -1;
+        }
+        for (int d = 0; d < OR_D; d++)
+            K[(size_t)n * OR_D + d] =
+                oracle_bf16_value(swa_rows[(size_t)(pos - swa_base) * OR_D + d]);
+        n++;
+    }
+    for (int t = 0; t < k; t++) {
+        int s = idx[t];
+        if (s < 0 || s >= n_slots)
+            continue;
+        for (int d = 0; d < OR_DN; d++)
+            K[(size_t)n * OR_D + d] = oracle_e4m3_value(codes[(size_t)s * OR_DN + d]) *
+                                      (double)scales[(size_t)s * (OR_DN / OR_QB) + d / OR_QB];
+        for (int d = 0; d < OR_DR; d++)
+            K[(size_t)n * OR_D + OR_DN + d] = oracle_bf16_value(rope[(size_t)s * OR_DR + d]);
+        n++;
+    }
+
+    for (int hh = 0; hh < h; hh++) {
+        double m = -INFINITY, se = 0.0, o[OR_DN];
+        const uint16_t *qh = q + (size_t)hh * OR_D;
+        for (int i = 0; i < n; i++) {
+            double dot = 0.0;
+            for (int d = 0; d < OR_D; d++)
+                dot += oracle_bf16_value(qh[d]) * K[(size_t)i * OR_D + d];
+            logit[i] = sm_scale * dot;
+            if (logit[i] > m)
+                m = logit[i];
+        }
+        for (int c = 0; c < OR_DN; c++)
+            o[c] = 0.0;
+        for (int i = 0; i < n; i++) {
+            double e = exp(logit[i] - m);
+            se += e;
+            for (int c = 0; c < OR_DN; c++)
+                o[c] += e * K[(size_t)i * OR_D + c];
+        }
+        for (int c = 0; c < OR_DN; c++) {
+            double v = n > 0 ? o[c] / se : 0.0;
+            out[(size_t)hh * OR_DN + c] = oracle_bf16_encode(v);
+            if (out64)
+                out64[(size_t)hh * OR_DN + c] = v;
+        }
+        {
+            double l = n > 0 ? m + log(se) : -INFINITY;
+            lse[hh] = (float)l;
+            if (lse64)
+                lse64[hh] = l;
+        }
+    }
+    free(K);
+    free(logit);
+    return 0;
+}
+
+/*
+ * Batch of n_q queries (decode: one per sequence; prefill: many per
+ * sequence).  Per sequence b: SWA rows start at row swa_off[b] of swa_rows
+ * and hold positions swa_base[b] .. swa_base[b]+swa_count[b]-1; compressed
+ * slots start at row cmp_off[b] of codes/scales/rope, n_slots[b] of them.
+ *   q [n_q, h, 576] bf16, idx [n_q, k] (NULL or k == 0: no compressed list)
+ *   out [n_q, h, 512] bf16, lse [n_q, h] fp32, out64/lse64 nullable doubles
+ * Returns 0, or -1 if any query's window is not covered by its SWA rows.
+ */
+int oracle_sparse_mla_batch(int n_q, int h, const uint16_t *q,
+                            const int32_t *q_pos, const int32_t *q_seq, int W,
+                            const int64_t *swa_off, const int32_t *swa_base,
+                            const int32_t *swa_count, const uint16_t *swa_rows,
+                            const int64_t *cmp_off, const int32_t *n_slots,
+                            const uint8_t *codes, const float *scales,
+                            const uint16_t *rope, int k, const int32_t *idx,
+                            double sm_scale, uint16_t *out, float *lse,
+                            double *out64, double *lse64)
+{
+    int rc = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < n_q; t++) {
+        int b = q_seq[t];
+        int kk = (idx && k > 0) ? k : 0;
+        int64_t co = cmp_off ? cmp_off[b] : 0;
+        int ns = n_slots ? n_slots[b] : 0;
+        int r1 = oracle_sparse_mla(
+            h, q + (size_t)t * h * OR_D, q_pos[t], W, swa_base[b], swa_count[b],
+            swa_rows + (size_t)swa_off[b] * OR_D, ns,
+            codes ? codes + (size_t)co * OR_DN : NULL,
+            scales ? scales + (size_t)co * (OR_DN / OR_QB) : NULL,
+            rope ? rope + (size_t)co * OR_DR : NULL, kk,
+            kk ? idx + (size_t)t * k : NULL, sm_scale,
+            out + (size_t)t * h * OR_DN, lse + (size_t)t * h,
+            out64 ? out64 + (size_t)t * h * OR_DN : NULL,
+            lse64 ? lse64 + (size_t)t * h : NULL);
+        if (r1) {
+#pragma omp atomic write
+            rc = -1;
+        }
+    }
+    return rc;
+}
+
+/* Threads an OpenMP region of this library uses (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+#endif
+    return n;
+}
+
+/* ------------------------------------------------ array forms of the codecs */
+
+void oracle_e4m3_decode_array(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_e4m3_value(in[i]);
+}
+
+void oracle_e4m3_encode_array(int64_t n, const double *in, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_e4m3_encode(in[i]);
+}
+
+void oracle_bf16_decode_array(int64_t n, const uint16_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_bf16_value(in[i]);
+}
+
+void oracle_bf16_encode_array(int64_t n, const double *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_bf16_encode(in[i]);
+}
+
+/* The pow2 quantisation scale the compressor picks for a block whose largest
+ * magnitude is amax (exposed for the scale-rule pins). */
+double oracle_pow2_scale(double amax)
+{
+    return ldexp(1.0, pow2_exponent_for(amax));
+}

@@ -1,0 +1,536 @@
+"""Pins of the CPU oracle against things other than itself: the pages' worked
+examples (tests/golden/), closed forms, invariants, library routines (torch's
+fp8/bf16 casts, numpy sorts and dots, scipy's softmax) and brute force over the
+whole pool.  Each test names what a plausible slip would break."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLD, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append(line.split())
+    return out
+
+
+def bf16_bits(t):
+    return t.to(torch.bfloat16).contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def fp8_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------- codecs
+def test_e4m3_decode_matches_torch_for_all_codes(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3_decode(codes)
+    ref = fp8_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_cast(oracle):
+    g = np.random.default_rng(1)
+    x = np.concatenate([
+        g.normal(0, 100, 20000), g.uniform(-448, 448, 20000), g.normal(0, 0.01, 5000),
+        np.ldexp(g.uniform(-1, 1, 5000), -9)]).astype(np.float32)
+    # every midpoint between adjacent finite codes (ties must go to even)
+    vals = np.unique(fp8_values(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids, vals.astype(np.float32), -vals.astype(np.float32)])
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = oracle.e4m3_encode(x.astype(np.float64))
+    assert np.array_equal(mine, ref)
+    # saturation above the largest finite value
+    assert oracle.e4m3_encode(np.array([500.0, -1e9]))[0] == 0x7E
+    assert oracle.e4m3_encode(np.array([500.0, -1e9]))[1] == 0xFE
+
+
+def test_bf16_encode_matches_torch_cast(oracle):
+    g = np.random.default_rng(2)
+    x = np.concatenate([g.normal(0, 1, 50000), g.normal(0, 1e-30, 2000),
+                        g.normal(0, 1e30, 2000)]).astype(np.float32)
+    # exact bf16 midpoints
+    b = bf16_bits(torch.from_numpy(g.normal(0, 1, 4000).astype(np.float32)))
+    lo = (b.astype(np.uint32) << 16).view(np.float32)
+    hi = ((b.astype(np.uint32) + 1) << 16).view(np.float32)
+    mids = ((lo.astype(np.float64) + hi.astype(np.float64)) / 2).astype(np.float32)
+    x = np.concatenate([x, mids])
+    ref = bf16_bits(torch.from_numpy(x))
+    mine = oracle.bf16_encode(x.astype(np.float64))
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(oracle.bf16_decode(ref), x.astype(np.float32).astype(np.float64) * 0 +
+                          torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+def _scale_exact(amax):
+    """Smallest power of two s with amax <= 448 s, by exact rational search."""
+    a = Fraction(amax)
+    if a == 0:
+        return 1.0
+    e = 0
+    while a > 448 * Fraction(2) ** e:
+        e += 1
+    while a <= 448 * Fraction(2) ** (e - 1):
+        e -= 1
+    return float(Fraction(2) ** e)
+
+
+def test_pow2_scale_rule(oracle):
+    for e in range(-20, 10):
+        edge = math.ldexp(448.0, e)
+        assert oracle.pow2_scale(edge) == math.ldexp(1.0, e)              # amax = 448*2^e
+        assert oracle.pow2_scale(np.nextafter(edge, np.inf)) == math.ldexp(1.0, e + 1)
+        assert oracle.pow2_scale(np.nextafter(edge, 0)) == math.ldexp(1.0, e)
+    g = np.random.default_rng(3)
+    for a in np.abs(g.normal(0, 10, 500)):
+        assert oracle.pow2_scale(a) == _scale_exact(a)
+    assert oracle.pow2_scale(0.0) == 1.0
+
+
+# -------------------------------------------------------------- slot algebra
+def test_slot_counts_are_ceil(oracle):
+    for r in (4, 128):
+        for L in range(0, 700):
+            assert oracle.n_slots(L, r) == -(-L // r)
+    assert oracle.n_slots(4096, 4) == 1024 and oracle.n_slots(131072, 128) == 1024
+    assert oracle.n_slots(65536, 4) == 16384
+
+
+def test_golden_windows(oracle):
+    for r, j, lo, hi, _anchor in (map(int, row) for row in _rows("windows.txt")):
+        L = 10 ** 6
+        got = oracle.window(j, r, L)
+        assert got == (max(lo, 0), hi), (r, j)
+
+
+def test_golden_slot_mapping(oracle):
+    for r, pos, boundary, slot, visible in (map(int, row) for row in _rows("slot_mapping.txt")):
+        # a boundary token completes slot pos // r: its window ends at pos
+        if boundary:
+            assert slot == pos // r
+            assert oracle.window(slot, r, 10 ** 6)[1] == pos
+        assert oracle.n_visible(pos, r, 10 ** 6) == visible
+    # causality on the r=4 page: position i sees slot j iff i >= 4j + 3
+    for i in range(0, 64):
+        for j in range(0, 20):
+            assert (j < oracle.n_visible(i, 4, 10 ** 6)) == (i >= 4 * j + 3)
+
+
+def test_byte_accounting_reproduces_the_pages():
+    from sparse_long_context_compressor_amd import pools as P
+    g = {k: int(v) for k, v in _rows("byte_accounting.txt")}
+    # the pages' formulas with the pages' widths
+    key = 128 + 128 // 128 * 4
+    ds_mla = 448 + 64 * 2 + 448 // 64 + 1
+    assert key == g["index_key_bytes"] and ds_mla == g["fp8_ds_mla_row_bytes"]
+    assert 64 * key == g["c4_indexer_block_bytes"] == P.KEY_BLOCK_BYTES
+    assert 64 * ds_mla == g["c4_attention_block_bytes"]
+    assert 2 * ds_mla == g["c128_attention_block_bytes"]
+    # the same per-row formula with this library's widths (512 fp8 nope,
+    # 64 bf16 rope, 8 fp32 scales)
+    assert P.CMP_BLOCK_BYTES == 64 * (512 + 64 * 2 + 512 // 64 * 4) == 64 * 672
+
+
+# ------------------------------------------------------------------ compress
+def _cs_identity(max_pos):
+    cs = np.zeros((max_pos, 64), np.float32)
+    cs[:, :32] = 1.0
+    return cs
+
+
+def _kv_onehot(L):
+    kv = np.zeros((L, 576), np.float32)
+    for t in range(L):
+        kv[t, t] = 1.0
+    return bf16_bits(torch.from_numpy(kv))
+
+
+@pytest.mark.parametrize("r,L", [(4, 16), (4, 14), (4, 5), (4, 1), (128, 300), (128, 128)])
+def test_pool_windows_by_onehot_tokens(oracle, r, L):
+    """Equal scores and one-hot token rows: pooled[j] is 1/|T_j| on exactly the
+    window's tokens, which pins the window, the clipping and ceil(L/r)."""
+    kv = _kv_onehot(L)
+    score = np.zeros((L, 576), np.float32)
+    res = oracle.compress_seq(r, kv, score, np.ones(576, np.float32), 1e-6, _cs_identity(L + 256))
+    n = -(-L // r)
+    assert res["pooled"].shape[0] == n
+    for j in range(n):
+        lo = max(0, r * j - (r if r == 4 else 0))
+        hi = min(L - 1, r * j + r - 1)
+        want = np.zeros(576)
+        want[lo:hi + 1] = 1.0 / (hi - lo + 1)
+        assert np.allclose(res["pooled"][j], want, rtol=0, atol=1e-15), j
+
+
+def test_pool_softmax_weights_closed_form(oracle):
+    """scores = ln(u): the pooled row is the u-weighted mean of the window."""
+    r, L = 4, 24
+    g = np.random.default_rng(5)
+    kvf = torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)).to(torch.bfloat16)
+    kv = bf16_bits(kvf)
+    u = g.uniform(0.1, 5.0, (L, 576))
+    score = np.log(u).astype(np.float32)
+    res = oracle.compress_seq(r, kv, score, np.ones(576, np.float32), 1e-6, _cs_identity(64))
+    kvd = kvf.double().numpy()
+    ud = np.exp(score.astype(np.float64))
+    for j in range(L // r):
+        lo, hi = max(0, 4 * j - 4), 4 * j + 3
+        want = (ud[lo:hi + 1] * kvd[lo:hi + 1]).sum(0) / ud[lo:hi + 1].sum(0)
+        assert np.allclose(res["pooled"][j], want, rtol=1e-12, atol=1e-14)
+
+
+def test_pool_dominant_score_and_invariants(oracle):
+    r, L = 4, 32
+    g = np.random.default_rng(6)
+    kvf = torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)).to(torch.bfloat16)
+    kv = bf16_bits(kvf)
+    score = g.normal(0, 1, (L, 576)).astype(np.float32)
+    cs = _cs_identity(64)
+    one = np.ones(576, np.float32)
+    base = oracle.compress_seq(r, kv, score, one, 1e-6, cs)["pooled"]
+    # adding a per-channel constant to every score changes nothing
+    sh = score + g.normal(0, 3, (1, 576)).astype(np.float32)
+    shifted = oracle.compress_seq(r, kv, sh, one, 1e-6, cs)["pooled"]
+    assert np.allclose(shifted, base, rtol=1e-5, atol=1e-6)
+    # permuting tokens inside one window (slot 3: tokens 8..15) only moves slot 3's
+    # neighbours; slot 3 itself is unchanged
+    perm = np.arange(L)
+    perm[8:12] = perm[8:12][::-1]
+    p2 = oracle.compress_seq(r, kv[perm], score[perm], one, 1e-6, cs)["pooled"]
+    assert np.allclose(p2[3], base[3], rtol=1e-12, atol=1e-14)
+    # a dominant score selects that token (softmax over scores, not -scores)
+    sd = np.zeros((L, 576), np.float32)
+    sd[13, :] = 100.0
+    pd = oracle.compress_seq(r, kv, sd, one, 1e-6, cs)["pooled"]
+    assert np.allclose(pd[3], kvf[13].double().numpy(), rtol=0, atol=1e-30 + 1e-40)
+    assert np.allclose(pd[4], kvf[13].double().numpy(), rtol=0, atol=1e-30 + 1e-40)
+    # constant rows pool to the constant
+    kc = bf16_bits(torch.full((L, 576), 0.375))
+    pc = oracle.compress_seq(r, kc, score, one, 1e-6, cs)["pooled"]
+    assert np.allclose(pc, 0.375, rtol=4e-15, atol=0)
+
+
+def test_rmsnorm_closed_form(oracle):
+    """Constant rows c: every output dim is c*gamma/sqrt(c^2+eps) before RoPE;
+    with the identity table the rope dims are unchanged."""
+    L, r, c, eps = 8, 4, 0.75, 1e-3
+    g = np.random.default_rng(7)
+    gamma = g.uniform(0.5, 2.0, 576).astype(np.float32)
+    kv = bf16_bits(torch.full((L, 576), c))
+    score = g.normal(0, 1, (L, 576)).astype(np.float32)
+    res = oracle.compress_seq(r, kv, score, gamma, eps, _cs_identity(16))
+    want = (c * gamma.astype(np.float64) / math.sqrt(c * c + eps)).astype(np.float32)
+    assert np.array_equal(res["prequant"][0], want)
+    # unit gamma: output RMS is sqrt(ms / (ms + eps)) for any row, and RoPE keeps it
+    kvr = bf16_bits(torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)))
+    cs = np.zeros((16, 64), np.float32)
+    ang = g.uniform(0, 6.28, (16, 32))
+    cs[:, :32], cs[:, 32:] = np.cos(ang), np.sin(ang)
+    res = oracle.compress_seq(r, kvr, score, np.ones(576, np.float32), 1e-6, cs)
+    for j in range(2):
+        ms = np.mean(res["pooled"][j] ** 2)
+        rms = np.sqrt(np.mean(res["prequant"][j].astype(np.float64) ** 2))
+        assert abs(rms - math.sqrt(ms / (ms + 1e-6))) < 1e-6
+
+
+def test_rope_anchor_pairing_and_sign(oracle):
+    """A table that is the identity everywhere except one row holding a 90 degree
+    turn (cos=0, sin=1): only the slot anchored at that row changes, and its
+    interleaved pairs (a, b) become (-b, a)."""
+    r, L = 4, 40
+    g = np.random.default_rng(8)
+    kv = bf16_bits(torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)))
+    score = g.normal(0, 1, (L, 576)).astype(np.float32)
+    one = np.ones(576, np.float32)
+    cs = _cs_identity(64)
+    base = oracle.compress_seq(r, kv, score, one, 1e-6, cs)["prequant"]
+    target = 6                                   # slot 6 -> anchor 4*6 = 24
+    cs2 = cs.copy()
+    cs2[24, :32], cs2[24, 32:] = 0.0, 1.0
+    turned = oracle.compress_seq(r, kv, score, one, 1e-6, cs2)["prequant"]
+    for j in range(L // r):
+        if j != target:
+            assert np.array_equal(turned[j], base[j])
+    a, b = base[target, 512::2], base[target, 513::2]
+    assert np.array_equal(turned[target, 512::2], -b)
+    assert np.array_equal(turned[target, 513::2], a)
+    assert np.array_equal(turned[target, :512], base[target, :512])
+    # r=128: slot 1 is anchored at position 128
+    L2 = 300
+    kv2 = bf16_bits(torch.from_numpy(g.normal(0, 1, (L2, 576)).astype(np.float32)))
+    s2 = g.normal(0, 1, (L2, 576)).astype(np.float32)
+    c3 = _cs_identity(400)
+    b2 = oracle.compress_seq(128, kv2, s2, one, 1e-6, c3)["prequant"]
+    c3[128, :32], c3[128, 32:] = 0.0, 1.0
+    t2 = oracle.compress_seq(128, kv2, s2, one, 1e-6, c3)["prequant"]
+    assert np.array_equal(t2[0], b2[0]) and np.array_equal(t2[2], b2[2])
+    assert np.array_equal(t2[1, 512::2], -b2[1, 513::2])
+
+
+def test_quantiser_against_library_casts(oracle):
+    """Codes = torch's e4m3 cast of prequant/scale, scale = exact pow2 rule on the
+    block amax, rope = torch's bf16 cast; dequantised values are exact in bf16."""
+    r, L = 4, 64
+    g = np.random.default_rng(9)
+    kv = bf16_bits(torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)))
+    score = g.normal(0, 1, (L, 576)).astype(np.float32)
+    gamma = g.uniform(0.01, 50.0, 576).astype(np.float32)    # spread block magnitudes
+    cs = np.zeros((64, 64), np.float32)
+    ang = g.uniform(0, 6.28, (64, 32))
+    cs[:, :32], cs[:, 32:] = np.cos(ang), np.sin(ang)
+    res = oracle.compress_seq(r, kv, score, gamma, 1e-6, cs)
+    pre = res["prequant"]
+    for j in range(pre.shape[0]):
+        for blk in range(8):
+            x = pre[j, 64 * blk: 64 * blk + 64]
+            s = _scale_exact(float(np.max(np.abs(x.astype(np.float64)))))
+            assert res["scales"][j, blk] == s
+            ref = torch.from_numpy((x.astype(np.float64) / s).astype(np.float32)).to(
+                torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(res["codes"][j, 64 * blk: 64 * blk + 64], ref)
+            deq = fp8_values(ref) * s
+            assert np.array_equal(torch.from_numpy(deq).to(torch.bfloat16).double().numpy(), deq)
+        assert np.array_equal(res["rope"][j], bf16_bits(torch.from_numpy(pre[j, 512:])))
+    assert int(np.max(np.abs(fp8_values(res["codes"])))) <= 448
+
+
+def test_compress_batch_equals_per_sequence(oracle):
+    g = np.random.default_rng(10)
+    lens = [13, 64, 1, 37]
+    T = sum(lens)
+    kv = bf16_bits(torch.from_numpy(g.normal(0, 1, (T, 576)).astype(np.float32)))
+    sc = g.normal(0, 1, (T, 576)).astype(np.float32)
+    one = np.ones(576, np.float32)
+    cs = _cs_identity(128)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    bat = oracle.compress_batch(4, cu, kv, sc, one, 1e-6, cs)
+    s0 = 0
+    for b, L in enumerate(lens):
+        one_seq = oracle.compress_seq(4, kv[cu[b]:cu[b + 1]], sc[cu[b]:cu[b + 1]], one, 1e-6, cs)
+        n = -(-L // 4)
+        assert np.array_equal(bat["codes"][s0:s0 + n], one_seq["codes"])
+        assert np.array_equal(bat["scales"][s0:s0 + n], one_seq["scales"])
+        assert np.array_equal(bat["rope"][s0:s0 + n], one_seq["rope"])
+        s0 += n
+
+
+# ------------------------------------------------------------------- indexer
+def _rand_codes(g, shape):
+    x = torch.from_numpy((g.normal(0, 64, shape)).clip(-448, 448).astype(np.float32))
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_index_single_head_is_relu_of_exact_dot(oracle):
+    g = np.random.default_rng(11)
+    q = _rand_codes(g, (1, 128))
+    keys = _rand_codes(g, (300, 128))
+    s32, s64 = oracle.index_scores(q, np.ones(1, np.float32), np.ones(1, np.float32), keys,
+                                   np.ones(300, np.float32))
+    dots = fp8_values(keys) @ fp8_values(q)[0]
+    assert np.array_equal(s64, np.maximum(dots, 0.0))
+    assert np.array_equal(s32, np.maximum(dots, 0.0).astype(np.float32))
+    assert np.any(dots < 0) and np.any(dots > 0)
+
+
+def test_index_heads_add_with_weights_and_scales(oracle):
+    g = np.random.default_rng(12)
+    H, n = 8, 200
+    q = _rand_codes(g, (H, 128))
+    keys = _rand_codes(g, (n, 128))
+    w = g.uniform(0, 1, H).astype(np.float32)
+    qs = np.ldexp(1.0, g.integers(-8, -4, H)).astype(np.float32)
+    ks = np.ldexp(1.0, g.integers(-8, -4, n)).astype(np.float32)
+    _, full = oracle.index_scores(q, qs, w, keys, ks)
+    parts = np.zeros(n)
+    for j in range(H):
+        _, unit = oracle.index_scores(q[j:j + 1], np.ones(1, np.float32), np.ones(1, np.float32),
+                                      keys, np.ones(n, np.float32))
+        parts += float(w[j]) * float(qs[j]) * ks.astype(np.float64) * unit
+    assert np.allclose(full, parts, rtol=1e-13, atol=0)
+    # a head whose query is the negated key scores that key at zero
+    qn = (keys[5:6].copy() ^ 0x80).astype(np.uint8)
+    _, z = oracle.index_scores(qn, np.ones(1, np.float32), np.ones(1, np.float32), keys[5:6],
+                               np.ones(1, np.float32))
+    assert z[0] == 0.0
+
+
+def test_topk_matches_full_sort(oracle):
+    g = np.random.default_rng(13)
+    for n, k, kind in [(1000, 64, "rand"), (1000, 64, "ties"), (50, 64, "rand"), (0, 8, "rand"),
+                       (300, 300, "ties"), (2048, 256, "zeros")]:
+        if kind == "rand":
+            s = g.normal(0, 1, n).astype(np.float32)
+        elif kind == "ties":
+            s = g.integers(0, 5, n).astype(np.float32)
+        else:
+            s = np.zeros(n, np.float32)
+        idx, ln = oracle.topk(s, k)
+        order = np.lexsort((np.arange(n), -s.astype(np.float64)))
+        want = order[:min(k, n)]
+        assert ln == min(k, n)
+        assert np.array_equal(idx[:ln], want)
+        assert np.all(idx[ln:] == -1)
+        if kind == "zeros":
+            assert np.array_equal(idx, np.arange(k))
+
+
+def test_index_topk_batch_respects_visibility(oracle):
+    g = np.random.default_rng(14)
+    ns = [37, 90]
+    key_off = np.array([0, 37], np.int64)
+    keys = _rand_codes(g, (127, 128))
+    ks = np.ones(127, np.float32)
+    qpos = np.array([0, 3, 50, 149, 500, 359], np.int32)
+    qseq = np.array([0, 0, 0, 0, 1, 1], np.int32)
+    H = 4
+    q = _rand_codes(g, (6, H, 128))
+    qs = np.ones((6, H), np.float32)
+    w = g.uniform(0, 1, (6, H)).astype(np.float32)
+    idx, ln, sc = oracle.index_topk_batch(16, q, qs, w, qpos, qseq, 4, key_off, ns, keys, ks,
+                                          want_scores=True)
+    for t in range(6):
+        nv = min(ns[qseq[t]], (qpos[t] + 1) // 4)
+        assert ln[t] == min(16, nv)
+        s32, _ = oracle.index_scores(q[t], qs[t], w[t], keys[key_off[qseq[t]]:][:nv], ks[:nv])
+        assert np.array_equal(sc[t, :nv], s32)
+        want, _ = oracle.topk(s32, 16)
+        assert np.array_equal(idx[t], want)
+
+
+# ----------------------------------------------------------------- attention
+def _attn_case(g, H=4, L=400, W=16, n_slots=40, k=12):
+    q = torch.from_numpy(g.normal(0, 1, (H, 576)).astype(np.float32)).to(torch.bfloat16)
+    swa = torch.from_numpy(g.normal(0, 1, (L, 576)).astype(np.float32)).to(torch.bfloat16)
+    codes = _rand_codes(g, (n_slots, 512))
+    scales = np.ldexp(1.0, g.integers(-8, -4, (n_slots, 8))).astype(np.float32)
+    rope = torch.from_numpy(g.normal(0, 1, (n_slots, 64)).astype(np.float32)).to(torch.bfloat16)
+    idx = g.permutation(n_slots)[:k].astype(np.int32)
+    return q, swa, codes, scales, rope, idx
+
+
+def _masked_full_attention(q, swa, codes, scales, rope, allowed_swa, allowed_cmp, sm):
+    """Full attention over every row of both pools with -inf outside the
+    allowed set (the attended-set definition, evaluated the dense way)."""
+    cmp = np.concatenate([fp8_values(codes) * np.repeat(scales.astype(np.float64), 64, axis=1),
+                          rope.double().numpy()], axis=1)
+    K = np.concatenate([swa.double().numpy(), cmp], axis=0)
+    mask = np.concatenate([allowed_swa, allowed_cmp])
+    logits = sm * (q.double().numpy() @ K.T)
+    logits[:, ~mask] = -np.inf
+    lse = logsumexp(logits, axis=1)
+    p = np.exp(logits - lse[:, None])
+    return p @ K[:, :512], lse
+
+
+def test_attention_equals_masked_full_attention(oracle):
+    g = np.random.default_rng(15)
+    q, swa, codes, scales, rope, idx = _attn_case(g)
+    p, W, sm = 399, 16, 1 / math.sqrt(576)
+    out, lse, o64, l64 = oracle.sparse_mla(bf16_bits(q), p, W, 0, bf16_bits(swa), sm, codes,
+                                           scales, bf16_bits(rope), idx)
+    allowed_swa = np.zeros(400, bool)
+    allowed_swa[p - W + 1: p + 1] = True
+    allowed_cmp = np.zeros(40, bool)
+    allowed_cmp[idx] = True
+    ro, rl = _masked_full_attention(q, swa, codes, scales, rope, allowed_swa, allowed_cmp, sm)
+    assert np.allclose(o64, ro, rtol=1e-11, atol=1e-13)
+    assert np.allclose(l64, rl, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(out, bf16_bits(torch.from_numpy(o64)))
+    # swaonly: the textbook window attention
+    out2, _, o2, l2 = oracle.sparse_mla(bf16_bits(q), p, W, 0, bf16_bits(swa), sm)
+    r2, rl2 = _masked_full_attention(q, swa, codes, scales, rope, allowed_swa,
+                                     np.zeros(40, bool), sm)
+    assert np.allclose(o2, r2, rtol=1e-11, atol=1e-13) and np.allclose(l2, rl2)
+    # window shorter than W at the sequence start
+    out3, _, o3, _ = oracle.sparse_mla(bf16_bits(q), 5, W, 0, bf16_bits(swa), sm, codes, scales,
+                                       bf16_bits(rope), idx)
+    a3 = np.zeros(400, bool)
+    a3[:6] = True
+    r3, _ = _masked_full_attention(q, swa, codes, scales, rope, a3, allowed_cmp, sm)
+    assert np.allclose(o3, r3, rtol=1e-11, atol=1e-13)
+
+
+def test_attention_skips_invalid_entries_and_covers_all_slots(oracle):
+    g = np.random.default_rng(16)
+    q, swa, codes, scales, rope, idx = _attn_case(g, n_slots=20, k=6)
+    sm = 0.05
+    args = (bf16_bits(q), 399, 16, 0, bf16_bits(swa), sm, codes, scales, bf16_bits(rope))
+    _, _, base, lb = oracle.sparse_mla(*args, idx)
+    noisy = np.concatenate([idx[:3], [-1, 20, 10 ** 6], idx[3:], [-7]]).astype(np.int32)
+    _, _, o2, l2 = oracle.sparse_mla(*args, noisy)
+    assert np.array_equal(o2, base) and np.array_equal(l2, lb)
+    # k covering every slot: dense attention over all slots plus the window
+    _, _, o3, _ = oracle.sparse_mla(*args, np.arange(20, dtype=np.int32))
+    aw = np.zeros(400, bool)
+    aw[384:400] = True
+    r3, _ = _masked_full_attention(q, swa, codes, scales, rope, aw, np.ones(20, bool), sm)
+    assert np.allclose(o3, r3, rtol=1e-11, atol=1e-13)
+
+
+def test_attention_one_key_and_repeated_keys(oracle):
+    g = np.random.default_rng(17)
+    q, swa, codes, scales, rope, _ = _attn_case(g, n_slots=4)
+    sm = 0.07
+    # window of one position, no compressed entries: out = V exactly, lse = logit
+    out, lse, o64, l64 = oracle.sparse_mla(bf16_bits(q), 10, 1, 0, bf16_bits(swa), sm)
+    assert np.array_equal(out, np.tile(bf16_bits(swa[10, :512]), (4, 1)))
+    logit = sm * (q.double().numpy() @ swa[10].double().numpy())
+    assert np.allclose(l64, logit, rtol=1e-14, atol=1e-14)
+    # the same slot listed n times: out = its value row, lse = logit + ln n
+    n = 5
+    _, _, o5, l5 = oracle.sparse_mla(bf16_bits(q), 0, 0, 0, bf16_bits(swa), sm, codes, scales,
+                                     bf16_bits(rope), np.full(n, 2, np.int32))
+    v = fp8_values(codes[2]) * np.repeat(scales[2].astype(np.float64), 64)
+    kfull = np.concatenate([v, rope[2].double().numpy()])
+    assert np.allclose(o5, np.tile(v, (4, 1)), rtol=1e-14, atol=1e-14)
+    assert np.allclose(l5, sm * (q.double().numpy() @ kfull) + math.log(n), rtol=1e-13)
+    # nothing to attend: zeros and -inf
+    out0, lse0, _, _ = oracle.sparse_mla(bf16_bits(q), 0, 0, 0, bf16_bits(swa), sm, codes, scales,
+                                         bf16_bits(rope), np.array([-1], np.int32))
+    assert np.all(out0 == 0) and np.all(np.isneginf(lse0))
+
+
+def test_attention_batch_equals_single(oracle):
+    g = np.random.default_rng(18)
+    H, n_slots = 4, 30
+    q = torch.from_numpy(g.normal(0, 1, (3, H, 576)).astype(np.float32)).to(torch.bfloat16)
+    swa = torch.from_numpy(g.normal(0, 1, (43, 576)).astype(np.float32)).to(torch.bfloat16)
+    codes = _rand_codes(g, (2 * n_slots, 512))
+    scales = np.ldexp(1.0, g.integers(-8, -4, (2 * n_slots, 8))).astype(np.float32)
+    rope = torch.from_numpy(g.normal(0, 1, (2 * n_slots, 64)).astype(np.float32)).to(torch.bfloat16)
+    idx = np.stack([g.permutation(n_slots)[:7] for _ in range(3)]).astype(np.int32)
+    qpos = np.array([119, 100, 59], np.int32)
+    qseq = np.array([0, 0, 1], np.int32)
+    # seq 0 SWA rows hold positions 85..119, seq 1 holds 52..59
+    swa_off = np.array([0, 35], np.int64)
+    swa_base = np.array([85, 52], np.int32)
+    swa_cnt = np.array([35, 8], np.int32)
+    out, lse = oracle.sparse_mla_batch(bf16_bits(q), qpos, qseq, 8, swa_off, swa_base, swa_cnt,
+                                       bf16_bits(swa), 0.04, np.array([0, n_slots], np.int64),
+                                       np.array([n_slots, n_slots], np.int32), codes, scales,
+                                       bf16_bits(rope), idx)
+    for t in range(3):
+        b = qseq[t]
+        o1, l1, _, _ = oracle.sparse_mla(
+            bf16_bits(q[t]), qpos[t], 8, swa_base[b],
+            bf16_bits(swa[swa_off[b]: swa_off[b] + swa_cnt[b]]), 0.04,
+            codes[b * n_slots:(b + 1) * n_slots], scales[b * n_slots:(b + 1) * n_slots],
+            bf16_bits(rope[b * n_slots:(b + 1) * n_slots]), idx[t])
+        assert np.array_equal(out[t], o1) and np.array_equal(lse[t], l1)
