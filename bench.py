@@ -1,0 +1,185 @@
+"""Benchmark: one C4A decode step at 64K context on one MI355X.
+
+A step is the whole hot path over one batch: index scores -> top-k select ->
+sparse MLA decode (+ split merge), for B=32 queries, H=64 heads, 16384
+compressed slots per sequence (context 65536, ratio 4), top-k 512, SWA 128,
+indexer 64 heads x 128 dims, 64-row paged blocks with permuted tables.
+Inputs are resident in HBM before timing; the step cycles through several
+independent input replicas so the 256 MB last-level cache cannot hold them.
+
+Prints one JSON line (see the repository's measurement notes for fields).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode queries/s + achieved HBM GB/s (C4A, 64K ctx, 1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+
+B, H, CTX, SLOTS, K, W, HI = 32, 64, 65536, 16384, 512, 128, 64
+
+# algorithmic bytes (each byte the step must move once)
+IDX_BYTES_PER_SLOT = 128 + 4 + 4            # key codes + key scale + score written
+IDX_BYTES_PER_QUERY = HI * 128 + HI * 8     # index query codes + scale + weight
+TOPK_BYTES_PER_QUERY = SLOTS * 4 + K * 4 + 4
+ATTN_BYTES_PER_QUERY = (H * 576 * 2 + W * 1152 + K * 672 + K * 4 + H * 512 * 2 + H * 4)
+STEP_BYTES = B * (SLOTS * 132 + IDX_BYTES_PER_QUERY + K * 4 + ATTN_BYTES_PER_QUERY)
+INDEX_KERNEL_BYTES = B * (SLOTS * IDX_BYTES_PER_SLOT + IDX_BYTES_PER_QUERY)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="queries the oracle times")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "sparse_long_context_compressor_amd", "csrc", "index.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per index-score launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "index_score_c4a_decode_64k_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("index_hip_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(n_q: int):
+    """The oracle (as it stands) on a bounded sample: n_q sequences of the same
+    workload shape, index top-k then attention, on the host's cores."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_attention, oracle_index_topk
+    from sparse_long_context_compressor_amd import inputs as I
+    lay = I.c4a_decode_64k(seed=2, device="cpu", batch=n_q)
+    t0 = time.perf_counter()
+    idx, _ = oracle_index_topk(O, lay, want_scores=False)
+    oracle_attention(O, lay, idx)
+    dt = time.perf_counter() - t0
+    return {"value": n_q / dt, "unit": "queries/s", "cores": int(O.num_threads()),
+            "kind": "oracle",
+            "sample": f"{n_q} of the 32 sequences (same per-query shapes: 16384 slots, H_I=64, "
+                      f"k=512, H=64, SWA 128), index top-k + attention, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU (the decode path shards by sequence with "
+              "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_long_context_compressor_amd import inputs as I
+    from sparse_long_context_compressor_amd import slc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    slc.lib()
+    reps = [I.c4a_decode_64k(seed=100 + r, device=dev) for r in range(args.replicas)]
+    torch.cuda.synchronize()
+
+    scores = torch.empty((B, SLOTS), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    ln = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_bytes = slc.sparse_mla_workspace_size(True, B, H, W, K)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(lay, ev=None):
+        if ev is not None:
+            ev[0].record()
+        slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
+                         lay.key_table, lay.n_slots, SLOTS, scores)
+        if ev is not None:
+            ev[1].record()
+        slc.topk_select(K, scores, SLOTS, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
+        if ev is not None:
+            ev[2].record()
+        slc.sparse_mla_decode(4, lay.q, lay.q_seq, lay.q_pos, W, lay.swa_pool, lay.swa_table,
+                              lay.cmp_pool, lay.cmp_table, idx, lay.n_slots, lay.sm_scale, out,
+                              lse, ws)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(reps[i % len(reps)], evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    topk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    achieved = INDEX_KERNEL_BYTES / (idx_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c4a_decode_64k", "batch": B, "heads": H, "context": CTX,
+                   "slots_per_seq": SLOTS, "topk": K, "window": W, "index_heads": HI,
+                   "block_rows": 64, "replicas": args.replicas},
+        "achieved_step_GBps": STEP_BYTES / (ms_step * 1e-3) / 1e9,
+        "step_hbm_frac": STEP_BYTES / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": {"index_scores": idx_ms * 1e3, "topk_select": topk_ms * 1e3,
+                       "sparse_mla_decode": attn_ms * 1e3},
+        "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profile(), "algorithmic_bytes": INDEX_KERNEL_BYTES},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

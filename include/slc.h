@@ -1,0 +1,252 @@
+/*
+ * slc.h -- C ABI of the MI355X (gfx950) compressed sparse attention library.
+ *
+ * One DeepSeek-V4-style attention layer with compressed history, in four
+ * calls (plus the two stages of the indexer on their own):
+ *
+ *   slc_compress            softmax-gated pooling of ratio-r token windows,
+ *                           RMSNorm, RoPE at the slot anchor, FP8 quantisation,
+ *                           paged store.
+ *   slc_index_scores        lightning-indexer scores of FP8 index queries
+ *                           against the FP8 index keys of the visible slots.
+ *   slc_topk_select         per-query global top-k over those scores.
+ *   slc_index_topk          the two above in one call.
+ *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
+ *   slc_sparse_mla_prefill  window plus the selected compressed slots.
+ *
+ * Sources, by page title and section:
+ *   "DeepSeek-V4 attention layer types" (juejin.cn post 7667401749827403791):
+ *       layer-type table (compress_ratio 1 / 4 / 128 -> swaonly / c4a /
+ *       c128a), "Compressor" (window overlap, anchor (pos//r)*r), "Indexer,
+ *       C4A and C128A top-k" (c4a computes a global top-k per step, c128a
+ *       takes a precomputed list; FlashMLA takes SWA and compressed indices).
+ *   "DeepseekV4Attention" (devpress.csdn.net, AMD): DeepseekCompressor
+ *       forward and its kernel arguments, CSA compressor formula and
+ *       boundary table, cache block layout, Indexer formula, forward_mqa,
+ *       _forward_prefill / _forward_decode call surfaces.
+ *   "From MLA to CSA + HCA" (forceinjection.github.io): Ch.2 absorbed MLA
+ *       (576-wide latent, values from its first 512 dims), 5.1 CSA, 5.2 HCA,
+ *       6.1 precisions, 6.3 compressed slot mapping.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers are device memory owned by the caller unless stated.  The
+ *   library allocates nothing, keeps no global state and never synchronises
+ *   the stream or reads device memory on the host; every call only enqueues
+ *   kernels on `stream` (a hipStream_t passed as void*; NULL = null stream).
+ * - Argument errors are found on the host before any launch and returned as
+ *   SLC_ERR_INVALID_ARG (nothing is enqueued); a too-small workspace is
+ *   SLC_ERR_WORKSPACE; a failed launch is SLC_ERR_HIP.  Nothing throws.
+ * - Device-side index contents (block tables, slot and position lists) are
+ *   never trusted: entries that are negative or out of range are skipped,
+ *   never dereferenced.
+ * - bf16 is passed as its 16-bit pattern (uint16_t), fp8 as OCP E4M3FN
+ *   bytes (bias 7, max 448, no infinities) -- the fp8 format of gfx950.
+ * - Paged pools: each pool is n_blocks blocks of SLC_BLOCK_ROWS rows; row j
+ *   of sequence b lives in physical block block_table[b*table_stride + j/64]
+ *   at row j%64.  Table entries < 0 or >= n_blocks mean "absent": reads of
+ *   such rows are skipped, writes to them are dropped.
+ *
+ * Pool byte layouts (per block):
+ *   SWA pool  bf16 [64][576]                                   73728 B
+ *   CMP pool  rows: 64 x (512 e4m3 codes | 64 bf16 rope) = 640 B each,
+ *             then scales: 64 x 8 fp32 (one per 64 nope dims)   43008 B
+ *   KEY pool  codes: 64 x 128 e4m3, then scales: 64 x fp32        8448 B
+ * (the pages store row data first and the block's scales after all its rows;
+ * this library keeps that order with its own row widths).
+ */
+#ifndef SLC_H
+#define SLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLC_BLOCK_ROWS 64
+#define SLC_D_LATENT 576        /* 512 nope + 64 rope */
+#define SLC_D_NOPE 512          /* value width */
+#define SLC_D_ROPE 64
+#define SLC_D_INDEX 128         /* indexer head dim */
+#define SLC_SWA_BLOCK_BYTES 73728
+#define SLC_CMP_ROW_BYTES 640
+#define SLC_CMP_SCALE_OFFSET 40960
+#define SLC_CMP_BLOCK_BYTES 43008
+#define SLC_KEY_SCALE_OFFSET 8192
+#define SLC_KEY_BLOCK_BYTES 8448
+
+#define SLC_MAX_HEADS 128       /* query heads: a multiple of 16, <= 128 */
+#define SLC_MAX_INDEX_HEADS 64  /* indexer heads: a multiple of 16, <= 64 */
+#define SLC_MAX_TOPK 4096
+#define SLC_MAX_WINDOW 1024
+#define SLC_MAX_SLOTS 1048576   /* compressed slots per sequence */
+
+typedef enum {
+    SLC_OK = 0,
+    SLC_ERR_INVALID_ARG = 1,
+    SLC_ERR_WORKSPACE = 2,
+    SLC_ERR_HIP = 3
+} slc_status_t;
+
+/* Layer types keyed by compress ratio ("DeepSeek-V4 attention layer types",
+ * layer-type table): swaonly attends the window only; c4a adds the indexer's
+ * top-k slots; c128a adds a given (precomputed) slot list. */
+typedef enum {
+    SLC_LAYER_SWAONLY = 1,
+    SLC_LAYER_C4A = 4,
+    SLC_LAYER_C128A = 128
+} slc_layer_t;
+
+typedef struct slc_pool {
+    void *base;                  /* device: n_blocks blocks                         */
+    const int32_t *block_table;  /* device: [n_seq][table_stride] physical block ids */
+    int32_t table_stride;        /* entries per sequence (logical blocks)           */
+    int64_t n_blocks;            /* physical blocks in base                         */
+} slc_pool_t;
+
+/* Human-readable name of a status code (static storage). */
+const char *slc_status_string(slc_status_t s);
+
+/* Last argument error of this thread, for diagnostics (static storage). */
+const char *slc_last_error(void);
+
+/*
+ * slc_compress -- "DeepseekV4Attention" (devpress), DeepseekCompressor forward
+ * and the CSA compressor section; "From MLA to CSA + HCA" 5.1, 5.2, 6.3.
+ *
+ * For each sequence b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1, length L,
+ * positions 0..L-1) and each slot j < ceil(L/ratio):
+ *   window T_j = [r*j - (coff-1)*r, r*j + r - 1] clipped to [0, L), coff = 2
+ *            for r = 4 (overlapping 8-token gather), 1 for r = 128;
+ *   pooled[d] = sum_t softmax_t(score[t][d]) * kv[t][d], per channel d;
+ *   y = pooled * gamma / sqrt(mean(pooled^2) + eps) over all 576 dims;
+ *   RoPE (GPT-J interleaved pairs (512+2i, 513+2i)) at position r*j with
+ *            cos = cos_sin[r*j][i], sin = cos_sin[r*j][32+i];
+ *   nope dims: 8 blocks of 64 -> scale = smallest 2^e with amax <= 448*2^e
+ *            (1 if amax = 0), code = e4m3(y/scale) round-to-nearest-even;
+ *   rope dims: bf16 round-to-nearest-even;
+ *   stored at slot j of sequence b in cmp_pool.
+ * A trailing partial slot (L % r != 0) is pooled over the tokens present.
+ *
+ *   ratio        4 or 128
+ *   n_seq        sequences (>= 1)
+ *   cu_seqlens   device int32 [n_seq+1], non-decreasing, cu_seqlens[0] = 0
+ *   max_seqlen   host bound on every L (sizes the grid); longer sequences
+ *                are truncated to max_seqlen tokens
+ *   kv           device bf16 [T][576];  score  device fp32 [T][576]
+ *   gamma        device fp32 [576];     eps >= 0
+ *   cos_sin      device fp32 [max_pos][64]; slots whose anchor r*j >= max_pos
+ *                are not written
+ *   cmp_pool     destination (CMP layout)
+ *   prequant     nullable device fp32 [cmp_pool.n_blocks*64][576]: the row
+ *                after RMSNorm and RoPE, at the slot's physical row (debug)
+ */
+slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int max_seqlen,
+                          const uint16_t *kv, const float *score, const float *gamma, float eps,
+                          const float *cos_sin, int max_pos, slc_pool_t cmp_pool,
+                          float *prequant, void *stream);
+
+/*
+ * slc_index_scores -- "DeepseekV4Attention" (devpress), Indexer section:
+ *   I[t][s] = sum_j w[t][j] * ReLU(q_scale[t][j] * k_scale[s] * (q[t][j] . k[s]))
+ * over the fp8 index query heads j < h_idx, for the slots s visible to query
+ * t: s < n_vis(t) = min(n_slots[q_seq[t]], (q_pos[t]+1) / ratio)
+ * ("From MLA to CSA + HCA" 5.1: position i sees slot j iff i >= r*j + r - 1).
+ * fp8 products accumulate in fp32.
+ *
+ *   n_q          queries;  h_idx  indexer heads (multiple of 16, <= 64)
+ *   q_fp8        device e4m3 [n_q][h_idx][128]
+ *   q_scale, w   device fp32 [n_q][h_idx]
+ *   q_seq, q_pos device int32 [n_q] (sequence and position of each query)
+ *   ratio        4 (the indexer exists for c4a layers)
+ *   key_pool     KEY layout, one table row per sequence
+ *   n_slots      device int32 [n_seq] compressed slots per sequence
+ *   max_slots    host bound on every n_vis (row stride of scores)
+ *   scores       device fp32 [n_q][max_slots]; entries s < n_vis(t) written
+ */
+slc_status_t slc_index_scores(int n_q, int h_idx, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const int32_t *q_seq, const int32_t *q_pos,
+                              int ratio, slc_pool_t key_pool, const int32_t *n_slots,
+                              int max_slots, float *scores, void *stream);
+
+/*
+ * slc_topk_select -- "DeepSeek-V4 attention layer types", Indexer / C4A
+ * branch (global top-k per query).  For each query t, the min(k, n_vis(t))
+ * slots with the largest scores (ties to the lower slot index; -0.0 equals
+ * +0.0), written to topk_idx[t][0 .. len) in increasing slot order, the rest
+ * of the row set to -1; topk_len[t] = min(k, n_vis(t)).
+ *
+ *   scores       device fp32 [n_q][max_slots] (as written by slc_index_scores)
+ *   k            1 .. SLC_MAX_TOPK
+ *   topk_idx     device int32 [n_q][k];  topk_len  device int32 [n_q]
+ */
+slc_status_t slc_topk_select(int n_q, int k, const float *scores, int max_slots,
+                             const int32_t *q_seq, const int32_t *q_pos, int ratio,
+                             const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
+                             void *stream);
+
+/* Bytes of workspace slc_index_topk needs (scores of every visible slot). */
+size_t slc_index_topk_workspace_size(int n_q, int max_slots);
+
+/* slc_index_scores followed by slc_topk_select, scores kept in `workspace`
+ * (device, >= slc_index_topk_workspace_size bytes, 256-byte aligned). */
+slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
+                            const float *q_scale, const float *w, const int32_t *q_seq,
+                            const int32_t *q_pos, int ratio, slc_pool_t key_pool,
+                            const int32_t *n_slots, int max_slots, int32_t *topk_idx,
+                            int32_t *topk_len, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * slc_sparse_mla_decode / slc_sparse_mla_prefill -- "DeepseekV4Attention"
+ * (devpress), forward_mqa with _forward_decode (flash_mla_with_kvcache with
+ * SWA and compressed indices) and _forward_prefill (flash_mla_sparse_fwd over
+ * top-k combined with SWA indices); "From MLA to CSA + HCA" Ch.2 (absorbed
+ * MQA: H query heads against one shared 576-wide latent head).
+ *
+ * For query t (sequence b = q_seq[t], position p = q_pos[t]) the attended
+ * list is, without deduplication,
+ *   SWA: positions max(0, p-window+1) .. p, rows of swa_pool;
+ *   CMP: cmp_idx[t][0..k) entries with 0 <= idx < n_slots[b] (others
+ *        skipped), rows of cmp_pool dequantised as code * scale (exact in bf16)
+ *        ++ the bf16 rope dims   [c4a, c128a only].
+ *   logit_i = sm_scale * q[t][h] . K_i (576 dims)
+ *   out[t][h] = sum_i softmax(logit)_i * K_i[0:512]  (bf16, round to nearest)
+ *   lse[t][h] = ln sum_i exp(logit_i)  (fp32; -inf and out = 0 if the list is empty)
+ *
+ *   layer_type   SLC_LAYER_SWAONLY (cmp_pool, cmp_idx ignored; k must be 0),
+ *                SLC_LAYER_C4A or SLC_LAYER_C128A (cmp_pool, cmp_idx required)
+ *   n_q, n_heads queries and query heads (multiple of 16, <= 128)
+ *   q            device bf16 [n_q][n_heads][576]
+ *   q_seq, q_pos device int32 [n_q]
+ *   window       sliding-window length, 0 .. SLC_MAX_WINDOW
+ *   cmp_idx      device int32 [n_q][k] logical slot ids (-1 = none)
+ *   n_slots      device int32 [n_seq]
+ *   out          device bf16 [n_q][n_heads][512];  lse nullable fp32 [n_q][n_heads]
+ *   workspace    device, >= the matching *_workspace_size bytes, 256-B aligned
+ * Decode splits each query's list across workgroups and merges the partial
+ * softmax states; prefill gives each query token its own workgroup.  Both
+ * compute the same function.
+ */
+size_t slc_sparse_mla_decode_workspace_size(int n_q, int n_heads, int window, int k);
+slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                   const int32_t *q_seq, const int32_t *q_pos, int window,
+                                   slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                                   const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                                   float sm_scale, uint16_t *out, float *lse, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
+size_t slc_sparse_mla_prefill_workspace_size(int n_q, int n_heads, int window, int k);
+slc_status_t slc_sparse_mla_prefill(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                    const int32_t *q_seq, const int32_t *q_pos, int window,
+                                    slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                                    const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                                    float sm_scale, uint16_t *out, float *lse, void *workspace,
+                                    size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLC_H */

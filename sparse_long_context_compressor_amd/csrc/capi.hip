@@ -1,0 +1,262 @@
+// capi.hip -- the extern "C" boundary declared in include/slc.h: host-side
+// argument validation, workspace arithmetic and kernel launches.  Nothing
+// here allocates, synchronises or reads device memory.
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "slc_internal.hpp"
+
+using namespace slc;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+slc_status_t fail(const char *msg) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+    return SLC_ERR_INVALID_ARG;
+}
+
+slc_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return SLC_OK;
+    std::snprintf(g_last_error, sizeof g_last_error, "HIP: %s", hipGetErrorString(e));
+    return SLC_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+slc_status_t check_pool(const slc_pool_t &p, const char *name) {
+    const char *why = nullptr;
+    if (!p.base || !p.block_table) why = "base and block_table are required";
+    else if (!aligned(p.base, 16)) why = "base must be 16-byte aligned";
+    else if (p.table_stride < 1 || p.n_blocks < 0 || p.n_blocks > (int64_t(1) << 40))
+        why = "table_stride must be >= 1 and n_blocks in [0, 2^40]";
+    if (!why) return SLC_OK;
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", name, why);
+    return SLC_ERR_INVALID_ARG;
+}
+
+bool heads_ok(int h, int max_h) { return h >= 16 && h <= max_h && h % 16 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *slc_status_string(slc_status_t s) {
+    switch (s) {
+    case SLC_OK: return "ok";
+    case SLC_ERR_INVALID_ARG: return "invalid argument";
+    case SLC_ERR_WORKSPACE: return "workspace too small";
+    case SLC_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+const char *slc_last_error(void) { return g_last_error; }
+
+slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int max_seqlen,
+                          const uint16_t *kv, const float *score, const float *gamma, float eps,
+                          const float *cos_sin, int max_pos, slc_pool_t cmp_pool,
+                          float *prequant, void *stream) {
+    if (ratio != 4 && ratio != 128) return fail("compress: ratio must be 4 or 128");
+    if (n_seq < 1 || n_seq > 65535) return fail("compress: n_seq must be in [1, 65535]");
+    if (max_seqlen < 0 || max_pos < 0) return fail("compress: max_seqlen and max_pos must be >= 0");
+    if (!cu_seqlens || !kv || !score || !gamma || !cos_sin)
+        return fail("compress: cu_seqlens, kv, score, gamma and cos_sin are required");
+    if (!aligned(kv, 16) || !aligned(score, 16) || !aligned(gamma, 16) ||
+        (prequant && !aligned(prequant, 16)))
+        return fail("compress: kv, score, gamma and prequant must be 16-byte aligned");
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail("compress: eps must be finite and >= 0");
+    slc_status_t st = check_pool(cmp_pool, "compress: cmp_pool");
+    if (st != SLC_OK) return st;
+    if (max_seqlen == 0) return SLC_OK;
+    CompressArgs a{ratio, max_seqlen, cu_seqlens, kv, score, gamma, eps, cos_sin, max_pos,
+                   cmp_pool, prequant};
+    return hip_status(launch_compress(a, n_seq, static_cast<hipStream_t>(stream)));
+}
+
+static slc_status_t check_index_common(int n_q, const int32_t *q_seq, const int32_t *q_pos,
+                                       int ratio, const int32_t *n_slots, int max_slots) {
+    if (n_q < 0) return fail("index: n_q must be >= 0");
+    if (ratio != 4 && ratio != 128) return fail("index: ratio must be 4 or 128");
+    if (max_slots < 1 || max_slots > SLC_MAX_SLOTS)
+        return fail("index: max_slots must be in [1, SLC_MAX_SLOTS]");
+    if (n_q > 0 && (!q_seq || !q_pos || !n_slots))
+        return fail("index: q_seq, q_pos and n_slots are required");
+    return SLC_OK;
+}
+
+slc_status_t slc_index_scores(int n_q, int h_idx, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const int32_t *q_seq, const int32_t *q_pos,
+                              int ratio, slc_pool_t key_pool, const int32_t *n_slots,
+                              int max_slots, float *scores, void *stream) {
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
+    if (st != SLC_OK) return st;
+    if (!heads_ok(h_idx, SLC_MAX_INDEX_HEADS))
+        return fail("index_scores: h_idx must be a multiple of 16 in [16, 64]");
+    if (n_q == 0) return SLC_OK;
+    if (!q_fp8 || !q_scale || !w || !scores)
+        return fail("index_scores: q_fp8, q_scale, w and scores are required");
+    if (!aligned(q_fp8, 16)) return fail("index_scores: q_fp8 must be 16-byte aligned");
+    st = check_pool(key_pool, "index_scores: key_pool");
+    if (st != SLC_OK) return st;
+    IndexArgs a{n_q, h_idx, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, n_slots, max_slots,
+                scores};
+    return hip_status(launch_index_scores(a, static_cast<hipStream_t>(stream)));
+}
+
+slc_status_t slc_topk_select(int n_q, int k, const float *scores, int max_slots,
+                             const int32_t *q_seq, const int32_t *q_pos, int ratio,
+                             const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
+                             void *stream) {
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
+    if (st != SLC_OK) return st;
+    if (k < 1 || k > SLC_MAX_TOPK) return fail("topk_select: k must be in [1, SLC_MAX_TOPK]");
+    if (n_q == 0) return SLC_OK;
+    if (!scores || !topk_idx || !topk_len)
+        return fail("topk_select: scores, topk_idx and topk_len are required");
+    TopkArgs a{n_q, k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx, topk_len};
+    return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t slc_index_topk_workspace_size(int n_q, int max_slots) {
+    if (n_q <= 0 || max_slots <= 0) return 0;
+    return (static_cast<size_t>(n_q) * static_cast<size_t>(max_slots) * sizeof(float) + 255) &
+           ~static_cast<size_t>(255);
+}
+
+slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
+                            const float *q_scale, const float *w, const int32_t *q_seq,
+                            const int32_t *q_pos, int ratio, slc_pool_t key_pool,
+                            const int32_t *n_slots, int max_slots, int32_t *topk_idx,
+                            int32_t *topk_len, void *workspace, size_t ws_bytes, void *stream) {
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
+    if (st != SLC_OK) return st;
+    if (k < 1 || k > SLC_MAX_TOPK) return fail("index_topk: k must be in [1, SLC_MAX_TOPK]");
+    if (!heads_ok(h_idx, SLC_MAX_INDEX_HEADS))
+        return fail("index_topk: h_idx must be a multiple of 16 in [16, 64]");
+    if (n_q == 0) return SLC_OK;
+    size_t need = slc_index_topk_workspace_size(n_q, max_slots);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 256)) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "index_topk: workspace needs %zu bytes, 256-byte aligned", need);
+        return SLC_ERR_WORKSPACE;
+    }
+    float *scores = static_cast<float *>(workspace);
+    st = slc_index_scores(n_q, h_idx, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, n_slots,
+                          max_slots, scores, stream);
+    if (st != SLC_OK) return st;
+    return slc_topk_select(n_q, k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx,
+                           topk_len, stream);
+}
+
+static size_t attn_ws(int n_q, int n_heads, int window, int k, bool decode) {
+    if (n_q <= 0 || n_heads <= 0) return 0;
+    int splits, cps;
+    attention_plan(n_q, window, k, decode, &splits, &cps);
+    if (splits <= 1) return 0;
+    size_t per = static_cast<size_t>(n_q) * splits * n_heads;
+    size_t bytes = per * kDN * sizeof(float) + per * 2 * sizeof(float) + 256;
+    return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+size_t slc_sparse_mla_decode_workspace_size(int n_q, int n_heads, int window, int k) {
+    return attn_ws(n_q, n_heads, window, k, true);
+}
+
+size_t slc_sparse_mla_prefill_workspace_size(int n_q, int n_heads, int window, int k) {
+    return attn_ws(n_q, n_heads, window, k, false);
+}
+
+static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads,
+                               const uint16_t *q, const int32_t *q_seq, const int32_t *q_pos,
+                               int window, slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                               const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                               float sm_scale, uint16_t *out, float *lse, void *workspace,
+                               size_t ws_bytes, void *stream) {
+    if (layer_type != SLC_LAYER_SWAONLY && layer_type != SLC_LAYER_C4A &&
+        layer_type != SLC_LAYER_C128A)
+        return fail("sparse_mla: layer_type must be SWAONLY (1), C4A (4) or C128A (128)");
+    if (n_q < 0) return fail("sparse_mla: n_q must be >= 0");
+    if (!heads_ok(n_heads, SLC_MAX_HEADS))
+        return fail("sparse_mla: n_heads must be a multiple of 16 in [16, 128]");
+    if (window < 0 || window > SLC_MAX_WINDOW)
+        return fail("sparse_mla: window must be in [0, SLC_MAX_WINDOW]");
+    if (k < 0 || k > SLC_MAX_TOPK) return fail("sparse_mla: k must be in [0, SLC_MAX_TOPK]");
+    if (layer_type == SLC_LAYER_SWAONLY && k != 0)
+        return fail("sparse_mla: a SWAONLY layer takes no compressed list (k must be 0)");
+    if (!std::isfinite(sm_scale)) return fail("sparse_mla: sm_scale must be finite");
+    if (n_q == 0) return SLC_OK;
+    if (!q || !q_seq || !q_pos || !out) return fail("sparse_mla: q, q_seq, q_pos and out are required");
+    if (!aligned(q, 16) || !aligned(out, 8))
+        return fail("sparse_mla: q must be 16-byte and out 8-byte aligned");
+    slc_status_t st;
+    if (window > 0) {
+        st = check_pool(swa_pool, "sparse_mla: swa_pool");
+        if (st != SLC_OK) return st;
+    }
+    if (layer_type != SLC_LAYER_SWAONLY) {
+        st = check_pool(cmp_pool, "sparse_mla: cmp_pool");
+        if (st != SLC_OK) return st;
+        if (k > 0 && (!cmp_idx || !n_slots))
+            return fail("sparse_mla: cmp_idx and n_slots are required for C4A / C128A");
+    }
+    int kk = layer_type == SLC_LAYER_SWAONLY ? 0 : k;
+    int splits, cps;
+    attention_plan(n_q, window, kk, decode, &splits, &cps);
+    size_t need = attn_ws(n_q, n_heads, window, kk, decode);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256))) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "sparse_mla: workspace needs %zu bytes, 256-byte aligned", need);
+        return SLC_ERR_WORKSPACE;
+    }
+    AttnArgs a{};
+    a.layer_type = layer_type;
+    a.n_q = n_q;
+    a.n_heads = n_heads;
+    a.q = q;
+    a.q_seq = q_seq;
+    a.q_pos = q_pos;
+    a.window = window;
+    a.swa = swa_pool;
+    a.cmp = cmp_pool;
+    a.cmp_idx = cmp_idx;
+    a.k = kk;
+    a.n_slots = n_slots;
+    a.sm_scale_log2 = sm_scale * kLog2e;
+    a.out = out;
+    a.lse = lse;
+    a.n_splits = splits;
+    a.chunks_per_split = cps;
+    if (splits > 1) {
+        size_t per = static_cast<size_t>(n_q) * splits * n_heads;
+        a.part_o = static_cast<float *>(workspace);
+        a.part_ml = a.part_o + per * kDN;
+    }
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                   const int32_t *q_seq, const int32_t *q_pos, int window,
+                                   slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                                   const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                                   float sm_scale, uint16_t *out, float *lse, void *workspace,
+                                   size_t ws_bytes, void *stream) {
+    return sparse_mla(true, layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool, cmp_pool,
+                      cmp_idx, k, n_slots, sm_scale, out, lse, workspace, ws_bytes, stream);
+}
+
+slc_status_t slc_sparse_mla_prefill(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                    const int32_t *q_seq, const int32_t *q_pos, int window,
+                                    slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                                    const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                                    float sm_scale, uint16_t *out, float *lse, void *workspace,
+                                    size_t ws_bytes, void *stream) {
+    return sparse_mla(false, layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool,
+                      cmp_pool, cmp_idx, k, n_slots, sm_scale, out, lse, workspace, ws_bytes,
+                      stream);
+}
+
+}  // extern "C"

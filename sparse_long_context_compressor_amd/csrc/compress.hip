@@ -1,0 +1,225 @@
+// compress.hip -- fused compressor kernel: window pooling -> RMSNorm -> RoPE ->
+// FP8 quantisation -> paged store, one slot per wave (r = 4) or per workgroup
+// (r = 128).
+//
+// Method: "DeepseekV4Attention" (devpress, AMD), DeepseekCompressor forward
+// and the CSA/HCA compressor sections (softmax-gated pooling of the window's
+// kv by per-channel scores; RMSNorm; GPT-J RoPE on the last 64 dims at
+// position (pos // r) * r; fp8 nope + bf16 rope with one scale per 64 dims);
+// "From MLA to CSA + HCA" 5.1 (slot j of r = 4 covers [4j-4, 4j+3]), 5.2
+// (r = 128 covers [128j, 128j+127]), 6.2 (one fused kernel: intermediates stay
+// in registers), 6.3 (slot j -> block j / 64, row j % 64).
+//
+// Layout on the wave: lane l owns nope channels [8l, 8l+8) and rope channel
+// 512 + l.  A quantisation block (64 channels) is then 8 adjacent lanes, the
+// RoPE pair (512+2i, 513+2i) is the lane pair (2i, 2i+1), and every token row
+// is read with fully coalesced 16/32-byte loads.
+
+#include "slc_internal.hpp"
+
+namespace slc {
+
+namespace {
+
+struct PoolState {
+    float m[9], l[9], acc[9];   // running max, sum of exp, weighted kv (8 nope + 1 rope)
+};
+
+__device__ __forceinline__ void state_init(PoolState &s) {
+#pragma unroll
+    for (int i = 0; i < 9; i++) {
+        s.m[i] = -INFINITY;
+        s.l[i] = 0.f;
+        s.acc[i] = 0.f;
+    }
+}
+
+__device__ __forceinline__ void state_add(PoolState &s, int i, float sc, float x) {
+    float mn = fmaxf(s.m[i], sc);
+    float a = __expf(s.m[i] - mn);   // 0 when m was -inf
+    float e = __expf(sc - mn);
+    s.l[i] = s.l[i] * a + e;
+    s.acc[i] = s.acc[i] * a + e * x;
+    s.m[i] = mn;
+}
+
+// Fold token t's kv/score row into the lane's 9 channels.
+__device__ __forceinline__ void pool_token(PoolState &s, const uint16_t *kv, const float *score,
+                                           int64_t t, int lane) {
+    const uint16_t *kr = kv + t * kD;
+    const float *sr = score + t * kD;
+    u32x4 kw = *reinterpret_cast<const u32x4 *>(kr + 8 * lane);
+    f32x4 s0 = *reinterpret_cast<const f32x4 *>(sr + 8 * lane);
+    f32x4 s1 = *reinterpret_cast<const f32x4 *>(sr + 8 * lane + 4);
+    uint16_t kr_rope = kr[kDN + lane];
+    float s_rope = sr[kDN + lane];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        state_add(s, 2 * i, i < 2 ? s0[2 * i] : s1[2 * i - 4], __uint_as_float(kw[i] << 16));
+        state_add(s, 2 * i + 1, i < 2 ? s0[2 * i + 1] : s1[2 * i - 3],
+                  __uint_as_float(kw[i] & 0xffff0000u));
+    }
+    state_add(s, 8, s_rope, bf16_to_f32(kr_rope));
+}
+
+// Smallest e with amax <= 448 * 2^e (exact comparisons); 0 for amax == 0.
+__device__ __forceinline__ int pow2_exponent(float amax) {
+    if (!(amax > 0.f)) return 0;
+    int ex;
+    frexpf(amax, &ex);            // amax = f * 2^ex, f in [0.5, 1); 448 = 0.875 * 2^9
+    int e = ex - 9;
+    while (amax > ldexpf(448.f, e)) e++;
+    while (amax <= ldexpf(448.f, e - 1)) e--;
+    return e;
+}
+
+// RMSNorm, RoPE, quantise and store one pooled slot held by one wave.
+__device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, int seq, int slot,
+                                            int ratio, const float *gamma, float eps,
+                                            const float *cos_sin, int max_pos, slc_pool_t pool,
+                                            float *prequant) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 9; i++) ss += pooled[i] * pooled[i];
+    ss = wave_sum(ss);
+    float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+
+    float y[9];
+    f32x4 g0 = *reinterpret_cast<const f32x4 *>(gamma + 8 * lane);
+    f32x4 g1 = *reinterpret_cast<const f32x4 *>(gamma + 8 * lane + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        y[i] = pooled[i] * inv * g0[i];
+        y[4 + i] = pooled[4 + i] * inv * g1[i];
+    }
+    y[8] = pooled[8] * inv * gamma[kDN + lane];
+
+    // RoPE on the rope channel: pair (512+2i, 513+2i) = lanes (2i, 2i+1)
+    int pos = ratio * slot;
+    if (pos >= max_pos) return;   // anchor outside the table: slot not written
+    float other = __shfl_xor(y[8], 1, 64);
+    int pi = lane >> 1;
+    float c = cos_sin[static_cast<int64_t>(pos) * kDR + pi];
+    float s = cos_sin[static_cast<int64_t>(pos) * kDR + kDR / 2 + pi];
+    y[8] = (lane & 1) ? (other * s + y[8] * c) : (y[8] * c - other * s);
+
+    int64_t row = pool_row(pool, seq, slot);
+    if (row < 0) return;
+    if (prequant) {
+        float *pq = prequant + row * kD;
+        *reinterpret_cast<f32x4 *>(pq + 8 * lane) = f32x4{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4 *>(pq + 8 * lane + 4) = f32x4{y[4], y[5], y[6], y[7]};
+        pq[kDN + lane] = y[8];
+    }
+
+    // per-64 block pow2 scale: block b = lanes 8b .. 8b+7
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    int e = pow2_exponent(amax);
+    float inv_scale = ldexpf(1.f, -e);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        w0 |= f32_to_e4m3(y[i] * inv_scale) << (8 * i);
+        w1 |= f32_to_e4m3(y[4 + i] * inv_scale) << (8 * i);
+    }
+    uint8_t *dst = cmp_row_ptr(pool, row);
+    *reinterpret_cast<u32x2 *>(dst + 8 * lane) = u32x2{w0, w1};
+    reinterpret_cast<uint16_t *>(dst + kDN)[lane] = f32_to_bf16(y[8]);
+    if ((lane & 7) == 0) cmp_scale_ptr(pool, row)[lane >> 3] = ldexpf(1.f, e);
+}
+
+}  // namespace
+
+// r = 4: one wave per slot, 4 slots per workgroup; window = [4j-4, 4j+3] ∩ [0, L).
+__global__ __launch_bounds__(256) void compress_r4_kernel(CompressArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int seq = blockIdx.y;
+    const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int64_t t0 = a.cu_seqlens[seq];
+    int L = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+    L = L < a.max_seqlen ? L : a.max_seqlen;
+    const int n_slots = (L + 3) / 4;
+    if (L <= 0 || slot >= n_slots) return;
+
+    int lo = 4 * slot - 4, hi = 4 * slot + 3;
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > L - 1 ? L - 1 : hi;
+    PoolState st;
+    state_init(st);
+    for (int t = lo; t <= hi; t++) pool_token(st, a.kv, a.score, t0 + t, lane);
+    float pooled[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) pooled[i] = st.acc[i] / st.l[i];
+    finish_slot(pooled, lane, seq, slot, 4, a.gamma, a.eps, a.cos_sin, a.max_pos, a.pool,
+                a.prequant);
+}
+
+// r = 128: one workgroup per slot; 4 waves pool 32 tokens each, wave 0 merges.
+__global__ __launch_bounds__(256) void compress_r128_kernel(CompressArgs a) {
+    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int seq = blockIdx.y;
+    const int slot = blockIdx.x;
+    int64_t t0 = a.cu_seqlens[seq];
+    int L = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+    L = L < a.max_seqlen ? L : a.max_seqlen;
+    const int n_slots = (L + 127) / 128;
+    if (L <= 0 || slot >= n_slots) return;
+
+    int lo = 128 * slot + 32 * w, hi = lo + 31;
+    hi = hi > L - 1 ? L - 1 : hi;
+    PoolState st;
+    state_init(st);
+    for (int t = lo; t <= hi; t++) pool_token(st, a.kv, a.score, t0 + t, lane);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        part_m[w][8 * lane + i] = st.m[i];
+        part_l[w][8 * lane + i] = st.l[i];
+        part_acc[w][8 * lane + i] = st.acc[i];
+    }
+    part_m[w][kDN + lane] = st.m[8];
+    part_l[w][kDN + lane] = st.l[8];
+    part_acc[w][kDN + lane] = st.acc[8];
+    __syncthreads();
+    if (w != 0) return;
+
+    float pooled[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) {
+        int d = i < 8 ? 8 * lane + i : kDN + lane;
+        float m = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) m = fmaxf(m, part_m[ww][d]);
+        float l = 0.f, acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            float sc = part_l[ww][d] > 0.f ? __expf(part_m[ww][d] - m) : 0.f;
+            l += part_l[ww][d] * sc;
+            acc += part_acc[ww][d] * sc;
+        }
+        pooled[i] = acc / l;
+    }
+    finish_slot(pooled, lane, seq, slot, 128, a.gamma, a.eps, a.cos_sin, a.max_pos, a.pool,
+                a.prequant);
+}
+
+hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream) {
+    if (a.ratio == 4) {
+        int max_slots = (a.max_seqlen + 3) / 4;
+        dim3 grid((max_slots + 3) / 4, n_seq);
+        hipLaunchKernelGGL(compress_r4_kernel, grid, dim3(256), 0, stream, a);
+    } else {
+        int max_slots = (a.max_seqlen + 127) / 128;
+        dim3 grid(max_slots, n_seq);
+        hipLaunchKernelGGL(compress_r128_kernel, grid, dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace slc

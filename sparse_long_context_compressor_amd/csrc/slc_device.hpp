@@ -1,0 +1,134 @@
+// slc_device.hpp -- device-side primitives shared by the gfx950 kernels:
+// bf16 / OCP-e4m3 conversions, wave64 reductions, MFMA operand types and the
+// paged-pool address arithmetic of the C ABI (slc.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "slc.h"
+
+namespace slc {
+
+constexpr int kD = SLC_D_LATENT;     // 576
+constexpr int kDN = SLC_D_NOPE;      // 512
+constexpr int kDR = SLC_D_ROPE;      // 64
+constexpr int kDI = SLC_D_INDEX;     // 128
+constexpr int kBR = SLC_BLOCK_ROWS;  // 64
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Two fp32 values whose low 16 mantissa bits are zero (exact bf16 values)
+// packed into one dword of bf16: lo in bits 0..15, hi in 16..31.
+__device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// --------------------------------------------------------------- fp8 e4m3
+// gfx950 converts OCP E4M3FN in hardware (the fp8 format of this ABI).
+// Four e4m3 bytes (one dword) -> four fp32, exactly.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float &a, float &b, float &c, float &d) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    a = lo[0];
+    b = lo[1];
+    c = hi[0];
+    d = hi[1];
+}
+
+// Four e4m3 bytes -> four bf16 (exact: e4m3 has 4 significant bits) in two
+// dwords, optionally multiplied by a power-of-two scale (still exact unless
+// the product leaves bf16's exponent range).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w, float scale) {
+    float a, b, c, d;
+    e4m3x4_to_f32(w, a, b, c, d);
+    u32x2 r;
+    r[0] = pack_exact_bf16(a * scale, b * scale);
+    r[1] = pack_exact_bf16(c * scale, d * scale);
+    return r;
+}
+
+// fp32 -> e4m3 byte, round to nearest even (hardware conversion; |x| <= 448
+// by construction of the caller's scale, so saturation never triggers).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false)) & 0xffu;
+}
+
+// ---------------------------------------------------------- wave64 helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// -------------------------------------------------------------- pool math
+// Physical row of logical row `row` of sequence `seq`, or -1 if the table
+// entry is absent / out of range.  Never dereferences out of bounds.
+__device__ __forceinline__ int64_t pool_row(const slc_pool_t &p, int seq, int64_t row) {
+    if (row < 0) return -1;
+    int64_t lb = row / kBR;
+    if (lb >= p.table_stride) return -1;
+    int32_t pb = p.block_table[static_cast<int64_t>(seq) * p.table_stride + lb];
+    if (pb < 0 || pb >= p.n_blocks) return -1;
+    return static_cast<int64_t>(pb) * kBR + (row % kBR);
+}
+
+// Byte addresses inside the three pool layouts (physical row r = block*64 + i).
+__device__ __forceinline__ const uint16_t *swa_row_ptr(const slc_pool_t &p, int64_t r) {
+    return reinterpret_cast<const uint16_t *>(p.base) + r * kD;
+}
+__device__ __forceinline__ uint8_t *cmp_row_ptr(const slc_pool_t &p, int64_t r) {
+    return reinterpret_cast<uint8_t *>(p.base) + (r / kBR) * SLC_CMP_BLOCK_BYTES +
+           (r % kBR) * SLC_CMP_ROW_BYTES;
+}
+__device__ __forceinline__ float *cmp_scale_ptr(const slc_pool_t &p, int64_t r) {
+    return reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(p.base) +
+                                     (r / kBR) * SLC_CMP_BLOCK_BYTES + SLC_CMP_SCALE_OFFSET) +
+           (r % kBR) * (kDN / 64);
+}
+__device__ __forceinline__ const uint8_t *key_code_ptr(const slc_pool_t &p, int64_t r) {
+    return reinterpret_cast<const uint8_t *>(p.base) + (r / kBR) * SLC_KEY_BLOCK_BYTES +
+           (r % kBR) * kDI;
+}
+__device__ __forceinline__ const float *key_scale_ptr(const slc_pool_t &p, int64_t r) {
+    return reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(p.base) +
+                                           (r / kBR) * SLC_KEY_BLOCK_BYTES +
+                                           SLC_KEY_SCALE_OFFSET) +
+           (r % kBR);
+}
+
+// Compressed slots visible to a query at position p ("From MLA to CSA + HCA",
+// 5.1: position i sees slot j iff i >= r*j + r - 1), capped by the slots stored.
+__device__ __forceinline__ int visible_slots(int p, int ratio, int n_slots) {
+    int v = (p + 1) / ratio;
+    v = v < n_slots ? v : n_slots;
+    return v < 0 ? 0 : v;
+}
+
+}  // namespace slc

@@ -1,0 +1,83 @@
+// slc_internal.hpp -- kernel argument blocks and launch entry points shared
+// between the C-ABI layer (capi.hip) and the kernel translation units.
+#pragma once
+
+#include "slc_device.hpp"
+
+namespace slc {
+
+struct CompressArgs {
+    int ratio;
+    int max_seqlen;
+    const int32_t *cu_seqlens;
+    const uint16_t *kv;
+    const float *score;
+    const float *gamma;
+    float eps;
+    const float *cos_sin;
+    int max_pos;
+    slc_pool_t pool;
+    float *prequant;
+};
+
+struct IndexArgs {
+    int n_q;
+    int h_idx;
+    const uint8_t *q;
+    const float *q_scale;
+    const float *w;
+    const int32_t *q_seq;
+    const int32_t *q_pos;
+    int ratio;
+    slc_pool_t keys;
+    const int32_t *n_slots;
+    int max_slots;
+    float *scores;
+};
+
+struct TopkArgs {
+    int n_q;
+    int k;
+    const float *scores;
+    int max_slots;
+    const int32_t *q_seq;
+    const int32_t *q_pos;
+    int ratio;
+    const int32_t *n_slots;
+    int32_t *idx;
+    int32_t *len;
+};
+
+struct AttnArgs {
+    int layer_type;
+    int n_q;
+    int n_heads;
+    const uint16_t *q;
+    const int32_t *q_seq;
+    const int32_t *q_pos;
+    int window;
+    slc_pool_t swa;
+    slc_pool_t cmp;
+    const int32_t *cmp_idx;
+    int k;
+    const int32_t *n_slots;
+    float sm_scale_log2;    // sm_scale * log2(e)
+    uint16_t *out;
+    float *lse;
+    int n_splits;           // workgroups per query along the attended list
+    int chunks_per_split;   // 32-entry chunks each split covers
+    float *part_o;          // [n_q][n_splits][H][512] (n_splits > 1)
+    float *part_ml;         // [n_q][n_splits][H][2]
+};
+
+constexpr int kAttnChunk = 32;
+
+hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream);
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
+
+// split plan for decode (host arithmetic only)
+void attention_plan(int n_q, int window, int k, bool decode, int *n_splits, int *chunks_per_split);
+
+}  // namespace slc

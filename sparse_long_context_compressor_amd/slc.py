@@ -1,0 +1,203 @@
+"""Thin Python binding of libslc.so (argument marshalling only).
+
+Every function here has the name of the C entry point without its ``slc_``
+prefix and forwards torch tensors' device pointers plus torch's current HIP
+stream.  All computation happens in the library's HIP kernels; there is no
+fallback: if libslc.so is missing, importing functions raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+from . import pools as P
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libslc.so")
+
+LAYER_SWAONLY, LAYER_C4A, LAYER_C128A = 1, 4, 128
+SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
+
+EXPORTED = [
+    "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
+    "slc_topk_select", "slc_index_topk_workspace_size", "slc_index_topk",
+    "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
+    "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
+]
+
+
+class Pool(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("block_table", C.c_void_p),
+                ("table_stride", C.c_int32), ("n_blocks", C.c_int64)]
+
+
+class SlcError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"slc status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libslc.so (build it with sparse_long_context_compressor_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python sparse_long_context_compressor_amd/build.py`")
+        L = C.CDLL(LIB_PATH)
+        i32, sz, vp, f32 = C.c_int, C.c_size_t, C.c_void_p, C.c_float
+        pool = Pool
+        L.slc_status_string.restype = C.c_char_p
+        L.slc_status_string.argtypes = [i32]
+        L.slc_last_error.restype = C.c_char_p
+        L.slc_last_error.argtypes = []
+        L.slc_compress.restype = i32
+        L.slc_compress.argtypes = [i32, i32, vp, i32, vp, vp, vp, f32, vp, i32, pool, vp, vp]
+        L.slc_index_scores.restype = i32
+        L.slc_index_scores.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, pool, vp, i32, vp, vp]
+        L.slc_topk_select.restype = i32
+        L.slc_topk_select.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp]
+        L.slc_index_topk_workspace_size.restype = sz
+        L.slc_index_topk_workspace_size.argtypes = [i32, i32]
+        L.slc_index_topk.restype = i32
+        L.slc_index_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, pool, vp, i32, vp,
+                                     vp, vp, sz, vp]
+        for name in ("slc_sparse_mla_decode", "slc_sparse_mla_prefill"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, i32, i32, vp, vp, vp, i32, pool, pool, vp, i32, vp, f32, vp, vp,
+                          vp, sz, vp]
+            g = getattr(L, name + "_workspace_size")
+            g.restype = sz
+            g.argtypes = [i32, i32, i32, i32]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != SLC_OK:
+        L = lib()
+        raise SlcError(status, L.slc_last_error().decode() or L.slc_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, dev):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name}: expected device {dev}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def pool(base: Optional[torch.Tensor], table: Optional[torch.Tensor]) -> Pool:
+    """slc_pool_t over a pool tensor [n_blocks, ...] and its block table [n_seq, stride]."""
+    if base is None:
+        return Pool(None, None, 0, 0)
+    if table.dtype != torch.int32 or not table.is_contiguous():
+        raise TypeError("block table must be contiguous int32")
+    return Pool(base.data_ptr(), table.data_ptr(), int(table.shape[1]), int(base.shape[0]))
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dtype == torch.int16 else t.view(torch.int16)
+
+
+# ----------------------------------------------------------------- compress
+def compress(ratio: int, cu_seqlens: torch.Tensor, max_seqlen: int, kv: torch.Tensor,
+             score: torch.Tensor, gamma: torch.Tensor, eps: float, cos_sin: torch.Tensor,
+             cmp_pool: torch.Tensor, cmp_table: torch.Tensor,
+             prequant: Optional[torch.Tensor] = None) -> None:
+    dev = kv.device
+    _need(kv, "kv", torch.bfloat16, dev)
+    _need(score, "score", torch.float32, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(cos_sin, "cos_sin", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(cmp_pool, "cmp_pool", torch.uint8, dev)
+    if prequant is not None:
+        _need(prequant, "prequant", torch.float32, dev)
+    _check(lib().slc_compress(int(ratio), int(cu_seqlens.numel() - 1), _ptr(cu_seqlens),
+                              int(max_seqlen), _ptr(kv), _ptr(score), _ptr(gamma), float(eps),
+                              _ptr(cos_sin), int(cos_sin.shape[0]), pool(cmp_pool, cmp_table),
+                              _ptr(prequant), _stream()))
+
+
+# ------------------------------------------------------------------ indexer
+def index_scores(q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, key_table, n_slots,
+                 max_slots, scores) -> None:
+    n_q, h_idx = int(q_fp8.shape[0]), int(q_fp8.shape[1])
+    _check(lib().slc_index_scores(n_q, h_idx, _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(q_seq),
+                                  _ptr(q_pos), int(ratio), pool(key_pool, key_table),
+                                  _ptr(n_slots), int(max_slots), _ptr(scores), _stream()))
+
+
+def topk_select(k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx, topk_len) -> None:
+    n_q = int(q_seq.numel())
+    _check(lib().slc_topk_select(n_q, int(k), _ptr(scores), int(max_slots), _ptr(q_seq),
+                                 _ptr(q_pos), int(ratio), _ptr(n_slots), _ptr(topk_idx),
+                                 _ptr(topk_len), _stream()))
+
+
+def index_topk_workspace_size(n_q: int, max_slots: int) -> int:
+    return int(lib().slc_index_topk_workspace_size(int(n_q), int(max_slots)))
+
+
+def index_topk(k, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, key_table, n_slots,
+               max_slots, topk_idx, topk_len, workspace: Optional[torch.Tensor] = None) -> None:
+    n_q, h_idx = int(q_fp8.shape[0]), int(q_fp8.shape[1])
+    need = index_topk_workspace_size(n_q, max_slots)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q_fp8.device)
+    _check(lib().slc_index_topk(n_q, h_idx, int(k), _ptr(q_fp8), _ptr(q_scale), _ptr(w),
+                                _ptr(q_seq), _ptr(q_pos), int(ratio), pool(key_pool, key_table),
+                                _ptr(n_slots), int(max_slots), _ptr(topk_idx), _ptr(topk_len),
+                                _ptr(workspace), int(workspace.numel()), _stream()))
+
+
+# ---------------------------------------------------------------- attention
+def sparse_mla_workspace_size(decode: bool, n_q: int, n_heads: int, window: int, k: int) -> int:
+    f = (lib().slc_sparse_mla_decode_workspace_size if decode
+         else lib().slc_sparse_mla_prefill_workspace_size)
+    return int(f(int(n_q), int(n_heads), int(window), int(k)))
+
+
+def _sparse_mla(decode, layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
+                cmp_table, cmp_idx, n_slots, sm_scale, out, lse, workspace):
+    n_q, H = int(q.shape[0]), int(q.shape[1])
+    k = 0 if cmp_idx is None else int(cmp_idx.shape[1])
+    need = sparse_mla_workspace_size(decode, n_q, H, window, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    f = lib().slc_sparse_mla_decode if decode else lib().slc_sparse_mla_prefill
+    _check(f(int(layer_type), n_q, H, _ptr(q), _ptr(q_seq), _ptr(q_pos), int(window),
+             pool(swa_pool, swa_table), pool(cmp_pool, cmp_table), _ptr(cmp_idx), k,
+             _ptr(n_slots), float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+             0 if workspace is None else int(workspace.numel()), _stream()))
+
+
+def sparse_mla_decode(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool=None,
+                      cmp_table=None, cmp_idx=None, n_slots=None, sm_scale=1.0, out=None,
+                      lse=None, workspace=None):
+    _sparse_mla(True, layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
+                cmp_table, cmp_idx, n_slots, sm_scale, out, lse, workspace)
+
+
+def sparse_mla_prefill(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool=None,
+                       cmp_table=None, cmp_idx=None, n_slots=None, sm_scale=1.0, out=None,
+                       lse=None, workspace=None):
+    _sparse_mla(False, layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
+                cmp_table, cmp_idx, n_slots, sm_scale, out, lse, workspace)

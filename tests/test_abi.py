@@ -1,0 +1,115 @@
+"""CPU checks of the boundary: the library exports every symbol include/slc.h
+declares, argument errors are returned before any launch, and the binding
+fails loudly without the library.  No compute call is made here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slc.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def S():
+    from sparse_long_context_compressor_amd import slc
+    if not os.path.exists(slc.LIB_PATH):
+        from sparse_long_context_compressor_amd import build
+        build.build()
+    try:
+        slc.lib()
+    except OSError as e:  # the HIP runtime itself is not loadable here
+        pytest.skip(f"cannot load libslc.so: {e}")
+    return slc
+
+
+def test_exports_every_declared_symbol(S):
+    names = declared_symbols()
+    assert len(names) >= 11
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(S.EXPORTED) == set(names)
+
+
+def test_status_strings(S):
+    L = S.lib()
+    assert L.slc_status_string(0) == b"ok"
+    assert L.slc_status_string(2) == b"workspace too small"
+
+
+def _null_pool(S):
+    return S.Pool(None, None, 0, 0)
+
+
+def test_invalid_arguments_are_rejected_before_launch(S):
+    L = S.lib()
+    P = _null_pool(S)
+    fake = C.c_void_p(256)   # never dereferenced: validation fails first
+    # ratio 3 is not a compress ratio
+    assert L.slc_compress(3, 1, fake, 8, fake, fake, fake, 1e-6, fake, 8, P, None, None) == 1
+    assert b"ratio" in L.slc_last_error()
+    # a ratio-4 compress without a destination pool
+    assert L.slc_compress(4, 1, fake, 8, fake, fake, fake, 1e-6, fake, 8, P, None, None) == 1
+    assert b"cmp_pool" in L.slc_last_error()
+    # indexer heads must be a multiple of 16 up to 64
+    assert L.slc_index_scores(1, 20, fake, fake, fake, fake, fake, 4, P, fake, 16, fake, None) == 1
+    assert L.slc_index_scores(1, 80, fake, fake, fake, fake, fake, 4, P, fake, 16, fake, None) == 1
+    # k above the cap
+    assert L.slc_topk_select(1, 5000, fake, 16, fake, fake, 4, fake, fake, fake, None) == 1
+    # layer type 2 does not exist; SWAONLY takes no compressed list
+    args = [1, 64, fake, fake, fake, 128, P, P, None, 0, None, 0.1, fake, None, None, 0, None]
+    assert L.slc_sparse_mla_decode(2, *args) == 1
+    a2 = list(args)
+    a2[9] = 8
+    assert L.slc_sparse_mla_decode(1, *a2) == 1
+    # C4A without its compressed pool
+    a3 = list(args)
+    a3[9] = 8
+    a3[5] = 0
+    assert L.slc_sparse_mla_decode(4, *a3) == 1
+    assert b"cmp_pool" in L.slc_last_error()
+    # heads not a multiple of 16
+    a4 = list(args)
+    a4[1] = 40
+    assert L.slc_sparse_mla_decode(1, *a4) == 1
+    # misaligned q
+    a5 = list(args)
+    a5[2] = C.c_void_p(258)
+    a5[5] = 0
+    assert L.slc_sparse_mla_decode(1, *a5) == 1
+    # a decode that needs a workspace but gets none
+    pool = S.Pool(C.c_void_p(256), C.c_void_p(256), 4, 4)
+    a6 = [32, 64, fake, fake, fake, 128, pool, pool, fake, 512, fake, 0.1, fake, None, None, 0, None]
+    assert L.slc_sparse_mla_decode(4, *a6) == 2
+    assert L.slc_sparse_mla_decode_workspace_size(32, 64, 128, 512) > 0
+    assert L.slc_sparse_mla_prefill_workspace_size(2048, 64, 128, 2048) == 0
+    # nothing to do is not an error
+    assert L.slc_topk_select(0, 8, None, 16, None, None, 4, None, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from sparse_long_context_compressor_amd import slc
+    monkeypatch.setattr(slc, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(slc, "_lib", None)
+    with pytest.raises(ImportError):
+        slc.lib()
+
+
+def test_package_never_imports_the_oracle():
+    """The product package never imports, loads or runs anything under oracle/."""
+    pat = re.compile(r"(^\s*(import|from)\s+oracle\b)|liboracle|slc_oracle|oracle_[a-z]+\(",
+                     re.M)
+    pkg = os.path.join(ROOT, "sparse_long_context_compressor_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), os.path.join(dirpath, f)
