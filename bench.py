@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16, help="queries the oracle times")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -109,40 +110,80 @@ def main():
     ws_bytes = slc.sparse_mla_workspace_size(True, B, H, W, K)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def step(lay, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def index_scores(lay):
         slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
                          lay.key_table, lay.n_slots, SLOTS, scores)
-        if ev is not None:
-            ev[1].record()
+
+    def topk(lay):
         slc.topk_select(K, scores, SLOTS, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
-        if ev is not None:
-            ev[2].record()
+
+    def decode(lay):
         slc.sparse_mla_decode(4, lay.q, lay.q_seq, lay.q_pos, W, lay.swa_pool, lay.swa_table,
                               lay.cmp_pool, lay.cmp_table, idx, lay.n_slots, lay.sm_scale, out,
                               lse, ws)
-        if ev is not None:
-            ev[3].record()
+
+    def step(lay):
+        index_scores(lay)
+        topk(lay)
+        decode(lay)
+
+    def timed(fn, n):
+        """Average ms of n back-to-back calls of fn(replica) bracketed by one event pair."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(reps[i % len(reps)])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for i in range(args.warmup):
         step(reps[i % len(reps)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    graph = None
+    if args.graph:
+        # one captured step per replica, replayed in turn
+        graph = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in reps:
+                step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for r in reps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graph.append(g)
+        for i in range(args.warmup):
+            graph[i % len(graph)].replay()
+        torch.cuda.synchronize()
+
+    # ---- headline: K whole steps, nothing else on the stream ----
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
-        step(reps[i % len(reps)], evs[i])
+    if graph is not None:
+        for i in range(args.steps):
+            graph[i % len(graph)].replay()
+    else:
+        for i in range(args.steps):
+            step(reps[i % len(reps)])
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    idx_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    topk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    eager_ms = timed(step, args.steps) if graph is not None else ms_step
+
+    # ---- per-kernel: back-to-back launches of one op over the replicas ----
+    idx_ms = timed(index_scores, args.steps)
+    topk_ms = timed(topk, args.steps)
+    attn_ms = timed(decode, args.steps)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -170,6 +211,8 @@ def main():
                    "block_rows": 64, "replicas": args.replicas},
         "achieved_step_GBps": STEP_BYTES / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": STEP_BYTES / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "timing": "hip_graph_replay" if graph is not None else "eager_launches",
+        "eager_ms_per_step": eager_ms,
         "kernels_us": {"index_scores": idx_ms * 1e3, "topk_select": topk_ms * 1e3,
                        "sparse_mla_decode": attn_ms * 1e3},
         "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": achieved,

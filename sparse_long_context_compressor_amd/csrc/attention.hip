@@ -1,7 +1,5 @@
 // attention.hip -- sparse MLA attention in absorbed (MQA) form over the
-// sliding window plus the selected compressed slots, for decode (split along
-// the attended list, partial softmax states merged by a second kernel) and
-// prefill (one workgroup per query token).
+// sliding window plus the selected compressed slots.
 //
 // Method: "From MLA to CSA + HCA", Ch.2 (absorbed MLA: every query head
 // attends one shared 576-wide latent row per entry, values are the row's
@@ -9,17 +7,26 @@
 // (the kernel takes SWA indices together with compressed top-k indices);
 // "DeepseekV4Attention" (devpress), _forward_decode / _forward_prefill.
 //
-// Per workgroup: 16 query heads per wave (n_heads / 16 waves), 32 attended
-// entries per chunk.  Each chunk's rows are gathered through the block tables
-// into an LDS tile as bf16 (compressed rows dequantised on the way: code *
-// scale), then per wave:
-//   S^T[32 x 16] = K[32 x 576] . Q^T[576 x 16]    (v_mfma_f32_16x16x32_bf16)
-//   online softmax per head (each lane owns one head: no cross-lane rescale)
-//   O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16]
-// The score accumulators' lane layout already is the B-operand layout P^T
-// needs (the MFMA k-order is a shared permutation of the 32 rows), and V^T
-// comes from the row-major tile through ds_read_tr16_b64 (LDS transpose read),
-// so the tile is written once and read twice with no transposed copy.
+// Common pieces.  Every attended entry of a query is first resolved through
+// the block tables into a physical row (SWA entries e < window are positions
+// p-window+1+e, the rest are compressed slot ids); the rows are then gathered
+// chunk by chunk into an LDS tile as bf16 (compressed rows dequantised on the
+// way: code * scale), with the next chunk's global loads in flight while the
+// current chunk is computed.  On the tile, per wave and 16 heads:
+//   S^T = K . Q^T               v_mfma_f32_16x16x32_bf16, Q^T held in registers
+//   online softmax per head     each lane owns one head: no cross-lane rescale
+//   O^T += V^T . P^T            the score accumulators' lane layout already is
+//                               the P^T operand layout (the MFMA k-order is a
+//                               shared permutation of the rows), and V^T comes
+//                               from the row-major tile via ds_read_tr16_b64.
+//
+// Decode (few queries, long lists): one workgroup per (query, 16-head group,
+// list split); its four waves take 16 rows each of every 64-row chunk and
+// merge their softmax states through LDS.  Head groups of one query are
+// numbered so that they land on the same XCD and share its L2 for the rows.
+// When a query's list is split across workgroups, a combine kernel merges
+// the partial (O, max, sum) states.  Prefill (many queries): one workgroup per
+// query token; its waves are the head groups and share each 32-row tile.
 
 #include "slc_internal.hpp"
 
@@ -27,10 +34,10 @@ namespace slc {
 
 namespace {
 
-constexpr int kKPitch = kD + 8;         // bf16 per LDS row: 1168 B, spreads banks
-constexpr int kUnits = kD / 8;          // 16-byte units per bf16 row (72)
+constexpr int kKPitch = kD + 8;        // bf16 per LDS row: 1168 B, spreads banks
+constexpr int kMaxEntries = SLC_MAX_WINDOW + SLC_MAX_TOPK;
 
-typedef short lds_i16x4 __attribute__((ext_vector_type(4), address_space(3)));
+typedef short i16x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -41,92 +48,387 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Physical row of attended entry e of query t (-1: skipped).
+__device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int t, int seq, int p, int ns,
+                                                 int e) {
+    int64_t r = -1;
+    if (e < a.window) {
+        int pos = p - a.window + 1 + e;
+        if (pos >= 0) r = pool_row(a.swa, seq, pos);
+    } else {
+        int s = a.cmp_idx[static_cast<int64_t>(t) * a.k + (e - a.window)];
+        if (s >= 0 && s < ns) r = pool_row(a.cmp, seq, s);
+    }
+    return static_cast<int32_t>(r);
+}
+
+// Row-wise gather by one producer wave: RPW rows per chunk.  For each row the
+// 64 lanes take the 512 nope dims (SWA: 8 bf16 = 16 B per lane; compressed:
+// 8 e4m3 codes = 8 B plus that block's scale), then the 64 rope dims of 8 rows
+// at a time (lane -> row lane/8, 16-byte unit lane%8).  A row's kind and base
+// address are the same for every lane.
+// Skipped rows read from this zero page instead of branching around their
+// loads: every row issues the same loads, so no load result has to be merged
+// at a control-flow join (which would force a wait on each row in turn).
+__device__ __attribute__((aligned(256))) uint8_t kZeroPage[2048];   // never written
+
+template <int RPW>
+struct RowGather {
+    u32x4 nope[RPW];        // SWA: 8 bf16; compressed: 8 codes in the low 8 bytes
+    float scl[RPW];         // compressed: the lane's 64-dim block scale
+    u32x4 rope[RPW / 8];
+
+    __device__ __forceinline__ void load(const AttnArgs &a, const int32_t *src, int e0, int e_end,
+                                         int pw, int lane) {
+#pragma unroll
+        for (int j = 0; j < RPW; j++) {
+            const int e = e0 + pw * RPW + j;
+            const int32_t row = e < e_end ? src[e] : -1;
+            const uint8_t *pn = kZeroPage + 16 * lane;
+            const float *ps = reinterpret_cast<const float *>(kZeroPage);
+            if (row >= 0) {
+                if (e >= a.window) {
+                    pn = cmp_row_ptr(a.cmp, row) + 8 * lane;   // 16-byte read, low 8 used
+                    ps = cmp_scale_ptr(a.cmp, row) + (lane >> 3);
+                } else {
+                    pn = reinterpret_cast<const uint8_t *>(swa_row_ptr(a.swa, row) + 8 * lane);
+                }
+            }
+            nope[j] = *reinterpret_cast<const u32x4 *>(pn);
+            scl[j] = *ps;
+        }
+#pragma unroll
+        for (int q = 0; q < RPW / 8; q++) {
+            const int e = e0 + pw * RPW + 8 * q + (lane >> 3);
+            const int part = lane & 7;
+            const int32_t row = e < e_end ? src[e] : -1;
+            const uint8_t *pr = kZeroPage + 16 * part;
+            if (row >= 0)
+                pr = (e >= a.window ? cmp_row_ptr(a.cmp, row) + kDN
+                                    : reinterpret_cast<const uint8_t *>(swa_row_ptr(a.swa, row) + kDN)) +
+                     16 * part;
+            rope[q] = *reinterpret_cast<const u32x4 *>(pr);
+        }
+    }
+
+    // Dequantise compressed rows (code * scale -> bf16; exact for the
+    // power-of-two scales compress writes) and write the rows into the tile.
+    // Entries e >= window are compressed rows (skipped ones hold zeros).
+    __device__ __forceinline__ void store(uint16_t *tile, const AttnArgs &a, int e0, int pw,
+                                          int lane) const {
+#pragma unroll
+        for (int j = 0; j < RPW; j++) {
+            u32x4 v = nope[j];
+            if (e0 + pw * RPW + j >= a.window) {
+                // e4m3 * scale -> bf16 in one packed conversion per pair; exact for
+                // power-of-two scales (the ABI's scale format)
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const float sc = scl[j];
+                bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(v[0]), sc, false);
+                bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(v[0]), sc, true);
+                bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(v[1]), sc, false);
+                bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(v[1]), sc, true);
+                v = u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                          __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+            }
+            *reinterpret_cast<u32x4 *>(tile + (pw * RPW + j) * kKPitch + 8 * lane) = v;
+        }
+#pragma unroll
+        for (int q = 0; q < RPW / 8; q++)
+            *reinterpret_cast<u32x4 *>(tile + (pw * RPW + 8 * q + (lane >> 3)) * kKPitch + kDN +
+                                       8 * (lane & 7)) = rope[q];
+    }
+};
+
+// Q^T as the B operand for 16 heads: lane (g, c) holds head h0 + c, dims 8g + 32s .. +8.
+__device__ __forceinline__ void load_q(const AttnArgs &a, int t, int h, int g, bf16x8 (&qb)[kD / 32]) {
+    const uint16_t *qp = a.q + (static_cast<int64_t>(t) * a.n_heads + h) * kD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kD / 32; s++)
+        qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + 32 * s));
+}
+
+// Online-softmax update for one head per lane.  x: this lane's logits (log2
+// domain, -inf for skipped rows); the row set spans the lane's x and the
+// same head's lanes in the other three 16-lane groups.  Returns p = 2^(x-m).
+template <int N>
+__device__ __forceinline__ float softmax_update(float (&x)[N], float &m_run, float &l_run,
+                                                float (&p)[N]) {
+    float cmax = x[0];
+#pragma unroll
+    for (int i = 1; i < N; i++) cmax = fmaxf(cmax, x[i]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run, cmax);
+    float alpha = 1.f, psum = 0.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < N; i++) p[i] = 0.f;
+    } else {
+        alpha = exp2f(m_run - m_new);
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            p[i] = exp2f(x[i] - m_new);
+            psum += p[i];
+        }
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    return alpha;
+}
+
+__device__ __forceinline__ void store_out(const AttnArgs &a, int t, int h, int g,
+                                          const f32x4 (&o)[kDN / 16], float m_run, float l_run) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t *op = a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < kDN / 16; ct++)
+        *reinterpret_cast<u32x2 *>(op + 16 * ct) =
+            u32x2{bf16_pair_rne(o[ct][0] * inv, o[ct][1] * inv),
+                  bf16_pair_rne(o[ct][2] * inv, o[ct][3] * inv)};
+    if (a.lse && g == 0)
+        a.lse[static_cast<int64_t>(t) * a.n_heads + h] =
+            l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+constexpr int kDecRows = 64;   // rows per decode chunk (16 per wave)
+constexpr int kPreRows = 32;   // rows per prefill chunk
+
 }  // namespace
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_attn_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ktile[kAttnChunk * kKPitch];
-    __shared__ int64_t row_src[kAttnChunk];
-    __shared__ int row_kind[kAttnChunk];   // 0: SWA row, 1: compressed row, -1: skipped
+// ------------------------------------------------------------------ decode
+// 512 threads: waves 0..3 compute (wave w: rows 16w..16w+15 of each 64-row
+// chunk, the group's 16 heads), waves 4..7 gather the next chunk meanwhile.
+__global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t ktile[kDecRows * kKPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t qtile[16 * kKPitch];   // the group's 16 heads
+    __shared__ int32_t src[kMaxEntries];
+    __shared__ float st_m[4][16], st_l[4][16];
 
-    constexpr int NT = NW * 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const int t = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
-    const int seq = a.q_seq[t], p = a.q_pos[t];
-    const int W = a.window;
-    const int kk = a.layer_type == SLC_LAYER_SWAONLY ? 0 : a.k;
-    const int E = W + kk;
-    const int e_begin = split * a.chunks_per_split * kAttnChunk;
-    int e_end = e_begin + a.chunks_per_split * kAttnChunk;
-    e_end = e_end < E ? e_end : E;
-    const int ns = kk > 0 ? a.n_slots[seq] : 0;
-    const int h = 16 * w + c;
+    const bool producer = w >= 4;
+    const int HG = a.n_heads / 16, S = a.n_splits;
+    // blocks with equal blockIdx % 8 run on one XCD: give all (head group,
+    // split) blocks of a query the same residue
+    const int per_group = 8 * HG * S;
+    const int grp = blockIdx.x / per_group, rem = blockIdx.x % per_group;
+    const int t = 8 * grp + (rem & 7);
+    const int hg = (rem >> 3) % HG, split = (rem >> 3) / HG;
+    if (t >= a.n_q) return;
 
-    // Q^T as the B operand: lane (g, c) holds head c, dims 8g + 32s .. +8.
-    bf16x8 qb[kD / 32];
+    const int seq = a.q_seq[t], p = a.q_pos[t];
+    const int E = a.window + a.k;
+    const int ns = a.k > 0 ? a.n_slots[seq] : 0;
+    const int e_begin = split * a.chunks_per_split * kDecRows;
+    int e_end = e_begin + a.chunks_per_split * kDecRows;
+    e_end = e_end < E ? e_end : E;
+    const int h = 16 * hg + c;
+
+    for (int e = e_begin + tid; e < e_end; e += 512) src[e] = resolve_entry(a, t, seq, p, ns, e);
     {
-        const uint16_t *qp = a.q + (static_cast<int64_t>(t) * a.n_heads + h) * kD + 8 * g;
-#pragma unroll
-        for (int s = 0; s < kD / 32; s++)
-            qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + 32 * s));
+        const u32x4 *qg = reinterpret_cast<const u32x4 *>(
+            a.q + (static_cast<int64_t>(t) * a.n_heads + 16 * hg) * kD);
+        for (int i = tid; i < 16 * kD / 8; i += 512)
+            *reinterpret_cast<u32x4 *>(qtile + (i / (kD / 8)) * kKPitch + 8 * (i % (kD / 8))) = qg[i];
+    }
+    __syncthreads();
+
+    if (producer) {
+        RowGather<kDecRows / 4> gat;
+        const int pw = w - 4;
+        for (int e0 = e_begin; e0 < e_end; e0 += kDecRows) {
+            gat.load(a, src, e0, e_end, pw, lane);
+            if (e0 != e_begin) __syncthreads();     // consumers are done with the tile
+            gat.store(ktile, a, e0, pw, lane);
+            __syncthreads();                        // tile ready
+        }
+        __syncthreads();                            // matches the consumers' last chunk
+        // the consumers' four merge-phase barriers
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        return;
     }
 
     f32x4 o[kDN / 16];
 #pragma unroll
     for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    const uint16_t *qr = qtile + c * kKPitch + 8 * g;
 
-    for (int e0 = e_begin; e0 < e_end; e0 += kAttnChunk) {
-        // ---- resolve the chunk's entries to physical rows ----
-        if (tid < kAttnChunk) {
-            int e = e0 + tid, kind = -1;
-            int64_t src = -1;
-            if (e < e_end) {
-                if (e < W) {
-                    int pos = p - W + 1 + e;
-                    if (pos >= 0) src = pool_row(a.swa, seq, pos);
-                    kind = src >= 0 ? 0 : -1;
-                } else {
-                    int s = a.cmp_idx[static_cast<int64_t>(t) * a.k + (e - W)];
-                    if (s >= 0 && s < ns) src = pool_row(a.cmp, seq, s);
-                    kind = src >= 0 ? 1 : -1;
-                }
-            }
-            row_kind[tid] = kind;
-            row_src[tid] = src;
+    for (int e0 = e_begin; e0 < e_end; e0 += kDecRows) {
+        if (e0 != e_begin) __syncthreads();        // previous chunk done (pairs with producers)
+        __syncthreads();                            // tile ready
+
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t *kr = ktile + (16 * w + c) * kKPitch + 8 * g;
+#pragma unroll
+        for (int s = 0; s < kD / 32; s++) {
+            bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * s));
+            bf16x8 qv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * s));
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv, sacc, 0, 0, 0);
         }
+        float x[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int e = e0 + 16 * w + 4 * g + i;
+            x[i] = (e < e_end && src[e] >= 0) ? sacc[i] * a.sm_scale_log2 : -INFINITY;
+        }
+        const float alpha = softmax_update<4>(x, m_run, l_run, pv);
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
+        }
+
+        // O^T += V^T . P^T over the wave's 16 rows (k = 16: rows 16w + 4g + 0..3)
+        i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
+                                                     bf16_pair_rne(pv[2], pv[3])});
+        const uint16_t *vr = ktile + (16 * w + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) {
+            i16x4 va = lds_read_tr16(vr + 16 * ct);
+            o[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4v, va), pb,
+                                                              o[ct], 0, 0, 0);
+        }
+    }
+    __syncthreads();                                // last chunk done
+
+    // ---- merge the four waves' softmax states (same 16 heads, disjoint rows) ----
+    if (g == 0) {
+        st_m[w][c] = m_run;
+        st_l[w][c] = l_run;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ww++)
+        if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
+    float L = 0.f, my_scale = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ww++) {
+        float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
+        L += st_l[ww][c] * sc;
+        if (ww == w) my_scale = sc;
+    }
+#pragma unroll
+    for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
+    // O exchange through the (now free) tile: [ct][lane] float4 per wave, 32 KB
+    f32x4 *xo = reinterpret_cast<f32x4 *>(ktile);
+    if (w >= 2) {
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) xo[((w - 2) * (kDN / 16) + ct) * 64 + lane] = o[ct];
+    }
+    __syncthreads();
+    if (w < 2) {
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(w * (kDN / 16) + ct) * 64 + lane];
+    }
+    __syncthreads();
+    if (w == 1) {
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) xo[ct * 64 + lane] = o[ct];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
+
+    if (S == 1) {
+        store_out(a, t, h, g, o, M, L);
+    } else {
+        // partial state: [t][split][h] (O unnormalised at max M, then M and L)
+        const int64_t slot = (static_cast<int64_t>(t) * S + split) * a.n_heads + h;
+        float *po = a.part_o + slot * kDN + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) *reinterpret_cast<f32x4 *>(po + 16 * ct) = o[ct];
+        if (g == 0) {
+            a.part_ml[2 * slot] = M;
+            a.part_ml[2 * slot + 1] = L;
+        }
+    }
+}
+
+// Merge the list splits: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// One thread per (query, head, 4 output columns).
+__global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
+    const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t per_q = static_cast<int64_t>(a.n_heads) * (kDN / 4);
+    if (id >= per_q * a.n_q) return;
+    const int t = static_cast<int>(id / per_q);
+    const int h = static_cast<int>((id % per_q) / (kDN / 4));
+    const int c4 = static_cast<int>(id % (kDN / 4));
+    const int S = a.n_splits;
+    float M = -INFINITY;
+    for (int s = 0; s < S; s++) {
+        const float *ml = a.part_ml + 2 * ((static_cast<int64_t>(t) * S + s) * a.n_heads + h);
+        if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+    }
+    float L = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; s++) {
+        const int64_t slot = (static_cast<int64_t>(t) * S + s) * a.n_heads + h;
+        const float l = a.part_ml[2 * slot + 1];
+        if (!(l > 0.f)) continue;
+        const float sc = exp2f(a.part_ml[2 * slot] - M);
+        L += l * sc;
+        acc += *reinterpret_cast<const f32x4 *>(a.part_o + slot * kDN + 4 * c4) * sc;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<u32x2 *>(a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + 4 * c4) =
+        u32x2{bf16_pair_rne(acc[0] * inv, acc[1] * inv), bf16_pair_rne(acc[2] * inv, acc[3] * inv)};
+    if (a.lse && c4 == 0)
+        a.lse[static_cast<int64_t>(t) * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ----------------------------------------------------------------- prefill
+// NW + 4 waves: waves 0..NW-1 compute (wave w: heads 16w..16w+15 of the block,
+// all rows of each 32-row chunk), four more waves gather the next chunk.
+template <int NW>
+__global__ __launch_bounds__((NW + 4) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mla_prefill_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t ktile[kPreRows * kKPitch];
+    __shared__ int32_t src[kMaxEntries];
+
+    constexpr int NT = (NW + 4) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int t = blockIdx.x;
+    const int h0 = 64 * blockIdx.y;                 // head block (up to 64 heads)
+    const int seq = a.q_seq[t], p = a.q_pos[t];
+    const int E = a.window + a.k;
+    const int ns = a.k > 0 ? a.n_slots[seq] : 0;
+
+    for (int e = tid; e < E; e += NT) src[e] = resolve_entry(a, t, seq, p, ns, e);
+    __syncthreads();
+
+    if (w >= NW) {
+        RowGather<kPreRows / 4> gat;
+        const int pw = w - NW;
+        for (int e0 = 0; e0 < E; e0 += kPreRows) {
+            gat.load(a, src, e0, E, pw, lane);
+            if (e0 != 0) __syncthreads();
+            gat.store(ktile, a, e0, pw, lane);
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int h = h0 + 16 * w + c;
+    bf16x8 qb[kD / 32];
+    load_q(a, t, h, g, qb);
+    f32x4 o[kDN / 16];
+#pragma unroll
+    for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int e0 = 0; e0 < E; e0 += kPreRows) {
+        if (e0 != 0) __syncthreads();
         __syncthreads();
 
-        // ---- gather rows into the bf16 tile ----
-        for (int u = tid; u < kAttnChunk * kUnits; u += NT) {
-            int r = u / kUnits, part = u - r * kUnits;
-            int kind = row_kind[r];
-            int64_t src = row_src[r];
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (kind == 0) {
-                v = *reinterpret_cast<const u32x4 *>(swa_row_ptr(a.swa, src) + 8 * part);
-            } else if (kind == 1) {
-                const uint8_t *rp = cmp_row_ptr(a.cmp, src);
-                if (part < kDN / 8) {
-                    u32x2 cw = *reinterpret_cast<const u32x2 *>(rp + 8 * part);
-                    float scl = cmp_scale_ptr(a.cmp, src)[part >> 3];
-                    float f[8];
-                    e4m3x4_to_f32(cw[0], f[0], f[1], f[2], f[3]);
-                    e4m3x4_to_f32(cw[1], f[4], f[5], f[6], f[7]);
-                    v = u32x4{bf16_pair_rne(f[0] * scl, f[1] * scl),
-                              bf16_pair_rne(f[2] * scl, f[3] * scl),
-                              bf16_pair_rne(f[4] * scl, f[5] * scl),
-                              bf16_pair_rne(f[6] * scl, f[7] * scl)};
-                } else {
-                    v = *reinterpret_cast<const u32x4 *>(rp + kDN + 16 * (part - kDN / 8));
-                }
-            }
-            *reinterpret_cast<u32x4 *>(ktile + r * kKPitch + 8 * part) = v;
-        }
-        __syncthreads();
-
-        // ---- S^T = K . Q^T for this wave's 16 heads ----
         f32x4 sacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
@@ -138,156 +440,78 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(AttnArgs a) {
                 sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
             }
         }
-
-        // ---- online softmax (log2 domain); lane (g, c) holds rows 4g+i and 16+4g+i of head c ----
-        float x[8];
+        float x[8], pv[8];
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                int r = 16 * mt + 4 * g + i;
-                x[4 * mt + i] = row_kind[r] >= 0 ? sacc[mt][i] * a.sm_scale_log2 : -INFINITY;
+                int e = e0 + 16 * mt + 4 * g + i;
+                x[4 * mt + i] = (e < E && src[e] >= 0) ? sacc[mt][i] * a.sm_scale_log2 : -INFINITY;
             }
-        float cmax = x[0];
+        const float alpha = softmax_update<8>(x, m_run, l_run, pv);
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int i = 1; i < 8; i++) cmax = fmaxf(cmax, x[i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-        const float m_new = fmaxf(m_run, cmax);
-        float pv[8], alpha = 1.f, psum = 0.f;
-        if (m_new == -INFINITY) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) pv[i] = 0.f;
-        } else {
-            alpha = exp2f(m_run - m_new);
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                pv[i] = exp2f(x[i] - m_new);
-                psum += pv[i];
-            }
+            for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
 
+        // k = 32 rows: 4g+0..3 then 16+4g+0..3 (same order as pv)
         bf16x8 pb = __builtin_bit_cast(
             bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
                           bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
-
-        // ---- O^T += V^T . P^T; V^T via LDS transpose reads ----
         const uint16_t *v1 = ktile + (4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
         const uint16_t *v2 = v1 + 16 * kKPitch;
 #pragma unroll
         for (int ct = 0; ct < kDN / 16; ct++) {
             i16x4 lo = lds_read_tr16(v1 + 16 * ct);
             i16x4 hi = lds_read_tr16(v2 + 16 * ct);
-            bf16x8 va = __builtin_bit_cast(
-                bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+            u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[ct], 0, 0, 0);
         }
-        __syncthreads();
     }
-
-    // ---- epilogue: lane (g, c) holds O^T[16ct + 4g + i][head c] ----
-    if (a.n_splits == 1) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        uint16_t *op = a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + 4 * g;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++)
-            *reinterpret_cast<u32x2 *>(op + 16 * ct) =
-                u32x2{bf16_pair_rne(o[ct][0] * inv, o[ct][1] * inv),
-                      bf16_pair_rne(o[ct][2] * inv, o[ct][3] * inv)};
-        if (a.lse && g == 0)
-            a.lse[static_cast<int64_t>(t) * a.n_heads + h] =
-                l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    } else {
-        const int64_t slot = (static_cast<int64_t>(t) * a.n_splits + split) * a.n_heads + h;
-        float *po = a.part_o + slot * kDN + 4 * g;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) *reinterpret_cast<f32x4 *>(po + 16 * ct) = o[ct];
-        if (g == 0) {
-            a.part_ml[2 * slot] = m_run;
-            a.part_ml[2 * slot + 1] = l_run;
-        }
-    }
+    store_out(a, t, h, g, o, m_run, l_run);
 }
 
-// Merge the decode splits of one query: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-__global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
-    __shared__ float sh_m[SLC_MAX_HEADS], sh_inv[SLC_MAX_HEADS];
-    const int t = blockIdx.x;
-    const int H = a.n_heads, S = a.n_splits;
-    const int64_t base = static_cast<int64_t>(t) * S * H;
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
-        float M = -INFINITY;
-        for (int s = 0; s < S; s++) {
-            const float *ml = a.part_ml + 2 * (base + static_cast<int64_t>(s) * H + h);
-            if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
-        }
-        float L = 0.f;
-        for (int s = 0; s < S; s++) {
-            const float *ml = a.part_ml + 2 * (base + static_cast<int64_t>(s) * H + h);
-            if (ml[1] > 0.f) L += ml[1] * exp2f(ml[0] - M);
-        }
-        sh_m[h] = M;
-        sh_inv[h] = L > 0.f ? 1.f / L : 0.f;
-        if (a.lse)
-            a.lse[static_cast<int64_t>(t) * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < H * (kDN / 4); e += blockDim.x) {
-        int h = e / (kDN / 4), c4 = e - h * (kDN / 4);
-        float M = sh_m[h];
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; s++) {
-            int64_t slot = base + static_cast<int64_t>(s) * H + h;
-            float l = a.part_ml[2 * slot + 1];
-            if (l > 0.f) {
-                float sc = exp2f(a.part_ml[2 * slot] - M);
-                acc += *reinterpret_cast<const f32x4 *>(a.part_o + slot * kDN + 4 * c4) * sc;
-            }
-        }
-        float inv = sh_inv[h];
-        uint16_t *op = a.out + (static_cast<int64_t>(t) * H + h) * kDN + 4 * c4;
-        *reinterpret_cast<u32x2 *>(op) = u32x2{bf16_pair_rne(acc[0] * inv, acc[1] * inv),
-                                               bf16_pair_rne(acc[2] * inv, acc[3] * inv)};
-    }
-}
-
-void attention_plan(int n_q, int window, int k, bool decode, int *n_splits, int *chunks_per_split) {
-    int entries = window + k;
-    int chunks = (entries + kAttnChunk - 1) / kAttnChunk;
+void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
+                    int *chunks_per_split) {
+    const int entries = window + k;
+    const int rows = decode ? kDecRows : kPreRows;
+    int chunks = (entries + rows - 1) / rows;
     if (chunks < 1) chunks = 1;
-    int target = 1;
+    int splits = 1;
     if (decode) {
-        const int want_wgs = 512;   // about two workgroups per CU
-        target = (want_wgs + n_q - 1) / (n_q > 0 ? n_q : 1);
-        if (target < 1) target = 1;
+        const int groups = (n_q > 0 ? n_q : 1) * (n_heads / 16);
+        splits = (256 + groups - 1) / groups;   // about one workgroup per CU
+        if (splits > chunks) splits = chunks;
+        if (splits < 1) splits = 1;
     }
-    int cps = (chunks + target - 1) / target;
+    int cps = (chunks + splits - 1) / splits;
     *chunks_per_split = cps;
     *n_splits = (chunks + cps - 1) / cps;
 }
 
-hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
-    dim3 grid(static_cast<unsigned>(a.n_q) * a.n_splits);
-    switch (a.n_heads / 16) {
-    case 1: hipLaunchKernelGGL(mla_attn_kernel<1>, grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(mla_attn_kernel<2>, grid, dim3(128), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(mla_attn_kernel<3>, grid, dim3(192), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(mla_attn_kernel<4>, grid, dim3(256), 0, stream, a); break;
-    case 5: hipLaunchKernelGGL(mla_attn_kernel<5>, grid, dim3(320), 0, stream, a); break;
-    case 6: hipLaunchKernelGGL(mla_attn_kernel<6>, grid, dim3(384), 0, stream, a); break;
-    case 7: hipLaunchKernelGGL(mla_attn_kernel<7>, grid, dim3(448), 0, stream, a); break;
-    default: hipLaunchKernelGGL(mla_attn_kernel<8>, grid, dim3(512), 0, stream, a); break;
+hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) {
+    if (decode) {
+        const int HG = a.n_heads / 16;
+        const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
+        dim3 grid(groups * 8u * HG * a.n_splits);
+        hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(512), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.n_splits == 1) return e;
+        const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / 4);
+        hipLaunchKernelGGL(mla_combine_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                           dim3(256), 0, stream, a);
+        return hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_splits == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.n_q), dim3(256), 0, stream, a);
+    const int hb = (a.n_heads + 63) / 64;          // head blocks of up to 64 heads
+    const int nw = a.n_heads / hb / 16;            // 16-head groups per block (uniform)
+    dim3 grid(a.n_q, hb);
+    switch (nw) {
+    case 1: hipLaunchKernelGGL(mla_prefill_kernel<1>, grid, dim3(320), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(mla_prefill_kernel<2>, grid, dim3(384), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(mla_prefill_kernel<3>, grid, dim3(448), 0, stream, a); break;
+    default: hipLaunchKernelGGL(mla_prefill_kernel<4>, grid, dim3(512), 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -31,8 +31,8 @@ slc_status_t check_pool(const slc_pool_t &p, const char *name) {
     const char *why = nullptr;
     if (!p.base || !p.block_table) why = "base and block_table are required";
     else if (!aligned(p.base, 16)) why = "base must be 16-byte aligned";
-    else if (p.table_stride < 1 || p.n_blocks < 0 || p.n_blocks > (int64_t(1) << 40))
-        why = "table_stride must be >= 1 and n_blocks in [0, 2^40]";
+    else if (p.table_stride < 1 || p.n_blocks < 0 || p.n_blocks > (int64_t(1) << 24))
+        why = "table_stride must be >= 1 and n_blocks in [0, 2^24]";
     if (!why) return SLC_OK;
     std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", name, why);
     return SLC_ERR_INVALID_ARG;
@@ -155,7 +155,7 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
 static size_t attn_ws(int n_q, int n_heads, int window, int k, bool decode) {
     if (n_q <= 0 || n_heads <= 0) return 0;
     int splits, cps;
-    attention_plan(n_q, window, k, decode, &splits, &cps);
+    attention_plan(n_q, n_heads, window, k, decode, &splits, &cps);
     if (splits <= 1) return 0;
     size_t per = static_cast<size_t>(n_q) * splits * n_heads;
     size_t bytes = per * kDN * sizeof(float) + per * 2 * sizeof(float) + 256;
@@ -205,7 +205,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     }
     int kk = layer_type == SLC_LAYER_SWAONLY ? 0 : k;
     int splits, cps;
-    attention_plan(n_q, window, kk, decode, &splits, &cps);
+    attention_plan(n_q, n_heads, window, kk, decode, &splits, &cps);
     size_t need = attn_ws(n_q, n_heads, window, kk, decode);
     if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256))) {
         std::snprintf(g_last_error, sizeof g_last_error,
@@ -235,7 +235,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
         a.part_o = static_cast<float *>(workspace);
         a.part_ml = a.part_o + per * kDN;
     }
-    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_attention(a, decode, static_cast<hipStream_t>(stream)));
 }
 
 slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,

@@ -11,13 +11,20 @@
 // bf16 MFMA accumulates at fp32 accuracy; gfx950's fp8 MFMAs accumulate the
 // 128 products at a reduced internal precision (measured errors up to 1e-4 of
 // sum|p|), which would break exact top-k agreement, so they are not used here.
-// The contraction is far below the bf16 ridge (the keys are the traffic), so
-// the kernel stays HBM-bound either way.
+// The contraction sits far below the bf16 ridge (the keys are the traffic),
+// so the kernel stays HBM-bound.  Quantisation scales are positive, so
+// ReLU(qs * ks * dot) = ks * qs * ReLU(dot) and the per-head factor w * qs is
+// applied once per head, the key scale once per slot.
 //
-// Top-k: one workgroup per query runs an MSB-first radix select (4 passes of
-// 8 bits) over order-preserving 32-bit keys of the fp32 scores, held in LDS,
-// then writes the selected slots in increasing slot order; ties at the
-// threshold go to the lower slot index.
+// Top-k: one workgroup of 1024 threads per query; each thread keeps up to 64
+// order-preserving 32-bit keys of consecutive slots in registers.  An
+// MSB-first radix select (8-bit digits, per-wave LDS histograms) finds the
+// k-th largest key, starting below the bits all keys share (scores of one
+// query sit in a narrow range, so their top bits agree and a first digit
+// over them would pile every key into one histogram bin); one block-wide
+// scan of (above, equal) counts then
+// places every selected slot, in increasing slot order, ties at the threshold
+// going to the lower slot index.
 
 #include "slc_internal.hpp"
 
@@ -25,26 +32,37 @@ namespace slc {
 
 namespace {
 
-// 16 bytes of e4m3 (4 dwords) at k positions [8s, 8s+8) for s = 0, 1 -> two
-// bf16x8 MFMA operands.
-__device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, float scale, bf16x8 &s0,
-                                                    bf16x8 &s1) {
-    u32x2 a = e4m3x4_to_bf16x4(w[0], scale);
-    u32x2 b = e4m3x4_to_bf16x4(w[1], scale);
-    u32x2 c = e4m3x4_to_bf16x4(w[2], scale);
-    u32x2 d = e4m3x4_to_bf16x4(w[3], scale);
-    s0 = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-    s1 = __builtin_bit_cast(bf16x8, u32x4{c[0], c[1], d[0], d[1]});
+// 16 e4m3 bytes (k positions [8s, 8s+16) of the lane's share) -> two bf16x8
+// MFMA operands, exactly (packed hardware conversion, unit scale).
+__device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 &s1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 p[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w[i]), 1.0f, false);
+        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w[i]), 1.0f, true);
+    }
+    s0 = bf16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+    s1 = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
-constexpr int kScoreTile = 256;   // slots per workgroup (4 waves x 4 sub-tiles x 16)
+constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
+constexpr int kScoreTile = 4 * kSubTiles * 16;      // 1024 slots per workgroup
+constexpr int kRing = 6;                            // sub-tiles in flight per wave
+
+struct KeyStage {
+    u32x4 lo, hi;
+    float scale;
+};
 
 }  // namespace
 
-// grid (n_q, ceil(max_slots / 256)), 256 threads.  Lane (g = lane/16, c = lane%16)
-// owns index-dim bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its head / key:
-// the k-ordering inside the MFMA is the same permutation for both operands, so
-// the dot product is unchanged.
+// grid (n_q, ceil(max_slots / 1024)), 256 threads.  Wave w's sub-tile j covers
+// slots s0 + 64j + 16w + (0..15): all four waves' sub-tile j lie in logical
+// block s0/64 + j, so one (wave-uniform) table lookup serves it.  Lane
+// (g = lane/16, c = lane%16) owns index-dim bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of its head and of its key; the MFMA k-order is the same
+// permutation for both operands, so the dot product is unchanged.
 template <int HT>
 __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     const int t = blockIdx.x;
@@ -56,49 +74,63 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     const int s0 = blockIdx.y * kScoreTile;
     if (s0 >= nv) return;
 
+    // ---- query operands and per-head factors ----
     bf16x8 qa[HT][4];
-    float hs[HT][4], hw[HT][4];
+    float hf[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) {
         const uint8_t *qp = a.q + (static_cast<int64_t>(t) * a.h_idx + 16 * ht + c) * kDI;
         u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
         u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
-        e4m3x16_to_operands(lo, 1.0f, qa[ht][0], qa[ht][1]);
-        e4m3x16_to_operands(hi, 1.0f, qa[ht][2], qa[ht][3]);
+        e4m3x16_to_operands(lo, qa[ht][0], qa[ht][1]);
+        e4m3x16_to_operands(hi, qa[ht][2], qa[ht][3]);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             int h = 16 * ht + 4 * g + i;
-            hs[ht][i] = a.q_scale[static_cast<int64_t>(t) * a.h_idx + h];
-            hw[ht][i] = a.w[static_cast<int64_t>(t) * a.h_idx + h];
+            int64_t o = static_cast<int64_t>(t) * a.h_idx + h;
+            hf[ht][i] = a.w[o] * a.q_scale[o];
         }
     }
 
-    // issue all four sub-tiles' key loads first
-    u32x4 klo[4], khi[4];
-    float ksc[4];
-    int64_t krow[4];
+    // the tile's block-table entries, read once (wave-uniform, scalar loads)
+    const int64_t table_row = static_cast<int64_t>(seq) * a.keys.table_stride;
+    int32_t pbs[kSubTiles];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        int s = s0 + 16 * (w + 4 * j) + c;
-        krow[j] = s < nv ? pool_row(a.keys, seq, s) : -1;
-        if (krow[j] >= 0) {
-            const uint8_t *kp = key_code_ptr(a.keys, krow[j]);
-            klo[j] = *reinterpret_cast<const u32x4 *>(kp + 16 * g);
-            khi[j] = *reinterpret_cast<const u32x4 *>(kp + 64 + 16 * g);
-            ksc[j] = *key_scale_ptr(a.keys, krow[j]);
+    for (int j = 0; j < kSubTiles; j++) {
+        const int64_t lb = (s0 >> 6) + j;
+        pbs[j] = lb < a.keys.table_stride ? a.keys.block_table[table_row + lb] : -1;
+    }
+    auto stage = [&](int j, KeyStage &st) {
+        int s = s0 + 64 * j + 16 * w + c;
+        const int32_t pb = pbs[j];
+        bool ok = s < nv && pb >= 0 && pb < a.keys.n_blocks;
+        if (ok) {
+            int64_t r = static_cast<int64_t>(pb) * kBR + 16 * w + c;
+            const uint8_t *kp = key_code_ptr(a.keys, r);
+            st.lo = *reinterpret_cast<const u32x4 *>(kp + 16 * g);
+            st.hi = *reinterpret_cast<const u32x4 *>(kp + 64 + 16 * g);
+            st.scale = *key_scale_ptr(a.keys, r);
         } else {
-            klo[j] = u32x4{0, 0, 0, 0};
-            khi[j] = u32x4{0, 0, 0, 0};
-            ksc[j] = 0.f;
+            st.lo = u32x4{0, 0, 0, 0};
+            st.hi = u32x4{0, 0, 0, 0};
+            st.scale = -INFINITY;   // absent row: scored -inf
         }
-    }
+    };
+
+    KeyStage ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; j++) stage(j, ring[j]);
 
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        int s = s0 + 16 * (w + 4 * j) + c;
+    for (int j = 0; j < kSubTiles; j++) {
+        KeyStage cur = ring[j % kRing];
+        if (j + kRing < kSubTiles) stage(j + kRing, ring[j % kRing]);
+        const int s = s0 + 64 * j + 16 * w + c;
+        if (s0 + 64 * j >= nv) break;   // wave-uniform: later sub-tiles are all invisible
+
         bf16x8 kb[4];
-        e4m3x16_to_operands(klo[j], 1.0f, kb[0], kb[1]);
-        e4m3x16_to_operands(khi[j], 1.0f, kb[2], kb[3]);
+        e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
+        e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
         f32x4 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) {
@@ -112,15 +144,13 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 #pragma unroll
         for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float v = acc[ht][i] * hs[ht][i] * ksc[j];
-                v = v > 0.f ? v : 0.f;
-                part += hw[ht][i] * v;
-            }
+            for (int i = 0; i < 4; i++) part += hf[ht][i] * fmaxf(acc[ht][i], 0.f);
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
-        if (g == 0 && s < nv)
-            a.scores[static_cast<int64_t>(t) * a.max_slots + s] = krow[j] >= 0 ? part : -INFINITY;
+        if (g == 0 && s < nv) {
+            float v = cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
+            a.scores[static_cast<int64_t>(t) * a.max_slots + s] = v;
+        }
     }
 }
 
@@ -139,9 +169,8 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
 
 namespace {
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkLdsKeys = 32768;   // 128 KB: scores of up to 32768 visible slots
 
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -149,35 +178,39 @@ __device__ __forceinline__ uint32_t order_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t lanes_below() {
-    return (1ull << (threadIdx.x & 63)) - 1ull;
-}
-
-// Block-wide exclusive prefix of per-wave counts; returns this wave's offset
-// and writes the block total to *total.  Uses sh[kTopkWaves].
-__device__ __forceinline__ int wave_offset(int wave_count, int *sh, int *total) {
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh[w] = wave_count;
-    __syncthreads();
-    int off = 0, tot = 0;
+// Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
+__device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int ia = a, ib = b;
 #pragma unroll
-    for (int i = 0; i < kTopkWaves; i++) {
-        int v = sh[i];
-        off += i < w ? v : 0;
-        tot += v;
+    for (int o = 1; o < 64; o <<= 1) {
+        int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
+        if (lane >= o) {
+            ia += va;
+            ib += vb;
+        }
     }
-    *total = tot;
+    if (lane == 63) {
+        sh[w] = ia;
+        sh[kTopkWaves + w] = ib;
+    }
     __syncthreads();
-    return off;
+    int pa = 0, pb = 0;
+    for (int i = 0; i < w; i++) {
+        pa += sh[i];
+        pb += sh[kTopkWaves + i];
+    }
+    a_before = pa + ia - a;
+    b_before = pb + ib - b;
 }
 
 }  // namespace
 
-template <bool LDS>
+// R keys per thread: thread tid owns slots [tid*R, tid*R + R).
+template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ uint32_t keys_lds[LDS ? kTopkLdsKeys : 1];
     __shared__ uint32_t hist[kTopkWaves][256];
-    __shared__ int scan_sh[kTopkWaves];
+    __shared__ int scan_sh[2 * kTopkWaves];
     __shared__ int sel_sh[2];
 
     const int t = blockIdx.x;
@@ -196,31 +229,65 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         return;
     }
 
-    if (LDS)
-        for (int i = tid; i < n; i += kTopkThreads) keys_lds[i] = order_key(sc[i]);
-    auto key_at = [&](int i) -> uint32_t { return LDS ? keys_lds[i] : order_key(sc[i]); };
+    uint32_t key[R];
+    const int base = tid * R;
+#pragma unroll
+    for (int j = 0; j < R; j++) key[j] = base + j < n ? order_key(sc[base + j]) : 0u;
+    // valid keys are never 0: order_key maps every non-NaN float above 0x007FFFFF
 
-    // ---- radix select of the k-th largest key ----
-    uint32_t prefix = 0;
-    int remaining = k;   // how many still to take among keys matching `prefix`
+    // Bits shared by every key need no radix pass: find the common prefix of
+    // the smallest and largest key and start at the first bit that differs.
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < R; j++)
+        if (base + j < n) {
+            kmin = min(kmin, key[j]);
+            kmax = max(kmax, key[j]);
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
+    }
+    if ((tid & 63) == 0) {
+        hist[0][w] = kmin;
+        hist[1][w] = kmax;
+    }
+    __syncthreads();
+    kmin = 0xffffffffu;
+    kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; i++) {
+        kmin = min(kmin, hist[0][i]);
+        kmax = max(kmax, hist[1][i]);
+    }
+    __syncthreads();
+    if (kmin == kmax) {   // every visible score equal: the lowest slots win
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i;
+        return;
+    }
+    int hi = 32 - __clz(kmin ^ kmax);          // bits [0, hi) still to resolve
+    uint32_t prefix = hi == 32 ? 0u : (kmin & (0xffffffffu << hi));
+    int remaining = k;
 #pragma unroll 1
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
+    while (hi > 0) {
+        const int width = hi < 8 ? hi : 8;
+        const int shift = hi - width;
         for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < n; i += kTopkThreads) {
-            uint32_t kk = key_at(i);
-            if ((kk & hi_mask) == prefix) atomicAdd(&hist[w][(kk >> shift) & 255u], 1u);
-        }
+        const uint32_t hi_mask = hi == 32 ? 0u : (0xffffffffu << hi);
+        const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+        for (int j = 0; j < R; j++)
+            if (base + j < n && (key[j] & hi_mask) == prefix)
+                atomicAdd(&hist[w][(key[j] >> shift) & dmask], 1u);
         __syncthreads();
-        // bins from the top: thread b (< 256) owns bin 255 - b
+        // thread b < 256 owns bin 255 - b (bins in descending order)
         int cnt = 0;
         if (tid < 256) {
 #pragma unroll
             for (int ww = 0; ww < kTopkWaves; ww++) cnt += hist[ww][255 - tid];
         }
-        // inclusive scan over tid (bins descending) within waves 0..3
         int incl = cnt;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -241,38 +308,132 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         __syncthreads();
         prefix |= static_cast<uint32_t>(sel_sh[0]) << shift;
         remaining = sel_sh[1];
+        hi = shift;
         __syncthreads();
     }
-    const uint32_t thr = prefix;     // the k-th largest key
-    const int take_eq = remaining;   // keys equal to thr to take, lowest slots first
+    const uint32_t thr = prefix;      // the k-th largest key
+    const int take_eq = remaining;    // keys equal to thr to take, lowest slots first
 
-    // ---- ordered write: slots with key > thr, plus the first take_eq with key == thr ----
-    int eq_before = 0, sel_before = 0;
-    for (int base = 0; base < n; base += kTopkThreads) {
-        int i = base + tid;
-        uint32_t kk = i < n ? key_at(i) : 0u;
-        bool gt = i < n && kk > thr;
-        bool eq = i < n && kk == thr;
-        uint64_t beq = __ballot(eq);
-        int eq_tot;
-        int eq_off = wave_offset(__popcll(beq), scan_sh, &eq_tot);
-        int eq_rank = eq_before + eq_off + __popcll(beq & lanes_below());
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        bool v = base + j < n;
+        n_gt += (v && key[j] > thr) ? 1 : 0;
+        n_eq += (v && key[j] == thr) ? 1 : 0;
+    }
+    int gt_before, eq_before;
+    block_scan2(n_gt, n_eq, scan_sh, gt_before, eq_before);
+    int pos = gt_before + (eq_before < take_eq ? eq_before : take_eq);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        bool v = base + j < n;
+        bool sel = v && (key[j] > thr || (key[j] == thr && eq_rank < take_eq));
+        eq_rank += (v && key[j] == thr) ? 1 : 0;
+        if (sel) out[pos++] = base + j;
+    }
+    for (int i = k_eff + tid; i < k; i += kTopkThreads) out[i] = -1;
+}
+
+
+// Visible lists longer than the register kernel holds (> 65536 slots, e.g. a
+// 1M-token context at ratio 4): the same radix select, re-reading the scores
+// from memory each pass, and an ordered write in 1024-slot rounds.
+__global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
+    __shared__ uint32_t hist[kTopkWaves][256];
+    __shared__ int scan_sh[2 * kTopkWaves];
+    __shared__ int sel_sh[2];
+
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int seq = a.q_seq[t];
+    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
+    n = n < a.max_slots ? n : a.max_slots;
+    const int k = a.k;
+    const int k_eff = n < k ? n : k;
+    int32_t *out = a.idx + static_cast<int64_t>(t) * k;
+    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
+    if (tid == 0) a.len[t] = k_eff;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        return;
+    }
+    uint32_t prefix = 0;
+    int remaining = k;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; pass++) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+        for (int i = tid; i < n; i += kTopkThreads) {
+            uint32_t kk = order_key(sc[i]);
+            if ((kk & hi_mask) == prefix) atomicAdd(&hist[w][(kk >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        int cnt = 0;
+        if (tid < 256)
+            for (int ww = 0; ww < kTopkWaves; ww++) cnt += hist[ww][255 - tid];
+        int incl = cnt;
+        for (int o = 1; o < 64; o <<= 1) {
+            int v = __shfl_up(incl, o, 64);
+            if ((tid & 63) >= o) incl += v;
+        }
+        if (tid < 256 && (tid & 63) == 63) scan_sh[w] = incl;
+        __syncthreads();
+        if (tid < 256) {
+            int before = 0;
+            for (int ww = 0; ww < w; ww++) before += scan_sh[ww];
+            int excl = before + incl - cnt;
+            if (excl < remaining && excl + cnt >= remaining) {
+                sel_sh[0] = 255 - tid;
+                sel_sh[1] = remaining - excl;
+            }
+        }
+        __syncthreads();
+        prefix |= static_cast<uint32_t>(sel_sh[0]) << shift;
+        remaining = sel_sh[1];
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;
+    const int take_eq = remaining;
+    int eq_done = 0, sel_done = 0;
+    for (int b0 = 0; b0 < n; b0 += kTopkThreads) {
+        int i = b0 + tid;
+        uint32_t kk = i < n ? order_key(sc[i]) : 0u;
+        int gt = (i < n && kk > thr) ? 1 : 0;
+        int eq = (i < n && kk == thr) ? 1 : 0;
+        int gt_b, eq_b;
+        block_scan2(gt, eq, scan_sh, gt_b, eq_b);
+        int eq_rank = eq_done + eq_b;
+        int before_sel = sel_done + gt_b + (eq_done + eq_b < take_eq ? eq_b : (take_eq > eq_done ? take_eq - eq_done : 0));
         bool sel = gt || (eq && eq_rank < take_eq);
-        uint64_t bsel = __ballot(sel);
-        int sel_tot;
-        int sel_off = wave_offset(__popcll(bsel), scan_sh, &sel_tot);
-        if (sel) out[sel_before + sel_off + __popcll(bsel & lanes_below())] = i;
-        eq_before += eq_tot;
-        sel_before += sel_tot;
+        if (sel) out[before_sel] = i;
+        // block totals (scan_sh holds per-wave inclusive totals)
+        int tot_gt = 0, tot_eq = 0;
+        for (int ww = 0; ww < kTopkWaves; ww++) {
+            tot_gt += scan_sh[ww];
+            tot_eq += scan_sh[kTopkWaves + ww];
+        }
+        int eq_taken = eq_done + tot_eq < take_eq ? tot_eq : (take_eq > eq_done ? take_eq - eq_done : 0);
+        sel_done += tot_gt + eq_taken;
+        eq_done += tot_eq;
+        __syncthreads();
     }
     for (int i = k_eff + tid; i < k; i += kTopkThreads) out[i] = -1;
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
-    if (a.max_slots <= kTopkLdsKeys)
-        hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTopkThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(topk_kernel<false>, dim3(a.n_q), dim3(kTopkThreads), 0, stream, a);
+    const int per = (a.max_slots + kTopkThreads - 1) / kTopkThreads;
+    dim3 grid(a.n_q), block(kTopkThreads);
+    if (per <= 1) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, stream, a);
+    else if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, stream, a);
+    else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
+    else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
+    else if (per <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);
+    else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, a);
+    else if (per <= 64) hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(topk_long_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

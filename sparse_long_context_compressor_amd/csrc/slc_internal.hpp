@@ -64,20 +64,20 @@ struct AttnArgs {
     float sm_scale_log2;    // sm_scale * log2(e)
     uint16_t *out;
     float *lse;
-    int n_splits;           // workgroups per query along the attended list
-    int chunks_per_split;   // 32-entry chunks each split covers
-    float *part_o;          // [n_q][n_splits][H][512] (n_splits > 1)
+    int n_splits;           // decode: workgroups per (query, head group) along the list
+    int chunks_per_split;   // row chunks each split covers
+    float *part_o;          // [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
 };
-
-constexpr int kAttnChunk = 32;
 
 hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
-hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);
 
-// split plan for decode (host arithmetic only)
-void attention_plan(int n_q, int window, int k, bool decode, int *n_splits, int *chunks_per_split);
+// split plan (host arithmetic only): decode splits each (query, head group)'s
+// list so that about one workgroup per CU runs; prefill never splits.
+void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
+                    int *chunks_per_split);
 
 }  // namespace slc
