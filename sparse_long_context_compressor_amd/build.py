@@ -18,15 +18,18 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source extra flags: the indexer keeps its MFMA accumulators in VGPRs
+# (its epilogue reads every accumulator element with VALU instructions)
+EXTRA_FLAGS = {
+    "index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(HERE, "csrc"), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,6 +39,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + msgs)
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in sources():
+        name = os.path.basename(src)
+        obj = os.path.join(objdir, name.replace(".hip", ".o"))
+        flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+        _run([hipcc, *flags, *EXTRA_FLAGS.get(name, []), *inc, "-c", src, "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

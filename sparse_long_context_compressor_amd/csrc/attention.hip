@@ -44,9 +44,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
         (__attribute__((address_space(3))) i16x4 *)(p));
 }
 
-__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) { return f32x2_to_bf16x2(lo, hi); }
 
 // Physical row of attended entry e of query t (-1: skipped).
 __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int t, int seq, int p, int ns,
@@ -80,28 +78,35 @@ struct RowGather {
 
     __device__ __forceinline__ void load(const AttnArgs &a, const int32_t *src, int e0, int e_end,
                                          int pw, int lane) {
+        // one LDS read brings this wave's RPW row ids; each is then moved to a
+        // scalar register (v_readlane), so row bases are scalar and the loads
+        // use a scalar base plus a per-lane offset
+        const int eb = __builtin_amdgcn_readfirstlane(e0 + pw * RPW);
+        const int my_e = eb + (lane % RPW);
+        const int32_t my_row = my_e < e_end ? src[my_e] : -1;
+        const int window = __builtin_amdgcn_readfirstlane(a.window);
 #pragma unroll
         for (int j = 0; j < RPW; j++) {
-            const int e = e0 + pw * RPW + j;
-            const int32_t row = e < e_end ? src[e] : -1;
-            const uint8_t *pn = kZeroPage + 16 * lane;
-            const float *ps = reinterpret_cast<const float *>(kZeroPage);
-            if (row >= 0) {
-                if (e >= a.window) {
-                    pn = cmp_row_ptr(a.cmp, row) + 8 * lane;   // 16-byte read, low 8 used
-                    ps = cmp_scale_ptr(a.cmp, row) + (lane >> 3);
-                } else {
-                    pn = reinterpret_cast<const uint8_t *>(swa_row_ptr(a.swa, row) + 8 * lane);
-                }
-            }
-            nope[j] = *reinterpret_cast<const u32x4 *>(pn);
-            scl[j] = *ps;
+            const int32_t row = __builtin_amdgcn_readlane(my_row, j);
+            const bool cmp = eb + j >= window;
+            const int64_t blk = row >> 6, r = row & 63;
+            const uint8_t *cbase = reinterpret_cast<const uint8_t *>(a.cmp.base) + blk * SLC_CMP_BLOCK_BYTES;
+            const uint8_t *sbase = reinterpret_cast<const uint8_t *>(a.swa.base) + static_cast<int64_t>(row) * (kD * 2);
+            const uint8_t *base = row < 0 ? kZeroPage : (cmp ? cbase : sbase);
+            const uint32_t noff = (row >= 0 && cmp) ? static_cast<uint32_t>(r * SLC_CMP_ROW_BYTES) + 8u * lane
+                                                    : 16u * lane;   // compressed: 16-byte read, low 8 used
+            const uint32_t soff = (row >= 0 && cmp)
+                                      ? static_cast<uint32_t>(SLC_CMP_SCALE_OFFSET + r * 32) + 4u * (lane >> 3)
+                                      : 0u;
+            nope[j] = *reinterpret_cast<const u32x4 *>(base + noff);
+            scl[j] = *reinterpret_cast<const float *>(base + soff);
         }
 #pragma unroll
         for (int q = 0; q < RPW / 8; q++) {
-            const int e = e0 + pw * RPW + 8 * q + (lane >> 3);
+            const int jr = 8 * q + (lane >> 3);
+            const int e = eb + jr;
             const int part = lane & 7;
-            const int32_t row = e < e_end ? src[e] : -1;
+            const int32_t row = __shfl(my_row, jr, 64);   // lanes read different rows here
             const uint8_t *pr = kZeroPage + 16 * part;
             if (row >= 0)
                 pr = (e >= a.window ? cmp_row_ptr(a.cmp, row) + kDN
@@ -237,13 +242,22 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __syncthreads();
 
     if (producer) {
-        RowGather<kDecRows / 4> gat;
-        const int pw = w - 4;
-        for (int e0 = e_begin; e0 < e_end; e0 += kDecRows) {
-            gat.load(a, src, e0, e_end, pw, lane);
+        // two chunks in flight: chunk c+2 loads while the consumers compute c
+        RowGather<kDecRows / 4> ga, gb;
+        const int pw = __builtin_amdgcn_readfirstlane(w - 4);
+        if (e_begin < e_end) ga.load(a, src, e_begin, e_end, pw, lane);
+        if (e_begin + kDecRows < e_end) gb.load(a, src, e_begin + kDecRows, e_end, pw, lane);
+        for (int e0 = e_begin; e0 < e_end; e0 += 2 * kDecRows) {
             if (e0 != e_begin) __syncthreads();     // consumers are done with the tile
-            gat.store(ktile, a, e0, pw, lane);
+            ga.store(ktile, a, e0, pw, lane);
             __syncthreads();                        // tile ready
+            if (e0 + 2 * kDecRows < e_end) ga.load(a, src, e0 + 2 * kDecRows, e_end, pw, lane);
+            if (e0 + kDecRows < e_end) {
+                __syncthreads();
+                gb.store(ktile, a, e0 + kDecRows, pw, lane);
+                __syncthreads();
+                if (e0 + 3 * kDecRows < e_end) gb.load(a, src, e0 + 3 * kDecRows, e_end, pw, lane);
+            }
         }
         __syncthreads();                            // matches the consumers' last chunk
         // the consumers' four merge-phase barriers
@@ -264,20 +278,48 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         if (e0 != e_begin) __syncthreads();        // previous chunk done (pairs with producers)
         __syncthreads();                            // tile ready
 
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t *kr = ktile + (16 * w + c) * kKPitch + 8 * g;
-#pragma unroll
-        for (int s = 0; s < kD / 32; s++) {
-            bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * s));
-            bf16x8 qv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * s));
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv, sacc, 0, 0, 0);
-        }
-        float x[4], pv[4];
+        // row validity of the lane's four rows (issued before the MFMAs need them)
+        int32_t rv[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            int e = e0 + 16 * w + 4 * g + i;
-            x[i] = (e < e_end && src[e] >= 0) ? sacc[i] * a.sm_scale_log2 : -INFINITY;
+            const int e = e0 + 16 * w + 4 * g + i;
+            rv[i] = e < e_end ? src[e] : -1;
         }
+        // S^T: software-pipelined LDS reads (group i+1 in flight while group i
+        // feeds the MFMAs), two accumulator chains; the order is pinned with
+        // scheduling group barriers so the reads really run ahead
+        const uint16_t *kr = ktile + (16 * w + c) * kKPitch + 8 * g;
+        f32x4 sacc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sacc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int G = 3, NG = kD / 32 / G;   // 6 groups of 3 k-steps
+            bf16x8 ka[2][G], qv[2][G];
+            auto rd = [&](int grp, int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++) {
+                    ka[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * (grp * G + u)));
+                    qv[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * (grp * G + u)));
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
+            };
+            auto mm = [&](int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++) {
+                    if (u & 1) sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qv[b][u], sacc1, 0, 0, 0);
+                    else sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qv[b][u], sacc0, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+            };
+            rd(0, 0);
+#pragma unroll
+            for (int grp = 0; grp < NG; grp++) {
+                if (grp + 1 < NG) rd(grp + 1, (grp + 1) & 1);
+                mm(grp & 1);
+            }
+        }
+        const f32x4 sacc = sacc0 + sacc1;
+        float x[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) x[i] = rv[i] >= 0 ? sacc[i] * a.sm_scale_log2 : -INFINITY;
         const float alpha = softmax_update<4>(x, m_run, l_run, pv);
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -288,11 +330,27 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
                                                      bf16_pair_rne(pv[2], pv[3])});
         const uint16_t *vr = ktile + (16 * w + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
+        {
+            constexpr int G = 4, NG = kDN / 16 / G;   // 8 groups of 4 column tiles
+            i16x4 va[2][G];
+            auto rd = [&](int grp, int b) {
 #pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) {
-            i16x4 va = lds_read_tr16(vr + 16 * ct);
-            o[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4v, va), pb,
-                                                              o[ct], 0, 0, 0);
+                for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (grp * G + u));
+                __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
+            };
+            auto mm = [&](int grp, int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++)
+                    o[grp * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(i16x4v, va[b][u]), pb, o[grp * G + u], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+            };
+            rd(0, 0);
+#pragma unroll
+            for (int grp = 0; grp < NG; grp++) {
+                if (grp + 1 < NG) rd(grp + 1, (grp + 1) & 1);
+                mm(grp, grp & 1);
+            }
         }
     }
     __syncthreads();                                // last chunk done
@@ -406,13 +464,21 @@ void mla_prefill_kernel(AttnArgs a) {
     __syncthreads();
 
     if (w >= NW) {
-        RowGather<kPreRows / 4> gat;
-        const int pw = w - NW;
-        for (int e0 = 0; e0 < E; e0 += kPreRows) {
-            gat.load(a, src, e0, E, pw, lane);
+        RowGather<kPreRows / 4> ga, gb;
+        const int pw = __builtin_amdgcn_readfirstlane(w - NW);
+        if (E > 0) ga.load(a, src, 0, E, pw, lane);
+        if (kPreRows < E) gb.load(a, src, kPreRows, E, pw, lane);
+        for (int e0 = 0; e0 < E; e0 += 2 * kPreRows) {
             if (e0 != 0) __syncthreads();
-            gat.store(ktile, a, e0, pw, lane);
+            ga.store(ktile, a, e0, pw, lane);
             __syncthreads();
+            if (e0 + 2 * kPreRows < E) ga.load(a, src, e0 + 2 * kPreRows, E, pw, lane);
+            if (e0 + kPreRows < E) {
+                __syncthreads();
+                gb.store(ktile, a, e0 + kPreRows, pw, lane);
+                __syncthreads();
+                if (e0 + 3 * kPreRows < E) gb.load(a, src, e0 + 3 * kPreRows, E, pw, lane);
+            }
         }
         return;
     }

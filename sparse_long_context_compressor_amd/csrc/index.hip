@@ -48,12 +48,21 @@ __device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 
 
 constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
 constexpr int kScoreTile = 4 * kSubTiles * 16;      // 1024 slots per workgroup
-constexpr int kRing = 6;                            // sub-tiles in flight per wave
+constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
+
+// ReLU on the bit pattern: non-negative floats compare as non-negative ints,
+// negative ones as negative ints, so one integer max does it (-0 -> +0).
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
 
 struct KeyStage {
     u32x4 lo, hi;
     float scale;
 };
+
+// Base of the zero-size buffer resource an absent block reads through.
+__device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never written
 
 }  // namespace
 
@@ -94,40 +103,26 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 
     // the tile's block-table entries, read once (wave-uniform, scalar loads)
     const int64_t table_row = static_cast<int64_t>(seq) * a.keys.table_stride;
-    int32_t pbs[kSubTiles];
-#pragma unroll
-    for (int j = 0; j < kSubTiles; j++) {
-        const int64_t lb = (s0 >> 6) + j;
-        pbs[j] = lb < a.keys.table_stride ? a.keys.block_table[table_row + lb] : -1;
-    }
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
+    const uint32_t lane_off = static_cast<uint32_t>((16 * w + c) * kDI + 16 * g);
+    const uint32_t scale_off = static_cast<uint32_t>(SLC_KEY_SCALE_OFFSET + 4 * (16 * w + c));
+
+    // sub-tile j reads through a buffer resource on its (wave-uniform) block;
+    // an absent block gets a zero-size resource, whose loads return zeros
     auto stage = [&](int j, KeyStage &st) {
-        int s = s0 + 64 * j + 16 * w + c;
-        const int32_t pb = pbs[j];
-        bool ok = s < nv && pb >= 0 && pb < a.keys.n_blocks;
-        if (ok) {
-            int64_t r = static_cast<int64_t>(pb) * kBR + 16 * w + c;
-            const uint8_t *kp = key_code_ptr(a.keys, r);
-            st.lo = *reinterpret_cast<const u32x4 *>(kp + 16 * g);
-            st.hi = *reinterpret_cast<const u32x4 *>(kp + 64 + 16 * g);
-            st.scale = *key_scale_ptr(a.keys, r);
-        } else {
-            st.lo = u32x4{0, 0, 0, 0};
-            st.hi = u32x4{0, 0, 0, 0};
-            st.scale = -INFINITY;   // absent row: scored -inf
-        }
+        const int64_t lb = (s0 >> 6) + j;
+        const int32_t pb = lb < a.keys.table_stride ? a.keys.block_table[table_row + lb] : -1;
+        const bool ok = pb >= 0 && pb < a.keys.n_blocks;
+        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : kIndexZeroPage;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(bp), 0, ok ? SLC_KEY_BLOCK_BYTES : 0, kBufferWord3);
+        st.lo = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0);
+        st.hi = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 64u, 0, 0);
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, scale_off, 0, 0));
+        st.scale = ok ? sc : -INFINITY;
     };
-
-    KeyStage ring[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; j++) stage(j, ring[j]);
-
-#pragma unroll
-    for (int j = 0; j < kSubTiles; j++) {
-        KeyStage cur = ring[j % kRing];
-        if (j + kRing < kSubTiles) stage(j + kRing, ring[j % kRing]);
+    auto compute = [&](int j, const KeyStage &cur) {
         const int s = s0 + 64 * j + 16 * w + c;
-        if (s0 + 64 * j >= nv) break;   // wave-uniform: later sub-tiles are all invisible
-
         bf16x8 kb[4];
         e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
         e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
@@ -144,13 +139,29 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 #pragma unroll
         for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) part += hf[ht][i] * fmaxf(acc[ht][i], 0.f);
+            for (int i = 0; i < 4; i++) part += hf[ht][i] * relu(acc[ht][i]);
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
-        if (g == 0 && s < nv) {
-            float v = cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
-            a.scores[static_cast<int64_t>(t) * a.max_slots + s] = v;
+        if (g == 0 && s < nv)
+            a.scores[static_cast<int64_t>(t) * a.max_slots + s] =
+                cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
+    };
+
+    // two explicit buffers of kRing sub-tiles: load group q+1 while computing q
+    KeyStage buf0[kRing], buf1[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
+#pragma unroll
+    for (int q = 0; q < kSubTiles / kRing; q++) {
+        KeyStage (&cur)[kRing] = (q & 1) ? buf1 : buf0;
+        KeyStage (&nxt)[kRing] = (q & 1) ? buf0 : buf1;
+        if (q + 1 < kSubTiles / kRing) {
+#pragma unroll
+            for (int j = 0; j < kRing; j++) stage((q + 1) * kRing + j, nxt[j]);
         }
+#pragma unroll
+        for (int j = 0; j < kRing; j++)
+            if (s0 + 64 * (q * kRing + j) < nv) compute(q * kRing + j, cur[j]);   // wave-uniform
     }
 }
 

@@ -16,6 +16,9 @@ constexpr int kDR = SLC_D_ROPE;      // 64
 constexpr int kDI = SLC_D_INDEX;     // 128
 constexpr int kBR = SLC_BLOCK_ROWS;  // 64
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family targets: 32-bit
+// data format, loads beyond num_records return zero.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -30,12 +33,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN): gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
 
 // Two fp32 values whose low 16 mantissa bits are zero (exact bf16 values)
