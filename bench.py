@@ -43,9 +43,16 @@ def parse():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="queries the oracle times")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="queries the oracle times")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration)")
+                    help="also run a plain elementwise copy (y = -x, fp32) of this size, "
+                         "the known-size kernel the HBM byte counters are scaled by")
+    ap.add_argument("--report-stats", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+                    help="summarise a rocprofv3 --stats csv directory into OUT_MD and exit")
+    ap.add_argument("--report-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_STEM"),
+                    help="turn FETCH_SIZE / WRITE_SIZE csv runs into OUT_STEM.json/.md and exit")
+    ap.add_argument("--cmd", action="append", default=[],
+                    help="a command recorded verbatim in a report (repeatable)")
     return ap.parse_args()
 
 
@@ -66,6 +73,93 @@ def traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    name = name.split("(")[0] if not name.startswith("void at::") else name[:60]
+    return name.replace("void ", "").strip()
+
+
+def report_stats(trace_dir: str, out_md: str, cmds):
+    """Kernel-time summary of one rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel time, c4a_decode_64k benchmark (rocprofv3 kernel trace)", "",
+             "Made by:", ""] + [f"    {c}" for c in cmds] + [
+        "", "| kernel | calls | avg us | min us | max us | share of GPU time |",
+        "|---|---:|---:|---:|---:|---:|"]
+    ours = [r for r in rows if "slc::" in r["Name"]]
+    for r in ours:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    rest = sum(float(r["Percentage"]) for r in rows if r not in ours)
+    lines += ["", f"The remaining {rest:.1f}% of GPU time is torch kernels that generate the "
+                  "synthetic inputs before timing starts."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def report_counters(fetch_dir: str, write_dir: str, stem: str, calib_mib: int, cmds):
+    """HBM bytes per index-score launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the kernel, each scaled by the same counter's reading for a
+    plain fp32 elementwise copy that reads and writes calib_mib MiB."""
+    if calib_mib <= 0:
+        raise SystemExit("--calib-copy-mib must give the calibration copy's size")
+
+    def per_dispatch(d, counter, match):
+        vals = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel in {d}")
+        v = sorted(vals.values())
+        return sum(v) / len(v), len(v), v[0], v[-1]
+
+    is_index = lambda n: "index_score_kernel" in n  # noqa: E731
+    is_copy = lambda n: "neg_kernel" in n           # noqa: E731
+    known = calib_mib * 1024.0                      # KiB read = KiB written by the copy
+    f_idx = per_dispatch(fetch_dir, "FETCH_SIZE", is_index)
+    w_idx = per_dispatch(write_dir, "WRITE_SIZE", is_index)
+    f_cp = per_dispatch(fetch_dir, "FETCH_SIZE", is_copy)
+    w_cp = per_dispatch(write_dir, "WRITE_SIZE", is_copy)
+    kf, kw = known / f_cp[0], known / w_cp[0]
+    traffic = (f_idx[0] * kf + w_idx[0] * kw) * 1024.0
+    rec = {"kernel": "index_score_kernel", "workload": "c4a_decode_64k",
+           "fetch_kib_per_dispatch": f_idx[0], "write_kib_per_dispatch": w_idx[0],
+           "dispatches": [f_idx[1], w_idx[1]],
+           "calibration": {"copy_mib": calib_mib, "fetch_kib": f_cp[0], "write_kib": w_cp[0],
+                           "fetch_factor": kf, "write_factor": kw},
+           "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": INDEX_KERNEL_BYTES,
+           "traffic_over_algorithmic": traffic / INDEX_KERNEL_BYTES,
+           "index_hip_sha256_16": kernel_source_hash(), "commands": cmds}
+    json.dump(rec, open(stem + ".json", "w"), indent=1)
+    md = ["# HBM traffic of index_score_kernel, c4a_decode_64k (rocprofv3 counters)", "",
+          "Made by:", ""] + [f"    {c}" for c in cmds] + [
+        "", f"- FETCH_SIZE: {f_idx[0]:.0f} KiB per dispatch (mean of {f_idx[1]}, "
+            f"range {f_idx[2]:.0f}..{f_idx[3]:.0f})",
+        f"- WRITE_SIZE: {w_idx[0]:.0f} KiB per dispatch (mean of {w_idx[1]})",
+        f"- calibration copy of {calib_mib} MiB: FETCH_SIZE {f_cp[0]:.0f} KiB, WRITE_SIZE "
+        f"{w_cp[0]:.0f} KiB -> factors {kf:.4f} (read), {kw:.4f} (write)",
+        f"- scaled HBM traffic per launch: {traffic / 1e6:.2f} MB; algorithmic "
+        f"{INDEX_KERNEL_BYTES / 1e6:.2f} MB; ratio {traffic / INDEX_KERNEL_BYTES:.3f}",
+        f"- index.hip sha256[:16] at the time: {kernel_source_hash()}"]
+    open(stem + ".md", "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def cpu_baseline(n_q: int):
     """The oracle (as it stands) on a bounded sample: n_q sequences of the same
     workload shape, index top-k then attention, on the host's cores."""
@@ -81,12 +175,20 @@ def cpu_baseline(n_q: int):
     dt = time.perf_counter() - t0
     return {"value": n_q / dt, "unit": "queries/s", "cores": int(O.num_threads()),
             "kind": "oracle",
-            "sample": f"{n_q} of the 32 sequences (same per-query shapes: 16384 slots, H_I=64, "
+            "sample": f"{n_q} of the 32 sequences (one query each, same shapes: 16384 slots, H_I=64, "
                       f"k=512, H=64, SWA 128), index top-k + attention, {dt:.2f} s wall"}
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
     args = parse()
+    if args.report_stats:
+        return report_stats(*args.report_stats, args.cmd)
+    if args.report_counters:
+        return report_counters(*args.report_counters, args.calib_copy_mib, args.cmd)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU (the decode path shards by sequence with "
               "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -101,6 +203,7 @@ def main():
     slc.lib()
     reps = [I.c4a_decode_64k(seed=100 + r, device=dev) for r in range(args.replicas)]
     torch.cuda.synchronize()
+    log(f"{args.replicas} input replicas resident")
 
     scores = torch.empty((B, SLOTS), dtype=torch.float32, device=dev)
     idx = torch.empty((B, K), dtype=torch.int32, device=dev)
@@ -163,6 +266,7 @@ def main():
             graph[i % len(graph)].replay()
         torch.cuda.synchronize()
 
+    log("warm-up done")
     # ---- headline: K whole steps, nothing else on the stream ----
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -186,12 +290,12 @@ def main():
     attn_ms = timed(decode, args.steps)
 
     if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a = torch.ones((args.calib_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
 
+    log(f"timed: {ms_step * 1e3:.1f} us/step")
     achieved = INDEX_KERNEL_BYTES / (idx_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -220,6 +324,7 @@ def main():
                      "traffic": traffic_from_profile(), "algorithmic_bytes": INDEX_KERNEL_BYTES},
     }
     if not args.no_cpu_baseline:
+        log("timing the oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample)
     print(json.dumps(rec), flush=True)
 

@@ -54,6 +54,11 @@
  *   KEY pool  codes: 64 x 128 e4m3, then scales: 64 x fp32        8448 B
  * (the pages store row data first and the block's scales after all its rows;
  * this library keeps that order with its own row widths).
+ * A pool holds at most 2^24 blocks (physical row ids fit in int32); larger
+ * n_blocks is SLC_ERR_INVALID_ARG.  base must be 16-byte aligned.
+ * CMP scales are powers of two (slc_compress writes nothing else): code *
+ * scale is then exact in bf16.  A pool filled by other means with other
+ * positive scales is dequantised with one bf16 rounding of code * scale.
  */
 #ifndef SLC_H
 #define SLC_H
@@ -154,7 +159,9 @@ slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int m
  * over the fp8 index query heads j < h_idx, for the slots s visible to query
  * t: s < n_vis(t) = min(n_slots[q_seq[t]], (q_pos[t]+1) / ratio)
  * ("From MLA to CSA + HCA" 5.1: position i sees slot j iff i >= r*j + r - 1).
- * fp8 products accumulate in fp32.
+ * fp8 products accumulate in fp32.  q_scale and the key scales must be
+ * positive: the kernel applies them outside the ReLU
+ * (ReLU(a*b*x) = a*b*ReLU(x) for a, b > 0).
  *
  *   n_q          queries;  h_idx  indexer heads (multiple of 16, <= 64)
  *   q_fp8        device e4m3 [n_q][h_idx][128]
