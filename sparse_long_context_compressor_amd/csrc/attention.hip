@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kKPitch = kD + 8;        // bf16 per LDS row: 1168 B, spreads banks
 constexpr int kMaxEntries = SLC_MAX_WINDOW + SLC_MAX_TOPK;
+constexpr int kDecMaxEntries = 1024;   // list entries one decode workgroup resolves
 
 typedef short i16x4v __attribute__((ext_vector_type(4)));
 
@@ -76,14 +77,15 @@ struct RowGather {
     float scl[RPW];         // compressed: the lane's 64-dim block scale
     u32x4 rope[RPW / 8];
 
-    __device__ __forceinline__ void load(const AttnArgs &a, const int32_t *src, int e0, int e_end,
-                                         int pw, int lane) {
+    // src holds the resolved rows of entries ebase, ebase+1, ...
+    __device__ __forceinline__ void load(const AttnArgs &a, const int32_t *src, int ebase, int e0,
+                                         int e_end, int pw, int lane) {
         // one LDS read brings this wave's RPW row ids; each is then moved to a
         // scalar register (v_readlane), so row bases are scalar and the loads
         // use a scalar base plus a per-lane offset
         const int eb = __builtin_amdgcn_readfirstlane(e0 + pw * RPW);
         const int my_e = eb + (lane % RPW);
-        const int32_t my_row = my_e < e_end ? src[my_e] : -1;
+        const int32_t my_row = my_e < e_end ? src[my_e - ebase] : -1;
         const int window = __builtin_amdgcn_readfirstlane(a.window);
 #pragma unroll
         for (int j = 0; j < RPW; j++) {
@@ -155,32 +157,38 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int t, int h, int g, b
 
 // Online-softmax update for one head per lane.  x: this lane's logits (log2
 // domain, -inf for skipped rows); the row set spans the lane's x and the
-// same head's lanes in the other three 16-lane groups.  Returns p = 2^(x-m).
+// same head's lanes in the other three 16-lane groups.  Writes p = 2^(x-m).
+// The reference point m moves only when a logit exceeds it by more than
+// kLazyLog2 (p then stays below 2^kLazyLog2, harmless in bf16 / fp32), so
+// the O accumulators are rescaled rarely; numerator and denominator share m,
+// which keeps the result exact in any case.  Returns the rescale factor.
+constexpr float kLazyLog2 = 8.0f;
+
 template <int N>
 __device__ __forceinline__ float softmax_update(float (&x)[N], float &m_run, float &l_run,
                                                 float (&p)[N]) {
     float cmax = x[0];
 #pragma unroll
     for (int i = 1; i < N; i++) cmax = fmaxf(cmax, x[i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    float alpha = 1.f, psum = 0.f;
-    if (m_new == -INFINITY) {
+    cmax = xor32_max(xor16_max(cmax));
+    float alpha = 1.f;
+    if (cmax > m_run + kLazyLog2) {      // also taken when m_run = -inf and cmax is finite
+        alpha = exp2f(m_run - cmax);
+        m_run = cmax;
+    }
+    float psum = 0.f;
+    if (m_run == -INFINITY) {
 #pragma unroll
         for (int i = 0; i < N; i++) p[i] = 0.f;
     } else {
-        alpha = exp2f(m_run - m_new);
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            p[i] = exp2f(x[i] - m_new);
+            p[i] = exp2f(x[i] - m_run);
             psum += p[i];
         }
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = xor32_sum(xor16_sum(psum));
     l_run = l_run * alpha + psum;
-    m_run = m_new;
     return alpha;
 }
 
@@ -198,73 +206,76 @@ __device__ __forceinline__ void store_out(const AttnArgs &a, int t, int h, int g
             l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
-constexpr int kDecRows = 64;   // rows per decode chunk (16 per wave)
+constexpr int kDecRows = 64;   // rows per decode chunk (16 per consumer wave)
 constexpr int kPreRows = 32;   // rows per prefill chunk
 
 }  // namespace
 
 // ------------------------------------------------------------------ decode
-// 512 threads: waves 0..3 compute (wave w: rows 16w..16w+15 of each 64-row
-// chunk, the group's 16 heads), waves 4..7 gather the next chunk meanwhile.
+// One workgroup per (query, block of 16*NG heads, list split); 512 threads.
+// Waves 4..7 gather 64-row chunks into two LDS tiles (chunk c+1 is stored
+// and chunk c+2 is in flight while the consumers compute chunk c; one barrier
+// per chunk).  Waves 0..3 compute: with NG = 1 each takes 16 rows of every
+// chunk for the block's 16 heads; with NG = 2 wave w takes head group w & 1
+// and rows 32*(w >> 1) .. +31, so every gathered row serves 32 heads (half
+// the row traffic of 16-head blocks).  The consumers then merge their
+// softmax states through LDS.
+template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ktile[kDecRows * kKPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t qtile[16 * kKPitch];   // the group's 16 heads
-    __shared__ int32_t src[kMaxEntries];
+    constexpr int RW = 16 * NG;                      // rows per consumer wave per chunk
+    __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
+    __shared__ int32_t src[kDecMaxEntries];
     __shared__ float st_m[4][16], st_l[4][16];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const bool producer = w >= 4;
-    const int HG = a.n_heads / 16, S = a.n_splits;
-    // blocks with equal blockIdx % 8 run on one XCD: give all (head group,
-    // split) blocks of a query the same residue
-    const int per_group = 8 * HG * S;
+    const int HB = a.n_heads / (16 * NG), S = a.n_splits;
+    // blocks with equal blockIdx % 8 run on one XCD: give all (head block,
+    // split) blocks of a query the same residue, so they share its L2
+    const int per_group = 8 * HB * S;
     const int grp = blockIdx.x / per_group, rem = blockIdx.x % per_group;
     const int t = 8 * grp + (rem & 7);
-    const int hg = (rem >> 3) % HG, split = (rem >> 3) / HG;
+    const int hb = (rem >> 3) % HB, split = (rem >> 3) / HB;
     if (t >= a.n_q) return;
+
+    const int hgw = NG == 2 ? (w & 1) : 0;
+    const int h = 16 * (NG * hb + hgw) + c;
+    const int row0 = NG == 2 ? 32 * ((w >> 1) & 1) : 16 * (w & 3);   // first chunk row of this wave
+    bf16x8 qb[kD / 32];
+    if (!producer) load_q(a, t, h, g, qb);   // issued first: depends on t only
 
     const int seq = a.q_seq[t], p = a.q_pos[t];
     const int E = a.window + a.k;
     const int ns = a.k > 0 ? a.n_slots[seq] : 0;
-    const int e_begin = split * a.chunks_per_split * kDecRows;
-    int e_end = e_begin + a.chunks_per_split * kDecRows;
+    const int e_begin = split * a.rows_per_split;
+    int e_end = e_begin + a.rows_per_split;
     e_end = e_end < E ? e_end : E;
-    const int h = 16 * hg + c;
+    const int nchunks = e_end > e_begin ? (e_end - e_begin + kDecRows - 1) / kDecRows : 0;
 
-    for (int e = e_begin + tid; e < e_end; e += 512) src[e] = resolve_entry(a, t, seq, p, ns, e);
-    {
-        const u32x4 *qg = reinterpret_cast<const u32x4 *>(
-            a.q + (static_cast<int64_t>(t) * a.n_heads + 16 * hg) * kD);
-        for (int i = tid; i < 16 * kD / 8; i += 512)
-            *reinterpret_cast<u32x4 *>(qtile + (i / (kD / 8)) * kKPitch + 8 * (i % (kD / 8))) = qg[i];
-    }
+    for (int e = e_begin + tid; e < e_end; e += 512) src[e - e_begin] = resolve_entry(a, t, seq, p, ns, e);
     __syncthreads();
 
+    constexpr int kMergeBarriers = NG == 2 ? 2 : 4;
     if (producer) {
-        // two chunks in flight: chunk c+2 loads while the consumers compute c
         RowGather<kDecRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - 4);
-        if (e_begin < e_end) ga.load(a, src, e_begin, e_end, pw, lane);
-        if (e_begin + kDecRows < e_end) gb.load(a, src, e_begin + kDecRows, e_end, pw, lane);
-        for (int e0 = e_begin; e0 < e_end; e0 += 2 * kDecRows) {
-            if (e0 != e_begin) __syncthreads();     // consumers are done with the tile
-            ga.store(ktile, a, e0, pw, lane);
-            __syncthreads();                        // tile ready
-            if (e0 + 2 * kDecRows < e_end) ga.load(a, src, e0 + 2 * kDecRows, e_end, pw, lane);
-            if (e0 + kDecRows < e_end) {
-                __syncthreads();
-                gb.store(ktile, a, e0 + kDecRows, pw, lane);
-                __syncthreads();
-                if (e0 + 3 * kDecRows < e_end) gb.load(a, src, e0 + 3 * kDecRows, e_end, pw, lane);
+        if (nchunks > 0) ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
+        if (nchunks > 1) gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
+        for (int ci = 0; ci < nchunks; ci += 2) {
+            const int e0 = e_begin + ci * kDecRows;
+            ga.store(ktile[0], a, e0, pw, lane);
+            __syncthreads();                            // chunk ci ready in tile 0
+            if (ci + 2 < nchunks) ga.load(a, src, e_begin, e0 + 2 * kDecRows, e_end, pw, lane);
+            if (ci + 1 < nchunks) {
+                // tile 1 last held chunk ci-1, whose consumers passed the barrier above
+                gb.store(ktile[1], a, e0 + kDecRows, pw, lane);
+                __syncthreads();                        // chunk ci+1 ready in tile 1
+                if (ci + 3 < nchunks) gb.load(a, src, e_begin, e0 + 3 * kDecRows, e_end, pw, lane);
             }
         }
-        __syncthreads();                            // matches the consumers' last chunk
-        // the consumers' four merge-phase barriers
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kMergeBarriers; i++) __syncthreads();   // the consumers' merge
         return;
     }
 
@@ -272,128 +283,187 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    const uint16_t *qr = qtile + c * kKPitch + 8 * g;
 
-    for (int e0 = e_begin; e0 < e_end; e0 += kDecRows) {
-        if (e0 != e_begin) __syncthreads();        // previous chunk done (pairs with producers)
-        __syncthreads();                            // tile ready
+    for (int ci = 0; ci < nchunks; ci++) {
+        __syncthreads();                                // chunk ci is in tile ci & 1
+        const uint16_t *tile = ktile[ci & 1];
+        const int e0 = e_begin + ci * kDecRows + row0;
 
-        // row validity of the lane's four rows (issued before the MFMAs need them)
-        int32_t rv[4];
+        // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need them)
+        int32_t rv[4 * NG];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int e = e0 + 16 * w + 4 * g + i;
-            rv[i] = e < e_end ? src[e] : -1;
-        }
-        // S^T: software-pipelined LDS reads (group i+1 in flight while group i
-        // feeds the MFMAs), two accumulator chains; the order is pinned with
-        // scheduling group barriers so the reads really run ahead
-        const uint16_t *kr = ktile + (16 * w + c) * kKPitch + 8 * g;
-        f32x4 sacc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sacc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-            constexpr int G = 3, NG = kD / 32 / G;   // 6 groups of 3 k-steps
-            bf16x8 ka[2][G], qv[2][G];
-            auto rd = [&](int grp, int b) {
+        for (int rt = 0; rt < NG; rt++)
 #pragma unroll
-                for (int u = 0; u < G; u++) {
-                    ka[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * (grp * G + u)));
-                    qv[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * (grp * G + u)));
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
+            for (int i = 0; i < 4; i++) {
+                const int e = e0 + 16 * rt + 4 * g + i;
+                rv[4 * rt + i] = e < e_end ? src[e - e_begin] : -1;
+            }
+        // S^T per 16-row tile: software-pipelined LDS reads (group i+1 in
+        // flight while group i feeds the MFMAs), two accumulator chains; the
+        // order is pinned with scheduling group barriers
+        f32x4 sacc[NG];
+#pragma unroll
+        for (int rt = 0; rt < NG; rt++) {
+            const uint16_t *kr = tile + (row0 + 16 * rt + c) * kKPitch + 8 * g;
+            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+            constexpr int G = 3, NGR = kD / 32 / G;   // 6 groups of 3 k-steps
+            bf16x8 ka[2][G];
+            auto rd = [&](int gi, int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++)
+                    ka[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * (gi * G + u)));
+                __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
             };
-            auto mm = [&](int b) {
+            auto mm = [&](int gi, int b) {
 #pragma unroll
                 for (int u = 0; u < G; u++) {
-                    if (u & 1) sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qv[b][u], sacc1, 0, 0, 0);
-                    else sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qv[b][u], sacc0, 0, 0, 0);
+                    if (u & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s1, 0, 0, 0);
+                    else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s0, 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
             };
             rd(0, 0);
 #pragma unroll
-            for (int grp = 0; grp < NG; grp++) {
-                if (grp + 1 < NG) rd(grp + 1, (grp + 1) & 1);
-                mm(grp & 1);
+            for (int gi = 0; gi < NGR; gi++) {
+                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
+                mm(gi, gi & 1);
             }
+            sacc[rt] = s0 + s1;
         }
-        const f32x4 sacc = sacc0 + sacc1;
-        float x[4], pv[4];
+        float x[4 * NG], pv[4 * NG];
 #pragma unroll
-        for (int i = 0; i < 4; i++) x[i] = rv[i] >= 0 ? sacc[i] * a.sm_scale_log2 : -INFINITY;
-        const float alpha = softmax_update<4>(x, m_run, l_run, pv);
+        for (int rt = 0; rt < NG; rt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                x[4 * rt + i] = rv[4 * rt + i] >= 0 ? sacc[rt][i] * a.sm_scale_log2 : -INFINITY;
+        const float alpha = softmax_update<4 * NG>(x, m_run, l_run, pv);
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
             for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
         }
 
-        // O^T += V^T . P^T over the wave's 16 rows (k = 16: rows 16w + 4g + 0..3)
-        i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
-                                                     bf16_pair_rne(pv[2], pv[3])});
-        const uint16_t *vr = ktile + (16 * w + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
-        {
-            constexpr int G = 4, NG = kDN / 16 / G;   // 8 groups of 4 column tiles
+        // O^T += V^T . P^T over the wave's rows; the k order (rows 4g+i, then
+        // 16+4g+i) is the score accumulators' lane order
+        const uint16_t *vr = tile + (row0 + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
+        if constexpr (NG == 1) {
+            i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
+                                                         bf16_pair_rne(pv[2], pv[3])});
+            constexpr int G = 4, NGR = kDN / 16 / G;   // 8 groups of 4 column tiles
             i16x4 va[2][G];
-            auto rd = [&](int grp, int b) {
+            auto rd = [&](int gi, int b) {
 #pragma unroll
-                for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (grp * G + u));
+                for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
                 __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
             };
-            auto mm = [&](int grp, int b) {
+            auto mm = [&](int gi, int b) {
 #pragma unroll
                 for (int u = 0; u < G; u++)
-                    o[grp * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(i16x4v, va[b][u]), pb, o[grp * G + u], 0, 0, 0);
+                    o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(i16x4v, va[b][u]), pb, o[gi * G + u], 0, 0, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
             };
             rd(0, 0);
 #pragma unroll
-            for (int grp = 0; grp < NG; grp++) {
-                if (grp + 1 < NG) rd(grp + 1, (grp + 1) & 1);
-                mm(grp, grp & 1);
+            for (int gi = 0; gi < NGR; gi++) {
+                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
+                mm(gi, gi & 1);
+            }
+        } else {
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
+                              bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
+            const uint16_t *vr2 = vr + 16 * kKPitch;
+            constexpr int G = 4, NGR = kDN / 16 / G;
+            i16x4 va[2][G], vb[2][G];
+            auto rd = [&](int gi, int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++) {
+                    va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
+                    vb[b][u] = lds_read_tr16(vr2 + 16 * (gi * G + u));
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
+            };
+            auto mm = [&](int gi, int b) {
+#pragma unroll
+                for (int u = 0; u < G; u++) {
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, va[b][u]), h2 = __builtin_bit_cast(u32x2, vb[b][u]);
+                    const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                    o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, o[gi * G + u], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+            };
+            rd(0, 0);
+#pragma unroll
+            for (int gi = 0; gi < NGR; gi++) {
+                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
+                mm(gi, gi & 1);
             }
         }
     }
-    __syncthreads();                                // last chunk done
 
-    // ---- merge the four waves' softmax states (same 16 heads, disjoint rows) ----
+    // ---- merge the consumers' softmax states (same heads, disjoint rows) ----
     if (g == 0) {
         st_m[w][c] = m_run;
         st_l[w][c] = l_run;
     }
-    __syncthreads();
-    float M = -INFINITY;
+    __syncthreads();                                // every wave is past its last chunk
+    f32x4 *xo = reinterpret_cast<f32x4 *>(&ktile[0][0]);   // the tiles are free now
+    float M = -INFINITY, L = 0.f, my_scale = 0.f;
+    if constexpr (NG == 2) {
+        // waves w and w ^ 2 hold the two row halves of head group w & 1
 #pragma unroll
-    for (int ww = 0; ww < 4; ww++)
-        if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
-    float L = 0.f, my_scale = 0.f;
+        for (int k2 = 0; k2 < 2; k2++) {
+            const int ww = hgw + 2 * k2;
+            if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
+        }
 #pragma unroll
-    for (int ww = 0; ww < 4; ww++) {
-        float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
-        L += st_l[ww][c] * sc;
-        if (ww == w) my_scale = sc;
+        for (int k2 = 0; k2 < 2; k2++) {
+            const int ww = hgw + 2 * k2;
+            const float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
+            L += st_l[ww][c] * sc;
+            if (ww == w) my_scale = sc;
+        }
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
+        if (w >= 2) {
+#pragma unroll
+            for (int ct = 0; ct < kDN / 16; ct++) xo[(hgw * (kDN / 16) + ct) * 64 + lane] = o[ct];
+        }
+        __syncthreads();
+        if (w >= 2) return;
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(hgw * (kDN / 16) + ct) * 64 + lane];
+    } else {
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++)
+            if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
+            L += st_l[ww][c] * sc;
+            if (ww == w) my_scale = sc;
+        }
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
+        if (w >= 2) {
+#pragma unroll
+            for (int ct = 0; ct < kDN / 16; ct++) xo[((w - 2) * (kDN / 16) + ct) * 64 + lane] = o[ct];
+        }
+        __syncthreads();
+        if (w < 2) {
+#pragma unroll
+            for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(w * (kDN / 16) + ct) * 64 + lane];
+        }
+        __syncthreads();
+        if (w == 1) {
+#pragma unroll
+            for (int ct = 0; ct < kDN / 16; ct++) xo[ct * 64 + lane] = o[ct];
+        }
+        __syncthreads();
+        if (w != 0) return;
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
     }
-#pragma unroll
-    for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
-    // O exchange through the (now free) tile: [ct][lane] float4 per wave, 32 KB
-    f32x4 *xo = reinterpret_cast<f32x4 *>(ktile);
-    if (w >= 2) {
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) xo[((w - 2) * (kDN / 16) + ct) * 64 + lane] = o[ct];
-    }
-    __syncthreads();
-    if (w < 2) {
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(w * (kDN / 16) + ct) * 64 + lane];
-    }
-    __syncthreads();
-    if (w == 1) {
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) xo[ct * 64 + lane] = o[ct];
-    }
-    __syncthreads();
-    if (w != 0) return;
-#pragma unroll
-    for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
 
     if (S == 1) {
         store_out(a, t, h, g, o, M, L);
@@ -466,18 +536,18 @@ void mla_prefill_kernel(AttnArgs a) {
     if (w >= NW) {
         RowGather<kPreRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - NW);
-        if (E > 0) ga.load(a, src, 0, E, pw, lane);
-        if (kPreRows < E) gb.load(a, src, kPreRows, E, pw, lane);
+        if (E > 0) ga.load(a, src, 0, 0, E, pw, lane);
+        if (kPreRows < E) gb.load(a, src, 0, kPreRows, E, pw, lane);
         for (int e0 = 0; e0 < E; e0 += 2 * kPreRows) {
             if (e0 != 0) __syncthreads();
             ga.store(ktile, a, e0, pw, lane);
             __syncthreads();
-            if (e0 + 2 * kPreRows < E) ga.load(a, src, e0 + 2 * kPreRows, E, pw, lane);
+            if (e0 + 2 * kPreRows < E) ga.load(a, src, 0, e0 + 2 * kPreRows, E, pw, lane);
             if (e0 + kPreRows < E) {
                 __syncthreads();
                 gb.store(ktile, a, e0 + kPreRows, pw, lane);
                 __syncthreads();
-                if (e0 + 3 * kPreRows < E) gb.load(a, src, e0 + 3 * kPreRows, E, pw, lane);
+                if (e0 + 3 * kPreRows < E) gb.load(a, src, 0, e0 + 3 * kPreRows, E, pw, lane);
             }
         }
         return;
@@ -538,30 +608,38 @@ void mla_prefill_kernel(AttnArgs a) {
     store_out(a, t, h, g, o, m_run, l_run);
 }
 
+int decode_groups(int n_heads) { return n_heads % 32 == 0 ? 2 : 1; }
+
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
-                    int *chunks_per_split) {
+                    int *rows_per_split) {
     const int entries = window + k;
-    const int rows = decode ? kDecRows : kPreRows;
-    int chunks = (entries + rows - 1) / rows;
-    if (chunks < 1) chunks = 1;
-    int splits = 1;
-    if (decode) {
-        const int groups = (n_q > 0 ? n_q : 1) * (n_heads / 16);
-        splits = (256 + groups - 1) / groups;   // about one workgroup per CU
-        if (splits > chunks) splits = chunks;
-        if (splits < 1) splits = 1;
+    if (!decode) {
+        *n_splits = 1;
+        *rows_per_split = entries;
+        return;
     }
-    int cps = (chunks + splits - 1) / splits;
-    *chunks_per_split = cps;
-    *n_splits = (chunks + cps - 1) / cps;
+    // split the list in 32-row units so that about one workgroup per CU runs,
+    // and no workgroup resolves more than kDecMaxEntries entries
+    const int blocks = (n_q > 0 ? n_q : 1) * (n_heads / (16 * decode_groups(n_heads)));
+    const int units = entries > 0 ? (entries + 31) / 32 : 1;
+    int splits = (256 + blocks - 1) / blocks;
+    if (splits > units) splits = units;
+    const int min_splits = (entries + kDecMaxEntries - 1) / kDecMaxEntries;
+    if (splits < min_splits) splits = min_splits;
+    if (splits < 1) splits = 1;
+    int per = (units + splits - 1) / splits;
+    while (per * 32 > kDecMaxEntries) per--;     // never taken (min_splits), kept as a bound
+    *rows_per_split = per * 32;
+    *n_splits = (units + per - 1) / per;
 }
 
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) {
     if (decode) {
-        const int HG = a.n_heads / 16;
+        const int ng = decode_groups(a.n_heads);
         const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
-        dim3 grid(groups * 8u * HG * a.n_splits);
-        hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(512), 0, stream, a);
+        dim3 grid(groups * 8u * (a.n_heads / (16 * ng)) * a.n_splits);
+        if (ng == 2) hipLaunchKernelGGL(mla_decode_kernel<2>, grid, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL(mla_decode_kernel<1>, grid, dim3(512), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.n_splits == 1) return e;
         const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / 4);

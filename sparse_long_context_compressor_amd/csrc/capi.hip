@@ -229,7 +229,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     a.out = out;
     a.lse = lse;
     a.n_splits = splits;
-    a.chunks_per_split = cps;
+    a.rows_per_split = cps;
     if (splits > 1) {
         size_t per = static_cast<size_t>(n_q) * splits * n_heads;
         a.part_o = static_cast<float *>(workspace);

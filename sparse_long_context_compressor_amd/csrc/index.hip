@@ -77,13 +77,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const int seq = a.q_seq[t];
-    int nv = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    nv = nv < a.max_slots ? nv : a.max_slots;
     const int s0 = blockIdx.y * kScoreTile;
-    if (s0 >= nv) return;
 
-    // ---- query operands and per-head factors ----
+    // ---- query operands and per-head factors (they depend on t only) ----
     bf16x8 qa[HT][4];
     float hf[HT][4];
 #pragma unroll
@@ -101,8 +97,20 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
         }
     }
 
-    // the tile's block-table entries, read once (wave-uniform, scalar loads)
+    // the tile's 16 block-table entries in one load (lane j % 16 takes entry
+    // j); each sub-tile then moves its entry to a scalar register, so no key
+    // load waits on a table lookup of its own
+    const int seq = a.q_seq[t];
     const int64_t table_row = static_cast<int64_t>(seq) * a.keys.table_stride;
+    int32_t my_pb = -1;
+    {
+        const int64_t lb = (s0 >> 6) + (lane & 15);
+        if (lb < a.keys.table_stride) my_pb = a.keys.block_table[table_row + lb];
+    }
+    int nv = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
+    nv = nv < a.max_slots ? nv : a.max_slots;
+    if (s0 >= nv) return;
+
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
     const uint32_t lane_off = static_cast<uint32_t>((16 * w + c) * kDI + 16 * g);
     const uint32_t scale_off = static_cast<uint32_t>(SLC_KEY_SCALE_OFFSET + 4 * (16 * w + c));
@@ -110,8 +118,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     // sub-tile j reads through a buffer resource on its (wave-uniform) block;
     // an absent block gets a zero-size resource, whose loads return zeros
     auto stage = [&](int j, KeyStage &st) {
-        const int64_t lb = (s0 >> 6) + j;
-        const int32_t pb = lb < a.keys.table_stride ? a.keys.block_table[table_row + lb] : -1;
+        const int32_t pb = __builtin_amdgcn_readlane(my_pb, j);
         const bool ok = pb >= 0 && pb < a.keys.n_blocks;
         const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : kIndexZeroPage;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -217,22 +224,52 @@ __device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before
 
 }  // namespace
 
-// R keys per thread: thread tid owns slots [tid*R, tid*R + R).
+// Lanes below this one in the wave whose predicate is set.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+}
+
+constexpr int kHistBits = 11;                 // first histogram: 2048 bins
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistCopies = 4;                // waves w, w+4, ... share copy w % 4
+constexpr int kRankCap = 256;                 // threshold-bin candidates ranked directly
+
+// R keys per thread.  Wave w owns slots [64Rw, 64R(w+1)); lane l holds slots
+// 64Rw + 64j + l (j < R), so each of its R loads is one coalesced 256-byte
+// row of scores and the wave's slots run in (j, lane) order.
+//
+// Threshold search: after the common-prefix skip, one histogram of the next
+// 11 key bits finds the bin holding the k-th largest key.  Its candidates
+// (usually a few dozen) are ranked exactly against each other (key
+// descending, slot ascending), which yields the k-th key and how many keys
+// equal to it are taken.  A crowded bin falls back to 8-bit radix passes over
+// the bits below it.  The ordered write then counts, with wave ballots,
+// the selected keys at lower slots.
 template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[kTopkWaves][256];
-    __shared__ int scan_sh[2 * kTopkWaves];
-    __shared__ int sel_sh[2];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB, reused below
+    __shared__ int red[2 * kTopkWaves];
+    __shared__ int sh[8];
 
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
+    const int wbase = w * 64 * R;
+    // the score loads depend on the query index only: issue them before the
+    // visible count (two dependent loads away) is known, mask afterwards
+    float sv[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const int s = wbase + 64 * j + lane;
+        sv[j] = s < a.max_slots ? sc[s] : 0.f;
+    }
     const int seq = a.q_seq[t];
     int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
     n = n < a.max_slots ? n : a.max_slots;
     const int k = a.k;
     const int k_eff = n < k ? n : k;
     int32_t *out = a.idx + static_cast<int64_t>(t) * k;
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
     if (tid == 0) a.len[t] = k_eff;
 
     if (n <= k) {   // everything visible is selected
@@ -241,17 +278,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
 
     uint32_t key[R];
-    const int base = tid * R;
 #pragma unroll
-    for (int j = 0; j < R; j++) key[j] = base + j < n ? order_key(sc[base + j]) : 0u;
+    for (int j = 0; j < R; j++) key[j] = wbase + 64 * j + lane < n ? order_key(sv[j]) : 0u;
     // valid keys are never 0: order_key maps every non-NaN float above 0x007FFFFF
 
-    // Bits shared by every key need no radix pass: find the common prefix of
-    // the smallest and largest key and start at the first bit that differs.
+    for (int i = tid; i < kHistCopies * kHistBins; i += kTopkThreads) hist[i] = 0u;
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < R; j++)
-        if (base + j < n) {
+        if (wbase + 64 * j + lane < n) {
             kmin = min(kmin, key[j]);
             kmax = max(kmax, key[j]);
         }
@@ -260,90 +295,193 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
         kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
     }
-    if ((tid & 63) == 0) {
-        hist[0][w] = kmin;
-        hist[1][w] = kmax;
+    if (lane == 0) {
+        red[w] = static_cast<int>(kmin);
+        red[kTopkWaves + w] = static_cast<int>(kmax);
     }
     __syncthreads();
     kmin = 0xffffffffu;
     kmax = 0u;
 #pragma unroll
     for (int i = 0; i < kTopkWaves; i++) {
-        kmin = min(kmin, hist[0][i]);
-        kmax = max(kmax, hist[1][i]);
+        kmin = min(kmin, static_cast<uint32_t>(red[i]));
+        kmax = max(kmax, static_cast<uint32_t>(red[kTopkWaves + i]));
     }
-    __syncthreads();
     if (kmin == kmax) {   // every visible score equal: the lowest slots win
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i;
         return;
     }
-    int hi = 32 - __clz(kmin ^ kmax);          // bits [0, hi) still to resolve
-    uint32_t prefix = hi == 32 ? 0u : (kmin & (0xffffffffu << hi));
-    int remaining = k;
-#pragma unroll 1
-    while (hi > 0) {
-        const int width = hi < 8 ? hi : 8;
-        const int shift = hi - width;
-        for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        const uint32_t hi_mask = hi == 32 ? 0u : (0xffffffffu << hi);
-        const uint32_t dmask = (1u << width) - 1u;
+    const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
+    const int shift = hi > kHistBits ? hi - kHistBits : 0;
+    const uint32_t bin_mask = kHistBins - 1;
 #pragma unroll
-        for (int j = 0; j < R; j++)
-            if (base + j < n && (key[j] & hi_mask) == prefix)
-                atomicAdd(&hist[w][(key[j] >> shift) & dmask], 1u);
-        __syncthreads();
-        // thread b < 256 owns bin 255 - b (bins in descending order)
-        int cnt = 0;
-        if (tid < 256) {
+    for (int j = 0; j < R; j++)
+        if (wbase + 64 * j + lane < n)
+            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] >> shift) & bin_mask)], 1u);
+    __syncthreads();
+
+    // thread i owns bins 2047-2i (c0) and 2046-2i (c1): descending key order
+    int c0 = 0, c1 = 0;
 #pragma unroll
-            for (int ww = 0; ww < kTopkWaves; ww++) cnt += hist[ww][255 - tid];
+    for (int cp = 0; cp < kHistCopies; cp++) {
+        c0 += hist[cp * kHistBins + kHistBins - 1 - 2 * tid];
+        c1 += hist[cp * kHistBins + kHistBins - 2 - 2 * tid];
+    }
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) red[w] = incl;                // red's min/max reads ended before the last barrier
+    __syncthreads();
+    {
+        int before = 0;
+        for (int i = 0; i < w; i++) before += red[i];
+        const int excl = before + incl - c0 - c1;
+        if (excl < k && excl + c0 >= k) {
+            sh[0] = kHistBins - 1 - 2 * tid;
+            sh[1] = excl;
+            sh[2] = c0;
+        } else if (excl + c0 < k && excl + c0 + c1 >= k) {
+            sh[0] = kHistBins - 2 - 2 * tid;
+            sh[1] = excl + c0;
+            sh[2] = c1;
         }
-        int incl = cnt;
+        if (tid == 0) sh[3] = 0;
+    }
+    __syncthreads();
+    const uint32_t bsel = static_cast<uint32_t>(sh[0]);
+    const int need = k - sh[1];                   // keys still to take from bin bsel (>= 1)
+    const int m = sh[2];                          // keys in bin bsel
+    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
+    uint32_t prefix = (kmin & hi_mask) | (bsel << shift);   // bits [shift, 32) of the bin's keys
+    uint32_t thr;
+    int take_eq;
+    if (shift == 0) {
+        // the bin is one key value
+        thr = prefix;
+        take_eq = need;
+    } else if (m <= kRankCap) {
+        uint32_t *ck = hist;                      // candidates: key, slot
+        int *cs = reinterpret_cast<int *>(hist + kRankCap);
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            int v = __shfl_up(incl, o, 64);
-            if ((tid & 63) >= o) incl += v;
-        }
-        if (tid < 256 && (tid & 63) == 63) scan_sh[w] = incl;
-        __syncthreads();
-        if (tid < 256) {
-            int before = 0;
-            for (int ww = 0; ww < w; ww++) before += scan_sh[ww];
-            int excl = before + incl - cnt;
-            if (excl < remaining && excl + cnt >= remaining) {
-                sel_sh[0] = 255 - tid;
-                sel_sh[1] = remaining - excl;
+        for (int j = 0; j < R; j++) {
+            const int s = wbase + 64 * j + lane;
+            if (s < n && (key[j] >> shift) == (prefix >> shift)) {
+                const int pos = atomicAdd(&sh[3], 1);
+                ck[pos] = key[j];
+                cs[pos] = s;
             }
         }
         __syncthreads();
-        prefix |= static_cast<uint32_t>(sel_sh[0]) << shift;
-        remaining = sel_sh[1];
-        hi = shift;
+        if (tid < m) {
+            const uint32_t ki = ck[tid];
+            const int si = cs[tid];
+            int rank = 0, gt = 0;
+            // four candidates per (broadcast) LDS read; entries past m are masked
+            for (int j0 = 0; j0 < m; j0 += 4) {
+                const u32x4 kq = *reinterpret_cast<const u32x4 *>(ck + j0);
+                const u32x4 sq = *reinterpret_cast<const u32x4 *>(cs + j0);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const bool in = j0 + u < m;
+                    const uint32_t kj = kq[u];
+                    const int sj = static_cast<int>(sq[u]);
+                    gt += (in && kj > ki) ? 1 : 0;
+                    rank += (in && (kj > ki || (kj == ki && sj < si))) ? 1 : 0;
+                }
+            }
+            if (rank == need - 1) {
+                sh[4] = static_cast<int>(ki);
+                sh[5] = need - gt;
+            }
+        }
         __syncthreads();
+        thr = static_cast<uint32_t>(sh[4]);
+        take_eq = sh[5];
+    } else {
+        // crowded bin: radix passes over bits [0, shift) of the bin's keys
+        uint32_t (*wh)[256] = reinterpret_cast<uint32_t (*)[256]>(hist);   // [kTopkWaves][256]
+        int remaining = need;
+        int h = shift;
+#pragma unroll 1
+        while (h > 0) {
+            const int width = h < 8 ? h : 8;
+            const int sft = h - width;
+            for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) hist[i] = 0u;
+            __syncthreads();
+            const uint32_t pm = 0xffffffffu << h;
+            const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+            for (int j = 0; j < R; j++)
+                if (wbase + 64 * j + lane < n && (key[j] & pm) == prefix)
+                    atomicAdd(&wh[w][(key[j] >> sft) & dmask], 1u);
+            __syncthreads();
+            int cnt = 0;
+            if (tid < 256) {
+#pragma unroll
+                for (int ww = 0; ww < kTopkWaves; ww++) cnt += wh[ww][255 - tid];
+            }
+            int inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += v;
+            }
+            if (tid < 256 && lane == 63) red[w] = inc;
+            __syncthreads();
+            if (tid < 256) {
+                int before = 0;
+                for (int ww = 0; ww < w; ww++) before += red[ww];
+                const int excl = before + inc - cnt;
+                if (excl < remaining && excl + cnt >= remaining) {
+                    sh[6] = 255 - tid;
+                    sh[7] = remaining - excl;
+                }
+            }
+            __syncthreads();
+            prefix |= static_cast<uint32_t>(sh[6]) << sft;
+            remaining = sh[7];
+            h = sft;
+            __syncthreads();
+        }
+        thr = prefix;
+        take_eq = remaining;
     }
-    const uint32_t thr = prefix;      // the k-th largest key
-    const int take_eq = remaining;    // keys equal to thr to take, lowest slots first
 
-    int n_gt = 0, n_eq = 0;
+    // ordered write: a selected slot's place is the number of selected slots
+    // below it, i.e. (keys > thr below it) + min(keys == thr below it, take_eq)
+    int wg = 0, we = 0;
 #pragma unroll
     for (int j = 0; j < R; j++) {
-        bool v = base + j < n;
-        n_gt += (v && key[j] > thr) ? 1 : 0;
-        n_eq += (v && key[j] == thr) ? 1 : 0;
+        const bool v = wbase + 64 * j + lane < n;
+        wg += __popcll(__ballot(v && key[j] > thr));
+        we += __popcll(__ballot(v && key[j] == thr));
     }
-    int gt_before, eq_before;
-    block_scan2(n_gt, n_eq, scan_sh, gt_before, eq_before);
-    int pos = gt_before + (eq_before < take_eq ? eq_before : take_eq);
-    int eq_rank = eq_before;
+    __syncthreads();                              // red / sh reads are done
+    if (lane == 0) {
+        red[w] = wg;
+        red[kTopkWaves + w] = we;
+    }
+    __syncthreads();
+    int g_before = 0, e_before = 0;
+    for (int i = 0; i < w; i++) {
+        g_before += red[i];
+        e_before += red[kTopkWaves + i];
+    }
 #pragma unroll
     for (int j = 0; j < R; j++) {
-        bool v = base + j < n;
-        bool sel = v && (key[j] > thr || (key[j] == thr && eq_rank < take_eq));
-        eq_rank += (v && key[j] == thr) ? 1 : 0;
-        if (sel) out[pos++] = base + j;
+        const int s = wbase + 64 * j + lane;
+        const bool v = s < n;
+        const bool gt = v && key[j] > thr, eq = v && key[j] == thr;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const int gp = g_before + lanes_below(bg);
+        const int ep = e_before + lanes_below(be);
+        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = s;
+        g_before += __popcll(bg);
+        e_before += __popcll(be);
     }
-    for (int i = k_eff + tid; i < k; i += kTopkThreads) out[i] = -1;
 }
 
 

@@ -65,7 +65,7 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     int n_splits;           // decode: workgroups per (query, head group) along the list
-    int chunks_per_split;   // row chunks each split covers
+    int rows_per_split;     // list entries each split covers (a multiple of 32)
     float *part_o;          // [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
 };
@@ -75,9 +75,11 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);
 
-// split plan (host arithmetic only): decode splits each (query, head group)'s
+// split plan (host arithmetic only): decode splits each (query, head block)'s
 // list so that about one workgroup per CU runs; prefill never splits.
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
-                    int *chunks_per_split);
+                    int *rows_per_split);
+// 16-head groups one decode workgroup serves (2 when n_heads allows, else 1)
+int decode_groups(int n_heads);
 
 }  // namespace slc

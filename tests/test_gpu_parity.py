@@ -193,6 +193,69 @@ def test_topk_beyond_lds_capacity(S, oracle):
     assert np.array_equal(idx, exact_topk_of(sc, nv, lay.k))
 
 
+def _crafted_rows():
+    """Score rows built to drive each threshold path of the select: a crowded
+    bin of exact ties, a crowded bin of distinct keys (several radix passes),
+    a range so narrow that a bin is one key, -inf / -0 / +0 mixes, wide
+    random ranges, and k at both extremes."""
+    rng = np.random.default_rng(7)
+    f32 = np.float32
+    rows = []
+    n = 16384
+    v = rng.uniform(0.0, 0.74, n).astype(f32)
+    ties = rng.choice(n, 2300, replace=False)
+    v[ties[:300]] = rng.uniform(0.76, 1.0, 300).astype(f32)
+    v[ties[300:]] = f32(0.75)
+    rows.append(("crowded_ties", v, 512))
+    n = 8192
+    v = np.full(n, 1e-20, f32)
+    pos = rng.permutation(n)
+    v[pos[:500]] = f32(1e20)
+    v[pos[500:3500]] = (np.float32(1.0).view(np.int32) + rng.permutation(3000)).astype(np.int32).view(f32)
+    rows.append(("crowded_distinct", v, 1000))
+    n = 4096
+    v = (np.float32(1.0).view(np.int32) + rng.integers(0, 600, n)).astype(np.int32).view(f32)
+    rows.append(("narrow_ties", v, 100))
+    n = 5000
+    v = -rng.uniform(0.1, 10.0, n).astype(f32)
+    pos = rng.permutation(n)
+    v[pos[:1000]] = -np.inf
+    v[pos[1000:1500]] = f32(-0.0)
+    v[pos[1500:2000]] = f32(0.0)
+    v[pos[2000:2300]] = rng.uniform(0.1, 5.0, 300).astype(f32)
+    rows.append(("inf_and_signed_zeros", v, 700))
+    n = 40000
+    v = (rng.lognormal(0.0, 4.0, n) * rng.choice([-1.0, 1.0], n)).astype(f32)
+    rows.append(("wide_random_40k", v, 4096))
+    n = 20000
+    v = rng.integers(0, 50, n).astype(f32)
+    rows.append(("k1_with_ties", v, 1))
+    n = 1000
+    v = rng.normal(size=n).astype(f32)
+    rows.append(("k_n_minus_1", v, 999))
+    n = 777
+    v = rng.normal(size=n).astype(f32)
+    rows.append(("short_row", v, 300))
+    return rows
+
+
+@pytest.mark.parametrize("name,row,k", _crafted_rows(), ids=[r[0] for r in _crafted_rows()])
+def test_topk_crafted_rows_match_oracle(S, oracle, name, row, k):
+    n = row.shape[0]
+    ref_idx, ref_len = oracle.topk(row, k)
+    sc = torch.from_numpy(row.reshape(1, n)).cuda()
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    ln = torch.empty(1, dtype=torch.int32, device="cuda")
+    S.topk_select(k, sc, n, one, torch.full((1,), 4 * n - 1, dtype=torch.int32, device="cuda"),
+                  4, torch.full((1,), n, dtype=torch.int32, device="cuda"), idx, ln)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()[0]
+    assert int(ln.item()) == ref_len == min(k, n)
+    assert np.array_equal(g[:ref_len], np.sort(ref_idx[:ref_len])), name
+    assert np.all(g[ref_len:] == -1)
+
+
 # --------------------------------------------------------------- attention
 def _noisy_idx(lay, seed=0):
     """Given lists with -1, out-of-range entries and a duplicate mixed in."""
