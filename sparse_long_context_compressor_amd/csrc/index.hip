@@ -66,6 +66,292 @@ __device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never
 
 }  // namespace
 
+// ------------------------------------------------------------------- top-k
+
+namespace {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+// Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
+__device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int ia = a, ib = b;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
+        if (lane >= o) {
+            ia += va;
+            ib += vb;
+        }
+    }
+    if (lane == 63) {
+        sh[w] = ia;
+        sh[kTopkWaves + w] = ib;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0;
+    for (int i = 0; i < w; i++) {
+        pa += sh[i];
+        pb += sh[kTopkWaves + i];
+    }
+    a_before = pa + ia - a;
+    b_before = pb + ib - b;
+}
+
+}  // namespace
+
+// Lanes below this one in the wave whose predicate is set.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+}
+
+constexpr int kHistBits = 11;                 // first histogram: 2048 bins
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistCopies = 4;                // waves w, w+4, ... share copy w % 4
+constexpr int kRankCap = 256;                 // threshold-bin candidates ranked directly
+
+// Top-k of one query's scores by one workgroup of THREADS threads, R keys
+// per thread.  Wave w owns slots [64Rw, 64R(w+1)); lane l holds slots
+// 64Rw + 64j + l (j < R), so each of its R loads is one coalesced 256-byte
+// row of scores and the wave's slots run in (j, lane) order.
+//
+// Threshold search: after the common-prefix skip, one histogram of the next
+// 11 key bits finds the bin holding the k-th largest key.  Its candidates
+// (usually a few dozen) are ranked exactly against each other (key
+// descending, slot ascending), which yields the k-th key and how many keys
+// equal to it are taken.  A crowded bin falls back to 8-bit radix passes over
+// the bits below it.  The ordered write then counts, with wave ballots,
+// the selected keys at lower slots.
+//
+// sv: this thread's scores (any value past n); requires n > k.  Shared
+// memory: hist (kHistCopies * kHistBins words, 16-byte aligned), red
+// (2 * WAVES ints), sh (8 ints).
+template <int THREADS, int R>
+__device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, int k, int32_t *out,
+                                                  uint32_t *hist, int *red, int *sh) {
+    constexpr int WAVES = THREADS / 64;
+    constexpr int BPT = kHistBins / THREADS;
+    static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wbase = w * 64 * R;
+
+    uint32_t key[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) key[j] = wbase + 64 * j + lane < n ? order_key(sv[j]) : 0u;
+    // valid keys are never 0: order_key maps every non-NaN float above 0x007FFFFF
+
+    for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < R; j++)
+        if (wbase + 64 * j + lane < n) {
+            kmin = min(kmin, key[j]);
+            kmax = max(kmax, key[j]);
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
+    }
+    if (lane == 0) {
+        red[w] = static_cast<int>(kmin);
+        red[WAVES + w] = static_cast<int>(kmax);
+    }
+    __syncthreads();
+    kmin = 0xffffffffu;
+    kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < WAVES; i++) {
+        kmin = min(kmin, static_cast<uint32_t>(red[i]));
+        kmax = max(kmax, static_cast<uint32_t>(red[WAVES + i]));
+    }
+    if (kmin == kmax) {   // every visible score equal: the lowest slots win
+        for (int i = tid; i < k; i += THREADS) out[i] = i;
+        return;
+    }
+    const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
+    const int shift = hi > kHistBits ? hi - kHistBits : 0;
+    const uint32_t bin_mask = kHistBins - 1;
+#pragma unroll
+    for (int j = 0; j < R; j++)
+        if (wbase + 64 * j + lane < n)
+            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] >> shift) & bin_mask)], 1u);
+    __syncthreads();
+
+    // thread i owns bins 2047 - BPT*i - b (b < BPT): descending key order
+    int cb[BPT], tot = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; b++) {
+        cb[b] = 0;
+#pragma unroll
+        for (int cp = 0; cp < kHistCopies; cp++) cb[b] += hist[cp * kHistBins + kHistBins - 1 - BPT * tid - b];
+        tot += cb[b];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) red[w] = incl;                // red's min/max reads ended before the last barrier
+    __syncthreads();
+    {
+        int before = 0;
+        for (int i = 0; i < w; i++) before += red[i];
+        int run = before + incl - tot;
+#pragma unroll
+        for (int b = 0; b < BPT; b++) {
+            if (run < k && run + cb[b] >= k) {
+                sh[0] = kHistBins - 1 - BPT * tid - b;
+                sh[1] = run;
+                sh[2] = cb[b];
+            }
+            run += cb[b];
+        }
+        if (tid == 0) sh[3] = 0;
+    }
+    __syncthreads();
+    const uint32_t bsel = static_cast<uint32_t>(sh[0]);
+    const int need = k - sh[1];                   // keys still to take from bin bsel (>= 1)
+    const int m = sh[2];                          // keys in bin bsel
+    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
+    uint32_t prefix = (kmin & hi_mask) | (bsel << shift);   // bits [shift, 32) of the bin's keys
+    uint32_t thr;
+    int take_eq;
+    if (shift == 0) {
+        // the bin is one key value
+        thr = prefix;
+        take_eq = need;
+    } else if (m <= kRankCap) {
+        uint32_t *ck = hist;                      // candidates: key, slot
+        int *cs = reinterpret_cast<int *>(hist + kRankCap);
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const int s = wbase + 64 * j + lane;
+            if (s < n && (key[j] >> shift) == (prefix >> shift)) {
+                const int pos = atomicAdd(&sh[3], 1);
+                ck[pos] = key[j];
+                cs[pos] = s;
+            }
+        }
+        __syncthreads();
+        if (tid < m) {
+            const uint32_t ki = ck[tid];
+            const int si = cs[tid];
+            int rank = 0, gt = 0;
+            // four candidates per (broadcast) LDS read; entries past m are masked
+            for (int j0 = 0; j0 < m; j0 += 4) {
+                const u32x4 kq = *reinterpret_cast<const u32x4 *>(ck + j0);
+                const u32x4 sq = *reinterpret_cast<const u32x4 *>(cs + j0);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const bool in = j0 + u < m;
+                    const uint32_t kj = kq[u];
+                    const int sj = static_cast<int>(sq[u]);
+                    gt += (in && kj > ki) ? 1 : 0;
+                    rank += (in && (kj > ki || (kj == ki && sj < si))) ? 1 : 0;
+                }
+            }
+            if (rank == need - 1) {
+                sh[4] = static_cast<int>(ki);
+                sh[5] = need - gt;
+            }
+        }
+        __syncthreads();
+        thr = static_cast<uint32_t>(sh[4]);
+        take_eq = sh[5];
+    } else {
+        // crowded bin: radix passes over bits [0, shift) of the bin's keys
+        uint32_t (*wh)[256] = reinterpret_cast<uint32_t (*)[256]>(hist);   // [WAVES][256]
+        int remaining = need;
+        int h = shift;
+#pragma unroll 1
+        while (h > 0) {
+            const int width = h < 8 ? h : 8;
+            const int sft = h - width;
+            for (int i = tid; i < WAVES * 256; i += THREADS) hist[i] = 0u;
+            __syncthreads();
+            const uint32_t pm = 0xffffffffu << h;
+            const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+            for (int j = 0; j < R; j++)
+                if (wbase + 64 * j + lane < n && (key[j] & pm) == prefix)
+                    atomicAdd(&wh[w][(key[j] >> sft) & dmask], 1u);
+            __syncthreads();
+            int cnt = 0;
+            if (tid < 256) {
+#pragma unroll
+                for (int ww = 0; ww < WAVES; ww++) cnt += wh[ww][255 - tid];
+            }
+            int inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += v;
+            }
+            if (tid < 256 && lane == 63) red[w] = inc;
+            __syncthreads();
+            if (tid < 256) {
+                int before = 0;
+                for (int ww = 0; ww < w; ww++) before += red[ww];
+                const int excl = before + inc - cnt;
+                if (excl < remaining && excl + cnt >= remaining) {
+                    sh[6] = 255 - tid;
+                    sh[7] = remaining - excl;
+                }
+            }
+            __syncthreads();
+            prefix |= static_cast<uint32_t>(sh[6]) << sft;
+            remaining = sh[7];
+            h = sft;
+            __syncthreads();
+        }
+        thr = prefix;
+        take_eq = remaining;
+    }
+
+    // ordered write: a selected slot's place is the number of selected slots
+    // below it, i.e. (keys > thr below it) + min(keys == thr below it, take_eq)
+    int wg = 0, we = 0;
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const bool v = wbase + 64 * j + lane < n;
+        wg += __popcll(__ballot(v && key[j] > thr));
+        we += __popcll(__ballot(v && key[j] == thr));
+    }
+    __syncthreads();                              // red / sh reads are done
+    if (lane == 0) {
+        red[w] = wg;
+        red[WAVES + w] = we;
+    }
+    __syncthreads();
+    int g_before = 0, e_before = 0;
+    for (int i = 0; i < w; i++) {
+        g_before += red[i];
+        e_before += red[WAVES + i];
+    }
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const int s = wbase + 64 * j + lane;
+        const bool v = s < n;
+        const bool gt = v && key[j] > thr, eq = v && key[j] == thr;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const int gp = g_before + lanes_below(bg);
+        const int ep = e_before + lanes_below(be);
+        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = s;
+        g_before += __popcll(bg);
+        e_before += __popcll(be);
+    }
+}
+
 // grid (n_q, ceil(max_slots / 1024)), 256 threads.  Wave w's sub-tile j covers
 // slots s0 + 64j + 16w + (0..15): all four waves' sub-tile j lie in logical
 // block s0/64 + j, so one (wave-uniform) table lookup serves it.  Lane
@@ -147,8 +433,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
         for (int ht = 0; ht < HT; ht++)
 #pragma unroll
             for (int i = 0; i < 4; i++) part += hf[ht][i] * relu(acc[ht][i]);
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
+        part = xor32_sum(xor16_sum(part));
         if (g == 0 && s < nv)
             a.scores[static_cast<int64_t>(t) * a.max_slots + s] =
                 cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
@@ -183,72 +468,10 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------- top-k
-
-namespace {
-
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-// Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float s) {
-    uint32_t u = __float_as_uint(s + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
-__device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int ia = a, ib = b;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
-        if (lane >= o) {
-            ia += va;
-            ib += vb;
-        }
-    }
-    if (lane == 63) {
-        sh[w] = ia;
-        sh[kTopkWaves + w] = ib;
-    }
-    __syncthreads();
-    int pa = 0, pb = 0;
-    for (int i = 0; i < w; i++) {
-        pa += sh[i];
-        pb += sh[kTopkWaves + i];
-    }
-    a_before = pa + ia - a;
-    b_before = pb + ib - b;
-}
-
-}  // namespace
-
-// Lanes below this one in the wave whose predicate is set.
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
-}
-
-constexpr int kHistBits = 11;                 // first histogram: 2048 bins
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kHistCopies = 4;                // waves w, w+4, ... share copy w % 4
-constexpr int kRankCap = 256;                 // threshold-bin candidates ranked directly
-
-// R keys per thread.  Wave w owns slots [64Rw, 64R(w+1)); lane l holds slots
-// 64Rw + 64j + l (j < R), so each of its R loads is one coalesced 256-byte
-// row of scores and the wave's slots run in (j, lane) order.
-//
-// Threshold search: after the common-prefix skip, one histogram of the next
-// 11 key bits finds the bin holding the k-th largest key.  Its candidates
-// (usually a few dozen) are ranked exactly against each other (key
-// descending, slot ascending), which yields the k-th key and how many keys
-// equal to it are taken.  A crowded bin falls back to 8-bit radix passes over
-// the bits below it.  The ordered write then counts, with wave ballots,
-// the selected keys at lower slots.
+// One 1024-thread workgroup per query.
 template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB, reused below
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB
     __shared__ int red[2 * kTopkWaves];
     __shared__ int sh[8];
 
@@ -271,217 +494,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int k_eff = n < k ? n : k;
     int32_t *out = a.idx + static_cast<int64_t>(t) * k;
     if (tid == 0) a.len[t] = k_eff;
-
     if (n <= k) {   // everything visible is selected
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
-
-    uint32_t key[R];
-#pragma unroll
-    for (int j = 0; j < R; j++) key[j] = wbase + 64 * j + lane < n ? order_key(sv[j]) : 0u;
-    // valid keys are never 0: order_key maps every non-NaN float above 0x007FFFFF
-
-    for (int i = tid; i < kHistCopies * kHistBins; i += kTopkThreads) hist[i] = 0u;
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < R; j++)
-        if (wbase + 64 * j + lane < n) {
-            kmin = min(kmin, key[j]);
-            kmax = max(kmax, key[j]);
-        }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
-    }
-    if (lane == 0) {
-        red[w] = static_cast<int>(kmin);
-        red[kTopkWaves + w] = static_cast<int>(kmax);
-    }
-    __syncthreads();
-    kmin = 0xffffffffu;
-    kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < kTopkWaves; i++) {
-        kmin = min(kmin, static_cast<uint32_t>(red[i]));
-        kmax = max(kmax, static_cast<uint32_t>(red[kTopkWaves + i]));
-    }
-    if (kmin == kmax) {   // every visible score equal: the lowest slots win
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i;
-        return;
-    }
-    const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
-    const int shift = hi > kHistBits ? hi - kHistBits : 0;
-    const uint32_t bin_mask = kHistBins - 1;
-#pragma unroll
-    for (int j = 0; j < R; j++)
-        if (wbase + 64 * j + lane < n)
-            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] >> shift) & bin_mask)], 1u);
-    __syncthreads();
-
-    // thread i owns bins 2047-2i (c0) and 2046-2i (c1): descending key order
-    int c0 = 0, c1 = 0;
-#pragma unroll
-    for (int cp = 0; cp < kHistCopies; cp++) {
-        c0 += hist[cp * kHistBins + kHistBins - 1 - 2 * tid];
-        c1 += hist[cp * kHistBins + kHistBins - 2 - 2 * tid];
-    }
-    int incl = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) red[w] = incl;                // red's min/max reads ended before the last barrier
-    __syncthreads();
-    {
-        int before = 0;
-        for (int i = 0; i < w; i++) before += red[i];
-        const int excl = before + incl - c0 - c1;
-        if (excl < k && excl + c0 >= k) {
-            sh[0] = kHistBins - 1 - 2 * tid;
-            sh[1] = excl;
-            sh[2] = c0;
-        } else if (excl + c0 < k && excl + c0 + c1 >= k) {
-            sh[0] = kHistBins - 2 - 2 * tid;
-            sh[1] = excl + c0;
-            sh[2] = c1;
-        }
-        if (tid == 0) sh[3] = 0;
-    }
-    __syncthreads();
-    const uint32_t bsel = static_cast<uint32_t>(sh[0]);
-    const int need = k - sh[1];                   // keys still to take from bin bsel (>= 1)
-    const int m = sh[2];                          // keys in bin bsel
-    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
-    uint32_t prefix = (kmin & hi_mask) | (bsel << shift);   // bits [shift, 32) of the bin's keys
-    uint32_t thr;
-    int take_eq;
-    if (shift == 0) {
-        // the bin is one key value
-        thr = prefix;
-        take_eq = need;
-    } else if (m <= kRankCap) {
-        uint32_t *ck = hist;                      // candidates: key, slot
-        int *cs = reinterpret_cast<int *>(hist + kRankCap);
-#pragma unroll
-        for (int j = 0; j < R; j++) {
-            const int s = wbase + 64 * j + lane;
-            if (s < n && (key[j] >> shift) == (prefix >> shift)) {
-                const int pos = atomicAdd(&sh[3], 1);
-                ck[pos] = key[j];
-                cs[pos] = s;
-            }
-        }
-        __syncthreads();
-        if (tid < m) {
-            const uint32_t ki = ck[tid];
-            const int si = cs[tid];
-            int rank = 0, gt = 0;
-            // four candidates per (broadcast) LDS read; entries past m are masked
-            for (int j0 = 0; j0 < m; j0 += 4) {
-                const u32x4 kq = *reinterpret_cast<const u32x4 *>(ck + j0);
-                const u32x4 sq = *reinterpret_cast<const u32x4 *>(cs + j0);
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const bool in = j0 + u < m;
-                    const uint32_t kj = kq[u];
-                    const int sj = static_cast<int>(sq[u]);
-                    gt += (in && kj > ki) ? 1 : 0;
-                    rank += (in && (kj > ki || (kj == ki && sj < si))) ? 1 : 0;
-                }
-            }
-            if (rank == need - 1) {
-                sh[4] = static_cast<int>(ki);
-                sh[5] = need - gt;
-            }
-        }
-        __syncthreads();
-        thr = static_cast<uint32_t>(sh[4]);
-        take_eq = sh[5];
-    } else {
-        // crowded bin: radix passes over bits [0, shift) of the bin's keys
-        uint32_t (*wh)[256] = reinterpret_cast<uint32_t (*)[256]>(hist);   // [kTopkWaves][256]
-        int remaining = need;
-        int h = shift;
-#pragma unroll 1
-        while (h > 0) {
-            const int width = h < 8 ? h : 8;
-            const int sft = h - width;
-            for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) hist[i] = 0u;
-            __syncthreads();
-            const uint32_t pm = 0xffffffffu << h;
-            const uint32_t dmask = (1u << width) - 1u;
-#pragma unroll
-            for (int j = 0; j < R; j++)
-                if (wbase + 64 * j + lane < n && (key[j] & pm) == prefix)
-                    atomicAdd(&wh[w][(key[j] >> sft) & dmask], 1u);
-            __syncthreads();
-            int cnt = 0;
-            if (tid < 256) {
-#pragma unroll
-                for (int ww = 0; ww < kTopkWaves; ww++) cnt += wh[ww][255 - tid];
-            }
-            int inc = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int v = __shfl_up(inc, o, 64);
-                if (lane >= o) inc += v;
-            }
-            if (tid < 256 && lane == 63) red[w] = inc;
-            __syncthreads();
-            if (tid < 256) {
-                int before = 0;
-                for (int ww = 0; ww < w; ww++) before += red[ww];
-                const int excl = before + inc - cnt;
-                if (excl < remaining && excl + cnt >= remaining) {
-                    sh[6] = 255 - tid;
-                    sh[7] = remaining - excl;
-                }
-            }
-            __syncthreads();
-            prefix |= static_cast<uint32_t>(sh[6]) << sft;
-            remaining = sh[7];
-            h = sft;
-            __syncthreads();
-        }
-        thr = prefix;
-        take_eq = remaining;
-    }
-
-    // ordered write: a selected slot's place is the number of selected slots
-    // below it, i.e. (keys > thr below it) + min(keys == thr below it, take_eq)
-    int wg = 0, we = 0;
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const bool v = wbase + 64 * j + lane < n;
-        wg += __popcll(__ballot(v && key[j] > thr));
-        we += __popcll(__ballot(v && key[j] == thr));
-    }
-    __syncthreads();                              // red / sh reads are done
-    if (lane == 0) {
-        red[w] = wg;
-        red[kTopkWaves + w] = we;
-    }
-    __syncthreads();
-    int g_before = 0, e_before = 0;
-    for (int i = 0; i < w; i++) {
-        g_before += red[i];
-        e_before += red[kTopkWaves + i];
-    }
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const int s = wbase + 64 * j + lane;
-        const bool v = s < n;
-        const bool gt = v && key[j] > thr, eq = v && key[j] == thr;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        const int gp = g_before + lanes_below(bg);
-        const int ep = e_before + lanes_below(be);
-        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = s;
-        g_before += __popcll(bg);
-        e_before += __popcll(be);
-    }
+    topk_select_block<kTopkThreads, R>(sv, n, k, out, hist, red, sh);
 }
 
 
