@@ -242,9 +242,6 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     const int hgw = NG == 2 ? (w & 1) : 0;
     const int h = 16 * (NG * hb + hgw) + c;
     const int row0 = NG == 2 ? 32 * ((w >> 1) & 1) : 16 * (w & 3);   // first chunk row of this wave
-    bf16x8 qb[kD / 32];
-    if (!producer) load_q(a, t, h, g, qb);   // issued first: depends on t only
-
     const int seq = a.q_seq[t], p = a.q_pos[t];
     const int E = a.window + a.k;
     const int ns = a.k > 0 ? a.n_slots[seq] : 0;
@@ -253,8 +250,12 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     e_end = e_end < E ? e_end : E;
     const int nchunks = e_end > e_begin ? (e_end - e_begin + kDecRows - 1) / kDecRows : 0;
 
+    // the row lists first: their short chain of dependent loads would
+    // otherwise queue behind the query loads of every workgroup
     for (int e = e_begin + tid; e < e_end; e += 512) src[e - e_begin] = resolve_entry(a, t, seq, p, ns, e);
     __syncthreads();
+    bf16x8 qb[kD / 32];
+    if (!producer) load_q(a, t, h, g, qb);   // lands while the first chunk is gathered
 
     constexpr int kMergeBarriers = NG == 2 ? 2 : 4;
     if (producer) {

@@ -82,15 +82,7 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 // Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
 __device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int ia = a, ib = b;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
-        if (lane >= o) {
-            ia += va;
-            ib += vb;
-        }
-    }
+    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
     if (lane == 63) {
         sh[w] = ia;
         sh[kTopkWaves + w] = ib;
@@ -131,22 +123,20 @@ constexpr int kRankCap = 256;                 // threshold-bin candidates ranked
 // the bits below it.  The ordered write then counts, with wave ballots,
 // the selected keys at lower slots.
 //
-// sv: this thread's scores (any value past n); requires n > k.  Shared
-// memory: hist (kHistCopies * kHistBins words, 16-byte aligned), red
-// (2 * WAVES ints), sh (8 ints).
+// key: this thread's order keys (entries past n are 0; valid keys never are:
+// order_key maps every non-NaN float above 0x007FFFFF); requires n > k.
+// Entry i of the list is written out as slot_map[i] (i itself when
+// slot_map is null).  Shared memory: hist (kHistCopies * kHistBins words,
+// 16-byte aligned), red (2 * WAVES ints), sh (8 ints).
 template <int THREADS, int R>
-__device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, int k, int32_t *out,
-                                                  uint32_t *hist, int *red, int *sh) {
+__device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n, int k,
+                                                 int32_t *out, const int32_t *slot_map,
+                                                 uint32_t *hist, int *red, int *sh) {
     constexpr int WAVES = THREADS / 64;
     constexpr int BPT = kHistBins / THREADS;
     static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wbase = w * 64 * R;
-
-    uint32_t key[R];
-#pragma unroll
-    for (int j = 0; j < R; j++) key[j] = wbase + 64 * j + lane < n ? order_key(sv[j]) : 0u;
-    // valid keys are never 0: order_key maps every non-NaN float above 0x007FFFFF
 
     for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
     uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -156,11 +146,8 @@ __device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, i
             kmin = min(kmin, key[j]);
             kmax = max(kmax, key[j]);
         }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
-    }
+    kmin = wave_umin(kmin);
+    kmax = wave_umax(kmax);
     if (lane == 0) {
         red[w] = static_cast<int>(kmin);
         red[WAVES + w] = static_cast<int>(kmax);
@@ -173,8 +160,8 @@ __device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, i
         kmin = min(kmin, static_cast<uint32_t>(red[i]));
         kmax = max(kmax, static_cast<uint32_t>(red[WAVES + i]));
     }
-    if (kmin == kmax) {   // every visible score equal: the lowest slots win
-        for (int i = tid; i < k; i += THREADS) out[i] = i;
+    if (kmin == kmax) {   // every entry equal: the lowest ones win
+        for (int i = tid; i < k; i += THREADS) out[i] = slot_map ? slot_map[i] : i;
         return;
     }
     const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
@@ -195,12 +182,7 @@ __device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, i
         for (int cp = 0; cp < kHistCopies; cp++) cb[b] += hist[cp * kHistBins + kHistBins - 1 - BPT * tid - b];
         tot += cb[b];
     }
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
+    const int incl = wave_incl_scan(tot);
     if (lane == 63) red[w] = incl;                // red's min/max reads ended before the last barrier
     __syncthreads();
     {
@@ -291,12 +273,7 @@ __device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, i
 #pragma unroll
                 for (int ww = 0; ww < WAVES; ww++) cnt += wh[ww][255 - tid];
             }
-            int inc = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int v = __shfl_up(inc, o, 64);
-                if (lane >= o) inc += v;
-            }
+            const int inc = wave_incl_scan(cnt);
             if (tid < 256 && lane == 63) red[w] = inc;
             __syncthreads();
             if (tid < 256) {
@@ -346,7 +323,7 @@ __device__ __forceinline__ void topk_select_block(const float (&sv)[R], int n, i
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
         const int gp = g_before + lanes_below(bg);
         const int ep = e_before + lanes_below(be);
-        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = s;
+        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = slot_map ? slot_map[s] : s;
         g_before += __popcll(bg);
         e_before += __popcll(be);
     }
@@ -468,25 +445,102 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// One 1024-thread workgroup per query.
+// A lower bound of the k-th largest of the values v (G per thread, 0 =
+// absent): the floor of the 11-bit histogram bin (below the bits all values
+// share) that holds the k-th largest; 0 if fewer than k values are present.
+// Shared memory as for topk_select_keys, red with 3 * WAVES ints.
+template <int THREADS, int G>
+__device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uint32_t *hist,
+                                              int *red, int *sh) {
+    constexpr int WAVES = THREADS / 64;
+    constexpr int BPT = kHistBins / THREADS;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t vmin = 0xffffffffu, vmax = 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int g = 0; g < G; g++)
+        if (v[g]) {
+            vmin = min(vmin, v[g]);
+            vmax = max(vmax, v[g]);
+            cnt++;
+        }
+    vmin = wave_umin(vmin);
+    vmax = wave_umax(vmax);
+    cnt = wave_isum(cnt);
+    for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
+    if (lane == 0) {
+        red[w] = static_cast<int>(vmin);
+        red[WAVES + w] = static_cast<int>(vmax);
+        red[2 * WAVES + w] = cnt;
+    }
+    __syncthreads();
+    vmin = 0xffffffffu;
+    vmax = 0u;
+    cnt = 0;
+#pragma unroll
+    for (int i = 0; i < WAVES; i++) {
+        vmin = min(vmin, static_cast<uint32_t>(red[i]));
+        vmax = max(vmax, static_cast<uint32_t>(red[WAVES + i]));
+        cnt += red[2 * WAVES + i];
+    }
+    if (cnt < k) return 0u;
+    if (vmin == vmax) return vmin;
+    const int hi = 32 - __clz(vmin ^ vmax);
+    const int shift = hi > kHistBits ? hi - kHistBits : 0;
+#pragma unroll
+    for (int g = 0; g < G; g++)
+        if (v[g]) atomicAdd(&hist[(v[g] >> shift) & (kHistBins - 1)], 1u);
+    __syncthreads();
+    int cb[BPT], tot = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; b++) {
+        cb[b] = static_cast<int>(hist[kHistBins - 1 - BPT * tid - b]);
+        tot += cb[b];
+    }
+    const int incl = wave_incl_scan(tot);
+    if (lane == 63) red[w] = incl;                // red's reads above precede the last barrier
+    __syncthreads();
+    {
+        int run = -tot + incl;
+        for (int i = 0; i < w; i++) run += red[i];
+#pragma unroll
+        for (int b = 0; b < BPT; b++) {
+            if (run < k && run + cb[b] >= k) sh[0] = kHistBins - 1 - BPT * tid - b;
+            run += cb[b];
+        }
+    }
+    __syncthreads();
+    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
+    return (vmin & hi_mask) | (static_cast<uint32_t>(sh[0]) << shift);
+}
+
+// One 1024-thread workgroup per query, R scores per thread (R >= 4): wave w
+// owns slots [64Rw, 64R(w+1)) and lane l reads slots 64Rw + 256q + 4l + e
+// (e < 4) with one 16-byte load per round q, so the wave's slots run in
+// (q, lane, e) order.
+//
+// Prefilter: the four keys of a load are a group; any k group maxima are k
+// distinct scores, so the k-th largest maximum (and the floor L of its
+// histogram bin) is at most the k-th largest score: no key below L can be
+// selected.  The keys >= L (a few per cent of the list) are compacted, in
+// slot order, into LDS and the exact select runs on them with at most four
+// per thread.  If more than kCandCap keys pass, the select runs on all keys.
+constexpr int kCandCap = 4 * kTopkThreads;
+
 template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+    static_assert(R >= 4, "16-byte score loads");
+    constexpr int R4 = R / 4;
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB
-    __shared__ int red[2 * kTopkWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t cand_key[kCandCap];             // 16 KB
+    __shared__ int32_t cand_slot[kCandCap];                                          // 16 KB
+    __shared__ int red[3 * kTopkWaves];
     __shared__ int sh[8];
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
-    const int wbase = w * 64 * R;
-    // the score loads depend on the query index only: issue them before the
-    // visible count (two dependent loads away) is known, mask afterwards
-    float sv[R];
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const int s = wbase + 64 * j + lane;
-        sv[j] = s < a.max_slots ? sc[s] : 0.f;
-    }
+    // the visible count first: its two dependent loads must not queue
+    // behind this workgroup's score loads
     const int seq = a.q_seq[t];
     int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
     n = n < a.max_slots ? n : a.max_slots;
@@ -498,7 +552,122 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
-    topk_select_block<kTopkThreads, R>(sv, n, k, out, hist, red, sh);
+
+    // rows are 16-byte aligned: the launcher takes this kernel only for a
+    // 16-byte aligned score array whose row length is a multiple of 4
+    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
+    const int wbase = w * 64 * R;
+    uint32_t key[R];                              // key[4q + e]: slot wbase + 256q + 4 lane + e
+#pragma unroll
+    for (int q = 0; q < R4; q++) {
+        const int s0 = wbase + 256 * q + 4 * lane;
+        if (s0 + 3 < n) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(sc + s0);
+#pragma unroll
+            for (int e = 0; e < 4; e++) key[4 * q + e] = order_key(v[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) key[4 * q + e] = s0 + e < n ? order_key(sc[s0 + e]) : 0u;
+        }
+    }
+    uint32_t gmax[R4];
+#pragma unroll
+    for (int q = 0; q < R4; q++)
+        gmax[q] = max(max(key[4 * q], key[4 * q + 1]), max(key[4 * q + 2], key[4 * q + 3]));
+    const uint32_t L = kth_floor<kTopkThreads, R4>(gmax, k, hist, red, sh);
+
+    // candidates per round and lane (keys are never 0 when valid)
+    int cl[R4], wc = 0;
+#pragma unroll
+    for (int q = 0; q < R4; q++) {
+        cl[q] = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) cl[q] += (key[4 * q + e] != 0u && key[4 * q + e] >= L) ? 1 : 0;
+        wc += cl[q];
+    }
+    wc = wave_isum(wc);
+    __syncthreads();                              // every thread has read kth_floor's result
+    if (lane == 0) red[w] = wc;
+    __syncthreads();
+    int m = 0, run = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; i++) {
+        m += red[i];
+        run += i < w ? red[i] : 0;
+    }
+    if (m > kCandCap) {
+        // crowded: the exact select over every key, in the one-key-per-lane layout
+        uint32_t key1[R];
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const int s = wbase + 64 * j + lane;
+            key1[j] = s < n ? order_key(sc[s]) : 0u;
+        }
+        __syncthreads();                          // red is reused by the select
+        topk_select_keys<kTopkThreads, R>(key1, n, k, out, nullptr, hist, red, sh);
+        return;
+    }
+    // compact the candidates in slot order: round by round, lanes in order,
+    // a lane's four slots in order
+#pragma unroll
+    for (int q = 0; q < R4; q++) {
+        const int incl = wave_incl_scan(cl[q]);
+        int pos = run + incl - cl[q];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t kk = key[4 * q + e];
+            if (kk != 0u && kk >= L) {
+                cand_key[pos] = kk;
+                cand_slot[pos] = wbase + 256 * q + 4 * lane + e;
+                pos++;
+            }
+        }
+        run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    __syncthreads();
+    if (m == k) {                                 // exactly the candidates
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = cand_slot[i];
+        return;
+    }
+    constexpr int Q = kCandCap / kTopkThreads;
+    uint32_t ck[Q];
+#pragma unroll
+    for (int i = 0; i < Q; i++) {
+        const int c = w * 64 * Q + 64 * i + lane;
+        ck[i] = c < m ? cand_key[c] : 0u;
+    }
+    topk_select_keys<kTopkThreads, Q>(ck, m, k, out, cand_slot, hist, red, sh);
+}
+
+// Short lists (up to 2048 visible slots) and rows not 16-byte aligned: the
+// exact select over every key, R per thread in the one-key-per-lane layout.
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(TopkArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];
+    __shared__ int red[2 * kTopkWaves];
+    __shared__ int sh[8];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int seq = a.q_seq[t];
+    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
+    n = n < a.max_slots ? n : a.max_slots;
+    const int k = a.k;
+    const int k_eff = n < k ? n : k;
+    int32_t *out = a.idx + static_cast<int64_t>(t) * k;
+    if (tid == 0) a.len[t] = k_eff;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        return;
+    }
+    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
+    const int wbase = w * 64 * R;
+    uint32_t key[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const int s = wbase + 64 * j + lane;
+        key[j] = s < n ? order_key(sc[s]) : 0u;
+    }
+    topk_select_keys<kTopkThreads, R>(key, n, k, out, nullptr, hist, red, sh);
 }
 
 
@@ -540,11 +709,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
         int cnt = 0;
         if (tid < 256)
             for (int ww = 0; ww < kTopkWaves; ww++) cnt += hist[ww][255 - tid];
-        int incl = cnt;
-        for (int o = 1; o < 64; o <<= 1) {
-            int v = __shfl_up(incl, o, 64);
-            if ((tid & 63) >= o) incl += v;
-        }
+        const int incl = wave_incl_scan(cnt);
         if (tid < 256 && (tid & 63) == 63) scan_sh[w] = incl;
         __syncthreads();
         if (tid < 256) {
@@ -591,9 +756,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
     const int per = (a.max_slots + kTopkThreads - 1) / kTopkThreads;
+    const bool vec = a.max_slots % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
     dim3 grid(a.n_q), block(kTopkThreads);
-    if (per <= 1) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, stream, a);
-    else if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, stream, a);
+    if (per <= 1) hipLaunchKernelGGL(topk_small_kernel<1>, grid, block, 0, stream, a);
+    else if (per <= 2) hipLaunchKernelGGL(topk_small_kernel<2>, grid, block, 0, stream, a);
+    else if (!vec && per <= 16) hipLaunchKernelGGL(topk_small_kernel<16>, grid, block, 0, stream, a);
+    else if (!vec && per <= 64) hipLaunchKernelGGL(topk_small_kernel<64>, grid, block, 0, stream, a);
     else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
     else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
     else if (per <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);

@@ -107,6 +107,55 @@ __device__ __forceinline__ float xor32_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wave-wide reductions and scans on DPP lane moves (VALU, no LDS): quad
+// permutes and row mirrors combine within 16 lanes, the permlane swaps across
+// 16 and 32.  Every lane receives the result.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(x),
+                                                             CTRL, ROW_MASK, 0xF, BOUND_ZERO));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t x, Op op) {
+    x = op(x, dpp_u32<kDppXor1>(x, x));
+    x = op(x, dpp_u32<kDppXor2>(x, x));
+    x = op(x, dpp_u32<kDppHalfMirror>(x, x));
+    x = op(x, dpp_u32<kDppMirror>(x, x));
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = op(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return op(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+    return wave_allreduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    return wave_allreduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int wave_isum(int x) {
+    return static_cast<int>(wave_allreduce_u32(static_cast<uint32_t>(x),
+                                               [](uint32_t a, uint32_t b) { return a + b; }));
+}
+// Inclusive prefix sum over lanes 0..63 (row shifts within 16 lanes, then
+// the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    uint32_t x = static_cast<uint32_t>(v);
+    x += dpp_u32<kDppShr1, 0xF, true>(0u, x);
+    x += dpp_u32<kDppShr2, 0xF, true>(0u, x);
+    x += dpp_u32<kDppShr4, 0xF, true>(0u, x);
+    x += dpp_u32<kDppShr8, 0xF, true>(0u, x);
+    x += dpp_u32<kDppBcast15, 0xA>(0u, x);
+    x += dpp_u32<kDppBcast31, 0xC>(0u, x);
+    return static_cast<int>(x);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
