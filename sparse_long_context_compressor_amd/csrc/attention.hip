@@ -222,7 +222,6 @@ constexpr int kPreRows = 32;   // rows per prefill chunk
 // softmax states through LDS.
 template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
-    constexpr int RW = 16 * NG;                      // rows per consumer wave per chunk
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
     __shared__ int32_t src[kDecMaxEntries];
     __shared__ float st_m[4][16], st_l[4][16];

@@ -1,10 +1,8 @@
-// index.hip -- lightning-indexer scores and the per-query global top-k.
+// index.hip -- lightning-indexer scores (the top-k select is in topk.hip).
 //
 // Method: "DeepseekV4Attention" (devpress, AMD), Indexer section:
 //   I[t][s] = sum_j w[t][j] * ReLU(q[t][j] . k[s]),  H_I heads sharing one
-//   key per slot, fp8 keys of 128 dims with one fp32 scale per key;
-// "DeepSeek-V4 attention layer types", Indexer / C4A branch: c4a computes a
-// global top-k over these scores for every query.
+//   key per slot, fp8 keys of 128 dims with one fp32 scale per key.
 //
 // Scores: the contraction [H_I x 128] . [128 x slots] runs on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16).  e4m3 codes convert to bf16 exactly, and the
@@ -15,16 +13,6 @@
 // so the kernel stays HBM-bound.  Quantisation scales are positive, so
 // ReLU(qs * ks * dot) = ks * qs * ReLU(dot) and the per-head factor w * qs is
 // applied once per head, the key scale once per slot.
-//
-// Top-k: one workgroup of 1024 threads per query; each thread keeps up to 64
-// order-preserving 32-bit keys of consecutive slots in registers.  An
-// MSB-first radix select (8-bit digits, per-wave LDS histograms) finds the
-// k-th largest key, starting below the bits all keys share (scores of one
-// query sit in a narrow range, so their top bits agree and a first digit
-// over them would pile every key into one histogram bin); one block-wide
-// scan of (above, equal) counts then
-// places every selected slot, in increasing slot order, ties at the threshold
-// going to the lower slot index.
 
 #include "slc_internal.hpp"
 
@@ -65,269 +53,6 @@ struct KeyStage {
 __device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never written
 
 }  // namespace
-
-// ------------------------------------------------------------------- top-k
-
-namespace {
-
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-// Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float s) {
-    uint32_t u = __float_as_uint(s + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
-__device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
-    if (lane == 63) {
-        sh[w] = ia;
-        sh[kTopkWaves + w] = ib;
-    }
-    __syncthreads();
-    int pa = 0, pb = 0;
-    for (int i = 0; i < w; i++) {
-        pa += sh[i];
-        pb += sh[kTopkWaves + i];
-    }
-    a_before = pa + ia - a;
-    b_before = pb + ib - b;
-}
-
-}  // namespace
-
-// Lanes below this one in the wave whose predicate is set.
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
-}
-
-constexpr int kHistBits = 11;                 // first histogram: 2048 bins
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kHistCopies = 4;                // waves w, w+4, ... share copy w % 4
-constexpr int kRankCap = 256;                 // threshold-bin candidates ranked directly
-
-// Top-k of one query's scores by one workgroup of THREADS threads, R keys
-// per thread.  Wave w owns slots [64Rw, 64R(w+1)); lane l holds slots
-// 64Rw + 64j + l (j < R), so each of its R loads is one coalesced 256-byte
-// row of scores and the wave's slots run in (j, lane) order.
-//
-// Threshold search: after the common-prefix skip, one histogram of the next
-// 11 key bits finds the bin holding the k-th largest key.  Its candidates
-// (usually a few dozen) are ranked exactly against each other (key
-// descending, slot ascending), which yields the k-th key and how many keys
-// equal to it are taken.  A crowded bin falls back to 8-bit radix passes over
-// the bits below it.  The ordered write then counts, with wave ballots,
-// the selected keys at lower slots.
-//
-// key: this thread's order keys (entries past n are 0; valid keys never are:
-// order_key maps every non-NaN float above 0x007FFFFF); requires n > k.
-// Entry i of the list is written out as slot_map[i] (i itself when
-// slot_map is null).  Shared memory: hist (kHistCopies * kHistBins words,
-// 16-byte aligned), red (2 * WAVES ints), sh (8 ints).
-template <int THREADS, int R>
-__device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n, int k,
-                                                 int32_t *out, const int32_t *slot_map,
-                                                 uint32_t *hist, int *red, int *sh) {
-    constexpr int WAVES = THREADS / 64;
-    constexpr int BPT = kHistBins / THREADS;
-    static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wbase = w * 64 * R;
-
-    for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < R; j++)
-        if (wbase + 64 * j + lane < n) {
-            kmin = min(kmin, key[j]);
-            kmax = max(kmax, key[j]);
-        }
-    kmin = wave_umin(kmin);
-    kmax = wave_umax(kmax);
-    if (lane == 0) {
-        red[w] = static_cast<int>(kmin);
-        red[WAVES + w] = static_cast<int>(kmax);
-    }
-    __syncthreads();
-    kmin = 0xffffffffu;
-    kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < WAVES; i++) {
-        kmin = min(kmin, static_cast<uint32_t>(red[i]));
-        kmax = max(kmax, static_cast<uint32_t>(red[WAVES + i]));
-    }
-    if (kmin == kmax) {   // every entry equal: the lowest ones win
-        for (int i = tid; i < k; i += THREADS) out[i] = slot_map ? slot_map[i] : i;
-        return;
-    }
-    const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
-    const int shift = hi > kHistBits ? hi - kHistBits : 0;
-    const uint32_t bin_mask = kHistBins - 1;
-#pragma unroll
-    for (int j = 0; j < R; j++)
-        if (wbase + 64 * j + lane < n)
-            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] >> shift) & bin_mask)], 1u);
-    __syncthreads();
-
-    // thread i owns bins 2047 - BPT*i - b (b < BPT): descending key order
-    int cb[BPT], tot = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; b++) {
-        cb[b] = 0;
-#pragma unroll
-        for (int cp = 0; cp < kHistCopies; cp++) cb[b] += hist[cp * kHistBins + kHistBins - 1 - BPT * tid - b];
-        tot += cb[b];
-    }
-    const int incl = wave_incl_scan(tot);
-    if (lane == 63) red[w] = incl;                // red's min/max reads ended before the last barrier
-    __syncthreads();
-    {
-        int before = 0;
-        for (int i = 0; i < w; i++) before += red[i];
-        int run = before + incl - tot;
-#pragma unroll
-        for (int b = 0; b < BPT; b++) {
-            if (run < k && run + cb[b] >= k) {
-                sh[0] = kHistBins - 1 - BPT * tid - b;
-                sh[1] = run;
-                sh[2] = cb[b];
-            }
-            run += cb[b];
-        }
-        if (tid == 0) sh[3] = 0;
-    }
-    __syncthreads();
-    const uint32_t bsel = static_cast<uint32_t>(sh[0]);
-    const int need = k - sh[1];                   // keys still to take from bin bsel (>= 1)
-    const int m = sh[2];                          // keys in bin bsel
-    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
-    uint32_t prefix = (kmin & hi_mask) | (bsel << shift);   // bits [shift, 32) of the bin's keys
-    uint32_t thr;
-    int take_eq;
-    if (shift == 0) {
-        // the bin is one key value
-        thr = prefix;
-        take_eq = need;
-    } else if (m <= kRankCap) {
-        uint32_t *ck = hist;                      // candidates: key, slot
-        int *cs = reinterpret_cast<int *>(hist + kRankCap);
-#pragma unroll
-        for (int j = 0; j < R; j++) {
-            const int s = wbase + 64 * j + lane;
-            if (s < n && (key[j] >> shift) == (prefix >> shift)) {
-                const int pos = atomicAdd(&sh[3], 1);
-                ck[pos] = key[j];
-                cs[pos] = s;
-            }
-        }
-        __syncthreads();
-        if (tid < m) {
-            const uint32_t ki = ck[tid];
-            const int si = cs[tid];
-            int rank = 0, gt = 0;
-            // four candidates per (broadcast) LDS read; entries past m are masked
-            for (int j0 = 0; j0 < m; j0 += 4) {
-                const u32x4 kq = *reinterpret_cast<const u32x4 *>(ck + j0);
-                const u32x4 sq = *reinterpret_cast<const u32x4 *>(cs + j0);
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const bool in = j0 + u < m;
-                    const uint32_t kj = kq[u];
-                    const int sj = static_cast<int>(sq[u]);
-                    gt += (in && kj > ki) ? 1 : 0;
-                    rank += (in && (kj > ki || (kj == ki && sj < si))) ? 1 : 0;
-                }
-            }
-            if (rank == need - 1) {
-                sh[4] = static_cast<int>(ki);
-                sh[5] = need - gt;
-            }
-        }
-        __syncthreads();
-        thr = static_cast<uint32_t>(sh[4]);
-        take_eq = sh[5];
-    } else {
-        // crowded bin: radix passes over bits [0, shift) of the bin's keys
-        uint32_t (*wh)[256] = reinterpret_cast<uint32_t (*)[256]>(hist);   // [WAVES][256]
-        int remaining = need;
-        int h = shift;
-#pragma unroll 1
-        while (h > 0) {
-            const int width = h < 8 ? h : 8;
-            const int sft = h - width;
-            for (int i = tid; i < WAVES * 256; i += THREADS) hist[i] = 0u;
-            __syncthreads();
-            const uint32_t pm = 0xffffffffu << h;
-            const uint32_t dmask = (1u << width) - 1u;
-#pragma unroll
-            for (int j = 0; j < R; j++)
-                if (wbase + 64 * j + lane < n && (key[j] & pm) == prefix)
-                    atomicAdd(&wh[w][(key[j] >> sft) & dmask], 1u);
-            __syncthreads();
-            int cnt = 0;
-            if (tid < 256) {
-#pragma unroll
-                for (int ww = 0; ww < WAVES; ww++) cnt += wh[ww][255 - tid];
-            }
-            const int inc = wave_incl_scan(cnt);
-            if (tid < 256 && lane == 63) red[w] = inc;
-            __syncthreads();
-            if (tid < 256) {
-                int before = 0;
-                for (int ww = 0; ww < w; ww++) before += red[ww];
-                const int excl = before + inc - cnt;
-                if (excl < remaining && excl + cnt >= remaining) {
-                    sh[6] = 255 - tid;
-                    sh[7] = remaining - excl;
-                }
-            }
-            __syncthreads();
-            prefix |= static_cast<uint32_t>(sh[6]) << sft;
-            remaining = sh[7];
-            h = sft;
-            __syncthreads();
-        }
-        thr = prefix;
-        take_eq = remaining;
-    }
-
-    // ordered write: a selected slot's place is the number of selected slots
-    // below it, i.e. (keys > thr below it) + min(keys == thr below it, take_eq)
-    int wg = 0, we = 0;
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const bool v = wbase + 64 * j + lane < n;
-        wg += __popcll(__ballot(v && key[j] > thr));
-        we += __popcll(__ballot(v && key[j] == thr));
-    }
-    __syncthreads();                              // red / sh reads are done
-    if (lane == 0) {
-        red[w] = wg;
-        red[WAVES + w] = we;
-    }
-    __syncthreads();
-    int g_before = 0, e_before = 0;
-    for (int i = 0; i < w; i++) {
-        g_before += red[i];
-        e_before += red[WAVES + i];
-    }
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const int s = wbase + 64 * j + lane;
-        const bool v = s < n;
-        const bool gt = v && key[j] > thr, eq = v && key[j] == thr;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        const int gp = g_before + lanes_below(bg);
-        const int ep = e_before + lanes_below(be);
-        if (gt || (eq && ep < take_eq)) out[gp + (ep < take_eq ? ep : take_eq)] = slot_map ? slot_map[s] : s;
-        g_before += __popcll(bg);
-        e_before += __popcll(be);
-    }
-}
 
 // grid (n_q, ceil(max_slots / 1024)), 256 threads.  Wave w's sub-tile j covers
 // slots s0 + 64j + 16w + (0..15): all four waves' sub-tile j lie in logical
@@ -442,332 +167,6 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     case 3: hipLaunchKernelGGL(index_score_kernel<3>, grid, dim3(256), 0, stream, a); break;
     default: hipLaunchKernelGGL(index_score_kernel<4>, grid, dim3(256), 0, stream, a); break;
     }
-    return hipGetLastError();
-}
-
-// A lower bound of the k-th largest of the values v (G per thread, 0 =
-// absent): the floor of the 11-bit histogram bin (below the bits all values
-// share) that holds the k-th largest; 0 if fewer than k values are present.
-// Shared memory as for topk_select_keys, red with 3 * WAVES ints.
-template <int THREADS, int G>
-__device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uint32_t *hist,
-                                              int *red, int *sh) {
-    constexpr int WAVES = THREADS / 64;
-    constexpr int BPT = kHistBins / THREADS;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    uint32_t vmin = 0xffffffffu, vmax = 0u;
-    int cnt = 0;
-#pragma unroll
-    for (int g = 0; g < G; g++)
-        if (v[g]) {
-            vmin = min(vmin, v[g]);
-            vmax = max(vmax, v[g]);
-            cnt++;
-        }
-    vmin = wave_umin(vmin);
-    vmax = wave_umax(vmax);
-    cnt = wave_isum(cnt);
-    for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
-    if (lane == 0) {
-        red[w] = static_cast<int>(vmin);
-        red[WAVES + w] = static_cast<int>(vmax);
-        red[2 * WAVES + w] = cnt;
-    }
-    __syncthreads();
-    vmin = 0xffffffffu;
-    vmax = 0u;
-    cnt = 0;
-#pragma unroll
-    for (int i = 0; i < WAVES; i++) {
-        vmin = min(vmin, static_cast<uint32_t>(red[i]));
-        vmax = max(vmax, static_cast<uint32_t>(red[WAVES + i]));
-        cnt += red[2 * WAVES + i];
-    }
-    if (cnt < k) return 0u;
-    if (vmin == vmax) return vmin;
-    const int hi = 32 - __clz(vmin ^ vmax);
-    const int shift = hi > kHistBits ? hi - kHistBits : 0;
-#pragma unroll
-    for (int g = 0; g < G; g++)
-        if (v[g]) atomicAdd(&hist[(v[g] >> shift) & (kHistBins - 1)], 1u);
-    __syncthreads();
-    int cb[BPT], tot = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; b++) {
-        cb[b] = static_cast<int>(hist[kHistBins - 1 - BPT * tid - b]);
-        tot += cb[b];
-    }
-    const int incl = wave_incl_scan(tot);
-    if (lane == 63) red[w] = incl;                // red's reads above precede the last barrier
-    __syncthreads();
-    {
-        int run = -tot + incl;
-        for (int i = 0; i < w; i++) run += red[i];
-#pragma unroll
-        for (int b = 0; b < BPT; b++) {
-            if (run < k && run + cb[b] >= k) sh[0] = kHistBins - 1 - BPT * tid - b;
-            run += cb[b];
-        }
-    }
-    __syncthreads();
-    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
-    return (vmin & hi_mask) | (static_cast<uint32_t>(sh[0]) << shift);
-}
-
-// One 1024-thread workgroup per query, R scores per thread (R >= 4): wave w
-// owns slots [64Rw, 64R(w+1)) and lane l reads slots 64Rw + 256q + 4l + e
-// (e < 4) with one 16-byte load per round q, so the wave's slots run in
-// (q, lane, e) order.
-//
-// Prefilter: the four keys of a load are a group; any k group maxima are k
-// distinct scores, so the k-th largest maximum (and the floor L of its
-// histogram bin) is at most the k-th largest score: no key below L can be
-// selected.  The keys >= L (a few per cent of the list) are compacted, in
-// slot order, into LDS and the exact select runs on them with at most four
-// per thread.  If more than kCandCap keys pass, the select runs on all keys.
-constexpr int kCandCap = 4 * kTopkThreads;
-
-template <int R>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    static_assert(R >= 4, "16-byte score loads");
-    constexpr int R4 = R / 4;
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB
-    __shared__ __attribute__((aligned(16))) uint32_t cand_key[kCandCap];             // 16 KB
-    __shared__ int32_t cand_slot[kCandCap];                                          // 16 KB
-    __shared__ int red[3 * kTopkWaves];
-    __shared__ int sh[8];
-
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // the visible count first: its two dependent loads must not queue
-    // behind this workgroup's score loads
-    const int seq = a.q_seq[t];
-    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    n = n < a.max_slots ? n : a.max_slots;
-    const int k = a.k;
-    const int k_eff = n < k ? n : k;
-    int32_t *out = a.idx + static_cast<int64_t>(t) * k;
-    if (tid == 0) a.len[t] = k_eff;
-    if (n <= k) {   // everything visible is selected
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-        return;
-    }
-
-    // rows are 16-byte aligned: the launcher takes this kernel only for a
-    // 16-byte aligned score array whose row length is a multiple of 4
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
-    const int wbase = w * 64 * R;
-    uint32_t key[R];                              // key[4q + e]: slot wbase + 256q + 4 lane + e
-#pragma unroll
-    for (int q = 0; q < R4; q++) {
-        const int s0 = wbase + 256 * q + 4 * lane;
-        if (s0 + 3 < n) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(sc + s0);
-#pragma unroll
-            for (int e = 0; e < 4; e++) key[4 * q + e] = order_key(v[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++) key[4 * q + e] = s0 + e < n ? order_key(sc[s0 + e]) : 0u;
-        }
-    }
-    uint32_t gmax[R4];
-#pragma unroll
-    for (int q = 0; q < R4; q++)
-        gmax[q] = max(max(key[4 * q], key[4 * q + 1]), max(key[4 * q + 2], key[4 * q + 3]));
-    const uint32_t L = kth_floor<kTopkThreads, R4>(gmax, k, hist, red, sh);
-
-    // candidates per round and lane (keys are never 0 when valid)
-    int cl[R4], wc = 0;
-#pragma unroll
-    for (int q = 0; q < R4; q++) {
-        cl[q] = 0;
-#pragma unroll
-        for (int e = 0; e < 4; e++) cl[q] += (key[4 * q + e] != 0u && key[4 * q + e] >= L) ? 1 : 0;
-        wc += cl[q];
-    }
-    wc = wave_isum(wc);
-    __syncthreads();                              // every thread has read kth_floor's result
-    if (lane == 0) red[w] = wc;
-    __syncthreads();
-    int m = 0, run = 0;
-#pragma unroll
-    for (int i = 0; i < kTopkWaves; i++) {
-        m += red[i];
-        run += i < w ? red[i] : 0;
-    }
-    if (m > kCandCap) {
-        // crowded: the exact select over every key, in the one-key-per-lane layout
-        uint32_t key1[R];
-#pragma unroll
-        for (int j = 0; j < R; j++) {
-            const int s = wbase + 64 * j + lane;
-            key1[j] = s < n ? order_key(sc[s]) : 0u;
-        }
-        __syncthreads();                          // red is reused by the select
-        topk_select_keys<kTopkThreads, R>(key1, n, k, out, nullptr, hist, red, sh);
-        return;
-    }
-    // compact the candidates in slot order: round by round, lanes in order,
-    // a lane's four slots in order
-#pragma unroll
-    for (int q = 0; q < R4; q++) {
-        const int incl = wave_incl_scan(cl[q]);
-        int pos = run + incl - cl[q];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t kk = key[4 * q + e];
-            if (kk != 0u && kk >= L) {
-                cand_key[pos] = kk;
-                cand_slot[pos] = wbase + 256 * q + 4 * lane + e;
-                pos++;
-            }
-        }
-        run += __builtin_amdgcn_readlane(incl, 63);
-    }
-    __syncthreads();
-    if (m == k) {                                 // exactly the candidates
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = cand_slot[i];
-        return;
-    }
-    constexpr int Q = kCandCap / kTopkThreads;
-    uint32_t ck[Q];
-#pragma unroll
-    for (int i = 0; i < Q; i++) {
-        const int c = w * 64 * Q + 64 * i + lane;
-        ck[i] = c < m ? cand_key[c] : 0u;
-    }
-    topk_select_keys<kTopkThreads, Q>(ck, m, k, out, cand_slot, hist, red, sh);
-}
-
-// Short lists (up to 2048 visible slots) and rows not 16-byte aligned: the
-// exact select over every key, R per thread in the one-key-per-lane layout.
-template <int R>
-__global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(TopkArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];
-    __shared__ int red[2 * kTopkWaves];
-    __shared__ int sh[8];
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int seq = a.q_seq[t];
-    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    n = n < a.max_slots ? n : a.max_slots;
-    const int k = a.k;
-    const int k_eff = n < k ? n : k;
-    int32_t *out = a.idx + static_cast<int64_t>(t) * k;
-    if (tid == 0) a.len[t] = k_eff;
-    if (n <= k) {
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-        return;
-    }
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
-    const int wbase = w * 64 * R;
-    uint32_t key[R];
-#pragma unroll
-    for (int j = 0; j < R; j++) {
-        const int s = wbase + 64 * j + lane;
-        key[j] = s < n ? order_key(sc[s]) : 0u;
-    }
-    topk_select_keys<kTopkThreads, R>(key, n, k, out, nullptr, hist, red, sh);
-}
-
-
-// Visible lists longer than the register kernel holds (> 65536 slots, e.g. a
-// 1M-token context at ratio 4): the same radix select, re-reading the scores
-// from memory each pass, and an ordered write in 1024-slot rounds.
-__global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[kTopkWaves][256];
-    __shared__ int scan_sh[2 * kTopkWaves];
-    __shared__ int sel_sh[2];
-
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, w = tid >> 6;
-    const int seq = a.q_seq[t];
-    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    n = n < a.max_slots ? n : a.max_slots;
-    const int k = a.k;
-    const int k_eff = n < k ? n : k;
-    int32_t *out = a.idx + static_cast<int64_t>(t) * k;
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
-    if (tid == 0) a.len[t] = k_eff;
-    if (n <= k) {
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-        return;
-    }
-    uint32_t prefix = 0;
-    int remaining = k;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < n; i += kTopkThreads) {
-            uint32_t kk = order_key(sc[i]);
-            if ((kk & hi_mask) == prefix) atomicAdd(&hist[w][(kk >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        int cnt = 0;
-        if (tid < 256)
-            for (int ww = 0; ww < kTopkWaves; ww++) cnt += hist[ww][255 - tid];
-        const int incl = wave_incl_scan(cnt);
-        if (tid < 256 && (tid & 63) == 63) scan_sh[w] = incl;
-        __syncthreads();
-        if (tid < 256) {
-            int before = 0;
-            for (int ww = 0; ww < w; ww++) before += scan_sh[ww];
-            int excl = before + incl - cnt;
-            if (excl < remaining && excl + cnt >= remaining) {
-                sel_sh[0] = 255 - tid;
-                sel_sh[1] = remaining - excl;
-            }
-        }
-        __syncthreads();
-        prefix |= static_cast<uint32_t>(sel_sh[0]) << shift;
-        remaining = sel_sh[1];
-        __syncthreads();
-    }
-    const uint32_t thr = prefix;
-    const int take_eq = remaining;
-    int eq_done = 0, sel_done = 0;
-    for (int b0 = 0; b0 < n; b0 += kTopkThreads) {
-        int i = b0 + tid;
-        uint32_t kk = i < n ? order_key(sc[i]) : 0u;
-        int gt = (i < n && kk > thr) ? 1 : 0;
-        int eq = (i < n && kk == thr) ? 1 : 0;
-        int gt_b, eq_b;
-        block_scan2(gt, eq, scan_sh, gt_b, eq_b);
-        int eq_rank = eq_done + eq_b;
-        int before_sel = sel_done + gt_b + (eq_done + eq_b < take_eq ? eq_b : (take_eq > eq_done ? take_eq - eq_done : 0));
-        bool sel = gt || (eq && eq_rank < take_eq);
-        if (sel) out[before_sel] = i;
-        // block totals (scan_sh holds per-wave inclusive totals)
-        int tot_gt = 0, tot_eq = 0;
-        for (int ww = 0; ww < kTopkWaves; ww++) {
-            tot_gt += scan_sh[ww];
-            tot_eq += scan_sh[kTopkWaves + ww];
-        }
-        int eq_taken = eq_done + tot_eq < take_eq ? tot_eq : (take_eq > eq_done ? take_eq - eq_done : 0);
-        sel_done += tot_gt + eq_taken;
-        eq_done += tot_eq;
-        __syncthreads();
-    }
-    for (int i = k_eff + tid; i < k; i += kTopkThreads) out[i] = -1;
-}
-
-hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
-    const int per = (a.max_slots + kTopkThreads - 1) / kTopkThreads;
-    const bool vec = a.max_slots % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
-    dim3 grid(a.n_q), block(kTopkThreads);
-    if (per <= 1) hipLaunchKernelGGL(topk_small_kernel<1>, grid, block, 0, stream, a);
-    else if (per <= 2) hipLaunchKernelGGL(topk_small_kernel<2>, grid, block, 0, stream, a);
-    else if (!vec && per <= 16) hipLaunchKernelGGL(topk_small_kernel<16>, grid, block, 0, stream, a);
-    else if (!vec && per <= 64) hipLaunchKernelGGL(topk_small_kernel<64>, grid, block, 0, stream, a);
-    else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
-    else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
-    else if (per <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);
-    else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, a);
-    else if (per <= 64) hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(topk_long_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
