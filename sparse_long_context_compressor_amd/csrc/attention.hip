@@ -468,11 +468,16 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     if (S == 1) {
         store_out(a, t, h, g, o, M, L);
     } else {
-        // partial state: [t][split][h] (O unnormalised at max M, then M and L)
+        // partial state: [t][split][h]: O / L in bf16 (each value at most the
+        // largest |V| of the split's rows), then M and L in fp32
         const int64_t slot = (static_cast<int64_t>(t) * S + split) * a.n_heads + h;
-        float *po = a.part_o + slot * kDN + 4 * g;
+        uint16_t *po = a.part_o + slot * kDN + 4 * g;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) *reinterpret_cast<f32x4 *>(po + 16 * ct) = o[ct];
+        for (int ct = 0; ct < kDN / 16; ct++)
+            *reinterpret_cast<u32x2 *>(po + 16 * ct) =
+                u32x2{bf16_pair_rne(o[ct][0] * inv, o[ct][1] * inv),
+                      bf16_pair_rne(o[ct][2] * inv, o[ct][3] * inv)};
         if (g == 0) {
             a.part_ml[2 * slot] = M;
             a.part_ml[2 * slot + 1] = L;
@@ -480,8 +485,12 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     }
 }
 
-// Merge the list splits: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// One thread per (query, head, 4 output columns).
+// Merge the list splits: with O_s the split's normalised output,
+// out = sum_s l_s 2^(m_s - M) O_s / sum_s l_s 2^(m_s - M).
+// One thread per (query, head, 4 output columns).  SN > 0: exactly SN
+// splits, every load issued before any is used (no data-dependent branch
+// between them); SN = 0: any number, in a loop.
+template <int SN>
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
     const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t per_q = static_cast<int64_t>(a.n_heads) * (kDN / 4);
@@ -489,21 +498,44 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
     const int t = static_cast<int>(id / per_q);
     const int h = static_cast<int>((id % per_q) / (kDN / 4));
     const int c4 = static_cast<int>(id % (kDN / 4));
-    const int S = a.n_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < S; s++) {
-        const float *ml = a.part_ml + 2 * ((static_cast<int64_t>(t) * S + s) * a.n_heads + h);
-        if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
-    }
-    float L = 0.f;
+    const int S = SN > 0 ? SN : a.n_splits;
+    auto slot_of = [&](int sp) { return (static_cast<int64_t>(t) * S + sp) * a.n_heads + h; };
+    auto widen = [](u32x2 v) {
+        return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                     __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+    };
+    float M = -INFINITY, L = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; s++) {
-        const int64_t slot = (static_cast<int64_t>(t) * S + s) * a.n_heads + h;
-        const float l = a.part_ml[2 * slot + 1];
-        if (!(l > 0.f)) continue;
-        const float sc = exp2f(a.part_ml[2 * slot] - M);
-        L += l * sc;
-        acc += *reinterpret_cast<const f32x4 *>(a.part_o + slot * kDN + 4 * c4) * sc;
+    if constexpr (SN > 0) {
+        float mv[SN], lv[SN];
+        u32x2 ov[SN];
+#pragma unroll
+        for (int sp = 0; sp < SN; sp++) {
+            const int64_t slot = slot_of(sp);
+            mv[sp] = a.part_ml[2 * slot];
+            lv[sp] = a.part_ml[2 * slot + 1];
+            ov[sp] = *reinterpret_cast<const u32x2 *>(a.part_o + slot * kDN + 4 * c4);
+        }
+#pragma unroll
+        for (int sp = 0; sp < SN; sp++) M = lv[sp] > 0.f ? fmaxf(M, mv[sp]) : M;
+#pragma unroll
+        for (int sp = 0; sp < SN; sp++) {
+            const float wgt = lv[sp] > 0.f ? lv[sp] * exp2f(mv[sp] - M) : 0.f;
+            L += wgt;
+            acc += widen(ov[sp]) * wgt;
+        }
+    } else {
+        for (int sp = 0; sp < S; sp++) {
+            const float *ml = a.part_ml + 2 * slot_of(sp);
+            if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+        }
+        for (int sp = 0; sp < S; sp++) {
+            const int64_t slot = slot_of(sp);
+            const float l = a.part_ml[2 * slot + 1];
+            const float wgt = l > 0.f ? l * exp2f(a.part_ml[2 * slot] - M) : 0.f;
+            L += wgt;
+            acc += widen(*reinterpret_cast<const u32x2 *>(a.part_o + slot * kDN + 4 * c4)) * wgt;
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     *reinterpret_cast<u32x2 *>(a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + 4 * c4) =
@@ -643,8 +675,17 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.n_splits == 1) return e;
         const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / 4);
-        hipLaunchKernelGGL(mla_combine_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                           dim3(256), 0, stream, a);
+        const dim3 cgrid(static_cast<unsigned>((threads + 255) / 256)), cblock(256);
+        switch (a.n_splits) {
+        case 2: hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(mla_combine_kernel<3>, cgrid, cblock, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, stream, a); break;
+        case 5: hipLaunchKernelGGL(mla_combine_kernel<5>, cgrid, cblock, 0, stream, a); break;
+        case 6: hipLaunchKernelGGL(mla_combine_kernel<6>, cgrid, cblock, 0, stream, a); break;
+        case 7: hipLaunchKernelGGL(mla_combine_kernel<7>, cgrid, cblock, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, stream, a); break;
+        default: hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, cblock, 0, stream, a); break;
+        }
         return hipGetLastError();
     }
     const int hb = (a.n_heads + 63) / 64;          // head blocks of up to 64 heads

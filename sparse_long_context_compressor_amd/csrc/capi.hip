@@ -158,7 +158,9 @@ static size_t attn_ws(int n_q, int n_heads, int window, int k, bool decode) {
     attention_plan(n_q, n_heads, window, k, decode, &splits, &cps);
     if (splits <= 1) return 0;
     size_t per = static_cast<size_t>(n_q) * splits * n_heads;
-    size_t bytes = per * kDN * sizeof(float) + per * 2 * sizeof(float) + 256;
+    // bf16 normalised outputs, then (max, sum) pairs on a 16-byte boundary
+    size_t bytes = ((per * kDN * sizeof(uint16_t) + 15) & ~static_cast<size_t>(15)) +
+                   per * 2 * sizeof(float) + 256;
     return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
@@ -232,8 +234,9 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     a.rows_per_split = cps;
     if (splits > 1) {
         size_t per = static_cast<size_t>(n_q) * splits * n_heads;
-        a.part_o = static_cast<float *>(workspace);
-        a.part_ml = a.part_o + per * kDN;
+        a.part_o = static_cast<uint16_t *>(workspace);
+        a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                              ((per * kDN * sizeof(uint16_t) + 15) & ~static_cast<size_t>(15)));
     }
     return hip_status(launch_attention(a, decode, static_cast<hipStream_t>(stream)));
 }

@@ -66,7 +66,7 @@ struct AttnArgs {
     float *lse;
     int n_splits;           // decode: workgroups per (query, head group) along the list
     int rows_per_split;     // list entries each split covers (a multiple of 32)
-    float *part_o;          // [n_q][n_splits][H][512] (decode, n_splits > 1)
+    uint16_t *part_o;       // bf16 [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
 };
 
