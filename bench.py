@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy (y = -x, fp32) of this size, "
                          "the known-size kernel the HBM byte counters are scaled by")
+    ap.add_argument("--workload", default="c4a_decode_64k",
+                    choices=["c4a_decode_64k", "c4a_prefill_2k", "c128a_decode_128k",
+                             "swaonly_decode_b64", "c4a_single_layer_4k"],
+                    help="c4a_decode_64k is the headline; the others print supplementary "
+                         "per-stage timings of the same kernels on the other workloads")
     ap.add_argument("--report-stats", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
                     help="summarise a rocprofv3 --stats csv directory into OUT_MD and exit")
     ap.add_argument("--report-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_STEM"),
@@ -185,6 +190,110 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def other_workload(args):
+    """Per-stage timings of one pass over a non-headline workload (synthetic,
+    inputs resident, replicas cycled): one JSON line."""
+    import torch
+    from sparse_long_context_compressor_amd import inputs as I
+    from sparse_long_context_compressor_amd import slc
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    slc.lib()
+    name = args.workload
+    n_rep = 2 if name == "c4a_prefill_2k" else args.replicas
+    reps = [I.CONFIGS[name](seed=200 + r, device=dev) for r in range(n_rep)]
+    torch.cuda.synchronize()
+    log(f"{n_rep} input replicas of {name} resident")
+    lay0 = reps[0]
+    Q, Hh, Ww, Kk, HIi, r = lay0.n_q, lay0.H, lay0.W, lay0.k, lay0.H_I, lay0.ratio
+    ms_ = lay0.max_slots
+    decode = name != "c4a_prefill_2k"
+    stages = {}
+    if name == "c4a_single_layer_4k":
+        def compress(lay):
+            slc.compress(4, lay.cu_seqlens, 4096, lay.kv, lay.score, lay.gamma, lay.eps,
+                         lay.cos_sin, lay.cmp_pool, lay.cmp_table)
+        stages["compress"] = compress
+    if r == 4 and HIi > 0:
+        sc = torch.empty((Q, ms_), dtype=torch.float32, device=dev)
+        idx = torch.empty((Q, Kk), dtype=torch.int32, device=dev)
+        ln = torch.empty(Q, dtype=torch.int32, device=dev)
+
+        def index_scores(lay):
+            slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
+                             lay.key_table, lay.n_slots, ms_, sc)
+
+        def topk(lay):
+            slc.topk_select(Kk, sc, ms_, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
+        stages["index_scores"] = index_scores
+        stages["topk_select"] = topk
+        get_idx = lambda lay: idx  # noqa: E731
+    else:
+        get_idx = lambda lay: lay.given_idx  # noqa: E731
+    out = torch.empty((Q, Hh, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Q, Hh), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(slc.sparse_mla_workspace_size(decode, Q, Hh, Ww, Kk), 256),
+                     dtype=torch.uint8, device=dev)
+    f = slc.sparse_mla_decode if decode else slc.sparse_mla_prefill
+
+    def attention(lay):
+        if r == 1:
+            f(1, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, sm_scale=lay.sm_scale,
+              out=out, lse=lse, workspace=ws)
+        else:
+            f(r, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, lay.cmp_pool,
+              lay.cmp_table, get_idx(lay), lay.n_slots, lay.sm_scale, out, lse, ws)
+    stages["sparse_mla_decode" if decode else "sparse_mla_prefill"] = attention
+
+    def step(lay):
+        for fn in stages.values():
+            fn(lay)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(reps[i % len(reps)])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    steps = max(10, args.steps // (10 if name == "c4a_prefill_2k" else 1))
+    for i in range(args.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    ms_step = timed(step, steps)
+    per = {k: timed(fn, steps) * 1e3 for k, fn in stages.items()}
+    rec = {"workload": name, "queries": Q, "heads": Hh, "window": Ww, "topk": Kk,
+           "ms_per_pass": ms_step, "queries_per_s": Q / (ms_step * 1e-3), "stages_us": per,
+           "steps": steps, "data": "synthetic"}
+    # algorithmic bytes / flops of the attention stage
+    n_cmp = Kk if r > 1 else 0
+    att_us = per["sparse_mla_decode" if decode else "sparse_mla_prefill"]
+    if decode:
+        cmp_row = 672
+        b = Q * (Hh * 576 * 2 + Ww * 1152 + n_cmp * (cmp_row + 4) + Hh * 512 * 2 + Hh * 4)
+        rec["attention_GBps"] = b / (att_us * 1e-6) / 1e9
+        rec["attention_hbm_frac"] = rec["attention_GBps"] / HBM_PEAK_GBPS
+    else:
+        flops = 2.0 * Q * Hh * (Ww + n_cmp) * (576 + 512)
+        rec["attention_TFLOPs"] = flops / (att_us * 1e-6) / 1e12
+        rec["attention_mfma_frac_bf16"] = rec["attention_TFLOPs"] / BF16_PEAK_TFLOPS
+        if "index_scores" in per:
+            import numpy as np
+            nv = np.minimum(lay0.n_slots.cpu().numpy()[lay0.q_seq.cpu().numpy()],
+                            (lay0.q_pos.cpu().numpy() + 1) // 4)
+            iflops = 2.0 * float(nv.sum()) * HIi * 128
+            rec["index_TFLOPs"] = iflops / (per["index_scores"] * 1e-6) / 1e12
+            rec["index_mfma_frac_bf16"] = rec["index_TFLOPs"] / BF16_PEAK_TFLOPS
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.report_stats:
@@ -195,6 +304,9 @@ def main():
         print("bench.py: this build measures one GPU (the decode path shards by sequence with "
               "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "c4a_decode_64k":
+        return other_workload(args)
 
     import torch
     from sparse_long_context_compressor_amd import inputs as I

@@ -37,6 +37,7 @@ namespace {
 constexpr int kKPitch = kD + 8;        // bf16 per LDS row: 1168 B, spreads banks
 constexpr int kMaxEntries = SLC_MAX_WINDOW + SLC_MAX_TOPK;
 constexpr int kDecMaxEntries = 1024;   // list entries one decode workgroup resolves
+constexpr int kMaxCombineSplits = 8;    // splits the combine kernel merges unrolled
 
 typedef short i16x4v __attribute__((ext_vector_type(4)));
 
@@ -650,19 +651,39 @@ void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n
         *rows_per_split = entries;
         return;
     }
-    // split the list in 32-row units so that about one workgroup per CU runs,
-    // and no workgroup resolves more than kDecMaxEntries entries
+    // Split each (query, head block)'s list in 32-row units.  Cost model, in
+    // units of one 64-row chunk's compute: the chunks of a split, plus a fixed
+    // kSplitCost for splitting at all (partial store, combine kernel), times
+    // the waves of workgroups (one workgroup per CU: 256 run at once).  A
+    // workgroup resolves at most kDecMaxEntries entries and the combine merges
+    // at most kMaxCombineSplits splits.
+    constexpr int kCUs = 256;
+    constexpr float kSplitCost = 3.2f;
     const int blocks = (n_q > 0 ? n_q : 1) * (n_heads / (16 * decode_groups(n_heads)));
     const int units = entries > 0 ? (entries + 31) / 32 : 1;
-    int splits = (256 + blocks - 1) / blocks;
-    if (splits > units) splits = units;
     const int min_splits = (entries + kDecMaxEntries - 1) / kDecMaxEntries;
-    if (splits < min_splits) splits = min_splits;
-    if (splits < 1) splits = 1;
-    int per = (units + splits - 1) / splits;
-    while (per * 32 > kDecMaxEntries) per--;     // never taken (min_splits), kept as a bound
-    *rows_per_split = per * 32;
-    *n_splits = (units + per - 1) / per;
+    int best = -1, best_per = units;
+    float best_cost = 0.f;
+    for (int sp = 1; sp <= kMaxCombineSplits && sp <= units; sp++) {
+        const int per = (units + sp - 1) / sp;
+        if (per * 32 > kDecMaxEntries) continue;
+        const int used = (units + per - 1) / per;           // splits actually formed
+        if (used != sp) continue;
+        const int waves = (blocks * used + kCUs - 1) / kCUs;
+        const float cost = (static_cast<float>((per * 32 + kDecRows - 1) / kDecRows) +
+                            (used > 1 ? kSplitCost : 0.f)) * static_cast<float>(waves);
+        if (best < 0 || cost < best_cost) {
+            best = used;
+            best_per = per;
+            best_cost = cost;
+        }
+    }
+    if (best < 0) {                                          // only when entries exceed the caps
+        best = min_splits > 0 ? min_splits : 1;
+        best_per = (units + best - 1) / best;
+    }
+    *rows_per_split = best_per * 32;
+    *n_splits = (units + best_per - 1) / best_per;
 }
 
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) {
