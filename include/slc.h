@@ -164,8 +164,8 @@ slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int m
  * (ReLU(a*b*x) = a*b*ReLU(x) for a, b > 0).
  *
  *   n_q          queries;  h_idx  indexer heads (multiple of 16, <= 64)
- *   q_fp8        device e4m3 [n_q][h_idx][128]
- *   q_scale, w   device fp32 [n_q][h_idx]
+ *   q_fp8        device e4m3 [n_q][h_idx][128], 16-byte aligned
+ *   q_scale, w   device fp32 [n_q][h_idx], 16-byte aligned
  *   q_seq, q_pos device int32 [n_q] (sequence and position of each query)
  *   ratio        4 (the indexer exists for c4a layers)
  *   key_pool     KEY layout, one table row per sequence

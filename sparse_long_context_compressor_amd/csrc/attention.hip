@@ -337,8 +337,9 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 x[4 * rt + i] = rv[4 * rt + i] >= 0 ? sacc[rt][i] * a.sm_scale_log2 : -INFINITY;
+        const bool had = m_run != -INFINITY;             // O holds something to rescale
         const float alpha = softmax_update<4 * NG>(x, m_run, l_run, pv);
-        if (__ballot(alpha != 1.f)) {
+        if (__ballot(had && alpha != 1.f)) {
 #pragma unroll
             for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
         }
@@ -617,8 +618,9 @@ void mla_prefill_kernel(AttnArgs a) {
                 int e = e0 + 16 * mt + 4 * g + i;
                 x[4 * mt + i] = (e < E && src[e] >= 0) ? sacc[mt][i] * a.sm_scale_log2 : -INFINITY;
             }
+        const bool had = m_run != -INFINITY;
         const float alpha = softmax_update<8>(x, m_run, l_run, pv);
-        if (__ballot(alpha != 1.f)) {
+        if (__ballot(had && alpha != 1.f)) {
 #pragma unroll
             for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
         }

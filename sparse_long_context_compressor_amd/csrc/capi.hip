@@ -99,7 +99,8 @@ slc_status_t slc_index_scores(int n_q, int h_idx, const uint8_t *q_fp8, const fl
     if (n_q == 0) return SLC_OK;
     if (!q_fp8 || !q_scale || !w || !scores)
         return fail("index_scores: q_fp8, q_scale, w and scores are required");
-    if (!aligned(q_fp8, 16)) return fail("index_scores: q_fp8 must be 16-byte aligned");
+    if (!aligned(q_fp8, 16) || !aligned(q_scale, 16) || !aligned(w, 16))
+        return fail("index_scores: q_fp8, q_scale and w must be 16-byte aligned");
     st = check_pool(key_pool, "index_scores: key_pool");
     if (st != SLC_OK) return st;
     IndexArgs a{n_q, h_idx, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, n_slots, max_slots,

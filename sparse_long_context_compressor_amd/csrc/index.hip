@@ -67,27 +67,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     const int g = lane >> 4, c = lane & 15;
     const int s0 = blockIdx.y * kScoreTile;
 
-    // ---- query operands and per-head factors (they depend on t only) ----
-    bf16x8 qa[HT][4];
-    float hf[HT][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ht++) {
-        const uint8_t *qp = a.q + (static_cast<int64_t>(t) * a.h_idx + 16 * ht + c) * kDI;
-        u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
-        u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
-        e4m3x16_to_operands(lo, qa[ht][0], qa[ht][1]);
-        e4m3x16_to_operands(hi, qa[ht][2], qa[ht][3]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int h = 16 * ht + 4 * g + i;
-            int64_t o = static_cast<int64_t>(t) * a.h_idx + h;
-            hf[ht][i] = a.w[o] * a.q_scale[o];
-        }
-    }
-
-    // the tile's 16 block-table entries in one load (lane j % 16 takes entry
-    // j); each sub-tile then moves its entry to a scalar register, so no key
-    // load waits on a table lookup of its own
+    // The tile's 16 block-table entries first, in one load (lane j % 16 takes
+    // entry j): the first key loads wait on them, and vector loads complete
+    // in issue order.  Each sub-tile later moves its entry to a scalar
+    // register, so no key load waits on a table lookup of its own.
     const int seq = a.q_seq[t];
     const int64_t table_row = static_cast<int64_t>(seq) * a.keys.table_stride;
     int32_t my_pb = -1;
@@ -95,9 +78,25 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
         const int64_t lb = (s0 >> 6) + (lane & 15);
         if (lb < a.keys.table_stride) my_pb = a.keys.block_table[table_row + lb];
     }
+
+    // ---- query operands and per-head factors (they depend on t only) ----
+    // raw loads now; the conversions follow the first key loads
+    u32x4 qlo[HT], qhi[HT];
+    f32x4 qw[HT], qs[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        const uint8_t *qp = a.q + (static_cast<int64_t>(t) * a.h_idx + 16 * ht + c) * kDI;
+        qlo[ht] = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
+        qhi[ht] = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
+        const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
+        qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
+        qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
+    }
     int nv = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
     nv = nv < a.max_slots ? nv : a.max_slots;
     if (s0 >= nv) return;
+    bf16x8 qa[HT][4];                            // filled after the first key loads are issued
+    float hf[HT][4];
 
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
     const uint32_t lane_off = static_cast<uint32_t>((16 * w + c) * kDI + 16 * g);
@@ -145,6 +144,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     KeyStage buf0[kRing], buf1[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
+
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        e4m3x16_to_operands(qlo[ht], qa[ht][0], qa[ht][1]);
+        e4m3x16_to_operands(qhi[ht], qa[ht][2], qa[ht][3]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) hf[ht][i] = qw[ht][i] * qs[ht][i];
+    }
 #pragma unroll
     for (int q = 0; q < kSubTiles / kRing; q++) {
         KeyStage (&cur)[kRing] = (q & 1) ? buf1 : buf0;
