@@ -225,12 +225,13 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
  *   layer_type   SLC_LAYER_SWAONLY (cmp_pool, cmp_idx ignored; k must be 0),
  *                SLC_LAYER_C4A or SLC_LAYER_C128A (cmp_pool, cmp_idx required)
  *   n_q, n_heads queries and query heads (multiple of 16, <= 128)
- *   q            device bf16 [n_q][n_heads][576]
+ *   q            device bf16 [n_q][n_heads][576], 16-byte aligned
  *   q_seq, q_pos device int32 [n_q]
  *   window       sliding-window length, 0 .. SLC_MAX_WINDOW
  *   cmp_idx      device int32 [n_q][k] logical slot ids (-1 = none)
  *   n_slots      device int32 [n_seq]
- *   out          device bf16 [n_q][n_heads][512];  lse nullable fp32 [n_q][n_heads]
+ *   out          device bf16 [n_q][n_heads][512], 16-byte aligned;
+ *                lse nullable fp32 [n_q][n_heads]
  *   workspace    device, >= the matching *_workspace_size bytes, 256-B aligned
  * Decode splits each query's list across workgroups and merges the partial
  * softmax states; prefill gives each query token its own workgroup.  Both

@@ -207,6 +207,30 @@ __device__ __forceinline__ void store_out(const AttnArgs &a, int t, int h, int g
             l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
+// A wave's O^T accumulators (lane (g, c): head c, dims 16ct + 4g + i) times
+// `scale`, as bf16 rows [16 heads][512] at dst (rows kDN apart).  The rows go
+// through LDS first (stage: 16 rows of kStagePitch bf16, this wave's own), so
+// that each global store writes one head's whole 1 KB row, 16 B per lane;
+// storing the accumulators directly would write 32-byte pieces of 16 rows
+// per instruction.  LDS operations of one wave complete in order, so the
+// wave reads back its own writes without a barrier.
+constexpr int kStagePitch = kDN + 8;   // 1040 B: the 8-byte writes of 32 lanes hit distinct banks
+
+__device__ __forceinline__ void store_rows_bf16(const f32x4 (&o)[kDN / 16], float scale,
+                                                uint16_t *stage, uint16_t *dst, int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int ct = 0; ct < kDN / 16; ct++)
+        *reinterpret_cast<u32x2 *>(stage + c * kStagePitch + 16 * ct + 4 * g) =
+            u32x2{bf16_pair_rne(o[ct][0] * scale, o[ct][1] * scale),
+                  bf16_pair_rne(o[ct][2] * scale, o[ct][3] * scale)};
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        *reinterpret_cast<u32x4 *>(dst + r * kDN + 8 * lane) =
+            *reinterpret_cast<const u32x4 *>(stage + r * kStagePitch + 8 * lane);
+}
+
 constexpr int kDecRows = 64;   // rows per decode chunk (16 per consumer wave)
 constexpr int kPreRows = 32;   // rows per prefill chunk
 
@@ -224,62 +248,148 @@ constexpr int kPreRows = 32;   // rows per prefill chunk
 template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
+    static_assert(2 * 16 * kStagePitch <= kDecRows * kKPitch, "tile 1 stages two waves' output rows");
     __shared__ int32_t src[kDecMaxEntries];
     __shared__ float st_m[4][16], st_l[4][16];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const bool producer = w >= 4;
+
+    // The prologue's kernel arguments in one round of loads, before anything
+    // branches on them (left alone, the compiler spreads them over several
+    // dependent rounds at the start, where each costs a full load latency).
+    const int32_t *q_seq_p = a.q_seq, *q_pos_p = a.q_pos, *n_slots_p = a.n_slots;
+    const int32_t *cmp_idx_p = a.cmp_idx, *swa_tab = a.swa.block_table, *cmp_tab = a.cmp.block_table;
+    const int swa_stride = a.swa.table_stride, cmp_stride = a.cmp.table_stride;
+    const int64_t swa_nb = a.swa.n_blocks, cmp_nb = a.cmp.n_blocks;
+    const int window = a.window, kk = a.k, n_q = a.n_q, rps = a.rows_per_split;
     const int HB = a.n_heads / (16 * NG), S = a.n_splits;
+    __asm__ volatile("" ::"s"(q_seq_p), "s"(q_pos_p), "s"(n_slots_p), "s"(cmp_idx_p), "s"(swa_tab),
+                     "s"(cmp_tab), "s"(swa_stride), "s"(cmp_stride), "s"(swa_nb), "s"(cmp_nb),
+                     "s"(window), "s"(kk), "s"(n_q), "s"(rps), "s"(HB), "s"(S));
+
     // blocks with equal blockIdx % 8 run on one XCD: give all (head block,
     // split) blocks of a query the same residue, so they share its L2
     const int per_group = 8 * HB * S;
     const int grp = blockIdx.x / per_group, rem = blockIdx.x % per_group;
     const int t = 8 * grp + (rem & 7);
     const int hb = (rem >> 3) % HB, split = (rem >> 3) / HB;
-    if (t >= a.n_q) return;
+    const int tc = t < n_q ? t : 0;                     // for the prologue's loads (n_q >= 1)
 
     const int hgw = NG == 2 ? (w & 1) : 0;
     const int h = 16 * (NG * hb + hgw) + c;
     const int row0 = NG == 2 ? 32 * ((w >> 1) & 1) : 16 * (w & 3);   // first chunk row of this wave
-    const int seq = a.q_seq[t], p = a.q_pos[t];
-    const int E = a.window + a.k;
-    const int ns = a.k > 0 ? a.n_slots[seq] : 0;
-    const int e_begin = split * a.rows_per_split;
-    int e_end = e_begin + a.rows_per_split;
+    const int E = window + kk;
+    const int e_begin = split * rps;
+    int e_end = e_begin + rps;
     e_end = e_end < E ? e_end : E;
     const int nchunks = e_end > e_begin ? (e_end - e_begin + kDecRows - 1) / kDecRows : 0;
 
-    // the row lists first: their short chain of dependent loads would
-    // otherwise queue behind the query loads of every workgroup
-    for (int e = e_begin + tid; e < e_end; e += 512) src[e - e_begin] = resolve_entry(a, t, seq, p, ns, e);
+    // The row list first, in two rounds of loads with no branch between them:
+    // the compressed entries' slot ids need only t and are loaded with the
+    // query's sequence and position; then every entry's block-table entry
+    // (one load each, from the SWA or the compressed table) and the
+    // sequence's slot count.  An entry with nothing to look up loads a valid
+    // dummy address instead.  The split plan keeps e_end - e_begin within
+    // kDecMaxEntries.
+    constexpr int kResIt = kDecMaxEntries / 512;
+    int32_t slot_id[kResIt];
+#pragma unroll
+    for (int i = 0; i < kResIt; i++) {
+        const int e = e_begin + tid + 512 * i;
+        const bool cmpe = e < e_end && e >= window;
+        slot_id[i] = *(cmpe ? cmp_idx_p + static_cast<int64_t>(tc) * kk + (e - window) : q_seq_p);
+    }
+    const int seq = q_seq_p[tc], p = q_pos_p[tc];
+    if (t >= n_q) return;
+    int32_t pb[kResIt];
+    int64_t lrow[kResIt];
+    bool look[kResIt];
+#pragma unroll
+    for (int i = 0; i < kResIt; i++) {
+        const int e = e_begin + tid + 512 * i;
+        const bool swa = e < window;
+        lrow[i] = swa ? static_cast<int64_t>(p - window + 1 + e) : static_cast<int64_t>(slot_id[i]);
+        const int64_t lb = lrow[i] >> 6;
+        look[i] = e < e_end && lrow[i] >= 0 && lb < (swa ? swa_stride : cmp_stride);
+        const int32_t *tab = swa ? swa_tab + static_cast<int64_t>(seq) * swa_stride
+                                 : cmp_tab + static_cast<int64_t>(seq) * cmp_stride;
+        pb[i] = *(look[i] ? tab + lb : q_seq_p);
+    }
+    const int ns = *(kk > 0 ? n_slots_p + seq : q_seq_p);   // read only where kk > 0
+#pragma unroll
+    for (int i = 0; i < kResIt; i++) {
+        const bool swa = e_begin + tid + 512 * i < window;
+        pb[i] = look[i] && pb[i] >= 0 && pb[i] < (swa ? swa_nb : cmp_nb) && (swa || lrow[i] < ns)
+                    ? pb[i] * kBR + static_cast<int32_t>(lrow[i] & (kBR - 1)) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kResIt; i++) {
+        const int e = e_begin + tid + 512 * i;
+        if (e < e_end) src[e - e_begin] = pb[i];
+    }
     __syncthreads();
-    bf16x8 qb[kD / 32];
-    if (!producer) load_q(a, t, h, g, qb);   // lands while the first chunk is gathered
+
+    // The block's 16*NG query heads are one contiguous run of q.  The
+    // consumers load it once, coalesced (every 128-byte line by one request;
+    // per-head operand loads would request each line four times), into tile 1,
+    // which is free until chunk 1 is stored; after one barrier (the producers
+    // take it before their first store) each wave reads its head group's
+    // operands from there, rows at the K tile's pitch.
+    constexpr int kQUnits = 16 * NG * kD / 8;            // 16-byte units
+    constexpr int kQIt = (kQUnits + 255) / 256;
+    if (!producer) {
+        const uint16_t *qsrc = a.q + (static_cast<int64_t>(t) * a.n_heads + 16 * NG * hb) * kD;
+        u32x4 qv[kQIt];
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = tid + 256 * i;
+            if (u < kQUnits) qv[i] = *reinterpret_cast<const u32x4 *>(qsrc + 8 * u);
+        }
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = tid + 256 * i;
+            if (u < kQUnits)
+                *reinterpret_cast<u32x4 *>(&ktile[1][(u / (kD / 8)) * kKPitch + 8 * (u % (kD / 8))]) = qv[i];
+        }
+    }
 
     constexpr int kMergeBarriers = NG == 2 ? 2 : 4;
     if (producer) {
+        // The loads are issued unconditionally (chunks past the list read the
+        // zero page): with the same number of loads in flight on every path,
+        // storing one buffer waits for that buffer's loads only, not for the
+        // other buffer's as well.
         RowGather<kDecRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - 4);
-        if (nchunks > 0) ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
-        if (nchunks > 1) gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
+        ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
+        gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
+        __syncthreads();                                // the consumers' Q is in tile 1
         for (int ci = 0; ci < nchunks; ci += 2) {
             const int e0 = e_begin + ci * kDecRows;
             ga.store(ktile[0], a, e0, pw, lane);
             __syncthreads();                            // chunk ci ready in tile 0
-            if (ci + 2 < nchunks) ga.load(a, src, e_begin, e0 + 2 * kDecRows, e_end, pw, lane);
+            ga.load(a, src, e_begin, e0 + 2 * kDecRows, e_end, pw, lane);
             if (ci + 1 < nchunks) {
                 // tile 1 last held chunk ci-1, whose consumers passed the barrier above
                 gb.store(ktile[1], a, e0 + kDecRows, pw, lane);
                 __syncthreads();                        // chunk ci+1 ready in tile 1
-                if (ci + 3 < nchunks) gb.load(a, src, e_begin, e0 + 3 * kDecRows, e_end, pw, lane);
             }
+            gb.load(a, src, e_begin, e0 + 3 * kDecRows, e_end, pw, lane);
         }
 #pragma unroll
         for (int i = 0; i < kMergeBarriers; i++) __syncthreads();   // the consumers' merge
         return;
     }
 
+    __syncthreads();                                    // Q staged in tile 1
+    bf16x8 qb[kD / 32];                                 // Q^T operands: head 16*hgw + c, dims 8g + 32s
+    {
+        const uint16_t *qs = &ktile[1][(16 * hgw + c) * kKPitch + 8 * g];
+#pragma unroll
+        for (int s = 0; s < kD / 32; s++) qb[s] = *reinterpret_cast<const bf16x8 *>(qs + 32 * s);
+    }
     f32x4 o[kDN / 16];
 #pragma unroll
     for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -467,19 +577,19 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
     }
 
+    // O / L as bf16 rows: the output, or with list splits the partial state
+    // [t][split][h] (each value at most the largest |V| of the split's rows)
+    // plus M and L in fp32.  Tile 1 is free now: it stages the rows.
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int hw0 = h - c;                              // the wave's first head
+    uint16_t *stage = &ktile[1][hgw * 16 * kStagePitch];
     if (S == 1) {
-        store_out(a, t, h, g, o, M, L);
+        store_rows_bf16(o, inv, stage, a.out + (static_cast<int64_t>(t) * a.n_heads + hw0) * kDN, lane);
+        if (a.lse && g == 0)
+            a.lse[static_cast<int64_t>(t) * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
     } else {
-        // partial state: [t][split][h]: O / L in bf16 (each value at most the
-        // largest |V| of the split's rows), then M and L in fp32
         const int64_t slot = (static_cast<int64_t>(t) * S + split) * a.n_heads + h;
-        uint16_t *po = a.part_o + slot * kDN + 4 * g;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++)
-            *reinterpret_cast<u32x2 *>(po + 16 * ct) =
-                u32x2{bf16_pair_rne(o[ct][0] * inv, o[ct][1] * inv),
-                      bf16_pair_rne(o[ct][2] * inv, o[ct][3] * inv)};
+        store_rows_bf16(o, inv, stage, a.part_o + (slot - c) * kDN, lane);
         if (g == 0) {
             a.part_ml[2 * slot] = M;
             a.part_ml[2 * slot + 1] = L;
@@ -570,19 +680,21 @@ void mla_prefill_kernel(AttnArgs a) {
     if (w >= NW) {
         RowGather<kPreRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - NW);
-        if (E > 0) ga.load(a, src, 0, 0, E, pw, lane);
-        if (kPreRows < E) gb.load(a, src, 0, kPreRows, E, pw, lane);
+        // unconditional loads (past the list: the zero page), so that a
+        // buffer's store waits for its own loads only
+        ga.load(a, src, 0, 0, E, pw, lane);
+        gb.load(a, src, 0, kPreRows, E, pw, lane);
         for (int e0 = 0; e0 < E; e0 += 2 * kPreRows) {
             if (e0 != 0) __syncthreads();
             ga.store(ktile, a, e0, pw, lane);
             __syncthreads();
-            if (e0 + 2 * kPreRows < E) ga.load(a, src, 0, e0 + 2 * kPreRows, E, pw, lane);
+            ga.load(a, src, 0, e0 + 2 * kPreRows, E, pw, lane);
             if (e0 + kPreRows < E) {
                 __syncthreads();
                 gb.store(ktile, a, e0 + kPreRows, pw, lane);
                 __syncthreads();
-                if (e0 + 3 * kPreRows < E) gb.load(a, src, 0, e0 + 3 * kPreRows, E, pw, lane);
             }
+            gb.load(a, src, 0, e0 + 3 * kPreRows, E, pw, lane);
         }
         return;
     }

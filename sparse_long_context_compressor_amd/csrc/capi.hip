@@ -193,8 +193,8 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     if (!std::isfinite(sm_scale)) return fail("sparse_mla: sm_scale must be finite");
     if (n_q == 0) return SLC_OK;
     if (!q || !q_seq || !q_pos || !out) return fail("sparse_mla: q, q_seq, q_pos and out are required");
-    if (!aligned(q, 16) || !aligned(out, 8))
-        return fail("sparse_mla: q must be 16-byte and out 8-byte aligned");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail("sparse_mla: q and out must be 16-byte aligned");
     slc_status_t st;
     if (window > 0) {
         st = check_pool(swa_pool, "sparse_mla: swa_pool");
