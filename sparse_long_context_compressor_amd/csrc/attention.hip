@@ -599,60 +599,68 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
 
 // Merge the list splits: with O_s the split's normalised output,
 // out = sum_s l_s 2^(m_s - M) O_s / sum_s l_s 2^(m_s - M).
-// One thread per (query, head, 4 output columns).  SN > 0: exactly SN
-// splits, every load issued before any is used (no data-dependent branch
-// between them); SN = 0: any number, in a loop.
+// One thread per (query, head, 8 output columns): one 16-byte load of O and
+// one 8-byte load of (m, l) per split.  SN > 0: exactly SN splits, every
+// load issued before any is used (no data-dependent branch between them);
+// SN = 0: any number, in a loop.
+constexpr int kCombCols = 8;
+
 template <int SN>
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
     const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t per_q = static_cast<int64_t>(a.n_heads) * (kDN / 4);
+    const int64_t per_q = static_cast<int64_t>(a.n_heads) * (kDN / kCombCols);
     if (id >= per_q * a.n_q) return;
     const int t = static_cast<int>(id / per_q);
-    const int h = static_cast<int>((id % per_q) / (kDN / 4));
-    const int c4 = static_cast<int>(id % (kDN / 4));
+    const int h = static_cast<int>((id % per_q) / (kDN / kCombCols));
+    const int c8 = static_cast<int>(id % (kDN / kCombCols));
     const int S = SN > 0 ? SN : a.n_splits;
     auto slot_of = [&](int sp) { return (static_cast<int64_t>(t) * S + sp) * a.n_heads + h; };
-    auto widen = [](u32x2 v) {
-        return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
-                     __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+    auto ml_of = [&](int64_t slot) { return *reinterpret_cast<const f32x2 *>(a.part_ml + 2 * slot); };
+    auto o_of = [&](int64_t slot) {
+        return *reinterpret_cast<const u32x4 *>(a.part_o + slot * kDN + kCombCols * c8);
     };
     float M = -INFINITY, L = 0.f;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float acc[kCombCols] = {};
+    auto add = [&](u32x4 v, float wgt) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            acc[2 * j] += __uint_as_float(v[j] << 16) * wgt;
+            acc[2 * j + 1] += __uint_as_float(v[j] & 0xffff0000u) * wgt;
+        }
+    };
     if constexpr (SN > 0) {
-        float mv[SN], lv[SN];
-        u32x2 ov[SN];
+        f32x2 ml[SN];
+        u32x4 ov[SN];
 #pragma unroll
         for (int sp = 0; sp < SN; sp++) {
-            const int64_t slot = slot_of(sp);
-            mv[sp] = a.part_ml[2 * slot];
-            lv[sp] = a.part_ml[2 * slot + 1];
-            ov[sp] = *reinterpret_cast<const u32x2 *>(a.part_o + slot * kDN + 4 * c4);
+            ml[sp] = ml_of(slot_of(sp));
+            ov[sp] = o_of(slot_of(sp));
         }
 #pragma unroll
-        for (int sp = 0; sp < SN; sp++) M = lv[sp] > 0.f ? fmaxf(M, mv[sp]) : M;
+        for (int sp = 0; sp < SN; sp++) M = ml[sp][1] > 0.f ? fmaxf(M, ml[sp][0]) : M;
 #pragma unroll
         for (int sp = 0; sp < SN; sp++) {
-            const float wgt = lv[sp] > 0.f ? lv[sp] * exp2f(mv[sp] - M) : 0.f;
+            const float wgt = ml[sp][1] > 0.f ? ml[sp][1] * exp2f(ml[sp][0] - M) : 0.f;
             L += wgt;
-            acc += widen(ov[sp]) * wgt;
+            add(ov[sp], wgt);
         }
     } else {
         for (int sp = 0; sp < S; sp++) {
-            const float *ml = a.part_ml + 2 * slot_of(sp);
+            const f32x2 ml = ml_of(slot_of(sp));
             if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
         }
         for (int sp = 0; sp < S; sp++) {
-            const int64_t slot = slot_of(sp);
-            const float l = a.part_ml[2 * slot + 1];
-            const float wgt = l > 0.f ? l * exp2f(a.part_ml[2 * slot] - M) : 0.f;
+            const f32x2 ml = ml_of(slot_of(sp));
+            const float wgt = ml[1] > 0.f ? ml[1] * exp2f(ml[0] - M) : 0.f;
             L += wgt;
-            acc += widen(*reinterpret_cast<const u32x2 *>(a.part_o + slot * kDN + 4 * c4)) * wgt;
+            add(o_of(slot_of(sp)), wgt);
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    *reinterpret_cast<u32x2 *>(a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + 4 * c4) =
-        u32x2{bf16_pair_rne(acc[0] * inv, acc[1] * inv), bf16_pair_rne(acc[2] * inv, acc[3] * inv)};
-    if (a.lse && c4 == 0)
+    *reinterpret_cast<u32x4 *>(a.out + (static_cast<int64_t>(t) * a.n_heads + h) * kDN + kCombCols * c8) =
+        u32x4{bf16_pair_rne(acc[0] * inv, acc[1] * inv), bf16_pair_rne(acc[2] * inv, acc[3] * inv),
+              bf16_pair_rne(acc[4] * inv, acc[5] * inv), bf16_pair_rne(acc[6] * inv, acc[7] * inv)};
+    if (a.lse && c8 == 0)
         a.lse[static_cast<int64_t>(t) * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -809,7 +817,7 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) 
         else hipLaunchKernelGGL(mla_decode_kernel<1>, grid, dim3(512), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.n_splits == 1) return e;
-        const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / 4);
+        const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / kCombCols);
         const dim3 cgrid(static_cast<unsigned>((threads + 255) / 256)), cblock(256);
         switch (a.n_splits) {
         case 2: hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, stream, a); break;
