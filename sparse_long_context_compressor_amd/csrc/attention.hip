@@ -234,6 +234,135 @@ __device__ __forceinline__ void store_rows_bf16(const f32x4 (&o)[kDN / 16], floa
 constexpr int kDecRows = 64;   // rows per decode chunk (16 per consumer wave)
 constexpr int kPreRows = 32;   // rows per prefill chunk
 
+// One slice of 16*NR rows of a chunk for one wave's 16 heads: the scores
+// S^T = K . Q^T of NR 16-row tiles, the online-softmax update, and
+// O^T += V^T . P^T.  The slice starts at tile row row0 = list entry e0;
+// entries at or past e_end are masked, src maps entries (counted from
+// e_begin) to physical rows (-1: skipped).
+template <int NR>
+__device__ __forceinline__ void attend_rows(const uint16_t *tile, int row0, int e0, int e_begin,
+                                            int e_end, const int32_t *src,
+                                            const bf16x8 (&qb)[kD / 32], float sm_scale_log2,
+                                            f32x4 (&o)[kDN / 16], float &m_run, float &l_run,
+                                            int g, int c) {
+    // a scheduling region of its own: the LDS-read and MFMA groups pinned
+    // below must not interleave with those of a neighbouring slice
+    __builtin_amdgcn_sched_barrier(0);
+    // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need them)
+    int32_t rv[4 * NR];
+#pragma unroll
+    for (int rt = 0; rt < NR; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = e0 + 16 * rt + 4 * g + i;
+            rv[4 * rt + i] = e < e_end ? src[e - e_begin] : -1;
+        }
+    // S^T per 16-row tile: software-pipelined LDS reads (group i+1 in
+    // flight while group i feeds the MFMAs), two accumulator chains; the
+    // order is pinned with scheduling group barriers
+    f32x4 sacc[NR];
+#pragma unroll
+    for (int rt = 0; rt < NR; rt++) {
+        const uint16_t *kr = tile + (row0 + 16 * rt + c) * kKPitch + 8 * g;
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int G = 3, NRR = kD / 32 / G;   // 6 groups of 3 k-steps
+        bf16x8 ka[2][G];
+        auto rd = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++)
+                ka[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * (gi * G + u)));
+            __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
+        };
+        auto mm = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++) {
+                if (u & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s1, 0, 0, 0);
+                else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s0, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int gi = 0; gi < NRR; gi++) {
+            if (gi + 1 < NRR) rd(gi + 1, (gi + 1) & 1);
+            mm(gi, gi & 1);
+        }
+        sacc[rt] = s0 + s1;
+    }
+    float x[4 * NR], pv[4 * NR];
+#pragma unroll
+    for (int rt = 0; rt < NR; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            x[4 * rt + i] = rv[4 * rt + i] >= 0 ? sacc[rt][i] * sm_scale_log2 : -INFINITY;
+    const bool had = m_run != -INFINITY;             // O holds something to rescale
+    const float alpha = softmax_update<4 * NR>(x, m_run, l_run, pv);
+    if (__ballot(had && alpha != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
+    }
+
+    // O^T += V^T . P^T over the wave's rows; the k order (rows 4g+i, then
+    // 16+4g+i) is the score accumulators' lane order
+    const uint16_t *vr = tile + (row0 + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
+    if constexpr (NR == 1) {
+        i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
+                                                     bf16_pair_rne(pv[2], pv[3])});
+        constexpr int G = 4, NRR = kDN / 16 / G;   // 8 groups of 4 column tiles
+        i16x4 va[2][G];
+        auto rd = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
+            __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
+        };
+        auto mm = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++)
+                o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(i16x4v, va[b][u]), pb, o[gi * G + u], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int gi = 0; gi < NRR; gi++) {
+            if (gi + 1 < NRR) rd(gi + 1, (gi + 1) & 1);
+            mm(gi, gi & 1);
+        }
+    } else {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
+                          bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
+        const uint16_t *vr2 = vr + 16 * kKPitch;
+        constexpr int G = 4, NRR = kDN / 16 / G;
+        i16x4 va[2][G], vb[2][G];
+        auto rd = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++) {
+                va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
+                vb[b][u] = lds_read_tr16(vr2 + 16 * (gi * G + u));
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
+        };
+        auto mm = [&](int gi, int b) {
+#pragma unroll
+            for (int u = 0; u < G; u++) {
+                const u32x2 l2 = __builtin_bit_cast(u32x2, va[b][u]), h2 = __builtin_bit_cast(u32x2, vb[b][u]);
+                const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, o[gi * G + u], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int gi = 0; gi < NRR; gi++) {
+            if (gi + 1 < NRR) rd(gi + 1, (gi + 1) & 1);
+            mm(gi, gi & 1);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+
 }  // namespace
 
 // ------------------------------------------------------------------ decode
@@ -244,7 +373,10 @@ constexpr int kPreRows = 32;   // rows per prefill chunk
 // chunk for the block's 16 heads; with NG = 2 wave w takes head group w & 1
 // and rows 32*(w >> 1) .. +31, so every gathered row serves 32 heads (half
 // the row traffic of 16-head blocks).  The consumers then merge their
-// softmax states through LDS.
+// softmax states through LDS.  (A 64-head variant, each wave on every row of
+// its own head group with no merge, measured about 1 us slower on the 64K
+// decode: its workgroups load twice the Q and its 8-way combine reads twice
+// the partials.)
 template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
@@ -400,117 +532,7 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         const uint16_t *tile = ktile[ci & 1];
         const int e0 = e_begin + ci * kDecRows + row0;
 
-        // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need them)
-        int32_t rv[4 * NG];
-#pragma unroll
-        for (int rt = 0; rt < NG; rt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int e = e0 + 16 * rt + 4 * g + i;
-                rv[4 * rt + i] = e < e_end ? src[e - e_begin] : -1;
-            }
-        // S^T per 16-row tile: software-pipelined LDS reads (group i+1 in
-        // flight while group i feeds the MFMAs), two accumulator chains; the
-        // order is pinned with scheduling group barriers
-        f32x4 sacc[NG];
-#pragma unroll
-        for (int rt = 0; rt < NG; rt++) {
-            const uint16_t *kr = tile + (row0 + 16 * rt + c) * kKPitch + 8 * g;
-            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            constexpr int G = 3, NGR = kD / 32 / G;   // 6 groups of 3 k-steps
-            bf16x8 ka[2][G];
-            auto rd = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++)
-                    ka[b][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * (gi * G + u)));
-                __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
-            };
-            auto mm = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++) {
-                    if (u & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s1, 0, 0, 0);
-                    else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b][u], qb[gi * G + u], s0, 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int gi = 0; gi < NGR; gi++) {
-                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
-                mm(gi, gi & 1);
-            }
-            sacc[rt] = s0 + s1;
-        }
-        float x[4 * NG], pv[4 * NG];
-#pragma unroll
-        for (int rt = 0; rt < NG; rt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                x[4 * rt + i] = rv[4 * rt + i] >= 0 ? sacc[rt][i] * a.sm_scale_log2 : -INFINITY;
-        const bool had = m_run != -INFINITY;             // O holds something to rescale
-        const float alpha = softmax_update<4 * NG>(x, m_run, l_run, pv);
-        if (__ballot(had && alpha != 1.f)) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
-        }
-
-        // O^T += V^T . P^T over the wave's rows; the k order (rows 4g+i, then
-        // 16+4g+i) is the score accumulators' lane order
-        const uint16_t *vr = tile + (row0 + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
-        if constexpr (NG == 1) {
-            i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
-                                                         bf16_pair_rne(pv[2], pv[3])});
-            constexpr int G = 4, NGR = kDN / 16 / G;   // 8 groups of 4 column tiles
-            i16x4 va[2][G];
-            auto rd = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
-                __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
-            };
-            auto mm = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++)
-                    o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(i16x4v, va[b][u]), pb, o[gi * G + u], 0, 0, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int gi = 0; gi < NGR; gi++) {
-                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
-                mm(gi, gi & 1);
-            }
-        } else {
-            const bf16x8 pb = __builtin_bit_cast(
-                bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
-                              bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
-            const uint16_t *vr2 = vr + 16 * kKPitch;
-            constexpr int G = 4, NGR = kDN / 16 / G;
-            i16x4 va[2][G], vb[2][G];
-            auto rd = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++) {
-                    va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
-                    vb[b][u] = lds_read_tr16(vr2 + 16 * (gi * G + u));
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
-            };
-            auto mm = [&](int gi, int b) {
-#pragma unroll
-                for (int u = 0; u < G; u++) {
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, va[b][u]), h2 = __builtin_bit_cast(u32x2, vb[b][u]);
-                    const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                    o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, o[gi * G + u], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int gi = 0; gi < NGR; gi++) {
-                if (gi + 1 < NGR) rd(gi + 1, (gi + 1) & 1);
-                mm(gi, gi & 1);
-            }
-        }
+        attend_rows<NG>(tile, row0, e0, e_begin, e_end, src, qb, a.sm_scale_log2, o, m_run, l_run, g, c);
     }
 
     // ---- merge the consumers' softmax states (same heads, disjoint rows) ----
@@ -576,6 +598,7 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
     }
+
 
     // O / L as bf16 rows: the output, or with list splits the partial state
     // [t][split][h] (each value at most the largest |V| of the split's rows)
@@ -763,36 +786,50 @@ void mla_prefill_kernel(AttnArgs a) {
     store_out(a, t, h, g, o, m_run, l_run);
 }
 
-int decode_groups(int n_heads) { return n_heads % 32 == 0 ? 2 : 1; }
-
+// Decode split plan (host arithmetic only).  Head groups per workgroup: 2
+// (32 heads) when H % 32 == 0, else 1.  Each (query, head block)'s list is
+// cut in 16-row units and the split count with the least modelled cost is
+// taken.  Cost, in units of one
+// wave's compute on 32 rows for 16 heads (about 2.7 us): the larger of
+//   compute  a split's rows times the share of the four consumer waves that
+//            compute on each row (NG / 4), per 32 rows, and
+//   gather   the bytes one workgroup pulls in (its Q rows plus its list rows
+//            at the list's mean row size), per kUnitBytes,
+// which overlap; plus kMergeCost for the merge of the waves sharing a head
+// group and kSplitCost for splitting at all (partial store, combine
+// kernel); times the waves of workgroups (one workgroup per CU: 256 run at
+// once).  A workgroup resolves at most kDecMaxEntries entries and the
+// combine merges at most kMaxCombineSplits splits.
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
-                    int *rows_per_split) {
+                    int *rows_per_split, int *head_groups) {
     const int entries = window + k;
     if (!decode) {
         *n_splits = 1;
         *rows_per_split = entries;
+        *head_groups = 1;
         return;
     }
-    // Split each (query, head block)'s list in 32-row units.  Cost model, in
-    // units of one 64-row chunk's compute: the chunks of a split, plus a fixed
-    // kSplitCost for splitting at all (partial store, combine kernel), times
-    // the waves of workgroups (one workgroup per CU: 256 run at once).  A
-    // workgroup resolves at most kDecMaxEntries entries and the combine merges
-    // at most kMaxCombineSplits splits.
-    constexpr int kCUs = 256;
-    constexpr float kSplitCost = 3.2f;
-    const int blocks = (n_q > 0 ? n_q : 1) * (n_heads / (16 * decode_groups(n_heads)));
-    const int units = entries > 0 ? (entries + 31) / 32 : 1;
+    constexpr int kCUs = 256, kUnit = 16;
+    constexpr float kSplitCost = 3.2f, kMergeCost = 0.8f, kUnitBytes = 67500.f;
+    const float row_bytes = entries > 0 ? (static_cast<float>(window) * (kD * 2) +
+                                           static_cast<float>(k) * SLC_CMP_ROW_BYTES) / entries
+                                        : 0.f;
+    const int units = entries > 0 ? (entries + kUnit - 1) / kUnit : 1;
     const int min_splits = (entries + kDecMaxEntries - 1) / kDecMaxEntries;
+    const int ng = n_heads % 32 == 0 ? 2 : 1;
     int best = -1, best_per = units;
     float best_cost = 0.f;
+    const int blocks = (n_q > 0 ? n_q : 1) * (n_heads / (16 * ng));
     for (int sp = 1; sp <= kMaxCombineSplits && sp <= units; sp++) {
         const int per = (units + sp - 1) / sp;
-        if (per * 32 > kDecMaxEntries) continue;
-        const int used = (units + per - 1) / per;           // splits actually formed
+        if (per * kUnit > kDecMaxEntries) continue;
+        const int used = (units + per - 1) / per;       // splits actually formed
         if (used != sp) continue;
         const int waves = (blocks * used + kCUs - 1) / kCUs;
-        const float cost = (static_cast<float>((per * 32 + kDecRows - 1) / kDecRows) +
+        const float rows = static_cast<float>(per * kUnit);
+        const float compute = rows * ng / (4 * 32);
+        const float gather = (16.f * ng * kD * 2 + rows * row_bytes) / kUnitBytes;
+        const float cost = ((compute > gather ? compute : gather) + kMergeCost +
                             (used > 1 ? kSplitCost : 0.f)) * static_cast<float>(waves);
         if (best < 0 || cost < best_cost) {
             best = used;
@@ -804,13 +841,14 @@ void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n
         best = min_splits > 0 ? min_splits : 1;
         best_per = (units + best - 1) / best;
     }
-    *rows_per_split = best_per * 32;
+    *rows_per_split = best_per * kUnit;
     *n_splits = (units + best_per - 1) / best_per;
+    *head_groups = ng;
 }
 
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) {
     if (decode) {
-        const int ng = decode_groups(a.n_heads);
+        const int ng = a.head_groups;
         const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
         dim3 grid(groups * 8u * (a.n_heads / (16 * ng)) * a.n_splits);
         if (ng == 2) hipLaunchKernelGGL(mla_decode_kernel<2>, grid, dim3(512), 0, stream, a);

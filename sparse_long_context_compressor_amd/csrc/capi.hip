@@ -155,8 +155,8 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
 
 static size_t attn_ws(int n_q, int n_heads, int window, int k, bool decode) {
     if (n_q <= 0 || n_heads <= 0) return 0;
-    int splits, cps;
-    attention_plan(n_q, n_heads, window, k, decode, &splits, &cps);
+    int splits, cps, groups;
+    attention_plan(n_q, n_heads, window, k, decode, &splits, &cps, &groups);
     if (splits <= 1) return 0;
     size_t per = static_cast<size_t>(n_q) * splits * n_heads;
     // bf16 normalised outputs, then (max, sum) pairs on a 16-byte boundary
@@ -207,8 +207,8 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
             return fail("sparse_mla: cmp_idx and n_slots are required for C4A / C128A");
     }
     int kk = layer_type == SLC_LAYER_SWAONLY ? 0 : k;
-    int splits, cps;
-    attention_plan(n_q, n_heads, window, kk, decode, &splits, &cps);
+    int splits, cps, groups;
+    attention_plan(n_q, n_heads, window, kk, decode, &splits, &cps, &groups);
     size_t need = attn_ws(n_q, n_heads, window, kk, decode);
     if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256))) {
         std::snprintf(g_last_error, sizeof g_last_error,
@@ -233,6 +233,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     a.lse = lse;
     a.n_splits = splits;
     a.rows_per_split = cps;
+    a.head_groups = groups;
     if (splits > 1) {
         size_t per = static_cast<size_t>(n_q) * splits * n_heads;
         a.part_o = static_cast<uint16_t *>(workspace);

@@ -64,8 +64,9 @@ struct AttnArgs {
     float sm_scale_log2;    // sm_scale * log2(e)
     uint16_t *out;
     float *lse;
-    int n_splits;           // decode: workgroups per (query, head group) along the list
-    int rows_per_split;     // list entries each split covers (a multiple of 32)
+    int n_splits;           // decode: workgroups per (query, head block) along the list
+    int rows_per_split;     // list entries each split covers (a multiple of 16)
+    int head_groups;        // decode: 16-head groups per workgroup (1, 2 or 4)
     uint16_t *part_o;       // bf16 [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
 };
@@ -78,8 +79,7 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);
 // split plan (host arithmetic only): decode splits each (query, head block)'s
 // list so that about one workgroup per CU runs; prefill never splits.
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
-                    int *rows_per_split);
+                    int *rows_per_split, int *head_groups);
 // 16-head groups one decode workgroup serves (2 when n_heads allows, else 1)
-int decode_groups(int n_heads);
 
 }  // namespace slc

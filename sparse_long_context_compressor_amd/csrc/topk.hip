@@ -4,13 +4,13 @@
 // computes a global top-k over the indexer scores for every query (the
 // IndexCache freq2 page: lists shorter than k are filled with -1).
 //
-// One workgroup of 1024 threads per query.  The select itself is an
-// MSB-first radix search over order-preserving 32-bit keys: the bits every
-// key shares are skipped, one 11-bit histogram finds the bin holding the
-// k-th largest key, its few candidates are ranked exactly (key descending,
-// slot ascending), and one ordered write places every selected slot in
-// increasing slot order, ties at the threshold going to the lower slot.  A
-// prefilter by group maxima first cuts the list to a few per cent of it.
+// One workgroup of 1024 threads per query.  The select itself is a radix
+// search over order-preserving 32-bit keys: one histogram of 2048 equal bins
+// over [min key, max key] finds the bin holding the k-th largest key, its few
+// candidates are ranked exactly (key descending, slot ascending), and one
+// ordered write places every selected slot in increasing slot order, ties at
+// the threshold going to the lower slot.  A prefilter by group maxima first
+// cuts the list to a few per cent of it.
 
 #include "slc_internal.hpp"
 
@@ -65,13 +65,13 @@ constexpr int kRankCap = 256;                 // threshold-bin candidates ranked
 // 64Rw + 64j + l (j < R), so each of its R loads is one coalesced 256-byte
 // row of scores and the wave's slots run in (j, lane) order.
 //
-// Threshold search: after the common-prefix skip, one histogram of the next
-// 11 key bits finds the bin holding the k-th largest key.  Its candidates
-// (usually a few dozen) are ranked exactly against each other (key
+// Threshold search: one histogram of 2048 equal bins over [kmin, kmax] (bin
+// (key - kmin) >> shift) finds the bin holding the k-th largest key.  Its
+// candidates (usually a handful) are ranked exactly against each other (key
 // descending, slot ascending), which yields the k-th key and how many keys
 // equal to it are taken.  A crowded bin falls back to 8-bit radix passes over
-// the bits below it.  The ordered write then counts, with wave ballots,
-// the selected keys at lower slots.
+// the lower bits of key - kmin.  The ordered write then counts, with wave
+// ballots, the selected keys at lower slots.
 //
 // key: this thread's order keys (entries past n are 0; valid keys never are:
 // order_key maps every non-NaN float above 0x007FFFFF); requires n > k.
@@ -114,13 +114,13 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
         for (int i = tid; i < k; i += THREADS) out[i] = slot_map ? slot_map[i] : i;
         return;
     }
-    const int hi = 32 - __clz(kmin ^ kmax);     // keys differ only in bits [0, hi)
+    // linear bins: key - kmin < 2^hi, bin (key - kmin) >> shift < 2^11
+    const int hi = 32 - __clz(kmax - kmin);
     const int shift = hi > kHistBits ? hi - kHistBits : 0;
-    const uint32_t bin_mask = kHistBins - 1;
 #pragma unroll
     for (int j = 0; j < R; j++)
         if (wbase + 64 * j + lane < n)
-            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] >> shift) & bin_mask)], 1u);
+            atomicAdd(&hist[(w % kHistCopies) * kHistBins + ((key[j] - kmin) >> shift)], 1u);
     __syncthreads();
 
     // thread i owns bins 2047 - BPT*i - b (b < BPT): descending key order
@@ -154,13 +154,12 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     const uint32_t bsel = static_cast<uint32_t>(sh[0]);
     const int need = k - sh[1];                   // keys still to take from bin bsel (>= 1)
     const int m = sh[2];                          // keys in bin bsel
-    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
-    uint32_t prefix = (kmin & hi_mask) | (bsel << shift);   // bits [shift, 32) of the bin's keys
+    uint32_t prefix = bsel << shift;              // bits [shift, 32) of the bin's keys - kmin
     uint32_t thr;
     int take_eq;
     if (shift == 0) {
         // the bin is one key value
-        thr = prefix;
+        thr = prefix + kmin;
         take_eq = need;
     } else if (m <= kRankCap) {
         uint32_t *ck = hist;                      // candidates: key, slot
@@ -168,7 +167,7 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
 #pragma unroll
         for (int j = 0; j < R; j++) {
             const int s = wbase + 64 * j + lane;
-            if (s < n && (key[j] >> shift) == (prefix >> shift)) {
+            if (s < n && ((key[j] - kmin) >> shift) == bsel) {
                 const int pos = atomicAdd(&sh[3], 1);
                 ck[pos] = key[j];
                 cs[pos] = s;
@@ -215,8 +214,8 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
             const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
             for (int j = 0; j < R; j++)
-                if (wbase + 64 * j + lane < n && (key[j] & pm) == prefix)
-                    atomicAdd(&wh[w][(key[j] >> sft) & dmask], 1u);
+                if (wbase + 64 * j + lane < n && ((key[j] - kmin) & pm) == prefix)
+                    atomicAdd(&wh[w][((key[j] - kmin) >> sft) & dmask], 1u);
             __syncthreads();
             int cnt = 0;
             if (tid < 256) {
@@ -241,7 +240,7 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
             h = sft;
             __syncthreads();
         }
-        thr = prefix;
+        thr = prefix + kmin;
         take_eq = remaining;
     }
 
@@ -280,8 +279,8 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
 }
 
 // A lower bound of the k-th largest of the values v (G per thread, 0 =
-// absent): the floor of the 11-bit histogram bin (below the bits all values
-// share) that holds the k-th largest; 0 if fewer than k values are present.
+// absent): the floor of the bin, among 2048 equal bins over [min, max], that
+// holds the k-th largest; 0 if fewer than k values are present.
 // Shared memory as for topk_select_keys, red with 3 * WAVES ints.
 template <int THREADS, int G>
 __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uint32_t *hist,
@@ -319,11 +318,15 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
     }
     if (cnt < k) return 0u;
     if (vmin == vmax) return vmin;
-    const int hi = 32 - __clz(vmin ^ vmax);
+    // linear bins over [vmin, vmax]: (v - vmin) >> shift < 2^11.  (Binning by
+    // the top bits below the shared prefix would put a few octaves' worth of
+    // values into a few dozen exponent-dominated bins and serialise the
+    // atomics on them.)
+    const int hi = 32 - __clz(vmax - vmin);
     const int shift = hi > kHistBits ? hi - kHistBits : 0;
 #pragma unroll
     for (int g = 0; g < G; g++)
-        if (v[g]) atomicAdd(&hist[(v[g] >> shift) & (kHistBins - 1)], 1u);
+        if (v[g]) atomicAdd(&hist[(v[g] - vmin) >> shift], 1u);
     __syncthreads();
     int cb[BPT], tot = 0;
 #pragma unroll
@@ -344,8 +347,7 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
         }
     }
     __syncthreads();
-    const uint32_t hi_mask = shift + kHistBits >= 32 ? 0u : (0xffffffffu << (shift + kHistBits));
-    return (vmin & hi_mask) | (static_cast<uint32_t>(sh[0]) << shift);
+    return vmin + (static_cast<uint32_t>(sh[0]) << shift);   // the bin's floor
 }
 
 // One 1024-thread workgroup per query, R scores per thread (R >= 4): wave w
