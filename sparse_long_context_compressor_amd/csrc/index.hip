@@ -37,6 +37,7 @@ __device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 
 constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
 constexpr int kScoreTile = 4 * kSubTiles * 16;      // 1024 slots per workgroup
 constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
+constexpr int kQPitch = kDI + 16;                   // LDS bytes per staged query head
 
 // ReLU on the bit pattern: non-negative floats compare as non-negative ints,
 // negative ones as negative ints, so one integer max does it (-0 -> +0).
@@ -80,14 +81,25 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     }
 
     // ---- query operands and per-head factors (they depend on t only) ----
-    // raw loads now; the conversions follow the first key loads
-    u32x4 qlo[HT], qhi[HT];
+    // The query's 16*HT heads x 128 codes are one contiguous run: the
+    // workgroup loads it once, coalesced (per-wave operand loads would fetch
+    // it four times, in half-line pieces), and stages it through LDS after
+    // the first key loads are issued.
+    constexpr int kQUnits = 16 * HT * kDI / 16;          // 16-byte units
+    constexpr int kQIt = (kQUnits + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * HT * kQPitch];
+    u32x4 qraw[kQIt];
+    {
+        const uint8_t *qp = a.q + static_cast<int64_t>(t) * a.h_idx * kDI;
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = threadIdx.x + 256 * i;
+            if (u < kQUnits) qraw[i] = *reinterpret_cast<const u32x4 *>(qp + 16 * u);
+        }
+    }
     f32x4 qw[HT], qs[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) {
-        const uint8_t *qp = a.q + (static_cast<int64_t>(t) * a.h_idx + 16 * ht + c) * kDI;
-        qlo[ht] = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
-        qhi[ht] = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
         const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
         qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
         qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
@@ -146,9 +158,17 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
     for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
 
 #pragma unroll
+    for (int i = 0; i < kQIt; i++) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < kQUnits)
+            *reinterpret_cast<u32x4 *>(qlds + (u / (kDI / 16)) * kQPitch + 16 * (u % (kDI / 16))) = qraw[i];
+    }
+    __syncthreads();
+#pragma unroll
     for (int ht = 0; ht < HT; ht++) {
-        e4m3x16_to_operands(qlo[ht], qa[ht][0], qa[ht][1]);
-        e4m3x16_to_operands(qhi[ht], qa[ht][2], qa[ht][3]);
+        const uint8_t *qr = qlds + (16 * ht + c) * kQPitch;
+        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + 16 * g), qa[ht][0], qa[ht][1]);
+        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + 64 + 16 * g), qa[ht][2], qa[ht][3]);
 #pragma unroll
         for (int i = 0; i < 4; i++) hf[ht][i] = qw[ht][i] * qs[ht][i];
     }
