@@ -57,7 +57,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 constexpr int kHistBits = 11;                 // first histogram: 2048 bins
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kHistCopies = 4;                // waves w, w+4, ... share copy w % 4
+constexpr int kHistCopies = 1;                // copies of the first histogram (waves w % copies share one)
+// words of the shared histogram array: the first histogram, or the crowded
+// bin's per-wave 256-bin histograms
+constexpr int kHistWords = kHistCopies * kHistBins > kTopkWaves * 256 ? kHistCopies * kHistBins : kTopkWaves * 256;
 constexpr int kRankCap = 256;                 // threshold-bin candidates ranked directly
 
 // Top-k of one query's scores by one workgroup of THREADS threads, R keys
@@ -76,7 +79,7 @@ constexpr int kRankCap = 256;                 // threshold-bin candidates ranked
 // key: this thread's order keys (entries past n are 0; valid keys never are:
 // order_key maps every non-NaN float above 0x007FFFFF); requires n > k.
 // Entry i of the list is written out as slot_map[i] (i itself when
-// slot_map is null).  Shared memory: hist (kHistCopies * kHistBins words,
+// slot_map is null).  Shared memory: hist (kHistWords words,
 // 16-byte aligned), red (2 * WAVES ints), sh (8 ints).
 template <int THREADS, int R>
 __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n, int k,
@@ -85,6 +88,7 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     constexpr int WAVES = THREADS / 64;
     constexpr int BPT = kHistBins / THREADS;
     static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
+    static_assert(WAVES * 256 <= kHistWords && 2 * kRankCap <= kHistWords, "histogram array size");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wbase = w * 64 * R;
 
@@ -367,7 +371,7 @@ template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     static_assert(R >= 4, "16-byte score loads");
     constexpr int R4 = R / 4;
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];   // 32 KB
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords];               // 16 KB
     __shared__ __attribute__((aligned(16))) uint32_t cand_key[kCandCap];             // 16 KB
     __shared__ int32_t cand_slot[kCandCap];                                          // 16 KB
     __shared__ int red[3 * kTopkWaves];
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 // exact select over every key, R per thread in the one-key-per-lane layout.
 template <int R>
 __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(TopkArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistCopies * kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords];
     __shared__ int red[2 * kTopkWaves];
     __shared__ int sh[8];
     const int t = blockIdx.x;
