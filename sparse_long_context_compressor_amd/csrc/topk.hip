@@ -38,10 +38,13 @@ __device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before
         sh[kTopkWaves + w] = ib;
     }
     __syncthreads();
+    // fixed trip count: every read is issued at once (a loop to w would wait
+    // on each in turn)
     int pa = 0, pb = 0;
-    for (int i = 0; i < w; i++) {
-        pa += sh[i];
-        pb += sh[kTopkWaves + i];
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; i++) {
+        pa += i < w ? sh[i] : 0;
+        pb += i < w ? sh[kTopkWaves + i] : 0;
     }
     a_before = pa + ia - a;
     b_before = pb + ib - b;
@@ -141,7 +144,8 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     __syncthreads();
     {
         int before = 0;
-        for (int i = 0; i < w; i++) before += red[i];
+#pragma unroll
+        for (int i = 0; i < WAVES; i++) before += i < w ? red[i] : 0;
         int run = before + incl - tot;
 #pragma unroll
         for (int b = 0; b < BPT; b++) {
@@ -231,7 +235,8 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
             __syncthreads();
             if (tid < 256) {
                 int before = 0;
-                for (int ww = 0; ww < w; ww++) before += red[ww];
+#pragma unroll
+                for (int ww = 0; ww < 4; ww++) before += ww < w ? red[ww] : 0;   // tid < 256: w < 4
                 const int excl = before + inc - cnt;
                 if (excl < remaining && excl + cnt >= remaining) {
                     sh[6] = 255 - tid;
@@ -264,9 +269,10 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     }
     __syncthreads();
     int g_before = 0, e_before = 0;
-    for (int i = 0; i < w; i++) {
-        g_before += red[i];
-        e_before += red[WAVES + i];
+#pragma unroll
+    for (int i = 0; i < WAVES; i++) {
+        g_before += i < w ? red[i] : 0;
+        e_before += i < w ? red[WAVES + i] : 0;
     }
 #pragma unroll
     for (int j = 0; j < R; j++) {
@@ -343,7 +349,8 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
     __syncthreads();
     {
         int run = -tot + incl;
-        for (int i = 0; i < w; i++) run += red[i];
+#pragma unroll
+        for (int i = 0; i < WAVES; i++) run += i < w ? red[i] : 0;
 #pragma unroll
         for (int b = 0; b < BPT; b++) {
             if (run < k && run + cb[b] >= k) sh[0] = kHistBins - 1 - BPT * tid - b;
@@ -554,7 +561,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
         __syncthreads();
         if (tid < 256) {
             int before = 0;
-            for (int ww = 0; ww < w; ww++) before += scan_sh[ww];
+#pragma unroll
+            for (int ww = 0; ww < 4; ww++) before += ww < w ? scan_sh[ww] : 0;   // tid < 256: w < 4
             int excl = before + incl - cnt;
             if (excl < remaining && excl + cnt >= remaining) {
                 sel_sh[0] = 255 - tid;
