@@ -34,8 +34,10 @@ __device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 
     s1 = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
+constexpr int kIdxWaves = 8;                        // waves per workgroup: one workgroup per CU
+constexpr int kIdxThreads = 64 * kIdxWaves;
 constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
-constexpr int kScoreTile = 4 * kSubTiles * 16;      // 1024 slots per workgroup
+constexpr int kScoreTile = kIdxWaves * kSubTiles * 16;   // 2048 slots per workgroup
 constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
 constexpr int kQPitch = kDI + 16;                   // LDS bytes per staged query head
 
@@ -55,71 +57,65 @@ __device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never
 
 }  // namespace
 
-// grid (n_q, ceil(max_slots / 1024)), 256 threads.  Wave w's sub-tile j covers
-// slots s0 + 64j + 16w + (0..15): all four waves' sub-tile j lie in logical
-// block s0/64 + j, so one (wave-uniform) table lookup serves it.  Lane
-// (g = lane/16, c = lane%16) owns index-dim bytes [16g, 16g+16) and
-// [64+16g, 64+16g+16) of its head and of its key; the MFMA k-order is the same
-// permutation for both operands, so the dot product is unchanged.
+// grid (n_q, ceil(max_slots / 2048)), 512 threads: one workgroup of eight
+// waves per CU.  (Two four-wave workgroups per CU measured 3 us slower: a
+// CU serves its loads roughly in issue order, so the second workgroup's
+// start waited behind the first's loads and it finished last.)  Sub-tile j
+// covers logical blocks s0/64 + 2j and + 2j + 1: wave w takes slots
+// 16*(w%4) + (0..15) of block 2j + w/4, so one (wave-uniform) table lookup
+// serves each wave's sub-tile.  Lane (g = lane/16, c = lane%16) owns
+// index-dim bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its head and of
+// its key; the MFMA k-order is the same permutation for both operands, so
+// the dot product is unchanged.
 template <int HT>
-__global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
+__global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
+    const int wq = w & 3;                                        // 16-slot quarter of a block
+    const int wb = __builtin_amdgcn_readfirstlane(w >> 2);       // block of a sub-tile's pair
     const int s0 = blockIdx.y * kScoreTile;
 
-    // The tile's 16 block-table entries first, in one load (lane j % 16 takes
-    // entry j): the first key loads wait on them, and vector loads complete
-    // in issue order.  Each sub-tile later moves its entry to a scalar
-    // register, so no key load waits on a table lookup of its own.
-    const int seq = a.q_seq[t];
-    const int64_t table_row = static_cast<int64_t>(seq) * a.keys.table_stride;
-    int32_t my_pb = -1;
+    // The kernel arguments of the start-up chain in one round of loads
+    // (left alone, the compiler spreads them over several dependent rounds,
+    // each a full load latency before the first key is requested).
+    const int32_t *q_seq_p = a.q_seq, *q_pos_p = a.q_pos, *n_slots_p = a.n_slots;
+    const int32_t *table_p = a.keys.block_table;
+    const int stride = a.keys.table_stride;
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
+    const uint8_t *zpage = kIndexZeroPage;
+    const int64_t n_blocks = a.keys.n_blocks;
+    __asm__ volatile("" ::"s"(q_seq_p), "s"(q_pos_p), "s"(n_slots_p), "s"(table_p), "s"(stride), "s"(kbase),
+                     "s"(zpage), "s"(n_blocks));
+
+    // The tile's 32 block-table entries first, in one load (lane j % 32 takes
+    // entry j; entries past the table read entry 0 and are discarded): the
+    // first key loads wait on them, and a wave's loads complete in issue
+    // order.  Each sub-tile later moves its entry to a scalar register, so no
+    // key load waits on a table lookup of its own.
+    const int seq = q_seq_p[t];
+    const int64_t table_row = static_cast<int64_t>(seq) * stride;
+    int32_t my_pb;
     {
-        const int64_t lb = (s0 >> 6) + (lane & 15);
-        if (lb < a.keys.table_stride) my_pb = a.keys.block_table[table_row + lb];
+        const int64_t lb = (s0 >> 6) + (lane & 31);
+        const bool in = lb < stride;
+        my_pb = table_p[table_row + (in ? lb : 0)];
+        my_pb = in ? my_pb : -1;
     }
 
-    // ---- query operands and per-head factors (they depend on t only) ----
-    // The query's 16*HT heads x 128 codes are one contiguous run: the
-    // workgroup loads it once, coalesced (per-wave operand loads would fetch
-    // it four times, in half-line pieces), and stages it through LDS after
-    // the first key loads are issued.
-    constexpr int kQUnits = 16 * HT * kDI / 16;          // 16-byte units
-    constexpr int kQIt = (kQUnits + 255) / 256;
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * HT * kQPitch];
-    u32x4 qraw[kQIt];
-    {
-        const uint8_t *qp = a.q + static_cast<int64_t>(t) * a.h_idx * kDI;
-#pragma unroll
-        for (int i = 0; i < kQIt; i++) {
-            const int u = threadIdx.x + 256 * i;
-            if (u < kQUnits) qraw[i] = *reinterpret_cast<const u32x4 *>(qp + 16 * u);
-        }
-    }
-    f32x4 qw[HT], qs[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ht++) {
-        const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
-        qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
-        qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
-    }
-    int nv = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    nv = nv < a.max_slots ? nv : a.max_slots;
-    if (s0 >= nv) return;
+    int nv = 0;                                  // visible slots: read after the first key loads
     bf16x8 qa[HT][4];                            // filled after the first key loads are issued
     float hf[HT][4];
 
-    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
-    const uint32_t lane_off = static_cast<uint32_t>((16 * w + c) * kDI + 16 * g);
-    const uint32_t scale_off = static_cast<uint32_t>(SLC_KEY_SCALE_OFFSET + 4 * (16 * w + c));
+    const uint32_t lane_off = static_cast<uint32_t>((16 * wq + c) * kDI + 16 * g);
+    const uint32_t scale_off = static_cast<uint32_t>(SLC_KEY_SCALE_OFFSET + 4 * (16 * wq + c));
 
     // sub-tile j reads through a buffer resource on its (wave-uniform) block;
     // an absent block gets a zero-size resource, whose loads return zeros
     auto stage = [&](int j, KeyStage &st) {
-        const int32_t pb = __builtin_amdgcn_readlane(my_pb, j);
-        const bool ok = pb >= 0 && pb < a.keys.n_blocks;
-        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : kIndexZeroPage;
+        const int32_t pb = __builtin_amdgcn_readlane(my_pb, 2 * j + wb);
+        const bool ok = pb >= 0 && pb < n_blocks;
+        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : zpage;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(bp), 0, ok ? SLC_KEY_BLOCK_BYTES : 0, kBufferWord3);
         st.lo = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0);
@@ -128,7 +124,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
         st.scale = ok ? sc : -INFINITY;
     };
     auto compute = [&](int j, const KeyStage &cur) {
-        const int s = s0 + 64 * j + 16 * w + c;
+        const int s = s0 + 128 * j + 64 * wb + 16 * wq + c;
         bf16x8 kb[4];
         e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
         e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
@@ -157,9 +153,39 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 #pragma unroll
     for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
 
+    // ---- query operands and per-head factors (they depend on t only) ----
+    // Loaded after the first key loads (which wait only on the table): the
+    // query's 16*HT heads x 128 codes are one contiguous run that the
+    // workgroup loads once, coalesced (per-wave operand loads would fetch it
+    // four times, in half-line pieces), and stages through LDS.  The visible
+    // count decides the early exit only now: the key loads already issued
+    // read in-range blocks or the zero page either way.
+    constexpr int kQUnits = 16 * HT * kDI / 16;          // 16-byte units
+    constexpr int kQIt = (kQUnits + kIdxThreads - 1) / kIdxThreads;
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * HT * kQPitch];
+    u32x4 qraw[kQIt];
+    {
+        const uint8_t *qp = a.q + static_cast<int64_t>(t) * a.h_idx * kDI;
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = threadIdx.x + kIdxThreads * i;
+            if (u < kQUnits) qraw[i] = *reinterpret_cast<const u32x4 *>(qp + 16 * u);
+        }
+    }
+    f32x4 qw[HT], qs[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
+        qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
+        qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
+    }
+    nv = visible_slots(q_pos_p[t], a.ratio, n_slots_p[seq]);
+    nv = nv < a.max_slots ? nv : a.max_slots;
+    if (s0 >= nv) return;
+
 #pragma unroll
     for (int i = 0; i < kQIt; i++) {
-        const int u = threadIdx.x + 256 * i;
+        const int u = threadIdx.x + kIdxThreads * i;
         if (u < kQUnits)
             *reinterpret_cast<u32x4 *>(qlds + (u / (kDI / 16)) * kQPitch + 16 * (u % (kDI / 16))) = qraw[i];
     }
@@ -182,17 +208,17 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < kRing; j++)
-            if (s0 + 64 * (q * kRing + j) < nv) compute(q * kRing + j, cur[j]);   // wave-uniform
+            if (s0 + 128 * (q * kRing + j) + 64 * wb < nv) compute(q * kRing + j, cur[j]);   // wave-uniform
     }
 }
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     dim3 grid(a.n_q, (a.max_slots + kScoreTile - 1) / kScoreTile);
     switch (a.h_idx / 16) {
-    case 1: hipLaunchKernelGGL(index_score_kernel<1>, grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(index_score_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(index_score_kernel<3>, grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(index_score_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(index_score_kernel<1>, grid, dim3(kIdxThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(index_score_kernel<2>, grid, dim3(kIdxThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(index_score_kernel<3>, grid, dim3(kIdxThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(index_score_kernel<4>, grid, dim3(kIdxThreads), 0, stream, a); break;
     }
     return hipGetLastError();
 }
