@@ -386,11 +386,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // the visible count first: its two dependent loads must not queue
-    // behind this workgroup's score loads
-    const int seq = a.q_seq[t];
-    int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
-    n = n < a.max_slots ? n : a.max_slots;
+    // The score loads first, bounded by the row length only: the visible
+    // count (two dependent scalar loads, which take their own path) arrives
+    // meanwhile and masks the keys past it.  Rows are 16-byte aligned: the
+    // launcher takes this kernel only for a 16-byte aligned score array whose
+    // row length is a multiple of 4.
+    const int seq = a.q_seq[t], pos = a.q_pos[t];
+    const int max_slots = a.max_slots;
+    const float *sc = a.scores + static_cast<int64_t>(t) * max_slots;
+    const int wbase = w * 64 * R;
+    f32x4 raw[R4];                                // raw[q]: slots wbase + 256q + 4 lane + (0..3)
+#pragma unroll
+    for (int q = 0; q < R4; q++) {
+        const int s0 = wbase + 256 * q + 4 * lane;
+        raw[q] = s0 < max_slots ? *reinterpret_cast<const f32x4 *>(sc + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int n = visible_slots(pos, a.ratio, a.n_slots[seq]);
+    n = n < max_slots ? n : max_slots;
     const int k = a.k;
     const int k_eff = n < k ? n : k;
     int32_t *out = a.idx + static_cast<int64_t>(t) * k;
@@ -400,22 +412,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         return;
     }
 
-    // rows are 16-byte aligned: the launcher takes this kernel only for a
-    // 16-byte aligned score array whose row length is a multiple of 4
-    const float *sc = a.scores + static_cast<int64_t>(t) * a.max_slots;
-    const int wbase = w * 64 * R;
     uint32_t key[R];                              // key[4q + e]: slot wbase + 256q + 4 lane + e
 #pragma unroll
     for (int q = 0; q < R4; q++) {
         const int s0 = wbase + 256 * q + 4 * lane;
-        if (s0 + 3 < n) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(sc + s0);
 #pragma unroll
-            for (int e = 0; e < 4; e++) key[4 * q + e] = order_key(v[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++) key[4 * q + e] = s0 + e < n ? order_key(sc[s0 + e]) : 0u;
-        }
+        for (int e = 0; e < 4; e++) key[4 * q + e] = s0 + e < n ? order_key(raw[q][e]) : 0u;
     }
     uint32_t gmax[R4];
 #pragma unroll
