@@ -370,18 +370,20 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
 // distinct scores, so the k-th largest maximum (and the floor L of its
 // histogram bin) is at most the k-th largest score: no key below L can be
 // selected.  The keys >= L (a few per cent of the list) are compacted, in
-// slot order, into LDS and the exact select runs on them with at most four
-// per thread.  If more than kCandCap keys pass, the select runs on all keys.
-constexpr int kCandCap = 4 * kTopkThreads;
+// slot order, into LDS and the exact select runs on them (kCandCap / THREADS
+// per thread).  If more than kCandCap keys pass, the select runs on all keys.
+// 1024 threads: with 256 (one wave per SIMD) the phases' latencies were
+// exposed (14.4 us on the 64K decode against 10.0), 512 measured no better.
+constexpr int kCandCap = 4096;
 
-template <int R>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+template <int THREADS, int R>
+__global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     static_assert(R >= 4, "16-byte score loads");
-    constexpr int R4 = R / 4;
+    constexpr int R4 = R / 4, WAVES = THREADS / 64;
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords];               // 16 KB
     __shared__ __attribute__((aligned(16))) uint32_t cand_key[kCandCap];             // 16 KB
     __shared__ int32_t cand_slot[kCandCap];                                          // 16 KB
-    __shared__ int red[3 * kTopkWaves];
+    __shared__ int red[3 * WAVES];
     __shared__ int sh[8];
 
     const int t = blockIdx.x;
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     int32_t *out = a.idx + static_cast<int64_t>(t) * k;
     if (tid == 0) a.len[t] = k_eff;
     if (n <= k) {   // everything visible is selected
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        for (int i = tid; i < k; i += THREADS) out[i] = i < n ? i : -1;
         return;
     }
 
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int q = 0; q < R4; q++)
         gmax[q] = max(max(key[4 * q], key[4 * q + 1]), max(key[4 * q + 2], key[4 * q + 3]));
-    const uint32_t L = kth_floor<kTopkThreads, R4>(gmax, k, hist, red, sh);
+    const uint32_t L = kth_floor<THREADS, R4>(gmax, k, hist, red, sh);
 
     // candidates per round and lane (keys are never 0 when valid)
     int cl[R4], wc = 0;
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     __syncthreads();
     int m = 0, run = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkWaves; i++) {
+    for (int i = 0; i < WAVES; i++) {
         m += red[i];
         run += i < w ? red[i] : 0;
     }
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             key1[j] = s < n ? order_key(sc[s]) : 0u;
         }
         __syncthreads();                          // red is reused by the select
-        topk_select_keys<kTopkThreads, R>(key1, n, k, out, nullptr, hist, red, sh);
+        topk_select_keys<THREADS, R>(key1, n, k, out, nullptr, hist, red, sh);
         return;
     }
     // compact the candidates in slot order: round by round, lanes in order,
@@ -475,17 +477,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     if (m == k) {                                 // exactly the candidates
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = cand_slot[i];
+        for (int i = tid; i < k; i += THREADS) out[i] = cand_slot[i];
         return;
     }
-    constexpr int Q = kCandCap / kTopkThreads;
+    constexpr int Q = kCandCap / THREADS;
     uint32_t ck[Q];
 #pragma unroll
     for (int i = 0; i < Q; i++) {
         const int c = w * 64 * Q + 64 * i + lane;
         ck[i] = c < m ? cand_key[c] : 0u;
     }
-    topk_select_keys<kTopkThreads, Q>(ck, m, k, out, cand_slot, hist, red, sh);
+    topk_select_keys<THREADS, Q>(ck, m, k, out, cand_slot, hist, red, sh);
 }
 
 // Short lists (up to 2048 visible slots) and rows not 16-byte aligned: the
@@ -612,11 +614,11 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
     else if (per <= 2) hipLaunchKernelGGL(topk_small_kernel<2>, grid, block, 0, stream, a);
     else if (!vec && per <= 16) hipLaunchKernelGGL(topk_small_kernel<16>, grid, block, 0, stream, a);
     else if (!vec && per <= 64) hipLaunchKernelGGL(topk_small_kernel<64>, grid, block, 0, stream, a);
-    else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
-    else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
-    else if (per <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);
-    else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, a);
-    else if (per <= 64) hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, stream, a);
+    else if (per <= 4) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 4>), grid, block, 0, stream, a);
+    else if (per <= 8) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 8>), grid, block, 0, stream, a);
+    else if (per <= 16) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 16>), grid, block, 0, stream, a);
+    else if (per <= 32) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32>), grid, block, 0, stream, a);
+    else if (per <= 64) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL(topk_long_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }
