@@ -232,6 +232,7 @@ __device__ __forceinline__ void store_rows_bf16(const f32x4 (&o)[kDN / 16], floa
 }
 
 constexpr int kDecRows = 64;   // rows per decode chunk (16 per consumer wave)
+static_assert(kDecMaxEntries % kDecRows == 0, "a chunk's list entries lie within the resolved list");
 constexpr int kPreRows = 32;   // rows per prefill chunk
 
 // One slice of 16*NR rows of a chunk for one wave's 16 heads: the scores
@@ -248,15 +249,18 @@ __device__ __forceinline__ void attend_rows(const uint16_t *tile, int row0, int 
     // a scheduling region of its own: the LDS-read and MFMA groups pinned
     // below must not interleave with those of a neighbouring slice
     __builtin_amdgcn_sched_barrier(0);
-    // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need them)
+    // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need
+    // them): four consecutive, 16-byte aligned entries per row tile, read
+    // unconditionally (a chunk's entries lie within src even past e_end) and
+    // masked after
     int32_t rv[4 * NR];
 #pragma unroll
-    for (int rt = 0; rt < NR; rt++)
+    for (int rt = 0; rt < NR; rt++) {
+        const int e = e0 + 16 * rt + 4 * g;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + (e - e_begin));
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int e = e0 + 16 * rt + 4 * g + i;
-            rv[4 * rt + i] = e < e_end ? src[e - e_begin] : -1;
-        }
+        for (int i = 0; i < 4; i++) rv[4 * rt + i] = e + i < e_end ? static_cast<int32_t>(v[i]) : -1;
+    }
     // S^T per 16-row tile: software-pipelined LDS reads (group i+1 in
     // flight while group i feeds the MFMAs), two accumulator chains; the
     // order is pinned with scheduling group barriers
@@ -381,7 +385,7 @@ template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
     static_assert(2 * 16 * kStagePitch <= kDecRows * kKPitch, "tile 1 stages two waves' output rows");
-    __shared__ int32_t src[kDecMaxEntries];
+    __shared__ __attribute__((aligned(16))) int32_t src[kDecMaxEntries];
     __shared__ float st_m[4][16], st_l[4][16];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
