@@ -84,10 +84,15 @@ constexpr int kRankCap = 256;                 // threshold-bin candidates ranked
 // Entry i of the list is written out as slot_map[i] (i itself when
 // slot_map is null).  Shared memory: hist (kHistWords words,
 // 16-byte aligned), red (2 * WAVES ints), sh (8 ints).
+//
+// range: if non-null, {lo, hi} bound every key from below and above (the
+// caller knows them) and the histogram's first kHistCopies * kHistBins words
+// are already zero; otherwise the select finds the range and clears them.
 template <int THREADS, int R>
 __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n, int k,
                                                  int32_t *out, const int32_t *slot_map,
-                                                 uint32_t *hist, int *red, int *sh) {
+                                                 uint32_t *hist, int *red, int *sh,
+                                                 const uint32_t *range = nullptr) {
     constexpr int WAVES = THREADS / 64;
     constexpr int BPT = kHistBins / THREADS;
     static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
@@ -95,27 +100,34 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wbase = w * 64 * R;
 
-    for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    uint32_t kmin, kmax;
+    if (range) {
+        kmin = range[0];
+        kmax = range[1];
+    } else {
+        for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
+        kmin = 0xffffffffu;
+        kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < R; j++)
-        if (wbase + 64 * j + lane < n) {
-            kmin = min(kmin, key[j]);
-            kmax = max(kmax, key[j]);
+        for (int j = 0; j < R; j++)
+            if (wbase + 64 * j + lane < n) {
+                kmin = min(kmin, key[j]);
+                kmax = max(kmax, key[j]);
+            }
+        kmin = wave_umin(kmin);
+        kmax = wave_umax(kmax);
+        if (lane == 0) {
+            red[w] = static_cast<int>(kmin);
+            red[WAVES + w] = static_cast<int>(kmax);
         }
-    kmin = wave_umin(kmin);
-    kmax = wave_umax(kmax);
-    if (lane == 0) {
-        red[w] = static_cast<int>(kmin);
-        red[WAVES + w] = static_cast<int>(kmax);
-    }
-    __syncthreads();
-    kmin = 0xffffffffu;
-    kmax = 0u;
+        __syncthreads();
+        kmin = 0xffffffffu;
+        kmax = 0u;
 #pragma unroll
-    for (int i = 0; i < WAVES; i++) {
-        kmin = min(kmin, static_cast<uint32_t>(red[i]));
-        kmax = max(kmax, static_cast<uint32_t>(red[WAVES + i]));
+        for (int i = 0; i < WAVES; i++) {
+            kmin = min(kmin, static_cast<uint32_t>(red[i]));
+            kmax = max(kmax, static_cast<uint32_t>(red[WAVES + i]));
+        }
     }
     if (kmin == kmax) {   // every entry equal: the lowest ones win
         for (int i = tid; i < k; i += THREADS) out[i] = slot_map ? slot_map[i] : i;
@@ -294,7 +306,7 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
 // Shared memory as for topk_select_keys, red with 3 * WAVES ints.
 template <int THREADS, int G>
 __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uint32_t *hist,
-                                              int *red, int *sh) {
+                                              int *red, int *sh, uint32_t &largest) {
     constexpr int WAVES = THREADS / 64;
     constexpr int BPT = kHistBins / THREADS;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -326,8 +338,17 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
         vmax = max(vmax, static_cast<uint32_t>(red[WAVES + i]));
         cnt += red[2 * WAVES + i];
     }
-    if (cnt < k) return 0u;
-    if (vmin == vmax) return vmin;
+    largest = vmax;
+    // (the early returns are block-uniform; their barrier ends the reads of
+    // red above before the caller reuses it)
+    if (cnt < k) {
+        __syncthreads();
+        return 0u;
+    }
+    if (vmin == vmax) {
+        __syncthreads();
+        return vmin;
+    }
     // linear bins over [vmin, vmax]: (v - vmin) >> shift < 2^11.  (Binning by
     // the top bits below the shared prefix would put a few octaves' worth of
     // values into a few dozen exponent-dominated bins and serialise the
@@ -425,7 +446,8 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int q = 0; q < R4; q++)
         gmax[q] = max(max(key[4 * q], key[4 * q + 1]), max(key[4 * q + 2], key[4 * q + 3]));
-    const uint32_t L = kth_floor<THREADS, R4>(gmax, k, hist, red, sh);
+    uint32_t top;                                 // the largest key
+    const uint32_t L = kth_floor<THREADS, R4>(gmax, k, hist, red, sh, top);
 
     // candidates per round and lane (keys are never 0 when valid)
     int cl[R4], wc = 0;
@@ -437,8 +459,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
         wc += cl[q];
     }
     wc = wave_isum(wc);
-    __syncthreads();                              // every thread has read kth_floor's result
-    if (lane == 0) red[w] = wc;
+    if (lane == 0) red[w] = wc;                   // kth_floor's reads of red ended at its last barrier
     __syncthreads();
     int m = 0, run = 0;
 #pragma unroll
@@ -458,6 +479,8 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
         topk_select_keys<THREADS, R>(key1, n, k, out, nullptr, hist, red, sh);
         return;
     }
+    // the select's histogram starts cleared (kth_floor is done with it)
+    for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
     // compact the candidates in slot order: round by round, lanes in order,
     // a lane's four slots in order
 #pragma unroll
@@ -487,7 +510,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
         const int c = w * 64 * Q + 64 * i + lane;
         ck[i] = c < m ? cand_key[c] : 0u;
     }
-    topk_select_keys<THREADS, Q>(ck, m, k, out, cand_slot, hist, red, sh);
+    // every candidate lies in [L, top]: the select skips its range reduction
+    // (L = 0, fewer than k groups: the range is found as usual)
+    const uint32_t range[2] = {L, top};
+    topk_select_keys<THREADS, Q>(ck, m, k, out, cand_slot, hist, red, sh, L > 0 ? range : nullptr);
 }
 
 // Short lists (up to 2048 visible slots) and rows not 16-byte aligned: the
