@@ -122,10 +122,15 @@ struct RowGather {
     // Dequantise compressed rows (code * scale -> bf16; exact for the
     // power-of-two scales compress writes) and write the rows into the tile.
     // Entries e >= window are compressed rows (skipped ones hold zeros).
-    __device__ __forceinline__ void store(uint16_t *tile, const AttnArgs &a, int e0, int pw,
-                                          int lane) const {
+    // Half H writes rows [H*RPW/2, (H+1)*RPW/2) and its share of the rope
+    // groups, so a chunk can be stored in two steps.
+    template <int H>
+    __device__ __forceinline__ void store_half(uint16_t *tile, const AttnArgs &a, int e0, int pw,
+                                               int lane) const {
+        constexpr int J0 = H * RPW / 2, J1 = (H + 1) * RPW / 2;
+        constexpr int NQ = RPW / 8, Q0 = H * (NQ / 2), Q1 = H == 0 ? NQ / 2 : NQ;
 #pragma unroll
-        for (int j = 0; j < RPW; j++) {
+        for (int j = J0; j < J1; j++) {
             u32x4 v = nope[j];
             if (e0 + pw * RPW + j >= a.window) {
                 // e4m3 * scale -> bf16 in one packed conversion per pair; exact for
@@ -142,9 +147,14 @@ struct RowGather {
             *reinterpret_cast<u32x4 *>(tile + (pw * RPW + j) * kKPitch + 8 * lane) = v;
         }
 #pragma unroll
-        for (int q = 0; q < RPW / 8; q++)
+        for (int q = Q0; q < Q1; q++)
             *reinterpret_cast<u32x4 *>(tile + (pw * RPW + 8 * q + (lane >> 3)) * kKPitch + kDN +
                                        8 * (lane & 7)) = rope[q];
+    }
+    __device__ __forceinline__ void store(uint16_t *tile, const AttnArgs &a, int e0, int pw,
+                                          int lane) const {
+        store_half<0>(tile, a, e0, pw, lane);
+        store_half<1>(tile, a, e0, pw, lane);
     }
 };
 
@@ -207,47 +217,26 @@ __device__ __forceinline__ void store_out(const AttnArgs &a, int t, int h, int g
             l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
-// A wave's O^T accumulators (lane (g, c): head c, dims 16ct + 4g + i) times
-// `scale`, as bf16 rows [16 heads][512] at dst (rows kDN apart).  The rows go
-// through LDS first (stage: 16 rows of kStagePitch bf16, this wave's own), so
-// that each global store writes one head's whole 1 KB row, 16 B per lane;
-// storing the accumulators directly would write 32-byte pieces of 16 rows
-// per instruction.  LDS operations of one wave complete in order, so the
-// wave reads back its own writes without a barrier.
-constexpr int kStagePitch = kDN + 8;   // 1040 B: the 8-byte writes of 32 lanes hit distinct banks
-
-__device__ __forceinline__ void store_rows_bf16(const f32x4 (&o)[kDN / 16], float scale,
-                                                uint16_t *stage, uint16_t *dst, int lane) {
-    const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-    for (int ct = 0; ct < kDN / 16; ct++)
-        *reinterpret_cast<u32x2 *>(stage + c * kStagePitch + 16 * ct + 4 * g) =
-            u32x2{bf16_pair_rne(o[ct][0] * scale, o[ct][1] * scale),
-                  bf16_pair_rne(o[ct][2] * scale, o[ct][3] * scale)};
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-        *reinterpret_cast<u32x4 *>(dst + r * kDN + 8 * lane) =
-            *reinterpret_cast<const u32x4 *>(stage + r * kStagePitch + 8 * lane);
-}
-
 constexpr int kDecRows = 64;   // rows per decode chunk (16 per consumer wave)
 static_assert(kDecMaxEntries % kDecRows == 0, "a chunk's list entries lie within the resolved list");
+// LDS pitch (bf16) of the decode's output staging rows (128 dims of one
+// head): 68 words, so the 8-byte writes of 32 lanes (16 heads x 2 dim
+// quads) fall on distinct banks
+constexpr int kOutPitch = 128 + 8;
 constexpr int kPreRows = 32;   // rows per prefill chunk
 
-// One slice of 16*NR rows of a chunk for one wave's 16 heads: the scores
-// S^T = K . Q^T of NR 16-row tiles, the online-softmax update, and
-// O^T += V^T . P^T.  The slice starts at tile row row0 = list entry e0;
-// entries at or past e_end are masked, src maps entries (counted from
-// e_begin) to physical rows (-1: skipped).
+// Scores of one wave's score block: 16*NR rows of a chunk (tile row row0 =
+// list entry e0) for the wave's 16 heads, S^T = K . Q^T, scaled to the log2
+// domain; entries at or past e_end and skipped rows (src: entries counted
+// from e_begin -> physical rows, -1 = skipped) give -inf.  x[4rt + i] is
+// row 16rt + 4g + i for head c.
 template <int NR>
-__device__ __forceinline__ void attend_rows(const uint16_t *tile, int row0, int e0, int e_begin,
-                                            int e_end, const int32_t *src,
-                                            const bf16x8 (&qb)[kD / 32], float sm_scale_log2,
-                                            f32x4 (&o)[kDN / 16], float &m_run, float &l_run,
-                                            int g, int c) {
+__device__ __forceinline__ void score_rows(const uint16_t *tile, int row0, int e0, int e_begin,
+                                           int e_end, const int32_t *src,
+                                           const bf16x8 (&qb)[kD / 32], float sm_scale_log2,
+                                           float (&x)[4 * NR], int g, int c) {
     // a scheduling region of its own: the LDS-read and MFMA groups pinned
-    // below must not interleave with those of a neighbouring slice
+    // below must not interleave with neighbouring work
     __builtin_amdgcn_sched_barrier(0);
     // validity of the lane's rows 16rt + 4g + i (issued before the MFMAs need
     // them): four consecutive, 16-byte aligned entries per row tile, read
@@ -293,79 +282,63 @@ __device__ __forceinline__ void attend_rows(const uint16_t *tile, int row0, int 
         }
         sacc[rt] = s0 + s1;
     }
-    float x[4 * NR], pv[4 * NR];
 #pragma unroll
     for (int rt = 0; rt < NR; rt++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
             x[4 * rt + i] = rv[4 * rt + i] >= 0 ? sacc[rt][i] * sm_scale_log2 : -INFINITY;
-    const bool had = m_run != -INFINITY;             // O holds something to rescale
-    const float alpha = softmax_update<4 * NR>(x, m_run, l_run, pv);
-    if (__ballot(had && alpha != 1.f)) {
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
-    }
-
-    // O^T += V^T . P^T over the wave's rows; the k order (rows 4g+i, then
-    // 16+4g+i) is the score accumulators' lane order
-    const uint16_t *vr = tile + (row0 + 4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
-    if constexpr (NR == 1) {
-        i16x4v pb = __builtin_bit_cast(i16x4v, u32x2{bf16_pair_rne(pv[0], pv[1]),
-                                                     bf16_pair_rne(pv[2], pv[3])});
-        constexpr int G = 4, NRR = kDN / 16 / G;   // 8 groups of 4 column tiles
-        i16x4 va[2][G];
-        auto rd = [&](int gi, int b) {
-#pragma unroll
-            for (int u = 0; u < G; u++) va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
-            __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
-        };
-        auto mm = [&](int gi, int b) {
-#pragma unroll
-            for (int u = 0; u < G; u++)
-                o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    __builtin_bit_cast(i16x4v, va[b][u]), pb, o[gi * G + u], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
-        };
-        rd(0, 0);
-#pragma unroll
-        for (int gi = 0; gi < NRR; gi++) {
-            if (gi + 1 < NRR) rd(gi + 1, (gi + 1) & 1);
-            mm(gi, gi & 1);
-        }
-    } else {
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
-                          bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
-        const uint16_t *vr2 = vr + 16 * kKPitch;
-        constexpr int G = 4, NRR = kDN / 16 / G;
-        i16x4 va[2][G], vb[2][G];
-        auto rd = [&](int gi, int b) {
-#pragma unroll
-            for (int u = 0; u < G; u++) {
-                va[b][u] = lds_read_tr16(vr + 16 * (gi * G + u));
-                vb[b][u] = lds_read_tr16(vr2 + 16 * (gi * G + u));
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
-        };
-        auto mm = [&](int gi, int b) {
-#pragma unroll
-            for (int u = 0; u < G; u++) {
-                const u32x2 l2 = __builtin_bit_cast(u32x2, va[b][u]), h2 = __builtin_bit_cast(u32x2, vb[b][u]);
-                const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                o[gi * G + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, o[gi * G + u], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
-        };
-        rd(0, 0);
-#pragma unroll
-        for (int gi = 0; gi < NRR; gi++) {
-            if (gi + 1 < NRR) rd(gi + 1, (gi + 1) & 1);
-            mm(gi, gi & 1);
-        }
-    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// O^T += V^T . P^T for one wave's 128 output dims (dims 128w + 16d + 4g + i
+// in o[d][hg], lane (g, c): head 16hg + c) over all 64 rows of a chunk, for
+// every head group.  pl[hg][j][lane] holds the P^T operand of the chunk's
+// k-step j (rows 32j .. 32j+31, in the order rows 4g+i, then 16+4g+i), which
+// the score waves wrote; the V^T operand is read transposed from the tile in
+// the same row order, once per workgroup.
+template <int NG>
+__device__ __forceinline__ void pv_rows(const uint16_t *tile, const u32x4 (*pl)[2][64],
+                                        f32x4 (&o)[8][NG], int w, int g, int c, int lane) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pb[2][NG];
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int hg = 0; hg < NG; hg++) pb[j][hg] = __builtin_bit_cast(bf16x8, pl[hg][j][lane]);
+    const uint16_t *vr = tile + (4 * g + (c >> 2)) * kKPitch + 4 * (c & 3) + 128 * w;
+    // four groups (k-step j, dims half dh) of four 16-dim tiles; group i+1's
+    // reads are in flight while group i feeds the MFMAs
+    constexpr int G = 4;
+    i16x4 va[2][G], vb[2][G];
+    auto rd = [&](int gi, int b) {
+        const int j = gi >> 1, dh = gi & 1;
+#pragma unroll
+        for (int u = 0; u < G; u++) {
+            va[b][u] = lds_read_tr16(vr + 32 * j * kKPitch + 16 * (G * dh + u));
+            vb[b][u] = lds_read_tr16(vr + (32 * j + 16) * kKPitch + 16 * (G * dh + u));
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * G, 0);
+    };
+    auto mm = [&](int gi, int b) {
+        const int j = gi >> 1, dh = gi & 1;
+#pragma unroll
+        for (int u = 0; u < G; u++) {
+            const u32x2 l2 = __builtin_bit_cast(u32x2, va[b][u]), h2 = __builtin_bit_cast(u32x2, vb[b][u]);
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+#pragma unroll
+            for (int hg = 0; hg < NG; hg++)
+                o[G * dh + u][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[j][hg], o[G * dh + u][hg], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, G * NG, 0);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int gi = 0; gi < 4; gi++) {
+        if (gi + 1 < 4) rd(gi + 1, (gi + 1) & 1);
+        mm(gi, gi & 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 }  // namespace
 
@@ -384,9 +357,10 @@ __device__ __forceinline__ void attend_rows(const uint16_t *tile, int row0, int 
 template <int NG>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
-    static_assert(2 * 16 * kStagePitch <= kDecRows * kKPitch, "tile 1 stages two waves' output rows");
+    static_assert(4 * 16 * NG * kOutPitch <= kDecRows * kKPitch, "tile 0 stages the output rows");
     __shared__ __attribute__((aligned(16))) int32_t src[kDecMaxEntries];
-    __shared__ float st_m[4][16], st_l[4][16];
+    __shared__ __attribute__((aligned(16))) u32x4 pl[NG][2][64];   // P^T operands [head group][k-step][lane]
+    __shared__ float cm[4][16], lp[4][16];              // score waves' chunk maxima, row sums
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -414,7 +388,6 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     const int tc = t < n_q ? t : 0;                     // for the prologue's loads (n_q >= 1)
 
     const int hgw = NG == 2 ? (w & 1) : 0;
-    const int h = 16 * (NG * hb + hgw) + c;
     const int row0 = NG == 2 ? 32 * ((w >> 1) & 1) : 16 * (w & 3);   // first chunk row of this wave
     const int E = window + kk;
     const int e_begin = split * rps;
@@ -491,31 +464,39 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         }
     }
 
-    constexpr int kMergeBarriers = NG == 2 ? 2 : 4;
     if (producer) {
-        // The loads are issued unconditionally (chunks past the list read the
-        // zero page): with the same number of loads in flight on every path,
-        // storing one buffer waits for that buffer's loads only, not for the
-        // other buffer's as well.
+        // Chunk c goes to tile c & 1.  Chunk c+1 is stored in two halves
+        // while the consumers work on chunk c (one beside its scores, one
+        // beside its value products) and chunk c+2 is in flight.  The loads
+        // are issued unconditionally (chunks past the list read the zero
+        // page): with the same number of loads in flight on every path,
+        // storing one buffer waits for that buffer's loads only.  The
+        // producers take every barrier the consumers take.
         RowGather<kDecRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - 4);
         ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
         gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
         __syncthreads();                                // the consumers' Q is in tile 1
+        if (nchunks > 0) ga.store(ktile[0], a, e_begin, pw, lane);
         for (int ci = 0; ci < nchunks; ci += 2) {
             const int e0 = e_begin + ci * kDecRows;
-            ga.store(ktile[0], a, e0, pw, lane);
+            const bool more1 = ci + 1 < nchunks, more2 = ci + 2 < nchunks;
             __syncthreads();                            // chunk ci ready in tile 0
             ga.load(a, src, e_begin, e0 + 2 * kDecRows, e_end, pw, lane);
-            if (ci + 1 < nchunks) {
-                // tile 1 last held chunk ci-1, whose consumers passed the barrier above
-                gb.store(ktile[1], a, e0 + kDecRows, pw, lane);
-                __syncthreads();                        // chunk ci+1 ready in tile 1
-            }
+            // tile 1 last held chunk ci-1 (or Q), whose readers passed the barrier above
+            if (more1) gb.template store_half<0>(ktile[1], a, e0 + kDecRows, pw, lane);
+            __syncthreads();                            // the chunk maxima
+            if (more1) gb.template store_half<1>(ktile[1], a, e0 + kDecRows, pw, lane);
+            __syncthreads();                            // the chunk's probabilities
+            if (!more1) break;
+            __syncthreads();                            // chunk ci+1 ready in tile 1
             gb.load(a, src, e_begin, e0 + 3 * kDecRows, e_end, pw, lane);
+            if (more2) ga.template store_half<0>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
+            __syncthreads();                            // the chunk maxima
+            if (more2) ga.template store_half<1>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
+            __syncthreads();                            // the chunk's probabilities
         }
-#pragma unroll
-        for (int i = 0; i < kMergeBarriers; i++) __syncthreads();   // the consumers' merge
+        __syncthreads();                                // the consumers' row sums
         return;
     }
 
@@ -526,100 +507,124 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < kD / 32; s++) qb[s] = *reinterpret_cast<const bf16x8 *>(qs + 32 * s);
     }
-    f32x4 o[kDN / 16];
+    // Score wave w covers head group hgw and chunk rows row0 .. row0+16NG-1;
+    // for the value products wave w takes output dims 128w .. 128w+127 of
+    // every head of the block.  All waves keep the same softmax reference
+    // per head (m_run), moved lazily by the largest score of a chunk, so the
+    // probabilities of different score waves add up in one accumulator.
+    constexpr int NB = 4 / NG;                          // score waves per head group
+    f32x4 o[8][NG];
 #pragma unroll
-    for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int d = 0; d < 8; d++)
+#pragma unroll
+        for (int hg = 0; hg < NG; hg++) o[d][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[NG];
+#pragma unroll
+    for (int hg = 0; hg < NG; hg++) m_run[hg] = -INFINITY;
+    float l_part = 0.f;                                 // this wave's rows' share of its head's sum
 
     for (int ci = 0; ci < nchunks; ci++) {
         __syncthreads();                                // chunk ci is in tile ci & 1
         const uint16_t *tile = ktile[ci & 1];
-        const int e0 = e_begin + ci * kDecRows + row0;
-
-        attend_rows<NG>(tile, row0, e0, e_begin, e_end, src, qb, a.sm_scale_log2, o, m_run, l_run, g, c);
+        float x[4 * NG];
+        score_rows<NG>(tile, row0, e_begin + ci * kDecRows + row0, e_begin, e_end, src, qb,
+                       a.sm_scale_log2, x, g, c);
+        float cmax = x[0];
+#pragma unroll
+        for (int i = 1; i < 4 * NG; i++) cmax = fmaxf(cmax, x[i]);
+        cmax = xor32_max(xor16_max(cmax));
+        if (g == 0) cm[w][c] = cmax;
+        __syncthreads();                                // every score wave's chunk maximum
+        float alpha[NG];
+        bool rescale[NG];
+#pragma unroll
+        for (int hg = 0; hg < NG; hg++) {
+            float cx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < NB; r++) cx = fmaxf(cx, cm[hg + NG * r][c]);
+            alpha[hg] = 1.f;
+            rescale[hg] = false;
+            if (cx > m_run[hg] + kLazyLog2) {           // also taken when m_run = -inf and cx is finite
+                rescale[hg] = m_run[hg] != -INFINITY;   // O holds something to rescale
+                alpha[hg] = exp2f(m_run[hg] - cx);
+                m_run[hg] = cx;
+            }
+        }
+        const float mr = (NG == 2 && hgw == 1) ? m_run[NG - 1] : m_run[0];
+        const float am = (NG == 2 && hgw == 1) ? alpha[NG - 1] : alpha[0];
+        float pv[4 * NG], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4 * NG; i++) {
+            pv[i] = mr == -INFINITY ? 0.f : exp2f(x[i] - mr);
+            psum += pv[i];
+        }
+        psum = xor32_sum(xor16_sum(psum));
+        l_part = l_part * am + psum;
+        // the P^T operand of k-step w >> 1 (rows 4g+i, then 16+4g+i)
+        if constexpr (NG == 2) {
+            pl[hgw][w >> 1][lane] = u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
+                                          bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])};
+        } else {
+            // score wave w holds rows 16w .. 16w+15: one half of k-step w >> 1
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint32_t *>(&pl[0][w >> 1][lane]) + 2 * (w & 1)) =
+                u32x2{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3])};
+        }
+#pragma unroll
+        for (int hg = 0; hg < NG; hg++)
+            if (__ballot(rescale[hg] && alpha[hg] != 1.f)) {
+#pragma unroll
+                for (int d = 0; d < 8; d++) o[d][hg] *= alpha[hg];
+            }
+        __syncthreads();                                // the chunk's probabilities
+        pv_rows<NG>(tile, pl, o, w, g, c, lane);
     }
 
-    // ---- merge the consumers' softmax states (same heads, disjoint rows) ----
-    if (g == 0) {
-        st_m[w][c] = m_run;
-        st_l[w][c] = l_run;
+    // ---- the heads' sums, then this wave's 128 output dims ----
+    if (g == 0) lp[w][c] = l_part;
+    __syncthreads();                                    // every wave is past its last chunk
+    float L[NG], inv[NG];
+#pragma unroll
+    for (int hg = 0; hg < NG; hg++) {
+        L[hg] = 0.f;
+#pragma unroll
+        for (int r = 0; r < NB; r++) L[hg] += lp[hg + NG * r][c];
+        inv[hg] = L[hg] > 0.f ? 1.f / L[hg] : 0.f;
     }
-    __syncthreads();                                // every wave is past its last chunk
-    f32x4 *xo = reinterpret_cast<f32x4 *>(&ktile[0][0]);   // the tiles are free now
-    float M = -INFINITY, L = 0.f, my_scale = 0.f;
-    if constexpr (NG == 2) {
-        // waves w and w ^ 2 hold the two row halves of head group w & 1
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
-            const int ww = hgw + 2 * k2;
-            if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
-            const int ww = hgw + 2 * k2;
-            const float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
-            L += st_l[ww][c] * sc;
-            if (ww == w) my_scale = sc;
-        }
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
-        if (w >= 2) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) xo[(hgw * (kDN / 16) + ct) * 64 + lane] = o[ct];
-        }
-        __syncthreads();
-        if (w >= 2) return;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(hgw * (kDN / 16) + ct) * 64 + lane];
-    } else {
-#pragma unroll
-        for (int ww = 0; ww < 4; ww++)
-            if (st_l[ww][c] > 0.f) M = fmaxf(M, st_m[ww][c]);
-#pragma unroll
-        for (int ww = 0; ww < 4; ww++) {
-            const float sc = st_l[ww][c] > 0.f ? exp2f(st_m[ww][c] - M) : 0.f;
-            L += st_l[ww][c] * sc;
-            if (ww == w) my_scale = sc;
-        }
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= my_scale;
-        if (w >= 2) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) xo[((w - 2) * (kDN / 16) + ct) * 64 + lane] = o[ct];
-        }
-        __syncthreads();
-        if (w < 2) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[(w * (kDN / 16) + ct) * 64 + lane];
-        }
-        __syncthreads();
-        if (w == 1) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) xo[ct * 64 + lane] = o[ct];
-        }
-        __syncthreads();
-        if (w != 0) return;
-#pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) o[ct] += xo[ct * 64 + lane];
-    }
-
-
-    // O / L as bf16 rows: the output, or with list splits the partial state
+    // O / L as bf16: the output, or with list splits the partial state
     // [t][split][h] (each value at most the largest |V| of the split's rows)
-    // plus M and L in fp32.  Tile 1 is free now: it stages the rows.
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int hw0 = h - c;                              // the wave's first head
-    uint16_t *stage = &ktile[1][hgw * 16 * kStagePitch];
-    if (S == 1) {
-        store_rows_bf16(o, inv, stage, a.out + (static_cast<int64_t>(t) * a.n_heads + hw0) * kDN, lane);
-        if (a.lse && g == 0)
-            a.lse[static_cast<int64_t>(t) * a.n_heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-    } else {
-        const int64_t slot = (static_cast<int64_t>(t) * S + split) * a.n_heads + h;
-        store_rows_bf16(o, inv, stage, a.part_o + (slot - c) * kDN, lane);
-        if (g == 0) {
-            a.part_ml[2 * slot] = M;
-            a.part_ml[2 * slot + 1] = L;
+    // plus M and L in fp32.  The rows go through LDS (tile 0 is free now,
+    // each wave in its own region; a wave's LDS operations complete in
+    // order) so that each store writes 256 contiguous bytes of one head.
+    uint16_t *stg = &ktile[0][0] + w * (16 * NG) * kOutPitch;
+#pragma unroll
+    for (int hg = 0; hg < NG; hg++)
+#pragma unroll
+        for (int d = 0; d < 8; d++)
+            *reinterpret_cast<u32x2 *>(stg + (16 * hg + c) * kOutPitch + 16 * d + 4 * g) =
+                u32x2{bf16_pair_rne(o[d][hg][0] * inv[hg], o[d][hg][1] * inv[hg]),
+                      bf16_pair_rne(o[d][hg][2] * inv[hg], o[d][hg][3] * inv[hg])};
+    __asm__ volatile("" ::: "memory");
+    const int h0 = 16 * NG * hb;                        // the block's first head
+    const int64_t row0_out = S == 1 ? static_cast<int64_t>(t) * a.n_heads + h0
+                                    : (static_cast<int64_t>(t) * S + split) * a.n_heads + h0;
+    uint16_t *dst = (S == 1 ? a.out : a.part_o) + row0_out * kDN + 128 * w;
+#pragma unroll
+    for (int it = 0; it < 4 * NG; it++) {
+        const int hh = 4 * it + (lane >> 4), col = 8 * (lane & 15);
+        *reinterpret_cast<u32x4 *>(dst + static_cast<int64_t>(hh) * kDN + col) =
+            *reinterpret_cast<const u32x4 *>(stg + hh * kOutPitch + col);
+    }
+    if (w == 0 && g == 0) {
+#pragma unroll
+        for (int hg = 0; hg < NG; hg++) {
+            const int64_t hrow = row0_out + 16 * hg + c;
+            if (S == 1) {
+                if (a.lse)
+                    a.lse[hrow] = L[hg] > 0.f ? (m_run[hg] + log2f(L[hg])) * kLn2 : -INFINITY;
+            } else {
+                a.part_ml[2 * hrow] = m_run[hg];
+                a.part_ml[2 * hrow + 1] = L[hg];
+            }
         }
     }
 }
