@@ -484,17 +484,17 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
             __syncthreads();                            // chunk ci ready in tile 0
             ga.load(a, src, e_begin, e0 + 2 * kDecRows, e_end, pw, lane);
             // tile 1 last held chunk ci-1 (or Q), whose readers passed the barrier above
-            if (more1) gb.template store_half<0>(ktile[1], a, e0 + kDecRows, pw, lane);
             __syncthreads();                            // the chunk maxima
-            if (more1) gb.template store_half<1>(ktile[1], a, e0 + kDecRows, pw, lane);
+            if (more1) gb.template store_half<0>(ktile[1], a, e0 + kDecRows, pw, lane);
             __syncthreads();                            // the chunk's probabilities
+            if (more1) gb.template store_half<1>(ktile[1], a, e0 + kDecRows, pw, lane);
             if (!more1) break;
             __syncthreads();                            // chunk ci+1 ready in tile 1
             gb.load(a, src, e_begin, e0 + 3 * kDecRows, e_end, pw, lane);
-            if (more2) ga.template store_half<0>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
             __syncthreads();                            // the chunk maxima
-            if (more2) ga.template store_half<1>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
+            if (more2) ga.template store_half<0>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
             __syncthreads();                            // the chunk's probabilities
+            if (more2) ga.template store_half<1>(ktile[0], a, e0 + 2 * kDecRows, pw, lane);
         }
         __syncthreads();                                // the consumers' row sums
         return;
