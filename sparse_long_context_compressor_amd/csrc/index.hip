@@ -34,10 +34,8 @@ __device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 
     s1 = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
-constexpr int kIdxWaves = 8;                        // waves per workgroup: one workgroup per CU
-constexpr int kIdxThreads = 64 * kIdxWaves;
 constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
-constexpr int kScoreTile = kIdxWaves * kSubTiles * 16;   // 2048 slots per workgroup
+constexpr int kBlockSlots = 64;                     // slots per key block (one table entry)
 constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
 constexpr int kQPitch = kDI + 16;                   // LDS bytes per staged query head
 
@@ -57,24 +55,29 @@ __device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never
 
 }  // namespace
 
-// grid (n_q, ceil(max_slots / 2048)), 512 threads: one workgroup of eight
-// waves per CU.  (Two four-wave workgroups per CU measured 3 us slower: a
-// CU serves its loads roughly in issue order, so the second workgroup's
-// start waited behind the first's loads and it finished last.)  Sub-tile j
-// covers logical blocks s0/64 + 2j and + 2j + 1: wave w takes slots
-// 16*(w%4) + (0..15) of block 2j + w/4, so one (wave-uniform) table lookup
-// serves each wave's sub-tile.  Lane (g = lane/16, c = lane%16) owns
-// index-dim bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its head and of
-// its key; the MFMA k-order is the same permutation for both operands, so
-// the dot product is unchanged.
-template <int HT>
-__global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
+// grid (n_q, ceil(max_slots / (1024 WB))), 256 WB threads: a workgroup of
+// 4 WB waves scores a tile of 16 sub-tiles of WB key blocks.  WB = 2 (eight
+// waves, 2048 slots) when the grid has about one workgroup per CU, as in a
+// decode step: two four-wave workgroups per CU measured 3 us slower there,
+// since a CU serves its loads roughly in issue order and the second
+// workgroup's start waited behind the first's loads.  WB = 1 for large
+// grids (prefill), where several four-wave workgroups per CU hide each
+// other's latency (the eight-wave tile measured 14% slower there).
+// Sub-tile j covers logical blocks s0/64 + WB j .. + WB j + WB-1: wave w
+// takes slots 16*(w%4) + (0..15) of block WB j + w/4, so one (wave-uniform)
+// table lookup serves each wave's sub-tile.  Lane (g = lane/16, c = lane%16)
+// owns index-dim bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its head
+// and of its key; the MFMA k-order is the same permutation for both
+// operands, so the dot product is unchanged.
+template <int HT, int WB>
+__global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
+    constexpr int kThreads = 256 * WB, kTile = kSubTiles * kBlockSlots * WB;
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int wq = w & 3;                                        // 16-slot quarter of a block
-    const int wb = __builtin_amdgcn_readfirstlane(w >> 2);       // block of a sub-tile's pair
-    const int s0 = blockIdx.y * kScoreTile;
+    const int wb = __builtin_amdgcn_readfirstlane(w >> 2);       // block within a sub-tile
+    const int s0 = blockIdx.y * kTile;
 
     // The kernel arguments of the start-up chain in one round of loads
     // (left alone, the compiler spreads them over several dependent rounds,
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
     const int64_t table_row = static_cast<int64_t>(seq) * stride;
     int32_t my_pb;
     {
-        const int64_t lb = (s0 >> 6) + (lane & 31);
+        const int64_t lb = (s0 >> 6) + (lane & (kSubTiles * WB - 1));
         const bool in = lb < stride;
         my_pb = table_p[table_row + (in ? lb : 0)];
         my_pb = in ? my_pb : -1;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
     // sub-tile j reads through a buffer resource on its (wave-uniform) block;
     // an absent block gets a zero-size resource, whose loads return zeros
     auto stage = [&](int j, KeyStage &st) {
-        const int32_t pb = __builtin_amdgcn_readlane(my_pb, 2 * j + wb);
+        const int32_t pb = __builtin_amdgcn_readlane(my_pb, WB * j + wb);
         const bool ok = pb >= 0 && pb < n_blocks;
         const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : zpage;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
         st.scale = ok ? sc : -INFINITY;
     };
     auto compute = [&](int j, const KeyStage &cur) {
-        const int s = s0 + 128 * j + 64 * wb + 16 * wq + c;
+        const int s = s0 + kBlockSlots * (WB * j + wb) + 16 * wq + c;
         bf16x8 kb[4];
         e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
         e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
@@ -148,44 +151,49 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
                 cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
     };
 
-    // two explicit buffers of kRing sub-tiles: load group q+1 while computing q
-    KeyStage buf0[kRing], buf1[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
-
     // ---- query operands and per-head factors (they depend on t only) ----
-    // Loaded after the first key loads (which wait only on the table): the
-    // query's 16*HT heads x 128 codes are one contiguous run that the
+    // The query's 16*HT heads x 128 codes are one contiguous run that the
     // workgroup loads once, coalesced (per-wave operand loads would fetch it
-    // four times, in half-line pieces), and stages through LDS.  The visible
-    // count decides the early exit only now: the key loads already issued
-    // read in-range blocks or the zero page either way.
+    // four times, in half-line pieces), and stages through LDS.  With one
+    // workgroup per CU (WB = 2) these loads follow the first key loads, which
+    // wait only on the table; with several four-wave workgroups per CU
+    // (WB = 1) they come first (measured 4% faster there), and the key
+    // loads' wait on the table, issued before them, does not cover them.
+    // The visible count decides the early exit after the first key loads
+    // either way: those read in-range blocks or the zero page.
     constexpr int kQUnits = 16 * HT * kDI / 16;          // 16-byte units
-    constexpr int kQIt = (kQUnits + kIdxThreads - 1) / kIdxThreads;
+    constexpr int kQIt = (kQUnits + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * HT * kQPitch];
     u32x4 qraw[kQIt];
-    {
+    f32x4 qw[HT], qs[HT];
+    auto load_query = [&]() {
         const uint8_t *qp = a.q + static_cast<int64_t>(t) * a.h_idx * kDI;
 #pragma unroll
         for (int i = 0; i < kQIt; i++) {
-            const int u = threadIdx.x + kIdxThreads * i;
+            const int u = threadIdx.x + kThreads * i;
             if (u < kQUnits) qraw[i] = *reinterpret_cast<const u32x4 *>(qp + 16 * u);
         }
-    }
-    f32x4 qw[HT], qs[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ht++) {
-        const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
-        qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
-        qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
-    }
+        for (int ht = 0; ht < HT; ht++) {
+            const int64_t o = static_cast<int64_t>(t) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
+            qw[ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
+            qs[ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
+        }
+    };
+
+    // two explicit buffers of kRing sub-tiles: load group q+1 while computing q
+    KeyStage buf0[kRing], buf1[kRing];
+    if constexpr (WB == 1) load_query();
+#pragma unroll
+    for (int j = 0; j < kRing; j++) stage(j, buf0[j]);
+    if constexpr (WB != 1) load_query();
     nv = visible_slots(q_pos_p[t], a.ratio, n_slots_p[seq]);
     nv = nv < a.max_slots ? nv : a.max_slots;
     if (s0 >= nv) return;
 
 #pragma unroll
     for (int i = 0; i < kQIt; i++) {
-        const int u = threadIdx.x + kIdxThreads * i;
+        const int u = threadIdx.x + kThreads * i;
         if (u < kQUnits)
             *reinterpret_cast<u32x4 *>(qlds + (u / (kDI / 16)) * kQPitch + 16 * (u % (kDI / 16))) = qraw[i];
     }
@@ -208,18 +216,29 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_kernel(IndexArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < kRing; j++)
-            if (s0 + 128 * (q * kRing + j) + 64 * wb < nv) compute(q * kRing + j, cur[j]);   // wave-uniform
+            if (s0 + kBlockSlots * (WB * (q * kRing + j) + wb) < nv) compute(q * kRing + j, cur[j]);   // wave-uniform
+    }
+}
+
+template <int WB>
+static void launch_index(const IndexArgs &a, hipStream_t stream) {
+    constexpr int tile = kSubTiles * kBlockSlots * WB;
+    const dim3 grid(a.n_q, (a.max_slots + tile - 1) / tile), block(256 * WB);
+    switch (a.h_idx / 16) {
+    case 1: hipLaunchKernelGGL((index_score_kernel<1, WB>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((index_score_kernel<2, WB>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((index_score_kernel<3, WB>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((index_score_kernel<4, WB>), grid, block, 0, stream, a); break;
     }
 }
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
-    dim3 grid(a.n_q, (a.max_slots + kScoreTile - 1) / kScoreTile);
-    switch (a.h_idx / 16) {
-    case 1: hipLaunchKernelGGL(index_score_kernel<1>, grid, dim3(kIdxThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(index_score_kernel<2>, grid, dim3(kIdxThreads), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(index_score_kernel<3>, grid, dim3(kIdxThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL(index_score_kernel<4>, grid, dim3(kIdxThreads), 0, stream, a); break;
-    }
+    // eight-wave 2048-slot tiles while the grid stays within about two
+    // workgroups per CU (256 CUs), four-wave 1024-slot tiles beyond
+    constexpr int64_t kCUs = 256;
+    const int64_t wide = static_cast<int64_t>(a.n_q) * ((a.max_slots + 2047) / 2048);
+    if (wide <= 2 * kCUs) launch_index<2>(a, stream);
+    else launch_index<1>(a, stream);
     return hipGetLastError();
 }
 
