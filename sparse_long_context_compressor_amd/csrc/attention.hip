@@ -475,8 +475,10 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         RowGather<kDecRows / 4> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - 4);
         ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
-        gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
         __syncthreads();                                // the consumers' Q is in tile 1
+        // chunk 1 only now: issued with chunk 0 and Q, its loads delayed both
+        // in the CU's in-order memory pipeline
+        gb.load(a, src, e_begin, e_begin + kDecRows, e_end, pw, lane);
         if (nchunks > 0) ga.store(ktile[0], a, e_begin, pw, lane);
         for (int ci = 0; ci < nchunks; ci += 2) {
             const int e0 = e_begin + ci * kDecRows;
