@@ -24,14 +24,16 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
+// Non-negative floats get the sign bit set, negative ones are inverted
+// (the arithmetic shift spreads the sign into the mask): no branch.
 __device__ __forceinline__ uint32_t order_key(float s) {
-    uint32_t u = __float_as_uint(s + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 
 // Block-wide exclusive scan of two counts (sh: 2 * kTopkWaves ints).
 __device__ __forceinline__ void block_scan2(int a, int b, int *sh, int &a_before, int &b_before) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
     if (lane == 63) {
         sh[w] = ia;
@@ -97,7 +99,7 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
     constexpr int BPT = kHistBins / THREADS;
     static_assert(THREADS >= 256 && kHistBins % THREADS == 0, "block size");
     static_assert(WAVES * 256 <= kHistWords && 2 * kRankCap <= kHistWords, "histogram array size");
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wbase = w * 64 * R;
 
     uint32_t kmin, kmax;
@@ -105,7 +107,8 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[R], int n
         kmin = range[0];
         kmax = range[1];
     } else {
-        for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < kHistCopies * kHistBins / THREADS; i++) hist[tid + THREADS * i] = 0u;
         kmin = 0xffffffffu;
         kmax = 0u;
 #pragma unroll
@@ -309,7 +312,7 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
                                               int *red, int *sh, uint32_t &largest) {
     constexpr int WAVES = THREADS / 64;
     constexpr int BPT = kHistBins / THREADS;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t vmin = 0xffffffffu, vmax = 0u;
     int cnt = 0;
 #pragma unroll
@@ -322,7 +325,8 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
     vmin = wave_umin(vmin);
     vmax = wave_umax(vmax);
     cnt = wave_isum(cnt);
-    for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < kHistBins / THREADS; i++) hist[tid + THREADS * i] = 0u;
     if (lane == 0) {
         red[w] = static_cast<int>(vmin);
         red[WAVES + w] = static_cast<int>(vmax);
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     __shared__ int sh[8];
 
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // The score loads first, bounded by the row length only: the visible
     // count (two dependent scalar loads, which take their own path) arrives
     // meanwhile and masks the keys past it.  Rows are 16-byte aligned: the
@@ -421,8 +425,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     f32x4 raw[R4];                                // raw[q]: slots wbase + 256q + 4 lane + (0..3)
 #pragma unroll
     for (int q = 0; q < R4; q++) {
+        // unconditional (a load under a branch costs a branch per load):
+        // units past the row re-read its last unit, whose keys lie past the
+        // visible count and are masked below
         const int s0 = wbase + 256 * q + 4 * lane;
-        raw[q] = s0 < max_slots ? *reinterpret_cast<const f32x4 *>(sc + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        raw[q] = *reinterpret_cast<const f32x4 *>(sc + (s0 < max_slots ? s0 : max_slots - 4));
     }
     int n = visible_slots(pos, a.ratio, a.n_slots[seq]);
     n = n < max_slots ? n : max_slots;
@@ -440,7 +447,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     for (int q = 0; q < R4; q++) {
         const int s0 = wbase + 256 * q + 4 * lane;
 #pragma unroll
-        for (int e = 0; e < 4; e++) key[4 * q + e] = s0 + e < n ? order_key(raw[q][e]) : 0u;
+        for (int e = 0; e < 4; e++) {
+            const uint32_t kk = order_key(raw[q][e]);   // computed for every slot, then masked
+            key[4 * q + e] = s0 + e < n ? kk : 0u;
+        }
     }
     uint32_t gmax[R4];
 #pragma unroll
@@ -449,13 +459,15 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     uint32_t top;                                 // the largest key
     const uint32_t L = kth_floor<THREADS, R4>(gmax, k, hist, red, sh, top);
 
-    // candidates per round and lane (keys are never 0 when valid)
+    // candidates per round and lane: key >= max(L, 1) (valid keys are never
+    // 0, so this also excludes the masked slots)
+    const uint32_t Lc = L > 1u ? L : 1u;
     int cl[R4], wc = 0;
 #pragma unroll
     for (int q = 0; q < R4; q++) {
         cl[q] = 0;
 #pragma unroll
-        for (int e = 0; e < 4; e++) cl[q] += (key[4 * q + e] != 0u && key[4 * q + e] >= L) ? 1 : 0;
+        for (int e = 0; e < 4; e++) cl[q] += key[4 * q + e] >= Lc ? 1 : 0;
         wc += cl[q];
     }
     wc = wave_isum(wc);
@@ -480,7 +492,8 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
         return;
     }
     // the select's histogram starts cleared (kth_floor is done with it)
-    for (int i = tid; i < kHistCopies * kHistBins; i += THREADS) hist[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < kHistCopies * kHistBins / THREADS; i++) hist[tid + THREADS * i] = 0u;
     // compact the candidates in slot order: round by round, lanes in order,
     // a lane's four slots in order
 #pragma unroll
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const uint32_t kk = key[4 * q + e];
-            if (kk != 0u && kk >= L) {
+            if (kk >= Lc) {
                 cand_key[pos] = kk;
                 cand_slot[pos] = wbase + 256 * q + 4 * lane + e;
                 pos++;
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(TopkArgs a) {
     __shared__ int red[2 * kTopkWaves];
     __shared__ int sh[8];
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int seq = a.q_seq[t];
     int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
     n = n < a.max_slots ? n : a.max_slots;
@@ -557,7 +570,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(TopkArgs a) {
     __shared__ int sel_sh[2];
 
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, w = tid >> 6;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int seq = a.q_seq[t];
     int n = visible_slots(a.q_pos[t], a.ratio, a.n_slots[seq]);
     n = n < a.max_slots ? n : a.max_slots;
