@@ -332,7 +332,10 @@ def main():
                          lay.key_table, lay.n_slots, SLOTS, scores)
 
     def topk(lay):
-        slc.topk_select(K, scores, SLOTS, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
+        # the select plus the decode's L2 warm-up (its queries and window rows
+        # are read beside the select, into the L2 the decode then reads)
+        slc.topk_select_warm(K, scores, SLOTS, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln,
+                             lay.q, W, lay.swa_pool, lay.swa_table)
 
     def decode(lay):
         slc.sparse_mla_decode(4, lay.q, lay.q_seq, lay.q_pos, W, lay.swa_pool, lay.swa_table,

@@ -194,6 +194,23 @@ slc_status_t slc_topk_select(int n_q, int k, const float *scores, int max_slots,
                              const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
                              void *stream);
 
+/*
+ * slc_topk_select_warm -- slc_topk_select, plus an L2 warm-up for the sparse
+ * MLA decode that follows it: spare workgroups of the same launch read, and
+ * discard, each query's inputs that do not depend on the selection (its
+ * query heads q[t][0..n_heads) and the latent rows of its window, the
+ * positions max(0, p-window+1) .. p of swa_pool), so that the decode finds
+ * them in cache.  The select uses one compute unit per query, so these
+ * reads run beside it.  Outputs are identical to slc_topk_select's.
+ *   q, n_heads, window, swa_pool  as for slc_sparse_mla_decode (q 16-byte
+ *                                 aligned; swa_pool required when window > 0)
+ */
+slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_slots,
+                                  const int32_t *q_seq, const int32_t *q_pos, int ratio,
+                                  const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
+                                  const uint16_t *q, int n_heads, int window, slc_pool_t swa_pool,
+                                  void *stream);
+
 /* Bytes of workspace slc_index_topk needs (scores of every visible slot). */
 size_t slc_index_topk_workspace_size(int n_q, int max_slots);
 

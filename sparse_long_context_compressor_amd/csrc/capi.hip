@@ -122,6 +122,34 @@ slc_status_t slc_topk_select(int n_q, int k, const float *scores, int max_slots,
     return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
+slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_slots,
+                                  const int32_t *q_seq, const int32_t *q_pos, int ratio,
+                                  const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
+                                  const uint16_t *q, int n_heads, int window, slc_pool_t swa_pool,
+                                  void *stream) {
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
+    if (st != SLC_OK) return st;
+    if (k < 1 || k > SLC_MAX_TOPK) return fail("topk_select_warm: k must be in [1, SLC_MAX_TOPK]");
+    if (!heads_ok(n_heads, SLC_MAX_HEADS))
+        return fail("topk_select_warm: n_heads must be a multiple of 16 in [16, 128]");
+    if (window < 0 || window > SLC_MAX_WINDOW)
+        return fail("topk_select_warm: window must be in [0, SLC_MAX_WINDOW]");
+    if (n_q == 0) return SLC_OK;
+    if (!scores || !topk_idx || !topk_len)
+        return fail("topk_select_warm: scores, topk_idx and topk_len are required");
+    if (!q || !aligned(q, 16)) return fail("topk_select_warm: q is required, 16-byte aligned");
+    if (window > 0) {
+        st = check_pool(swa_pool, "topk_select_warm: swa_pool");
+        if (st != SLC_OK) return st;
+    }
+    TopkArgs a{n_q, k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx, topk_len};
+    a.warm_q = q;
+    a.warm_heads = n_heads;
+    a.warm_window = window;
+    a.warm_swa = swa_pool;
+    return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t slc_index_topk_workspace_size(int n_q, int max_slots) {
     if (n_q <= 0 || max_slots <= 0) return 0;
     return (static_cast<size_t>(n_q) * static_cast<size_t>(max_slots) * sizeof(float) + 255) &

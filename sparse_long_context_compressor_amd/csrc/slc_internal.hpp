@@ -46,6 +46,13 @@ struct TopkArgs {
     const int32_t *n_slots;
     int32_t *idx;
     int32_t *len;
+    // optional L2 warm-up for the attention that follows (warm_q null: none):
+    // query t's heads warm_q[t][warm_heads][576] and the latent rows of its
+    // window (positions p - warm_window + 1 .. p) in warm_swa
+    const uint16_t *warm_q;
+    int warm_heads;
+    int warm_window;
+    slc_pool_t warm_swa;
 };
 
 struct AttnArgs {

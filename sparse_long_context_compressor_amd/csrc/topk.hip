@@ -386,6 +386,64 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
     return vmin + (static_cast<uint32_t>(sh[0]) << shift);   // the bin's floor
 }
 
+// L2 warm-up for the attention that follows the select (blocks past the
+// queries' when the launcher adds them): reads, and discards, query t's
+// inputs that do not depend on the selection -- its query heads and the
+// latent rows of its window -- so that the decode finds them in the L2 of
+// this XCD (block t' = t + 8m shares blockIdx % 8 with the decode's blocks of
+// query t).  Every load is in bounds: rows of absent blocks read the query
+// instead.  blk: scratch LDS for up to 32 block ids.
+template <int THREADS>
+__device__ __forceinline__ void warm_attention_inputs(const TopkArgs &a, int t, int32_t *blk) {
+    const int tid = threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    constexpr int kRowUnits = kD * 2 / 16;              // 16-byte units per latent row (72)
+    const u32x4 *qp = reinterpret_cast<const u32x4 *>(a.warm_q + static_cast<int64_t>(t) * a.warm_heads * kD);
+    const int qunits = a.warm_heads * kRowUnits;
+    for (int u0 = 0; u0 < qunits; u0 += 4 * THREADS) {
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int u = u0 + THREADS * i + tid;
+            v[i] = qp[u < qunits ? u : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc ^= v[i];
+    }
+    const slc_pool_t &sp = a.warm_swa;
+    const int seq = a.q_seq[t], p = a.q_pos[t];
+    const int lo = p - a.warm_window + 1 > 0 ? p - a.warm_window + 1 : 0;
+    const int rows = p - lo + 1;
+    if (sp.base && a.warm_window > 0 && rows > 0) {
+        const int lb0 = lo >> 6, nb = (p >> 6) - lb0 + 1;   // at most 17 blocks (window <= 1024)
+        if (tid < nb && tid < 32) {
+            const int64_t lb = lb0 + tid;
+            const int32_t pb = lb < sp.table_stride ? sp.block_table[static_cast<int64_t>(seq) * sp.table_stride + lb] : -1;
+            blk[tid] = pb >= 0 && pb < sp.n_blocks ? pb : -1;
+        }
+        __syncthreads();
+        const int total = rows * kRowUnits;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(sp.base);
+        for (int u0 = 0; u0 < total; u0 += 4 * THREADS) {
+            u32x4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int u = u0 + THREADS * i + tid;
+                const int uu = u < total ? u : 0;
+                const int r = lo + uu / kRowUnits, j = uu % kRowUnits;
+                const int32_t pb = blk[(r >> 6) - lb0];
+                const u32x4 *row = pb >= 0 ? reinterpret_cast<const u32x4 *>(
+                                                 base + (static_cast<int64_t>(pb) * kBR + (r & (kBR - 1))) * (kD * 2))
+                                           : qp;
+                v[i] = row[j];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc ^= v[i];
+        }
+    }
+    __asm__ volatile("" ::"v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]));   // keeps the loads
+}
+
 // One 1024-thread workgroup per query, R scores per thread (R >= 4): wave w
 // owns slots [64Rw, 64R(w+1)) and lane l reads slots 64Rw + 256q + 4l + e
 // (e < 4) with one 16-byte load per round q, so the wave's slots run in
@@ -411,6 +469,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     __shared__ int red[3 * WAVES];
     __shared__ int sh[8];
 
+    if (static_cast<int>(blockIdx.x) >= a.n_q) {       // L2 warm-up blocks (and padding)
+        const int t = static_cast<int>(blockIdx.x) - ((a.n_q + 7) & ~7);
+        if (t >= 0 && t < a.n_q) warm_attention_inputs<THREADS>(a, t, reinterpret_cast<int32_t *>(hist));
+        return;
+    }
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // The score loads first, bounded by the row length only: the visible
@@ -649,15 +712,17 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
     const int per = (a.max_slots + kTopkThreads - 1) / kTopkThreads;
     const bool vec = a.max_slots % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
     dim3 grid(a.n_q), block(kTopkThreads);
+    // the L2 warm-up blocks ride along with the main select kernel only
+    const dim3 wgrid(a.warm_q ? static_cast<unsigned>(((a.n_q + 7) & ~7) + a.n_q) : a.n_q);
     if (per <= 1) hipLaunchKernelGGL(topk_small_kernel<1>, grid, block, 0, stream, a);
     else if (per <= 2) hipLaunchKernelGGL(topk_small_kernel<2>, grid, block, 0, stream, a);
     else if (!vec && per <= 16) hipLaunchKernelGGL(topk_small_kernel<16>, grid, block, 0, stream, a);
     else if (!vec && per <= 64) hipLaunchKernelGGL(topk_small_kernel<64>, grid, block, 0, stream, a);
-    else if (per <= 4) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 4>), grid, block, 0, stream, a);
-    else if (per <= 8) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 8>), grid, block, 0, stream, a);
-    else if (per <= 16) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 16>), grid, block, 0, stream, a);
-    else if (per <= 32) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32>), grid, block, 0, stream, a);
-    else if (per <= 64) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64>), grid, block, 0, stream, a);
+    else if (per <= 4) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 4>), wgrid, block, 0, stream, a);
+    else if (per <= 8) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 8>), wgrid, block, 0, stream, a);
+    else if (per <= 16) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 16>), wgrid, block, 0, stream, a);
+    else if (per <= 32) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32>), wgrid, block, 0, stream, a);
+    else if (per <= 64) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64>), wgrid, block, 0, stream, a);
     else hipLaunchKernelGGL(topk_long_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }

@@ -23,7 +23,7 @@ SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
-    "slc_topk_select", "slc_index_topk_workspace_size", "slc_index_topk",
+    "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -63,6 +63,9 @@ def lib():
         L.slc_index_scores.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, pool, vp, i32, vp, vp]
         L.slc_topk_select.restype = i32
         L.slc_topk_select.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp]
+        L.slc_topk_select_warm.restype = i32
+        L.slc_topk_select_warm.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32,
+                                           pool, vp]
         L.slc_index_topk_workspace_size.restype = sz
         L.slc_index_topk_workspace_size.argtypes = [i32, i32]
         L.slc_index_topk.restype = i32
@@ -150,6 +153,16 @@ def topk_select(k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx, to
     _check(lib().slc_topk_select(n_q, int(k), _ptr(scores), int(max_slots), _ptr(q_seq),
                                  _ptr(q_pos), int(ratio), _ptr(n_slots), _ptr(topk_idx),
                                  _ptr(topk_len), _stream()))
+
+
+def topk_select_warm(k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx, topk_len,
+                     q, window, swa_pool, swa_table) -> None:
+    """topk_select plus the L2 warm-up of the decode's queries and window rows."""
+    n_q = int(q_seq.shape[0])
+    _check(lib().slc_topk_select_warm(n_q, int(k), _ptr(scores), int(max_slots), _ptr(q_seq),
+                                      _ptr(q_pos), int(ratio), _ptr(n_slots), _ptr(topk_idx),
+                                      _ptr(topk_len), _ptr(q), int(q.shape[1]), int(window),
+                                      pool(swa_pool, swa_table), _stream()))
 
 
 def index_topk_workspace_size(n_q: int, max_slots: int) -> int:
