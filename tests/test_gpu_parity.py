@@ -165,6 +165,25 @@ def test_index_scores_and_topk_match_oracle(S, oracle, h_idx):
     print(f"h_idx={h_idx}: near-tie slots excluded: {near}")
 
 
+@pytest.mark.parametrize("H", [16, 48])
+def test_topk_select_warm_equals_select(S, oracle, H):
+    """The select with the decode's L2 warm-up (extra read-only workgroups) gives
+    the plain select's lists bit for bit, on lists long enough for the main
+    select kernel, with windows that reach before position 0."""
+    lay = I.build_layer(19, ratio=4, H=H, ctx=[12000, 9000],
+                        queries=[(0, 11999), (0, 5), (1, 8999), (1, 100), (0, 130)],
+                        n_slots=[3000, 2250], W=128, k=64, H_I=16)
+    to_device(lay)
+    sc, idx, ln = gpu_index_topk(S, lay)
+    idx_w = torch.full_like(idx, -7)
+    ln_w = torch.full_like(ln, -7)
+    S.topk_select_warm(lay.k, sc, lay.max_slots, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx_w, ln_w,
+                       lay.q, lay.W, lay.swa_pool, lay.swa_table)
+    torch.cuda.synchronize()
+    assert lay.max_slots > 2048
+    assert torch.equal(idx_w, idx) and torch.equal(ln_w, ln)
+
+
 def test_topk_ties_and_short_lists(S, oracle):
     lay = I.build_layer(14, ratio=4, H=16, ctx=[2000, 40],
                         queries=[(0, 1999), (0, 2), (1, 39), (0, 100)], n_slots=[500, 10], W=16,
