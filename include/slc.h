@@ -223,6 +223,29 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
                             int32_t *topk_len, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * slc_indexcache_skips -- "DeepSeek-V4 IndexCache freq2 cross-layer TopK
+ * reuse" (the IndexCache freq2 page), section 2: which layers reuse an
+ * earlier layer's top-k list instead of running the indexer and the select.
+ * Only layers with compress ratio 4 take part.  A layer's sequence index is
+ * the number of ratio-4 layers before it.  Without a pattern it reuses when
+ * that index is not a multiple of freq (freq <= 1: never).  A non-empty
+ * pattern takes priority: it must begin with 'F' and hold only 'F'
+ * (compute) and 'S' (reuse), position i deciding for sequence index i;
+ * layers past its end compute.  A reusing layer passes the list of the
+ * layer that last computed one to its attention as a given top-k (the
+ * compressor keeps running on every layer).
+ *   n_layers         layers in the stack
+ *   compress_ratios  HOST int32 [n_layers] (4 marks the indexed layers)
+ *   freq             reuse frequency
+ *   pattern          HOST, NUL-terminated, nullable or "" for none
+ *   skip             HOST int32 [n_layers] out: 1 = reuse, 0 = compute
+ * Host arithmetic only (no GPU).  Errors: SLC_ERR_INVALID_ARG for a bad
+ * pattern or missing pointers.
+ */
+slc_status_t slc_indexcache_skips(int n_layers, const int32_t *compress_ratios, int freq,
+                                  const char *pattern, int32_t *skip);
+
+/*
  * slc_sparse_mla_decode / slc_sparse_mla_prefill -- "DeepseekV4Attention"
  * (devpress), forward_mqa with _forward_decode (flash_mla_with_kvcache with
  * SWA and compressed indices) and _forward_prefill (flash_mla_sparse_fwd over

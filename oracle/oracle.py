@@ -16,7 +16,7 @@ __all__ = [
     "build", "lib", "e4m3_decode", "e4m3_encode", "bf16_decode", "bf16_encode",
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
-    "num_threads",
+    "indexcache_skips", "num_threads",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -295,6 +295,37 @@ def sparse_mla_batch(q_bits, q_pos, q_seq, W, swa_off, swa_base, swa_count, swa_
     if want_f64:
         return out, lse, o64, l64
     return out, lse
+
+
+# ------------------------------------------------------------- IndexCache
+def indexcache_skips(compress_ratios, freq: int, pattern: str = ""):
+    """Per layer: 1 if the layer reuses an earlier layer's top-k, else 0.
+
+    "DeepSeek-V4 IndexCache freq2 cross-layer TopK reuse" page, section 2:
+    only layers with compress ratio 4 take part; a layer's indexer sequence
+    index is the number of ratio-4 layers before it; without a pattern the
+    layer reuses when that index is not a multiple of the frequency; a
+    pattern string, when given, takes priority: it must begin with 'F'
+    (compute), 'S' at the layer's sequence index means reuse, and layers past
+    the end of the string compute.  A frequency of 1 (or less) never reuses.
+    """
+    if pattern and pattern[0] != "F":
+        raise ValueError("an IndexCache pattern must begin with 'F'")
+    if pattern and any(ch not in "FS" for ch in pattern):
+        raise ValueError("an IndexCache pattern holds only 'F' and 'S'")
+    out = []
+    seq = 0                                   # ratio-4 layers seen before this one
+    for r in compress_ratios:
+        if r != 4:
+            out.append(0)
+            continue
+        if pattern:
+            skip = seq < len(pattern) and pattern[seq] == "S"
+        else:
+            skip = freq > 1 and seq % freq != 0
+        out.append(1 if skip else 0)
+        seq += 1
+    return out
 
 
 def num_threads() -> int:

@@ -150,6 +150,36 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
     return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
+slc_status_t slc_indexcache_skips(int n_layers, const int32_t *compress_ratios, int freq,
+                                  const char *pattern, int32_t *skip) {
+    if (n_layers < 0) return fail("indexcache_skips: n_layers must be >= 0");
+    if (n_layers == 0) return SLC_OK;
+    if (!compress_ratios || !skip) return fail("indexcache_skips: compress_ratios and skip are required");
+    size_t plen = 0;
+    if (pattern) {
+        plen = std::strlen(pattern);
+        if (plen > 0 && pattern[0] != 'F')
+            return fail("indexcache_skips: a pattern must begin with 'F'");
+        for (size_t i = 0; i < plen; i++)
+            if (pattern[i] != 'F' && pattern[i] != 'S')
+                return fail("indexcache_skips: a pattern holds only 'F' and 'S'");
+    }
+    // a ratio-4 layer's place among the ratio-4 layers decides; others never reuse
+    int64_t seq = 0;
+    for (int l = 0; l < n_layers; l++) {
+        if (compress_ratios[l] != 4) {
+            skip[l] = 0;
+            continue;
+        }
+        bool reuse;
+        if (plen > 0) reuse = seq < static_cast<int64_t>(plen) && pattern[seq] == 'S';
+        else reuse = freq > 1 && seq % freq != 0;
+        skip[l] = reuse ? 1 : 0;
+        seq++;
+    }
+    return SLC_OK;
+}
+
 size_t slc_index_topk_workspace_size(int n_q, int max_slots) {
     if (n_q <= 0 || max_slots <= 0) return 0;
     return (static_cast<size_t>(n_q) * static_cast<size_t>(max_slots) * sizeof(float) + 255) &

@@ -24,6 +24,7 @@ SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
 EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
+    "slc_indexcache_skips",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -66,6 +67,8 @@ def lib():
         L.slc_topk_select_warm.restype = i32
         L.slc_topk_select_warm.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                            pool, vp]
+        L.slc_indexcache_skips.restype = i32
+        L.slc_indexcache_skips.argtypes = [i32, vp, i32, C.c_char_p, vp]
         L.slc_index_topk_workspace_size.restype = sz
         L.slc_index_topk_workspace_size.argtypes = [i32, i32]
         L.slc_index_topk.restype = i32
@@ -163,6 +166,16 @@ def topk_select_warm(k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_id
                                       _ptr(q_pos), int(ratio), _ptr(n_slots), _ptr(topk_idx),
                                       _ptr(topk_len), _ptr(q), int(q.shape[1]), int(window),
                                       pool(swa_pool, swa_table), _stream()))
+
+
+def indexcache_skips(compress_ratios, freq: int, pattern: str = "") -> list:
+    """Per layer 1 = reuse an earlier layer's top-k, 0 = compute (host only)."""
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(compress_ratios, dtype=np.int32))
+    out = np.zeros(r.shape[0], np.int32)
+    _check(lib().slc_indexcache_skips(int(r.shape[0]), r.ctypes.data, int(freq),
+                                      pattern.encode() if pattern else None, out.ctypes.data))
+    return out.tolist()
 
 
 def index_topk_workspace_size(n_q: int, max_slots: int) -> int:

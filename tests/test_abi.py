@@ -113,3 +113,23 @@ def test_package_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not pat.search(text), os.path.join(dirpath, f)
+
+
+def test_indexcache_skips_match_the_oracle(S, oracle):
+    """The library's schedule (host arithmetic) against the oracle's, on random
+    ratio layouts, frequencies and patterns, plus its argument errors."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(rng.integers(0, 60))
+        ratios = rng.choice([1, 4, 4, 4, 128], size=n).tolist()
+        freq = int(rng.integers(0, 6))
+        pattern = ""
+        if rng.random() < 0.4:
+            m = int(rng.integers(1, 12))
+            pattern = "F" + "".join(rng.choice(["F", "S"], size=m - 1).tolist())
+        assert S.indexcache_skips(ratios, freq, pattern) == oracle.indexcache_skips(ratios, freq, pattern)
+    with pytest.raises(S.SlcError):
+        S.indexcache_skips([4, 4], 2, "SF")
+    with pytest.raises(S.SlcError):
+        S.indexcache_skips([4, 4], 2, "FX")

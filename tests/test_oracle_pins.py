@@ -534,3 +534,36 @@ def test_attention_batch_equals_single(oracle):
             codes[b * n_slots:(b + 1) * n_slots], scales[b * n_slots:(b + 1) * n_slots],
             bf16_bits(rope[b * n_slots:(b + 1) * n_slots]), idx[t])
         assert np.array_equal(out[t], o1) and np.array_equal(lse[t], l1)
+
+
+# ------------------------------------------------------------- IndexCache
+def test_golden_indexcache_skips(oracle):
+    """The IndexCache freq2 page's worked example: 21 ratio-4 layers, 10 of them
+    reuse, ids [4, 8, ..., 40] (tests/golden/indexcache_skips.txt).  Counting
+    tokens or raw layer ids instead of ratio-4 layers, or reusing on the
+    multiples instead of the others, gives other ids."""
+    rows = {r[0]: r[1:] for r in _rows("indexcache_skips.txt")}
+    ratios = [int(x) for x in rows["ratios"]]
+    skips = oracle.indexcache_skips(ratios, int(rows["freq"][0]))
+    assert sum(r == 4 for r in ratios) == int(rows["ratio4_layers"][0])
+    assert sum(skips) == int(rows["reusing_layers"][0])
+    assert [i for i, s in enumerate(skips) if s] == [int(x) for x in rows["reusing_ids"]]
+
+
+def test_indexcache_skips_closed_forms(oracle):
+    """Cases the rule fixes by itself: freq 1 never reuses; layers without
+    ratio 4 never do and do not advance the count; on an all-ratio-4 stack
+    freq f reuses exactly the layers whose index is not a multiple of f; the
+    pattern 'FS' repeated equals freq 2, a pattern outranks freq, layers past
+    the pattern compute, and a pattern must begin with 'F'."""
+    all4 = [4] * 12
+    assert oracle.indexcache_skips(all4, 1) == [0] * 12
+    for f in (2, 3, 5):
+        assert oracle.indexcache_skips(all4, f) == [int(i % f != 0) for i in range(12)]
+    mixed = [128, 4, 1, 4, 4, 128, 4]           # ratio-4 layers: 1, 3, 4, 6 -> indices 0..3
+    assert oracle.indexcache_skips(mixed, 2) == [0, 0, 0, 1, 0, 0, 1]
+    assert oracle.indexcache_skips(all4, 2, "FS" * 6) == oracle.indexcache_skips(all4, 2)
+    assert oracle.indexcache_skips(all4, 2, "FSS") == [0, 1, 1] + [0] * 9
+    assert oracle.indexcache_skips(all4, 7, "FFFS") == [0, 0, 0, 1] + [0] * 8
+    with pytest.raises(ValueError):
+        oracle.indexcache_skips(all4, 2, "SF")
