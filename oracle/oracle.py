@@ -16,7 +16,7 @@ __all__ = [
     "build", "lib", "e4m3_decode", "e4m3_encode", "bf16_decode", "bf16_encode",
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
-    "indexcache_skips", "num_threads",
+    "swa_insert", "swa_dequant", "indexcache_skips", "num_threads",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,7 @@ def _declare(L):
                                     dbl, _P, _P, _P, _P]),
         "oracle_sparse_mla_batch": (i32, [i32, i32, _P, _P, _P, i32, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, i32, _P, dbl, _P, _P, _P, _P]),
+        "oracle_swa_insert": (i32, [i32, _P, _P, _P, i32, _P, _P, _P, _P]),
         "oracle_num_threads": (i32, []),
         "oracle_e4m3_decode_array": (None, [i64, _P, _P]),
         "oracle_e4m3_encode_array": (None, [i64, _P, _P]),
@@ -295,6 +296,39 @@ def sparse_mla_batch(q_bits, q_pos, q_seq, W, swa_off, swa_base, swa_count, swa_
     if want_f64:
         return out, lse, o64, l64
     return out, lse
+
+
+# --------------------------------------------------------- FP8 SWA rows
+def swa_insert(kv_bits, pos, cos_sin):
+    """SWA KV insert of n tokens (kv [n,576] bf16 bits, not yet rotated; pos
+    [n] their positions): RoPE at each token's own position, then the cache
+    row format.  Returns codes u8 [n,512], scales f32 [n,8], rope u16 [n,64]
+    and the fp32 rows before quantisation [n,576]."""
+    kv = _c(kv_bits, np.uint16).reshape(-1, D)
+    n = kv.shape[0]
+    ps = _c(pos, np.int32)
+    cs = _c(cos_sin, np.float32)
+    codes = np.zeros((n, DN), np.uint8)
+    scales = np.zeros((n, DN // 64), np.float32)
+    rope = np.zeros((n, DR), np.uint16)
+    pre = np.zeros((n, D), np.float32)
+    if lib().oracle_swa_insert(n, _p(kv), _p(ps), _p(cs), cs.shape[0], _p(codes), _p(scales),
+                               _p(rope), _p(pre)):
+        raise ValueError("a position is outside the cos/sin table")
+    return codes, scales, rope, pre
+
+
+def swa_dequant(codes, scales, rope):
+    """The latent rows an fp8 cache row stands for, as bf16 bits [n,576]:
+    code * scale for the nope dims (exact in bf16 for power-of-two scales,
+    which is checked), the rope dims as stored."""
+    cd = _c(codes, np.uint8)
+    n = cd.shape[0]
+    v = e4m3_decode(cd) * np.repeat(_c(scales, np.float32).astype(np.float64), 64, axis=1)
+    nope = bf16_encode(v)
+    if not np.array_equal(bf16_decode(nope), v):
+        raise ValueError("code * scale is not exact in bf16")
+    return np.concatenate([nope, _c(rope, np.uint16).reshape(n, DR)], axis=1)
 
 
 # ------------------------------------------------------------- IndexCache

@@ -183,6 +183,28 @@ static int pow2_exponent_for(double amax)
     return e;
 }
 
+/* The cache row format ["DeepseekV4Attention", cache block layout; "From
+ * MLA to CSA + HCA" 6.1]: the 512 nope dims of the fp32 row y32 in 8 blocks of
+ * 64, each with the pow2 scale of its largest magnitude and e4m3 codes of
+ * y / scale (round to nearest even); the 64 rope dims rounded to bf16. */
+static void quantise_row(const float *y32, uint8_t *codes, float *scales, uint16_t *rope)
+{
+    for (int blk = 0; blk < OR_DN / OR_QB; blk++) {
+        double amax = 0.0, scale;
+        for (int i = 0; i < OR_QB; i++) {
+            double a = fabs((double)y32[blk * OR_QB + i]);
+            if (a > amax)
+                amax = a;
+        }
+        scale = ldexp(1.0, pow2_exponent_for(amax));
+        scales[blk] = (float)scale;
+        for (int i = 0; i < OR_QB; i++)
+            codes[blk * OR_QB + i] = oracle_e4m3_encode((double)y32[blk * OR_QB + i] / scale);
+    }
+    for (int i = 0; i < OR_DR; i++)
+        rope[i] = oracle_bf16_encode((double)y32[OR_DN + i]);
+}
+
 /*
  * One sequence of L tokens, ratio r in {4, 128}.
  *   kv    [L, 576] bf16 bits     per-token latent kv
@@ -254,22 +276,51 @@ int oracle_compress_seq(int r, int L, const uint16_t *kv, const float *score,
             y32[d] = (float)y[d];
         if (prequant_out)
             memcpy(prequant_out + (size_t)j * OR_D, y32, sizeof y32);
+        quantise_row(y32, codes + (size_t)j * OR_DN, scales + (size_t)j * (OR_DN / OR_QB),
+                     rope + (size_t)j * OR_DR);
+    }
+    return 0;
+}
 
-        for (int blk = 0; blk < OR_DN / OR_QB; blk++) {
-            double amax = 0.0, scale;
-            for (int i = 0; i < OR_QB; i++) {
-                double a = fabs((double)y32[blk * OR_QB + i]);
-                if (a > amax)
-                    amax = a;
-            }
-            scale = ldexp(1.0, pow2_exponent_for(amax));
-            scales[(size_t)j * (OR_DN / OR_QB) + blk] = (float)scale;
-            for (int i = 0; i < OR_QB; i++)
-                codes[(size_t)j * OR_DN + blk * OR_QB + i] =
-                    oracle_e4m3_encode((double)y32[blk * OR_QB + i] / scale);
+/*
+ * SWA KV insert ["From MLA to CSA + HCA" 6.2: the fused q-norm / RoPE / KV
+ * insert kernel's KV side (GPT-J RoPE, fp8 quantisation, paged write); 5.5:
+ * the SWA cache holds fp8 nope + bf16 rope + one scale per 64 dims;
+ * "DeepseekV4Attention", HCA compressor workflow stage 3 (KV: RoPE + FP8
+ * quant + SWA cache write)].
+ *   kv [n, 576] bf16 bits: the tokens' latent rows, not yet rotated
+ *   pos [n]: each token's own position (row of the cos/sin table)
+ * Each row: RoPE on the pairs (512+2i, 513+2i) at pos, the row rounded to
+ * fp32, then the compressed rows' quantisation (codes [n,512], scales [n,8],
+ * rope [n,64]); prequant [n,576] (nullable) receives the fp32 row.
+ * Returns 0, or -1 when a position is outside the table (nothing after that
+ * token is written).
+ */
+int oracle_swa_insert(int n, const uint16_t *kv, const int32_t *pos, const float *cos_sin,
+                      int max_pos, uint8_t *codes, float *scales, uint16_t *rope,
+                      float *prequant_out)
+{
+    for (int t = 0; t < n; t++) {
+        double y[OR_D];
+        float y32[OR_D];
+        int p = pos[t];
+        if (p < 0 || p >= max_pos)
+            return -1;
+        for (int d = 0; d < OR_D; d++)
+            y[d] = oracle_bf16_value(kv[(size_t)t * OR_D + d]);
+        for (int i = 0; i < OR_DR / 2; i++) {
+            double c = cos_sin[(size_t)p * OR_DR + i];
+            double s = cos_sin[(size_t)p * OR_DR + OR_DR / 2 + i];
+            double a = y[OR_DN + 2 * i], b = y[OR_DN + 2 * i + 1];
+            y[OR_DN + 2 * i] = a * c - b * s;
+            y[OR_DN + 2 * i + 1] = a * s + b * c;
         }
-        for (int i = 0; i < OR_DR; i++)
-            rope[(size_t)j * OR_DR + i] = oracle_bf16_encode((double)y32[OR_DN + i]);
+        for (int d = 0; d < OR_D; d++)
+            y32[d] = (float)y[d];
+        if (prequant_out)
+            memcpy(prequant_out + (size_t)t * OR_D, y32, sizeof y32);
+        quantise_row(y32, codes + (size_t)t * OR_DN, scales + (size_t)t * (OR_DN / OR_QB),
+                     rope + (size_t)t * OR_DR);
     }
     return 0;
 }

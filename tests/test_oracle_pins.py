@@ -567,3 +567,66 @@ def test_indexcache_skips_closed_forms(oracle):
     assert oracle.indexcache_skips(all4, 7, "FFFS") == [0, 0, 0, 1] + [0] * 8
     with pytest.raises(ValueError):
         oracle.indexcache_skips(all4, 2, "SF")
+
+
+# ------------------------------------------------------------ FP8 SWA insert
+def test_swa_insert_quantises_like_the_library_casts(oracle):
+    """At positions whose table row is the identity (cos 1, sin 0) the insert
+    is the row format alone: prequant = the bf16 values, scale = the exact pow2
+    rule on each block's amax, codes = torch's e4m3 cast of value/scale, rope =
+    the input bits; codes never exceed 448 and dequantise within half a step."""
+    g = np.random.default_rng(31)
+    n = 40
+    x = g.normal(0, 1, (n, 576)) * np.repeat(g.uniform(0.01, 80.0, (n, 9)), 64, axis=1)
+    kv = bf16_bits(torch.from_numpy(x.astype(np.float32)))
+    pos = g.integers(0, 50, n).astype(np.int32)
+    codes, scales, rope, pre = oracle.swa_insert(kv, pos, _cs_identity(50))
+    vals = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(pre.astype(np.float64), vals)
+    assert np.array_equal(rope, kv[:, 512:])
+    for t in range(n):
+        for blk in range(8):
+            v = vals[t, 64 * blk: 64 * blk + 64]
+            s = _scale_exact(float(np.max(np.abs(v))))
+            assert scales[t, blk] == s
+            ref = torch.from_numpy((v / s).astype(np.float32)).to(torch.float8_e4m3fn).view(
+                torch.uint8).numpy()
+            assert np.array_equal(codes[t, 64 * blk: 64 * blk + 64], ref)
+    deq = oracle.bf16_decode(oracle.swa_dequant(codes, scales, rope))
+    err = np.abs(deq[:, :512] - vals[:, :512])
+    step = np.maximum(np.abs(vals[:, :512]) * 2.0 ** -4, np.repeat(scales, 64, axis=1) * 2.0 ** -10)
+    assert np.all(err <= step)
+    assert np.array_equal(deq[:, 512:], vals[:, 512:])
+
+
+def test_swa_insert_rotates_at_the_tokens_own_position(oracle):
+    """A table whose row 17 is a 90 degree turn: only tokens at position 17
+    change, their interleaved rope pairs (a, b) become (-b, a), and the nope
+    codes are independent of the position; a general angle keeps each pair's
+    norm to fp32 rounding, and a position past the table is an error."""
+    g = np.random.default_rng(32)
+    n = 24
+    kv = bf16_bits(torch.from_numpy(g.normal(0, 1, (n, 576)).astype(np.float32)))
+    pos = np.array([17 if t % 3 == 0 else t for t in range(n)], np.int32)
+    cs = _cs_identity(40)
+    base = oracle.swa_insert(kv, pos, cs)
+    cs[17, :32], cs[17, 32:] = 0.0, 1.0
+    turned = oracle.swa_insert(kv, pos, cs)
+    for t in range(n):
+        assert np.array_equal(turned[0][t], base[0][t]) and np.array_equal(turned[1][t], base[1][t])
+        if pos[t] != 17:
+            assert np.array_equal(turned[3][t], base[3][t])
+            continue
+        a, b = base[3][t, 512::2], base[3][t, 513::2]
+        assert np.array_equal(turned[3][t, 512::2], -b)
+        assert np.array_equal(turned[3][t, 513::2], a)
+    ang = g.uniform(0, 6.28, 32)
+    cs[17, :32], cs[17, 32:] = np.cos(ang), np.sin(ang)
+    pre = oracle.swa_insert(kv, pos, cs)[3].astype(np.float64)
+    vals = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for t in np.nonzero(pos == 17)[0]:
+        n0 = np.hypot(vals[t, 512::2], vals[t, 513::2])
+        n1 = np.hypot(pre[t, 512::2], pre[t, 513::2])
+        assert np.allclose(n1, n0, rtol=1e-6, atol=1e-30)
+    with pytest.raises(ValueError):
+        oracle.swa_insert(kv[:1], np.array([40], np.int32), cs)
