@@ -51,7 +51,8 @@ def parse():
                          "the known-size kernel the HBM byte counters are scaled by")
     ap.add_argument("--workload", default="c4a_decode_64k",
                     choices=["c4a_decode_64k", "c4a_prefill_2k", "c128a_decode_128k",
-                             "swaonly_decode_b64", "c4a_single_layer_4k"],
+                             "swaonly_decode_b64", "c4a_single_layer_4k",
+                             "c4a_decode_64k_stages", "c4a_decode_64k_fp8swa"],
                     help="c4a_decode_64k is the headline; the others print supplementary "
                          "per-stage timings of the same kernels on the other workloads")
     ap.add_argument("--report-stats", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
@@ -204,7 +205,14 @@ def other_workload(args):
     slc.lib()
     name = args.workload
     n_rep = 2 if name == "c4a_prefill_2k" else args.replicas
-    reps = [I.CONFIGS[name](seed=200 + r, device=dev) for r in range(n_rep)]
+    fp8 = name == "c4a_decode_64k_fp8swa"
+    if name.startswith("c4a_decode_64k_"):
+        # the headline workload with per-stage timings (stages), or with its
+        # SWA pool in fp8 rows (fp8swa)
+        reps = [I.c4a_decode_64k(seed=200 + r, device=dev, swa_fp8=fp8) for r in range(n_rep)]
+    else:
+        reps = [I.CONFIGS[name](seed=200 + r, device=dev) for r in range(n_rep)]
+    fl = slc.SWA_FP8 if fp8 else 0
     torch.cuda.synchronize()
     log(f"{n_rep} input replicas of {name} resident")
     lay0 = reps[0]
@@ -227,7 +235,11 @@ def other_workload(args):
                              lay.key_table, lay.n_slots, ms_, sc)
 
         def topk(lay):
-            slc.topk_select(Kk, sc, ms_, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
+            if decode:      # with the decode's L2 warm-up, as the headline step runs it
+                slc.topk_select_warm(Kk, sc, ms_, lay.q_seq, lay.q_pos, 4 | fl, lay.n_slots, idx,
+                                     ln, lay.q, Ww, lay.swa_pool, lay.swa_table)
+            else:
+                slc.topk_select(Kk, sc, ms_, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx, ln)
         stages["index_scores"] = index_scores
         stages["topk_select"] = topk
         get_idx = lambda lay: idx  # noqa: E731
@@ -241,10 +253,10 @@ def other_workload(args):
 
     def attention(lay):
         if r == 1:
-            f(1, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, sm_scale=lay.sm_scale,
-              out=out, lse=lse, workspace=ws)
+            f(1 | fl, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table,
+              sm_scale=lay.sm_scale, out=out, lse=lse, workspace=ws)
         else:
-            f(r, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, lay.cmp_pool,
+            f(r | fl, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, lay.cmp_pool,
               lay.cmp_table, get_idx(lay), lay.n_slots, lay.sm_scale, out, lse, ws)
     stages["sparse_mla_decode" if decode else "sparse_mla_prefill"] = attention
 
@@ -275,9 +287,14 @@ def other_workload(args):
     # algorithmic bytes / flops of the attention stage
     n_cmp = Kk if r > 1 else 0
     att_us = per["sparse_mla_decode" if decode else "sparse_mla_prefill"]
+    if "index_scores" in per and decode:
+        # IndexCache freq 2: every other ratio-4 layer reuses the previous
+        # layer's list and runs the attention alone
+        rec["indexcache_freq2_us_per_layer"] = (ms_step * 1e3 + att_us) / 2
     if decode:
         cmp_row = 672
-        b = Q * (Hh * 576 * 2 + Ww * 1152 + n_cmp * (cmp_row + 4) + Hh * 512 * 2 + Hh * 4)
+        swa_row = 672 if fp8 else 1152
+        b = Q * (Hh * 576 * 2 + Ww * swa_row + n_cmp * (cmp_row + 4) + Hh * 512 * 2 + Hh * 4)
         rec["attention_GBps"] = b / (att_us * 1e-6) / 1e9
         rec["attention_hbm_frac"] = rec["attention_GBps"] / HBM_PEAK_GBPS
     else:

@@ -11,6 +11,8 @@
  *                           against the FP8 index keys of the visible slots.
  *   slc_topk_select         per-query global top-k over those scores.
  *   slc_index_topk          the two above in one call.
+ *   slc_swa_insert          RoPE + fp8 quantisation + paged write of new tokens
+ *                           into an fp8 sliding-window pool
  *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
  *   slc_sparse_mla_prefill  window plus the selected compressed slots.
  *
@@ -104,6 +106,13 @@ typedef enum {
     SLC_LAYER_C128A = 128
 } slc_layer_t;
 
+/* Flag OR'ed into the layer type of slc_sparse_mla_decode / _prefill (and
+ * into the ratio of slc_topk_select_warm): the SWA pool holds fp8 rows in the
+ * compressed-row (CMP) layout, as slc_swa_insert writes them, instead of
+ * bf16 rows ("From MLA to CSA + HCA" 5.5: the V4 SWA cache stores fp8 nope
+ * dims, bf16 rope dims and one scale per 64 dims). */
+#define SLC_SWA_FP8 0x100
+
 typedef struct slc_pool {
     void *base;                  /* device: n_blocks blocks                         */
     const int32_t *block_table;  /* device: [n_seq][table_stride] physical block ids */
@@ -152,6 +161,37 @@ slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int m
                           const uint16_t *kv, const float *score, const float *gamma, float eps,
                           const float *cos_sin, int max_pos, slc_pool_t cmp_pool,
                           float *prequant, void *stream);
+
+/*
+ * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J
+ * RoPE, fp8 quantisation and the paged write in one kernel) and 5.5 (the V4
+ * SWA cache row: fp8 nope, bf16 rope, one scale per 64 dims);
+ * "DeepseekV4Attention" (devpress), HCA compressor workflow, stage 3 (KV:
+ * RoPE + FP8 quant + SWA cache write).
+ *
+ * For each token t (sequence tok_seq[t], position p = tok_pos[t]):
+ *   y = kv[t] (576 dims, not yet rotated);
+ *   RoPE (GPT-J interleaved pairs (512+2i, 513+2i)) at position p with
+ *            cos = cos_sin[p][i], sin = cos_sin[p][32+i];
+ *   nope dims: 8 blocks of 64 -> the same scale rule and e4m3 codes as
+ *            slc_compress; rope dims: bf16 round-to-nearest-even;
+ *   stored at row p of sequence tok_seq[t] in swa_pool.
+ * Attend to such a pool with layer_type | SLC_SWA_FP8.
+ *
+ *   n_tok        tokens (>= 0)
+ *   kv           device bf16 [n_tok][576], 16-byte aligned
+ *   tok_seq, tok_pos  device int32 [n_tok]; tok_seq indexes swa_pool's table
+ *   cos_sin      device fp32 [max_pos][64]; tokens with p outside
+ *                [0, max_pos) are not written, nor are rows whose block is
+ *                absent from the table
+ *   swa_pool     destination, CMP layout (SLC_CMP_BLOCK_BYTES per block)
+ *   prequant_debug  nullable device fp32 [n_tok][576], 16-byte aligned: the
+ *                row after RoPE, before quantisation
+ * Tokens must not share a (sequence, position): their rows would race.
+ */
+slc_status_t slc_swa_insert(int n_tok, const uint16_t *kv, const int32_t *tok_seq,
+                            const int32_t *tok_pos, const float *cos_sin, int max_pos,
+                            slc_pool_t swa_pool, float *prequant_debug, void *stream);
 
 /*
  * slc_index_scores -- "DeepseekV4Attention" (devpress), Indexer section:
@@ -204,6 +244,8 @@ slc_status_t slc_topk_select(int n_q, int k, const float *scores, int max_slots,
  * reads run beside it.  Outputs are identical to slc_topk_select's.
  *   q, n_heads, window, swa_pool  as for slc_sparse_mla_decode (q 16-byte
  *                                 aligned; swa_pool required when window > 0)
+ *   ratio        as for slc_topk_select, OR'ed with SLC_SWA_FP8 when swa_pool
+ *                holds fp8 rows (CMP layout)
  */
 slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_slots,
                                   const int32_t *q_seq, const int32_t *q_pos, int ratio,
@@ -263,7 +305,10 @@ slc_status_t slc_indexcache_skips(int n_layers, const int32_t *compress_ratios, 
  *   lse[t][h] = ln sum_i exp(logit_i)  (fp32; -inf and out = 0 if the list is empty)
  *
  *   layer_type   SLC_LAYER_SWAONLY (cmp_pool, cmp_idx ignored; k must be 0),
- *                SLC_LAYER_C4A or SLC_LAYER_C128A (cmp_pool, cmp_idx required)
+ *                SLC_LAYER_C4A or SLC_LAYER_C128A (cmp_pool, cmp_idx required);
+ *                OR'ed with SLC_SWA_FP8 when swa_pool holds fp8 rows in the
+ *                CMP layout (dequantised like compressed rows; the SWA rows
+ *                are then K_i = code * scale ++ rope as well)
  *   n_q, n_heads queries and query heads (multiple of 16, <= 128)
  *   q            device bf16 [n_q][n_heads][576], 16-byte aligned
  *   q_seq, q_pos device int32 [n_q]

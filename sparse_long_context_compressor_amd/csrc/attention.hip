@@ -11,7 +11,9 @@
 // the block tables into a physical row (SWA entries e < window are positions
 // p-window+1+e, the rest are compressed slot ids); the rows are then gathered
 // chunk by chunk into an LDS tile as bf16 (compressed rows dequantised on the
-// way: code * scale), with the next chunk's global loads in flight while the
+// way: code * scale; SWA rows too when the SWA pool holds fp8 rows, as "From
+// MLA to CSA + HCA" 5.5 describes the V4 SWA cache), with the next chunk's
+// global loads in flight while the
 // current chunk is computed.  On the tile, per wave and 16 heads:
 //   S^T = K . Q^T               v_mfma_f32_16x16x32_bf16, Q^T held in registers
 //   online softmax per head     each lane owns one head: no cross-lane rescale
@@ -72,7 +74,8 @@ __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int t, int s
 // at a control-flow join (which would force a wait on each row in turn).
 __device__ __attribute__((aligned(256))) uint8_t kZeroPage[2048];   // never written
 
-template <int RPW>
+// F8: the SWA pool holds fp8 rows in the compressed-row layout too.
+template <int RPW, bool F8>
 struct RowGather {
     u32x4 nope[RPW];        // SWA: 8 bf16; compressed: 8 codes in the low 8 bytes
     float scl[RPW];         // compressed: the lane's 64-dim block scale
@@ -92,13 +95,15 @@ struct RowGather {
         for (int j = 0; j < RPW; j++) {
             const int32_t row = __builtin_amdgcn_readlane(my_row, j);
             const bool cmp = eb + j >= window;
+            const bool f8 = F8 || cmp;                  // a row in the compressed-row layout
             const int64_t blk = row >> 6, r = row & 63;
-            const uint8_t *cbase = reinterpret_cast<const uint8_t *>(a.cmp.base) + blk * SLC_CMP_BLOCK_BYTES;
+            const uint8_t *cbase = reinterpret_cast<const uint8_t *>(cmp ? a.cmp.base : a.swa.base) +
+                                   blk * SLC_CMP_BLOCK_BYTES;
             const uint8_t *sbase = reinterpret_cast<const uint8_t *>(a.swa.base) + static_cast<int64_t>(row) * (kD * 2);
-            const uint8_t *base = row < 0 ? kZeroPage : (cmp ? cbase : sbase);
-            const uint32_t noff = (row >= 0 && cmp) ? static_cast<uint32_t>(r * SLC_CMP_ROW_BYTES) + 8u * lane
-                                                    : 16u * lane;   // compressed: 16-byte read, low 8 used
-            const uint32_t soff = (row >= 0 && cmp)
+            const uint8_t *base = row < 0 ? kZeroPage : (f8 ? cbase : sbase);
+            const uint32_t noff = (row >= 0 && f8) ? static_cast<uint32_t>(r * SLC_CMP_ROW_BYTES) + 8u * lane
+                                                   : 16u * lane;   // fp8: 16-byte read, low 8 used
+            const uint32_t soff = (row >= 0 && f8)
                                       ? static_cast<uint32_t>(SLC_CMP_SCALE_OFFSET + r * 32) + 4u * (lane >> 3)
                                       : 0u;
             nope[j] = *reinterpret_cast<const u32x4 *>(base + noff);
@@ -113,6 +118,7 @@ struct RowGather {
             const uint8_t *pr = kZeroPage + 16 * part;
             if (row >= 0)
                 pr = (e >= a.window ? cmp_row_ptr(a.cmp, row) + kDN
+                      : F8          ? cmp_row_ptr(a.swa, row) + kDN
                                     : reinterpret_cast<const uint8_t *>(swa_row_ptr(a.swa, row) + kDN)) +
                      16 * part;
             rope[q] = *reinterpret_cast<const u32x4 *>(pr);
@@ -132,7 +138,7 @@ struct RowGather {
 #pragma unroll
         for (int j = J0; j < J1; j++) {
             u32x4 v = nope[j];
-            if (e0 + pw * RPW + j >= a.window) {
+            if (F8 || e0 + pw * RPW + j >= a.window) {
                 // e4m3 * scale -> bf16 in one packed conversion per pair; exact for
                 // power-of-two scales (the ABI's scale format)
                 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -354,7 +360,7 @@ __device__ __forceinline__ void pv_rows(const uint16_t *tile, const u32x4 (*pl)[
 // its own head group with no merge, measured about 1 us slower on the 64K
 // decode: its workgroups load twice the Q and its 8-way combine reads twice
 // the partials.)
-template <int NG>
+template <int NG, bool F8>
 __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kDecRows * kKPitch];
     static_assert(4 * 16 * NG * kOutPitch <= kDecRows * kKPitch, "tile 0 stages the output rows");
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(512) void mla_decode_kernel(AttnArgs a) {
         // page): with the same number of loads in flight on every path,
         // storing one buffer waits for that buffer's loads only.  The
         // producers take every barrier the consumers take.
-        RowGather<kDecRows / 4> ga, gb;
+        RowGather<kDecRows / 4, F8> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - 4);
         ga.load(a, src, e_begin, e_begin, e_end, pw, lane);
         __syncthreads();                                // the consumers' Q is in tile 1
@@ -701,7 +707,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
 // ----------------------------------------------------------------- prefill
 // NW + 4 waves: waves 0..NW-1 compute (wave w: heads 16w..16w+15 of the block,
 // all rows of each 32-row chunk), four more waves gather the next chunk.
-template <int NW>
+template <int NW, bool F8>
 __global__ __launch_bounds__((NW + 4) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ktile[kPreRows * kKPitch];
@@ -720,7 +726,7 @@ void mla_prefill_kernel(AttnArgs a) {
     __syncthreads();
 
     if (w >= NW) {
-        RowGather<kPreRows / 4> ga, gb;
+        RowGather<kPreRows / 4, F8> ga, gb;
         const int pw = __builtin_amdgcn_readfirstlane(w - NW);
         // unconditional loads (past the list: the zero page), so that a
         // buffer's store waits for its own loads only
@@ -862,8 +868,13 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) 
         const int ng = a.head_groups;
         const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
         dim3 grid(groups * 8u * (a.n_heads / (16 * ng)) * a.n_splits);
-        if (ng == 2) hipLaunchKernelGGL(mla_decode_kernel<2>, grid, dim3(512), 0, stream, a);
-        else hipLaunchKernelGGL(mla_decode_kernel<1>, grid, dim3(512), 0, stream, a);
+        if (a.swa_fp8) {
+            if (ng == 2) hipLaunchKernelGGL((mla_decode_kernel<2, true>), grid, dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((mla_decode_kernel<1, true>), grid, dim3(512), 0, stream, a);
+        } else {
+            if (ng == 2) hipLaunchKernelGGL((mla_decode_kernel<2, false>), grid, dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((mla_decode_kernel<1, false>), grid, dim3(512), 0, stream, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.n_splits == 1) return e;
         const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / kCombCols);
@@ -883,11 +894,20 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) 
     const int hb = (a.n_heads + 63) / 64;          // head blocks of up to 64 heads
     const int nw = a.n_heads / hb / 16;            // 16-head groups per block (uniform)
     dim3 grid(a.n_q, hb);
-    switch (nw) {
-    case 1: hipLaunchKernelGGL(mla_prefill_kernel<1>, grid, dim3(320), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(mla_prefill_kernel<2>, grid, dim3(384), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(mla_prefill_kernel<3>, grid, dim3(448), 0, stream, a); break;
-    default: hipLaunchKernelGGL(mla_prefill_kernel<4>, grid, dim3(512), 0, stream, a); break;
+    if (a.swa_fp8) {
+        switch (nw) {
+        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, true>), grid, dim3(320), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, true>), grid, dim3(384), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, true>), grid, dim3(448), 0, stream, a); break;
+        default: hipLaunchKernelGGL((mla_prefill_kernel<4, true>), grid, dim3(512), 0, stream, a); break;
+        }
+    } else {
+        switch (nw) {
+        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, false>), grid, dim3(320), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, false>), grid, dim3(384), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, false>), grid, dim3(448), 0, stream, a); break;
+        default: hipLaunchKernelGGL((mla_prefill_kernel<4, false>), grid, dim3(512), 0, stream, a); break;
+        }
     }
     return hipGetLastError();
 }

@@ -127,6 +127,8 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
                                   const int32_t *n_slots, int32_t *topk_idx, int32_t *topk_len,
                                   const uint16_t *q, int n_heads, int window, slc_pool_t swa_pool,
                                   void *stream) {
+    const bool swa_fp8 = (ratio & SLC_SWA_FP8) != 0;
+    ratio &= ~SLC_SWA_FP8;
     slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
     if (st != SLC_OK) return st;
     if (k < 1 || k > SLC_MAX_TOPK) return fail("topk_select_warm: k must be in [1, SLC_MAX_TOPK]");
@@ -147,7 +149,24 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
     a.warm_heads = n_heads;
     a.warm_window = window;
     a.warm_swa = swa_pool;
+    a.warm_swa_fp8 = swa_fp8 ? 1 : 0;
     return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+slc_status_t slc_swa_insert(int n_tok, const uint16_t *kv, const int32_t *tok_seq,
+                            const int32_t *tok_pos, const float *cos_sin, int max_pos,
+                            slc_pool_t swa_pool, float *prequant_debug, void *stream) {
+    if (n_tok < 0) return fail("swa_insert: n_tok must be >= 0");
+    if (max_pos < 1) return fail("swa_insert: max_pos must be >= 1");
+    if (n_tok == 0) return SLC_OK;
+    if (!kv || !tok_seq || !tok_pos || !cos_sin)
+        return fail("swa_insert: kv, tok_seq, tok_pos and cos_sin are required");
+    if (!aligned(kv, 16) || (prequant_debug && !aligned(prequant_debug, 16)))
+        return fail("swa_insert: kv and prequant_debug must be 16-byte aligned");
+    slc_status_t st = check_pool(swa_pool, "swa_insert: swa_pool");
+    if (st != SLC_OK) return st;
+    SwaInsertArgs a{n_tok, kv, tok_seq, tok_pos, cos_sin, max_pos, swa_pool, prequant_debug};
+    return hip_status(launch_swa_insert(a, static_cast<hipStream_t>(stream)));
 }
 
 slc_status_t slc_indexcache_skips(int n_layers, const int32_t *compress_ratios, int freq,
@@ -237,9 +256,12 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
                                const int32_t *cmp_idx, int k, const int32_t *n_slots,
                                float sm_scale, uint16_t *out, float *lse, void *workspace,
                                size_t ws_bytes, void *stream) {
+    const bool swa_fp8 = (layer_type & SLC_SWA_FP8) != 0;
+    layer_type &= ~SLC_SWA_FP8;
     if (layer_type != SLC_LAYER_SWAONLY && layer_type != SLC_LAYER_C4A &&
         layer_type != SLC_LAYER_C128A)
-        return fail("sparse_mla: layer_type must be SWAONLY (1), C4A (4) or C128A (128)");
+        return fail("sparse_mla: layer_type must be SWAONLY (1), C4A (4) or C128A (128), "
+                    "optionally with SLC_SWA_FP8");
     if (n_q < 0) return fail("sparse_mla: n_q must be >= 0");
     if (!heads_ok(n_heads, SLC_MAX_HEADS))
         return fail("sparse_mla: n_heads must be a multiple of 16 in [16, 128]");
@@ -281,6 +303,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
     a.q_seq = q_seq;
     a.q_pos = q_pos;
     a.window = window;
+    a.swa_fp8 = swa_fp8 ? 1 : 0;
     a.swa = swa_pool;
     a.cmp = cmp_pool;
     a.cmp_idx = cmp_idx;

@@ -1,6 +1,7 @@
 // compress.hip -- fused compressor kernel: window pooling -> RMSNorm -> RoPE ->
 // FP8 quantisation -> paged store, one slot per wave (r = 4) or per workgroup
-// (r = 128).
+// (r = 128); and the SWA KV insert (RoPE -> FP8 quantisation -> paged store of
+// single tokens into an fp8 sliding-window pool), which shares the row format.
 //
 // Method: "DeepseekV4Attention" (devpress, AMD), DeepseekCompressor forward
 // and the CSA/HCA compressor sections (softmax-gated pooling of the window's
@@ -73,6 +74,47 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
     return e;
 }
 
+// GPT-J RoPE of the lane's rope channel at position pos: the pair
+// (512+2i, 513+2i) is the lane pair (2i, 2i+1).
+__device__ __forceinline__ float rope_lane(float v, int lane, int pos, const float *cos_sin) {
+    float other = __shfl_xor(v, 1, 64);
+    int pi = lane >> 1;
+    float c = cos_sin[static_cast<int64_t>(pos) * kDR + pi];
+    float s = cos_sin[static_cast<int64_t>(pos) * kDR + kDR / 2 + pi];
+    return (lane & 1) ? (other * s + v * c) : (v * c - other * s);
+}
+
+__device__ __forceinline__ void store_prequant(float *pq, const float (&y)[9], int lane) {
+    *reinterpret_cast<f32x4 *>(pq + 8 * lane) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4 *>(pq + 8 * lane + 4) = f32x4{y[4], y[5], y[6], y[7]};
+    pq[kDN + lane] = y[8];
+}
+
+// The wave's row y in the cache row format, stored at physical row `row` of a
+// pool with the compressed-row layout: per 64-dim block (lanes 8b .. 8b+7)
+// the pow2 scale of its amax and e4m3 codes of y / scale; rope -> bf16.
+__device__ __forceinline__ void quant_store(const float (&y)[9], int lane, slc_pool_t pool,
+                                            int64_t row) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    int e = pow2_exponent(amax);
+    float inv_scale = ldexpf(1.f, -e);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        w0 |= f32_to_e4m3(y[i] * inv_scale) << (8 * i);
+        w1 |= f32_to_e4m3(y[4 + i] * inv_scale) << (8 * i);
+    }
+    uint8_t *dst = cmp_row_ptr(pool, row);
+    *reinterpret_cast<u32x2 *>(dst + 8 * lane) = u32x2{w0, w1};
+    reinterpret_cast<uint16_t *>(dst + kDN)[lane] = f32_to_bf16(y[8]);
+    if ((lane & 7) == 0) cmp_scale_ptr(pool, row)[lane >> 3] = ldexpf(1.f, e);
+}
+
 // RMSNorm, RoPE, quantise and store one pooled slot held by one wave.
 __device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, int seq, int slot,
                                             int ratio, const float *gamma, float eps,
@@ -94,43 +136,14 @@ __device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, 
     }
     y[8] = pooled[8] * inv * gamma[kDN + lane];
 
-    // RoPE on the rope channel: pair (512+2i, 513+2i) = lanes (2i, 2i+1)
     int pos = ratio * slot;
     if (pos >= max_pos) return;   // anchor outside the table: slot not written
-    float other = __shfl_xor(y[8], 1, 64);
-    int pi = lane >> 1;
-    float c = cos_sin[static_cast<int64_t>(pos) * kDR + pi];
-    float s = cos_sin[static_cast<int64_t>(pos) * kDR + kDR / 2 + pi];
-    y[8] = (lane & 1) ? (other * s + y[8] * c) : (y[8] * c - other * s);
+    y[8] = rope_lane(y[8], lane, pos, cos_sin);
 
     int64_t row = pool_row(pool, seq, slot);
     if (row < 0) return;
-    if (prequant) {
-        float *pq = prequant + row * kD;
-        *reinterpret_cast<f32x4 *>(pq + 8 * lane) = f32x4{y[0], y[1], y[2], y[3]};
-        *reinterpret_cast<f32x4 *>(pq + 8 * lane + 4) = f32x4{y[4], y[5], y[6], y[7]};
-        pq[kDN + lane] = y[8];
-    }
-
-    // per-64 block pow2 scale: block b = lanes 8b .. 8b+7
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-    int e = pow2_exponent(amax);
-    float inv_scale = ldexpf(1.f, -e);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        w0 |= f32_to_e4m3(y[i] * inv_scale) << (8 * i);
-        w1 |= f32_to_e4m3(y[4 + i] * inv_scale) << (8 * i);
-    }
-    uint8_t *dst = cmp_row_ptr(pool, row);
-    *reinterpret_cast<u32x2 *>(dst + 8 * lane) = u32x2{w0, w1};
-    reinterpret_cast<uint16_t *>(dst + kDN)[lane] = f32_to_bf16(y[8]);
-    if ((lane & 7) == 0) cmp_scale_ptr(pool, row)[lane >> 3] = ldexpf(1.f, e);
+    if (prequant) store_prequant(prequant + row * kD, y, lane);
+    quant_store(y, lane, pool, row);
 }
 
 }  // namespace
@@ -207,6 +220,37 @@ __global__ __launch_bounds__(256) void compress_r128_kernel(CompressArgs a) {
     }
     finish_slot(pooled, lane, seq, slot, 128, a.gamma, a.eps, a.cos_sin, a.max_pos, a.pool,
                 a.prequant);
+}
+
+// SWA KV insert, one token per wave: RoPE at the token's own position, then
+// the cache row format, written at the position's row of its sequence.
+// "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J RoPE, fp8
+// quantisation, paged write) and 5.5 (the SWA cache's fp8 row).
+__global__ __launch_bounds__(256) void swa_insert_kernel(SwaInsertArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
+    const int seq = a.tok_seq[t], pos = a.tok_pos[t];
+    if (pos < 0 || pos >= a.max_pos) return;        // uniform over the wave
+    const uint16_t *kr = a.kv + static_cast<int64_t>(t) * kD;
+    const u32x4 kw = *reinterpret_cast<const u32x4 *>(kr + 8 * lane);
+    float y[9];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        y[2 * i] = __uint_as_float(kw[i] << 16);
+        y[2 * i + 1] = __uint_as_float(kw[i] & 0xffff0000u);
+    }
+    y[8] = rope_lane(bf16_to_f32(kr[kDN + lane]), lane, pos, a.cos_sin);
+    if (a.prequant) store_prequant(a.prequant + static_cast<int64_t>(t) * kD, y, lane);
+    const int64_t row = pool_row(a.pool, seq, pos);
+    if (row < 0) return;
+    quant_store(y, lane, a.pool, row);
+}
+
+hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream) {
+    if (a.n_tok <= 0) return hipSuccess;
+    hipLaunchKernelGGL(swa_insert_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream) {

@@ -20,6 +20,20 @@ struct CompressArgs {
     float *prequant;
 };
 
+// SWA KV insert: token t (sequence tok_seq[t], position tok_pos[t]) of kv
+// [n_tok][576] bf16 -> row tok_pos[t] of its sequence in a pool of the
+// compressed-row layout; prequant (nullable) [n_tok][576] fp32.
+struct SwaInsertArgs {
+    int n_tok;
+    const uint16_t *kv;
+    const int32_t *tok_seq;
+    const int32_t *tok_pos;
+    const float *cos_sin;
+    int max_pos;
+    slc_pool_t pool;
+    float *prequant;
+};
+
 struct IndexArgs {
     int n_q;
     int h_idx;
@@ -53,6 +67,7 @@ struct TopkArgs {
     int warm_heads;
     int warm_window;
     slc_pool_t warm_swa;
+    int warm_swa_fp8;       // warm_swa holds fp8 rows in the compressed-row layout
 };
 
 struct AttnArgs {
@@ -63,6 +78,7 @@ struct AttnArgs {
     const int32_t *q_seq;
     const int32_t *q_pos;
     int window;
+    int swa_fp8;            // swa holds fp8 rows in the compressed-row layout
     slc_pool_t swa;
     slc_pool_t cmp;
     const int32_t *cmp_idx;
@@ -79,6 +95,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream);
+hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);

@@ -393,13 +393,16 @@ __device__ __forceinline__ uint32_t kth_floor(const uint32_t (&v)[G], int k, uin
 // this XCD (block t' = t + 8m shares blockIdx % 8 with the decode's blocks of
 // query t).  Every load is in bounds: rows of absent blocks read the query
 // instead.  blk: scratch LDS for up to 32 block ids.
-template <int THREADS>
+// F8: the SWA pool has the compressed-row layout (640 bytes of codes and rope
+// per row, then 32 bytes of scales in the block's scale area).
+template <int THREADS, bool F8>
 __device__ __forceinline__ void warm_attention_inputs(const TopkArgs &a, int t, int32_t *blk) {
     const int tid = threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    constexpr int kRowUnits = kD * 2 / 16;              // 16-byte units per latent row (72)
+    constexpr int kQUnits = kD * 2 / 16;                // 16-byte units per bf16 latent row (72)
+    constexpr int kRowUnits = F8 ? (SLC_CMP_ROW_BYTES + 32) / 16 : kQUnits;   // per pool row
     const u32x4 *qp = reinterpret_cast<const u32x4 *>(a.warm_q + static_cast<int64_t>(t) * a.warm_heads * kD);
-    const int qunits = a.warm_heads * kRowUnits;
+    const int qunits = a.warm_heads * kQUnits;
     for (int u0 = 0; u0 < qunits; u0 += 4 * THREADS) {
         u32x4 v[4];
 #pragma unroll
@@ -432,10 +435,15 @@ __device__ __forceinline__ void warm_attention_inputs(const TopkArgs &a, int t, 
                 const int uu = u < total ? u : 0;
                 const int r = lo + uu / kRowUnits, j = uu % kRowUnits;
                 const int32_t pb = blk[(r >> 6) - lb0];
-                const u32x4 *row = pb >= 0 ? reinterpret_cast<const u32x4 *>(
-                                                 base + (static_cast<int64_t>(pb) * kBR + (r & (kBR - 1))) * (kD * 2))
-                                           : qp;
-                v[i] = row[j];
+                const uint8_t *src;
+                if (F8)
+                    src = base + static_cast<int64_t>(pb) * SLC_CMP_BLOCK_BYTES +
+                          (j < SLC_CMP_ROW_BYTES / 16
+                               ? (r & (kBR - 1)) * SLC_CMP_ROW_BYTES + 16 * j
+                               : SLC_CMP_SCALE_OFFSET + (r & (kBR - 1)) * 32 + 16 * (j - SLC_CMP_ROW_BYTES / 16));
+                else
+                    src = base + (static_cast<int64_t>(pb) * kBR + (r & (kBR - 1))) * (kD * 2) + 16 * j;
+                v[i] = *(pb >= 0 ? reinterpret_cast<const u32x4 *>(src) : qp);
             }
 #pragma unroll
             for (int i = 0; i < 4; i++) acc ^= v[i];
@@ -471,7 +479,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 
     if (static_cast<int>(blockIdx.x) >= a.n_q) {       // L2 warm-up blocks (and padding)
         const int t = static_cast<int>(blockIdx.x) - ((a.n_q + 7) & ~7);
-        if (t >= 0 && t < a.n_q) warm_attention_inputs<THREADS>(a, t, reinterpret_cast<int32_t *>(hist));
+        if (t >= 0 && t < a.n_q) {
+            if (a.warm_swa_fp8) warm_attention_inputs<THREADS, true>(a, t, reinterpret_cast<int32_t *>(hist));
+            else warm_attention_inputs<THREADS, false>(a, t, reinterpret_cast<int32_t *>(hist));
+        }
         return;
     }
     const int t = blockIdx.x;

@@ -94,7 +94,7 @@ class Layer:
     q_pos: torch.Tensor             # [Q] int32
     swa_base: torch.Tensor          # [n_seq] int32: first position with a SWA row
     swa_count: torch.Tensor         # [n_seq] int32
-    swa_rows: torch.Tensor          # [sum counts, 576] bf16, sequences back to back
+    swa_rows: Optional[torch.Tensor]  # [sum counts, 576] bf16, sequences back to back
     swa_off: torch.Tensor           # [n_seq] int64 row offsets into swa_rows
     swa_pool: torch.Tensor
     swa_table: torch.Tensor
@@ -122,6 +122,11 @@ class Layer:
     eps: float = 1e-6
     cos_sin: Optional[torch.Tensor] = None
     cmp_blocks: int = 0
+    # fp8 SWA pool (compressed-row layout) instead of bf16 rows
+    swa_fp8: bool = False
+    swa_codes: Optional[torch.Tensor] = None   # [sum counts, 512] uint8
+    swa_scales: Optional[torch.Tensor] = None  # [sum counts, 8] f32
+    swa_rope: Optional[torch.Tensor] = None    # [sum counts, 64] bf16
     extra: dict = field(default_factory=dict)
 
     @property
@@ -135,7 +140,7 @@ class Layer:
 
 def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_slots: list,
                 W: int = 128, k: int = 0, H_I: int = 0, given_topk: bool = False,
-                permute: bool = True, compress_inputs: bool = False,
+                permute: bool = True, compress_inputs: bool = False, swa_fp8: bool = False,
                 gamma_random: bool = False, sm_scale: Optional[float] = None,
                 device="cpu") -> Layer:
     """ctx[b]: context length of sequence b; queries: list of (seq, position);
@@ -183,11 +188,27 @@ def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_sl
                   if swa_count[b] > 0 else [] for b in range(n_seq)]
     width = max(1, -(-max(ctx) // BR))
     swa_table, nsb = block_table(swa_blocks, width, seed, "swa_table", dev, permute)
-    swa_pool = P.swa_pool_empty(nsb, dev)
-    for b in range(n_seq):
-        if swa_count[b] > 0:
-            P.swa_pool_put(swa_pool, swa_table[b], swa_base[b],
-                           swa_rows[offs[b]: offs[b] + swa_count[b]])
+    swa_codes = swa_scales = swa_rope = None
+    if swa_fp8:
+        # fp8 SWA rows in the compressed-row layout: random codes, pow2 scales
+        # and bf16 rope dims (swa_rows is then left unset)
+        nrow = swa_rows.shape[0]
+        swa_codes = _fp8_codes((nrow, DN), seed, "swa_codes", dev)
+        swa_scales = _pow2((nrow, DN // 64), seed, "swa_scales", dev)
+        swa_rope = _randn((nrow, DR), seed, "swa_rope", dev, torch.bfloat16)
+        swa_rows = None
+        swa_pool = P.cmp_pool_empty(nsb, dev)
+        for b in range(n_seq):
+            if swa_count[b] > 0:
+                sl = slice(offs[b], offs[b] + swa_count[b])
+                P.cmp_pool_put(swa_pool, swa_table[b], swa_base[b], swa_codes[sl],
+                               swa_scales[sl], swa_rope[sl])
+    else:
+        swa_pool = P.swa_pool_empty(nsb, dev)
+        for b in range(n_seq):
+            if swa_count[b] > 0:
+                P.swa_pool_put(swa_pool, swa_table[b], swa_base[b],
+                               swa_rows[offs[b]: offs[b] + swa_count[b]])
 
     lay = Layer(ratio=ratio, n_seq=n_seq, H=H, W=W, k=k, H_I=H_I,
                 sm_scale=(1.0 / math.sqrt(D)) if sm_scale is None else sm_scale,
@@ -198,7 +219,9 @@ def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_sl
                 swa_pool=swa_pool, swa_table=swa_table,
                 n_slots=torch.tensor(n_slots if ratio > 1 else [0] * n_seq, dtype=torch.int32,
                                      device=dev),
-                cu_seqlens=cu.to(dev), kv=kv, score=score, gamma=gamma, cos_sin=cos_sin)
+                cu_seqlens=cu.to(dev), kv=kv, score=score, gamma=gamma, cos_sin=cos_sin,
+                swa_fp8=swa_fp8, swa_codes=swa_codes, swa_scales=swa_scales,
+                swa_rope=swa_rope)
     if ratio <= 1:
         return lay
 
@@ -272,12 +295,13 @@ def swaonly_decode_b64(seed=1, device="cpu") -> Layer:
                        permute=False, device=device)
 
 
-def c4a_decode_64k(seed=2, device="cpu", batch=32) -> Layer:
+def c4a_decode_64k(seed=2, device="cpu", batch=32, swa_fp8=False) -> Layer:
     """C4A decode, batch 32, H=64, context 65536 -> 16384 slots per sequence,
-    indexer 64 heads x 128, top-k 512 + SWA 128, 64-row blocks, permuted tables."""
+    indexer 64 heads x 128, top-k 512 + SWA 128, 64-row blocks, permuted tables
+    (swa_fp8: the SWA pool holds fp8 rows in the compressed-row layout)."""
     return build_layer(seed, ratio=4, H=64, ctx=[65536] * batch,
                        queries=[(b, 65535) for b in range(batch)], n_slots=[16384] * batch,
-                       W=128, k=512, H_I=64, device=device)
+                       W=128, k=512, H_I=64, swa_fp8=swa_fp8, device=device)
 
 
 def c128a_decode_128k(seed=3, device="cpu", batch=32) -> Layer:

@@ -19,12 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libslc.so")
 
 LAYER_SWAONLY, LAYER_C4A, LAYER_C128A = 1, 4, 128
+SWA_FP8 = 0x100     # OR'ed into a layer type (or the warm select's ratio): fp8 SWA pool
 SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
-    "slc_indexcache_skips",
+    "slc_indexcache_skips", "slc_swa_insert",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -67,6 +68,8 @@ def lib():
         L.slc_topk_select_warm.restype = i32
         L.slc_topk_select_warm.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                            pool, vp]
+        L.slc_swa_insert.restype = i32
+        L.slc_swa_insert.argtypes = [i32, vp, vp, vp, vp, i32, pool, vp, vp]
         L.slc_indexcache_skips.restype = i32
         L.slc_indexcache_skips.argtypes = [i32, vp, i32, C.c_char_p, vp]
         L.slc_index_topk_workspace_size.restype = sz
@@ -140,6 +143,24 @@ def compress(ratio: int, cu_seqlens: torch.Tensor, max_seqlen: int, kv: torch.Te
                               int(max_seqlen), _ptr(kv), _ptr(score), _ptr(gamma), float(eps),
                               _ptr(cos_sin), int(cos_sin.shape[0]), pool(cmp_pool, cmp_table),
                               _ptr(prequant), _stream()))
+
+
+def swa_insert(kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
+               cos_sin: torch.Tensor, swa_pool: torch.Tensor, swa_table: torch.Tensor,
+               prequant: Optional[torch.Tensor] = None) -> None:
+    """RoPE + fp8 row format + paged write of new tokens into an fp8 SWA pool
+    (CMP layout); attend to it with layer_type | SWA_FP8."""
+    dev = kv.device
+    _need(kv, "kv", torch.bfloat16, dev)
+    _need(tok_seq, "tok_seq", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(cos_sin, "cos_sin", torch.float32, dev)
+    _need(swa_pool, "swa_pool", torch.uint8, dev)
+    if prequant is not None:
+        _need(prequant, "prequant", torch.float32, dev)
+    _check(lib().slc_swa_insert(int(kv.shape[0]), _ptr(kv), _ptr(tok_seq), _ptr(tok_pos),
+                                _ptr(cos_sin), int(cos_sin.shape[0]), pool(swa_pool, swa_table),
+                                _ptr(prequant), _stream()))
 
 
 # ------------------------------------------------------------------ indexer

@@ -78,10 +78,19 @@ def oracle_index_topk(O, lay, queries=None, want_scores=True):
     return res
 
 
+def oracle_swa_rows(O, lay):
+    """The layer's SWA rows as bf16 bits (an fp8 SWA pool: the rows its codes,
+    scales and rope stand for)."""
+    if getattr(lay, "swa_fp8", False):
+        return O.swa_dequant(np_u8(lay.swa_codes), np_f32(lay.swa_scales), bits16(lay.swa_rope))
+    return bits16(lay.swa_rows)
+
+
 def oracle_attention(O, lay, idx, cmp=None, queries=None, want_f64=False):
     """idx: [Q,k] int32 compressed list (None for swaonly).  cmp: dict of logical
     codes/scales/rope (defaults to the layer's given pool contents)."""
     qs = np.arange(lay.n_q) if queries is None else np.asarray(queries)
+    swa_rows = oracle_swa_rows(O, lay)
     if lay.ratio > 1 and idx is not None:
         if cmp is None:
             cmp = dict(codes=np_u8(lay.cmp_codes), scales=np_f32(lay.cmp_scales),
@@ -89,12 +98,12 @@ def oracle_attention(O, lay, idx, cmp=None, queries=None, want_f64=False):
         return O.sparse_mla_batch(
             bits16(lay.q)[qs], np_i32(lay.q_pos)[qs], np_i32(lay.q_seq)[qs], lay.W,
             lay.swa_off.numpy(), np_i32(lay.swa_base), np_i32(lay.swa_count),
-            bits16(lay.swa_rows), lay.sm_scale, lay.cmp_off.numpy(), np_i32(lay.n_slots),
+            swa_rows, lay.sm_scale, lay.cmp_off.numpy(), np_i32(lay.n_slots),
             cmp["codes"], cmp["scales"], cmp["rope"], np.ascontiguousarray(idx, np.int32),
             want_f64=want_f64)
     return O.sparse_mla_batch(
         bits16(lay.q)[qs], np_i32(lay.q_pos)[qs], np_i32(lay.q_seq)[qs], lay.W,
-        lay.swa_off.numpy(), np_i32(lay.swa_base), np_i32(lay.swa_count), bits16(lay.swa_rows),
+        lay.swa_off.numpy(), np_i32(lay.swa_base), np_i32(lay.swa_count), swa_rows,
         lay.sm_scale, want_f64=want_f64)
 
 
@@ -124,11 +133,12 @@ def gpu_attention(S, lay, idx, decode=True, cmp_pool=None):
     out = torch.empty((lay.n_q, lay.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((lay.n_q, lay.H), dtype=torch.float32, device=dev)
     f = S.sparse_mla_decode if decode else S.sparse_mla_prefill
+    fl = S.SWA_FP8 if getattr(lay, "swa_fp8", False) else 0
     if lay.ratio == 1:
-        f(1, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool, lay.swa_table,
+        f(1 | fl, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool, lay.swa_table,
           sm_scale=lay.sm_scale, out=out, lse=lse)
     else:
-        f(lay.ratio, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool, lay.swa_table,
+        f(lay.ratio | fl, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool, lay.swa_table,
           lay.cmp_pool if cmp_pool is None else cmp_pool, lay.cmp_table, idx, lay.n_slots,
           sm_scale=lay.sm_scale, out=out, lse=lse)
     return out, lse

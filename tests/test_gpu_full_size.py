@@ -58,11 +58,13 @@ def test_swaonly_decode_b64_full(S, oracle):
     print(f"swaonly_decode_b64: max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
 
-def test_c4a_decode_64k_full(S, oracle):
+@pytest.mark.parametrize("swa_fp8", [False, True], ids=["bf16_swa", "fp8_swa"])
+def test_c4a_decode_64k_full(S, oracle, swa_fp8):
     """The whole decode step at B=32, every query checked: scores, top-k sets,
     the selection rule on the GPU's own scores, then attention over the GPU's
-    own selection against the oracle's attention over the oracle's selection."""
-    lay = I.c4a_decode_64k()
+    own selection against the oracle's attention over the oracle's selection.
+    fp8_swa: the same step over an fp8 SWA pool (compressed-row layout)."""
+    lay = I.c4a_decode_64k(swa_fp8=swa_fp8)
     t0 = time.perf_counter()
     idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay)
     out_ref, lse_ref = oracle_attention(oracle, lay, idx_ref)
@@ -73,7 +75,8 @@ def test_c4a_decode_64k_full(S, oracle):
     # the same lists, bit for bit
     idx_w = torch.full_like(idx, -7)
     ln_w = torch.full_like(ln, -7)
-    S.topk_select_warm(lay.k, sc, lay.max_slots, lay.q_seq, lay.q_pos, 4, lay.n_slots, idx_w, ln_w,
+    S.topk_select_warm(lay.k, sc, lay.max_slots, lay.q_seq, lay.q_pos,
+                       4 | (S.SWA_FP8 if swa_fp8 else 0), lay.n_slots, idx_w, ln_w,
                        lay.q, lay.W, lay.swa_pool, lay.swa_table)
     out, lse = gpu_attention(S, lay, idx)
     torch.cuda.synchronize()
@@ -92,7 +95,8 @@ def test_c4a_decode_64k_full(S, oracle):
     keep = np.nonzero(same)[0]
     kt = torch.as_tensor(keep, device=out.device)
     e = check_attention(out[kt], lse[kt], out_ref[keep], lse_ref[keep])
-    print(f"c4a_decode_64k: near-tie slots {near}; {len(keep)}/{lay.n_q} queries compared; "
+    print(f"c4a_decode_64k (fp8 SWA {swa_fp8}): near-tie slots {near}; "
+          f"{len(keep)}/{lay.n_q} queries compared; "
           f"max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
 
