@@ -177,14 +177,17 @@ def cpu_baseline(n_q: int):
     from helpers import oracle_attention, oracle_index_topk
     from sparse_long_context_compressor_amd import inputs as I
     lay = I.c4a_decode_64k(seed=2, device="cpu", batch=n_q)
-    t0 = time.perf_counter()
-    idx, _ = oracle_index_topk(O, lay, want_scores=False)
-    oracle_attention(O, lay, idx)
+    passes, t0 = 0, time.perf_counter()
+    while passes == 0 or time.perf_counter() - t0 < 10.0:     # about 10 s of CPU work
+        idx, _ = oracle_index_topk(O, lay, want_scores=False)
+        oracle_attention(O, lay, idx)
+        passes += 1
     dt = time.perf_counter() - t0
-    return {"value": n_q / dt, "unit": "queries/s", "cores": int(O.num_threads()),
+    return {"value": passes * n_q / dt, "unit": "queries/s", "cores": int(O.num_threads()),
             "kind": "oracle",
-            "sample": f"{n_q} of the 32 sequences (one query each, same shapes: 16384 slots, H_I=64, "
-                      f"k=512, H=64, SWA 128), index top-k + attention, {dt:.2f} s wall"}
+            "sample": f"{passes} passes over {n_q} of the 32 sequences (one query each, same "
+                      f"shapes: 16384 slots, H_I=64, k=512, H=64, SWA 128), index top-k + "
+                      f"attention, {dt:.2f} s wall"}
 
 
 def log(msg: str):
