@@ -16,7 +16,8 @@ __all__ = [
     "build", "lib", "e4m3_decode", "e4m3_encode", "bf16_decode", "bf16_encode",
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
-    "swa_insert", "swa_dequant", "indexcache_skips", "num_threads",
+    "swa_insert", "swa_dequant", "e2m1_value", "e8m0_value", "index_scores_mxfp4",
+    "index_topk_batch_mxfp4", "indexcache_skips", "num_threads",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,11 @@ def _declare(L):
         "oracle_sparse_mla_batch": (i32, [i32, i32, _P, _P, _P, i32, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, i32, _P, dbl, _P, _P, _P, _P]),
         "oracle_swa_insert": (i32, [i32, _P, _P, _P, i32, _P, _P, _P, _P]),
+        "oracle_e2m1_value": (dbl, [C.c_uint8]),
+        "oracle_e8m0_value": (dbl, [C.c_uint8]),
+        "oracle_index_scores_mxfp4": (None, [i32, i32, _P, _P, _P, _P, _P, _P, _P]),
+        "oracle_index_topk_batch_mxfp4": (None, [i32, i32, i32, _P, _P, _P, _P, _P, i32, _P,
+                                                 _P, _P, _P, _P, _P, _P, i32]),
         "oracle_num_threads": (i32, []),
         "oracle_e4m3_decode_array": (None, [i64, _P, _P]),
         "oracle_e4m3_encode_array": (None, [i64, _P, _P]),
@@ -230,6 +236,49 @@ def index_topk_batch(k, q_codes, q_scale, w, q_pos, q_seq, r, key_off, n_slots_,
     sc = np.full((nq, ms), np.nan, np.float32) if want_scores else None
     lib().oracle_index_topk_batch(nq, hI, k, _p(q), _p(qs), _p(ww), _p(qp), _p(qsq), r, _p(ko),
                                   _p(ns), _p(kc), _p(ksc), _p(idx), _p(ln), _p(sc), ms)
+    return (idx, ln, sc) if want_scores else (idx, ln)
+
+
+def e2m1_value(nibble: int) -> float:
+    return lib().oracle_e2m1_value(int(nibble))
+
+
+def e8m0_value(b: int) -> float:
+    return lib().oracle_e8m0_value(int(b))
+
+
+def index_scores_mxfp4(q_codes, q_scale, w, keys4, key_e8m0):
+    """One query against MXFP4 keys: keys4 [n,64] u8 (two e2m1 per byte, even
+    element low), key_e8m0 [n,4] u8.  Returns (fp32 scores [n], float64 [n])."""
+    q = _c(q_codes, np.uint8)
+    qs = _c(q_scale, np.float32)
+    ww = _c(w, np.float32)
+    k = _c(keys4, np.uint8)
+    ke = _c(key_e8m0, np.uint8)
+    n = k.shape[0]
+    s32 = np.zeros(n, np.float32)
+    s64 = np.zeros(n, np.float64)
+    lib().oracle_index_scores_mxfp4(q.shape[0], n, _p(q), _p(qs), _p(ww), _p(k), _p(ke), _p(s32),
+                                    _p(s64))
+    return s32, s64
+
+
+def index_topk_batch_mxfp4(k, q_codes, q_scale, w, q_pos, q_seq, r, key_off, n_slots_,
+                           keys4, key_e8m0, max_slots=None, want_scores=False):
+    q = _c(q_codes, np.uint8)
+    nq, hI = q.shape[0], q.shape[1]
+    ns = _c(n_slots_, np.int32)
+    idx = np.zeros((nq, k), np.int32)
+    ln = np.zeros(nq, np.int32)
+    ms = int(max_slots if max_slots is not None else (ns.max() if ns.size else 0))
+    sc = np.full((nq, ms), np.nan, np.float32) if want_scores else None
+    args = [_c(q_scale, np.float32), _c(w, np.float32), _c(q_pos, np.int32),
+            _c(q_seq, np.int32)]
+    ko = _c(key_off, np.int64)
+    k4 = _c(keys4, np.uint8)
+    ke = _c(key_e8m0, np.uint8)
+    lib().oracle_index_topk_batch_mxfp4(nq, hI, k, _p(q), *map(_p, args), r, _p(ko), _p(ns),
+                                        _p(k4), _p(ke), _p(idx), _p(ln), _p(sc), ms)
     return (idx, ln, sc) if want_scores else (idx, ln)
 
 

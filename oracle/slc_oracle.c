@@ -388,6 +388,69 @@ void oracle_index_scores(int h_idx, int n, const uint8_t *q, const float *q_scal
     free(acc);
 }
 
+/* ------------------------------------------------------- MXFP4 index keys */
+
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no inf or NaN;
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 [P5 6.1: FP4 / MXFP4 indexer K
+ * cache]. */
+double oracle_e2m1_value(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -mag : mag;
+}
+
+/* OCP E8M0 block scale: 2^(byte - 127); 255 is NaN. */
+double oracle_e8m0_value(uint8_t b)
+{
+    return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+/*
+ * Index scores against MXFP4 keys ["DeepseekV4Attention", Indexer: the FP4
+ * indexer cache takes half the FP8 cache's bytes; "From MLA to CSA + HCA"
+ * 6.1: FP4 / MXFP4 indexer keys; "DeepSeek-V4 attention layer types": the
+ * FP4 indexer cache option]: key s holds 128 e2m1 values, two per byte (the
+ * even element in the low nibble), keys4 [n, 64], and one E8M0 scale per 32
+ * dims, key_e8m0 [n, 4].  Element d of the key is e2m1 * 2^(e - 127) of its
+ * block, so the block scales sit inside the dot product:
+ *   I[s] = sum_j w[j] * max(0, q_scale[j] * sum_d q[j][d] * k[s][d]).
+ * Evaluated in double (the query side as in oracle_index_scores).
+ */
+void oracle_index_scores_mxfp4(int h_idx, int n, const uint8_t *q, const float *q_scale,
+                               const float *w, const uint8_t *keys4,
+                               const uint8_t *key_e8m0, float *out32, double *out64)
+{
+    double qv[OR_DI], kv[OR_DI];
+    double *acc = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    for (int s = 0; s < n; s++) {
+        for (int d = 0; d < OR_DI; d++) {
+            uint8_t byte = keys4[(size_t)s * (OR_DI / 2) + d / 2];
+            uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+            kv[d] = oracle_e2m1_value(nib) *
+                    oracle_e8m0_value(key_e8m0[(size_t)s * (OR_DI / 32) + d / 32]);
+        }
+        for (int j = 0; j < h_idx; j++) {
+            double dot = 0.0, v;
+            for (int d = 0; d < OR_DI; d++) {
+                qv[d] = oracle_e4m3_value(q[(size_t)j * OR_DI + d]);
+                dot += qv[d] * kv[d];
+            }
+            v = (double)q_scale[j] * dot;
+            if (v < 0.0)
+                v = 0.0;
+            acc[s] += (double)w[j] * v;
+        }
+    }
+    for (int s = 0; s < n; s++) {
+        if (out64)
+            out64[s] = acc[s];
+        if (out32)
+            out32[s] = (float)acc[s];
+    }
+    free(acc);
+}
+
 struct or_pair { float v; int32_t i; };
 
 static int cmp_score_desc_index_asc(const void *pa, const void *pb)
@@ -443,6 +506,31 @@ void oracle_index_topk_batch(int n_q, int h_idx, int k, const uint8_t *q,
                             q_scale + (size_t)t * h_idx, w + (size_t)t * h_idx,
                             keys + (size_t)key_off[b] * OR_DI,
                             key_scale + key_off[b], sc, NULL);
+        len[t] = oracle_topk(nv, sc, k, idx + (size_t)t * k);
+        if (scores32)
+            memcpy(scores32 + (size_t)t * max_slots, sc, sizeof(float) * (size_t)nv);
+        free(sc);
+    }
+}
+
+/* The batch form of index top-k over MXFP4 keys: as oracle_index_topk_batch,
+ * keys4 [.., 64] and key_e8m0 [.., 4] indexed from key_off[b]. */
+void oracle_index_topk_batch_mxfp4(int n_q, int h_idx, int k, const uint8_t *q,
+                                   const float *q_scale, const float *w,
+                                   const int32_t *q_pos, const int32_t *q_seq, int r,
+                                   const int64_t *key_off, const int32_t *n_slots,
+                                   const uint8_t *keys4, const uint8_t *key_e8m0,
+                                   int32_t *idx, int32_t *len, float *scores32, int max_slots)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < n_q; t++) {
+        int b = q_seq[t];
+        int nv = oracle_n_visible(q_pos[t], r, n_slots[b]);
+        float *sc = (float *)malloc(sizeof(float) * (size_t)(nv > 0 ? nv : 1));
+        oracle_index_scores_mxfp4(h_idx, nv, q + (size_t)t * h_idx * OR_DI,
+                                  q_scale + (size_t)t * h_idx, w + (size_t)t * h_idx,
+                                  keys4 + (size_t)key_off[b] * (OR_DI / 2),
+                                  key_e8m0 + (size_t)key_off[b] * (OR_DI / 32), sc, NULL);
         len[t] = oracle_topk(nv, sc, k, idx + (size_t)t * k);
         if (scores32)
             memcpy(scores32 + (size_t)t * max_slots, sc, sizeof(float) * (size_t)nv);

@@ -630,3 +630,93 @@ def test_swa_insert_rotates_at_the_tokens_own_position(oracle):
         assert np.allclose(n1, n0, rtol=1e-6, atol=1e-30)
     with pytest.raises(ValueError):
         oracle.swa_insert(kv[:1], np.array([40], np.int32), cs)
+
+
+# ---------------------------------------------------------- MXFP4 index keys
+# OCP Microscaling (MX) formats v1.0: FP4 E2M1 magnitudes by code 0..7, and
+# the E8M0 scale 2^(byte - 127)
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _unpack_e2m1(keys4):
+    """[n,64] packed bytes -> [n,128] values; element 2i in the low nibble."""
+    lo, hi = keys4 & 15, keys4 >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(keys4.shape[0], -1)
+    mag = np.array(E2M1_MAGNITUDES)[nib & 7]
+    return np.where(nib >= 8, -mag, mag)
+
+
+def test_e2m1_and_e8m0_values(oracle):
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        assert v == (-1 if c >= 8 else 1) * E2M1_MAGNITUDES[c & 7]
+        assert math.copysign(1.0, v) == (-1.0 if c >= 8 else 1.0)
+    for b in range(255):
+        assert oracle.e8m0_value(b) == math.ldexp(1.0, b - 127)
+    assert math.isnan(oracle.e8m0_value(255))
+
+
+def _mx_case(g, n, hI, equal_blocks):
+    keys4 = g.integers(0, 256, (n, 64), dtype=np.uint8)
+    e = g.integers(118, 131, (n, 1 if equal_blocks else 4)).astype(np.uint8)
+    e8 = np.repeat(e, 4, axis=1) if equal_blocks else e
+    q = g.integers(0, 256, (hI, 128), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x10                     # no NaN codes
+    qs = np.ldexp(1.0, g.integers(-6, 1, hI)).astype(np.float32)
+    w = g.uniform(0, 1, hI).astype(np.float32)
+    return keys4, e8, q, qs, w
+
+
+def test_mxfp4_scores_equal_fp8_scores_for_one_scale_per_key(oracle):
+    """With one scale for all four blocks, an MXFP4 key is an fp8 key (e2m1
+    values are e4m3 values; torch's cast gives the codes) with that scale, so
+    the two index paths must agree exactly."""
+    g = np.random.default_rng(41)
+    keys4, e8, q, qs, w = _mx_case(g, 300, 16, True)
+    vals = _unpack_e2m1(keys4)
+    codes = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8_values(codes), vals)
+    kscale = np.ldexp(1.0, e8[:, 0].astype(np.int64) - 127).astype(np.float32)
+    s8 = oracle.index_scores(q, qs, w, codes, kscale)[1]
+    s4 = oracle.index_scores_mxfp4(q, qs, w, keys4, e8)[1]
+    assert np.array_equal(s4, s8)
+    assert np.count_nonzero(s4) > 200
+
+
+def test_mxfp4_scores_by_brute_force(oracle):
+    """Four different block scales per key: the scores equal the pages'
+    formula evaluated with numpy on independently decoded values."""
+    g = np.random.default_rng(42)
+    keys4, e8, q, qs, w = _mx_case(g, 257, 32, False)
+    kv = _unpack_e2m1(keys4) * np.repeat(np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=1)
+    qv = fp8_values(q)
+    ref = (np.maximum(0.0, (qv @ kv.T) * qs[:, None].astype(np.float64)) * w[:, None]).sum(0)
+    s32, s64 = oracle.index_scores_mxfp4(q, qs, w, keys4, e8)
+    assert np.allclose(s64, ref, rtol=1e-12, atol=0)
+    assert np.array_equal(s32, s64.astype(np.float32))
+    # a nibble-order slip (element 2i taken from the high nibble) changes them
+    swapped = ((keys4 & 15) << 4) | (keys4 >> 4)
+    assert not np.allclose(oracle.index_scores_mxfp4(q, qs, w, swapped, e8)[1], ref)
+
+
+def test_mxfp4_batch_respects_visibility(oracle):
+    g = np.random.default_rng(43)
+    n = [500, 90]
+    keys4, e8, _, _, _ = _mx_case(g, sum(n), 16, False)
+    q = g.integers(0, 0x7E, (3, 16, 128), dtype=np.uint8)
+    qs = np.full((3, 16), 0.125, np.float32)
+    w = g.uniform(0, 1, (3, 16)).astype(np.float32)
+    q_pos = np.array([1999, 359, 37], np.int32)
+    q_seq = np.array([0, 1, 0], np.int32)
+    off = np.array([0, n[0]], np.int64)
+    idx, ln, sc = oracle.index_topk_batch_mxfp4(32, q, qs, w, q_pos, q_seq, 4, off,
+                                                np.array(n, np.int32), keys4, e8,
+                                                max_slots=500, want_scores=True)
+    for t in range(3):
+        b = q_seq[t]
+        nv = min(n[b], (q_pos[t] + 1) // 4)
+        ref = oracle.index_scores_mxfp4(q[t], qs[t], w[t], keys4[off[b]:off[b] + nv],
+                                        e8[off[b]:off[b] + nv])[0]
+        assert np.array_equal(sc[t, :nv], ref) and np.all(np.isnan(sc[t, nv:]))
+        want, wl = oracle.topk(ref, 32)
+        assert ln[t] == wl == min(32, nv) and np.array_equal(idx[t], want)
