@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--workload", default="c4a_decode_64k",
                     choices=["c4a_decode_64k", "c4a_prefill_2k", "c128a_decode_128k",
                              "swaonly_decode_b64", "c4a_single_layer_4k",
-                             "c4a_decode_64k_stages", "c4a_decode_64k_fp8swa"],
+                             "c4a_decode_64k_stages", "c4a_decode_64k_fp8swa",
+                             "c4a_decode_64k_fp4keys", "c4a_decode_64k_fp8swa_fp4keys"],
                     help="c4a_decode_64k is the headline; the others print supplementary "
                          "per-stage timings of the same kernels on the other workloads")
     ap.add_argument("--report-stats", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
@@ -208,14 +209,16 @@ def other_workload(args):
     slc.lib()
     name = args.workload
     n_rep = 2 if name == "c4a_prefill_2k" else args.replicas
-    fp8 = name == "c4a_decode_64k_fp8swa"
+    fp8, fp4 = "fp8swa" in name, "fp4keys" in name
     if name.startswith("c4a_decode_64k_"):
-        # the headline workload with per-stage timings (stages), or with its
-        # SWA pool in fp8 rows (fp8swa)
-        reps = [I.c4a_decode_64k(seed=200 + r, device=dev, swa_fp8=fp8) for r in range(n_rep)]
+        # the headline workload with per-stage timings (stages), with its SWA
+        # pool in fp8 rows (fp8swa), with MXFP4 index keys (fp4keys)
+        reps = [I.c4a_decode_64k(seed=200 + r, device=dev, swa_fp8=fp8, key_fp4=fp4)
+                for r in range(n_rep)]
     else:
         reps = [I.CONFIGS[name](seed=200 + r, device=dev) for r in range(n_rep)]
     fl = slc.SWA_FP8 if fp8 else 0
+    kf = slc.KEY_MXFP4 if fp4 else 0
     torch.cuda.synchronize()
     log(f"{n_rep} input replicas of {name} resident")
     lay0 = reps[0]
@@ -234,8 +237,8 @@ def other_workload(args):
         ln = torch.empty(Q, dtype=torch.int32, device=dev)
 
         def index_scores(lay):
-            slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
-                             lay.key_table, lay.n_slots, ms_, sc)
+            slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4 | kf,
+                             lay.key_pool, lay.key_table, lay.n_slots, ms_, sc)
 
         def topk(lay):
             if decode:      # with the decode's L2 warm-up, as the headline step runs it
@@ -291,6 +294,14 @@ def other_workload(args):
     n_cmp = Kk if r > 1 else 0
     att_us = per["sparse_mla_decode" if decode else "sparse_mla_prefill"]
     if "index_scores" in per and decode:
+        # algorithmic bytes of the index stage: every visible key (132 B fp8,
+        # 68 B MXFP4) plus the query's heads, weights and scales
+        key_b = 68 if fp4 else 132
+        nv_tot = float(sum(min(int(lay0.n_slots[int(s)]), (int(p) + 1) // 4)
+                           for s, p in zip(lay0.q_seq.tolist(), lay0.q_pos.tolist())))
+        ib = nv_tot * key_b + Q * HIi * (128 + 8)
+        rec["index_GBps"] = ib / (per["index_scores"] * 1e-6) / 1e9
+        rec["index_hbm_frac"] = rec["index_GBps"] / HBM_PEAK_GBPS
         # IndexCache freq 2: every other ratio-4 layer reuses the previous
         # layer's list and runs the attention alone
         rec["indexcache_freq2_us_per_layer"] = (ms_step * 1e3 + att_us) / 2

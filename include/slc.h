@@ -83,6 +83,8 @@ extern "C" {
 #define SLC_CMP_BLOCK_BYTES 43008
 #define SLC_KEY_SCALE_OFFSET 8192
 #define SLC_KEY_BLOCK_BYTES 8448
+#define SLC_KEY4_SCALE_OFFSET 4096  /* MXFP4 key block: 64 x 64 B e2m1 pairs, */
+#define SLC_KEY4_BLOCK_BYTES 4352   /* then 64 x 4 E8M0 scale bytes           */
 
 #define SLC_MAX_HEADS 128       /* query heads: a multiple of 16, <= 128 */
 #define SLC_MAX_INDEX_HEADS 64  /* indexer heads: a multiple of 16, <= 64 */
@@ -112,6 +114,18 @@ typedef enum {
  * bf16 rows ("From MLA to CSA + HCA" 5.5: the V4 SWA cache stores fp8 nope
  * dims, bf16 rope dims and one scale per 64 dims). */
 #define SLC_SWA_FP8 0x100
+
+/* Flag OR'ed into the ratio of slc_index_scores / slc_index_topk: the key
+ * pool holds MXFP4 keys (the KEY4 layout: per key 128 e2m1 values, two per
+ * byte with the even element in the low nibble, and one E8M0 scale byte per
+ * 32 dims, 68 bytes in all) instead of fp8 keys with one fp32 scale.  "From
+ * MLA to CSA + HCA" 6.1 (FP4 / MXFP4 indexer K cache); "DeepseekV4Attention"
+ * (devpress), Indexer (the FP4 indexer cache).  The scores are then
+ *   I[t][s] = sum_j w[t][j] * ReLU(q_scale[t][j] * sum_d q[t][j][d] * k[s][d]),
+ *   k[s][d] = e2m1 * 2^(e - 127) with e the scale byte of d's 32-dim block,
+ * exact in the bf16 operands for scale bytes 2..254 (0 reads as a zero
+ * block; 255, NaN in E8M0, is not a valid key). */
+#define SLC_KEY_MXFP4 0x200
 
 typedef struct slc_pool {
     void *base;                  /* device: n_blocks blocks                         */
@@ -207,8 +221,9 @@ slc_status_t slc_swa_insert(int n_tok, const uint16_t *kv, const int32_t *tok_se
  *   q_fp8        device e4m3 [n_q][h_idx][128], 16-byte aligned
  *   q_scale, w   device fp32 [n_q][h_idx], 16-byte aligned
  *   q_seq, q_pos device int32 [n_q] (sequence and position of each query)
- *   ratio        4 (the indexer exists for c4a layers)
- *   key_pool     KEY layout, one table row per sequence
+ *   ratio        4 (the indexer exists for c4a layers), OR'ed with
+ *                SLC_KEY_MXFP4 for MXFP4 keys in the KEY4 layout
+ *   key_pool     KEY layout (KEY4 with SLC_KEY_MXFP4), one table row per sequence
  *   n_slots      device int32 [n_seq] compressed slots per sequence
  *   max_slots    host bound on every n_vis (row stride of scores)
  *   scores       device fp32 [n_q][max_slots]; entries s < n_vis(t) written
@@ -257,7 +272,8 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
 size_t slc_index_topk_workspace_size(int n_q, int max_slots);
 
 /* slc_index_scores followed by slc_topk_select, scores kept in `workspace`
- * (device, >= slc_index_topk_workspace_size bytes, 256-byte aligned). */
+ * (device, >= slc_index_topk_workspace_size bytes, 256-byte aligned); ratio
+ * may carry SLC_KEY_MXFP4 as for slc_index_scores. */
 slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
                             const float *q_scale, const float *w, const int32_t *q_seq,
                             const int32_t *q_pos, int ratio, slc_pool_t key_pool,

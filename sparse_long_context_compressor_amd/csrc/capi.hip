@@ -92,6 +92,8 @@ slc_status_t slc_index_scores(int n_q, int h_idx, const uint8_t *q_fp8, const fl
                               const float *w, const int32_t *q_seq, const int32_t *q_pos,
                               int ratio, slc_pool_t key_pool, const int32_t *n_slots,
                               int max_slots, float *scores, void *stream) {
+    const bool key_fp4 = (ratio & SLC_KEY_MXFP4) != 0;
+    ratio &= ~SLC_KEY_MXFP4;
     slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
     if (st != SLC_OK) return st;
     if (!heads_ok(h_idx, SLC_MAX_INDEX_HEADS))
@@ -104,7 +106,7 @@ slc_status_t slc_index_scores(int n_q, int h_idx, const uint8_t *q_fp8, const fl
     st = check_pool(key_pool, "index_scores: key_pool");
     if (st != SLC_OK) return st;
     IndexArgs a{n_q, h_idx, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, n_slots, max_slots,
-                scores};
+                scores, key_fp4 ? 1 : 0};
     return hip_status(launch_index_scores(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -210,7 +212,8 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
                             const int32_t *q_pos, int ratio, slc_pool_t key_pool,
                             const int32_t *n_slots, int max_slots, int32_t *topk_idx,
                             int32_t *topk_len, void *workspace, size_t ws_bytes, void *stream) {
-    slc_status_t st = check_index_common(n_q, q_seq, q_pos, ratio, n_slots, max_slots);
+    const int r = ratio & ~SLC_KEY_MXFP4;        // the key format flag goes to the scores only
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, r, n_slots, max_slots);
     if (st != SLC_OK) return st;
     if (k < 1 || k > SLC_MAX_TOPK) return fail("index_topk: k must be in [1, SLC_MAX_TOPK]");
     if (!heads_ok(h_idx, SLC_MAX_INDEX_HEADS))
@@ -226,7 +229,7 @@ slc_status_t slc_index_topk(int n_q, int h_idx, int k, const uint8_t *q_fp8,
     st = slc_index_scores(n_q, h_idx, q_fp8, q_scale, w, q_seq, q_pos, ratio, key_pool, n_slots,
                           max_slots, scores, stream);
     if (st != SLC_OK) return st;
-    return slc_topk_select(n_q, k, scores, max_slots, q_seq, q_pos, ratio, n_slots, topk_idx,
+    return slc_topk_select(n_q, k, scores, max_slots, q_seq, q_pos, r, n_slots, topk_idx,
                            topk_len, stream);
 }
 

@@ -2,7 +2,9 @@
 //
 // Method: "DeepseekV4Attention" (devpress, AMD), Indexer section:
 //   I[t][s] = sum_j w[t][j] * ReLU(q[t][j] . k[s]),  H_I heads sharing one
-//   key per slot, fp8 keys of 128 dims with one fp32 scale per key.
+//   key per slot, fp8 keys of 128 dims with one fp32 scale per key, or MXFP4
+//   keys ("From MLA to CSA + HCA" 6.1): e2m1 values with one E8M0 scale per
+//   32 dims, converted exactly to bf16 with their scale.
 //
 // Scores: the contraction [H_I x 128] . [128 x slots] runs on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16).  e4m3 codes convert to bf16 exactly, and the
@@ -34,6 +36,26 @@ __device__ __forceinline__ void e4m3x16_to_operands(u32x4 w, bf16x8 &s0, bf16x8 
     s1 = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
+// 16 bytes of e2m1 pairs (the lane's 32 key dims, even element in the low
+// nibble) times the block's E8M0 scale -> four bf16x8 MFMA operands, exactly
+// (packed hardware conversion).
+__device__ __forceinline__ void e2m1x32_to_operands(u32x4 w, float scale, bf16x8 (&kb)[4]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0);
+        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1);
+        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2);
+        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3);
+        kb[i] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+}
+
+// E8M0 byte -> the fp32 power of two it encodes (byte 0 -> 0: a zero block).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+    return __uint_as_float(e << 23);
+}
+
 constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
 constexpr int kBlockSlots = 64;                     // slots per key block (one table entry)
 constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
@@ -46,8 +68,8 @@ __device__ __forceinline__ float relu(float x) {
 }
 
 struct KeyStage {
-    u32x4 lo, hi;
-    float scale;
+    u32x4 lo, hi;           // fp8: the lane's two 16-byte pieces; MXFP4: lo only
+    float scale;            // fp8: the key's scale; MXFP4: the lane's block scale word
 };
 
 // Base of the zero-size buffer resource an absent block reads through.
@@ -68,8 +90,10 @@ __device__ __attribute__((aligned(256))) uint8_t kIndexZeroPage[256];   // never
 // table lookup serves each wave's sub-tile.  Lane (g = lane/16, c = lane%16)
 // owns index-dim bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its head
 // and of its key; the MFMA k-order is the same permutation for both
-// operands, so the dot product is unchanged.
-template <int HT, int WB>
+// operands, so the dot product is unchanged.  F4 (MXFP4 keys): lane (g, c)
+// owns dims [32g, 32g+32) instead, one 16-byte load and exactly one E8M0
+// block scale, which the conversion applies.
+template <int HT, int WB, bool F4>
 __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
     constexpr int kThreads = 256 * WB, kTile = kSubTiles * kBlockSlots * WB;
     const int t = blockIdx.x;
@@ -110,27 +134,35 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
     bf16x8 qa[HT][4];                            // filled after the first key loads are issued
     float hf[HT][4];
 
-    const uint32_t lane_off = static_cast<uint32_t>((16 * wq + c) * kDI + 16 * g);
-    const uint32_t scale_off = static_cast<uint32_t>(SLC_KEY_SCALE_OFFSET + 4 * (16 * wq + c));
+    constexpr uint32_t kKeyBytes = F4 ? kDI / 2 : kDI;
+    constexpr uint32_t kBlkBytes = F4 ? SLC_KEY4_BLOCK_BYTES : SLC_KEY_BLOCK_BYTES;
+    constexpr uint32_t kScaleOff = F4 ? SLC_KEY4_SCALE_OFFSET : SLC_KEY_SCALE_OFFSET;
+    const uint32_t lane_off = static_cast<uint32_t>((16 * wq + c) * kKeyBytes + 16 * g);
+    const uint32_t scale_off = static_cast<uint32_t>(kScaleOff + 4 * (16 * wq + c));
 
     // sub-tile j reads through a buffer resource on its (wave-uniform) block;
     // an absent block gets a zero-size resource, whose loads return zeros
     auto stage = [&](int j, KeyStage &st) {
         const int32_t pb = __builtin_amdgcn_readlane(my_pb, WB * j + wb);
         const bool ok = pb >= 0 && pb < n_blocks;
-        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * SLC_KEY_BLOCK_BYTES : zpage;
+        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * kBlkBytes : zpage;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(bp), 0, ok ? SLC_KEY_BLOCK_BYTES : 0, kBufferWord3);
+            const_cast<uint8_t *>(bp), 0, ok ? kBlkBytes : 0, kBufferWord3);
         st.lo = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0);
-        st.hi = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 64u, 0, 0);
+        if constexpr (!F4) st.hi = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 64u, 0, 0);
         const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, scale_off, 0, 0));
         st.scale = ok ? sc : -INFINITY;
     };
     auto compute = [&](int j, const KeyStage &cur) {
         const int s = s0 + kBlockSlots * (WB * j + wb) + 16 * wq + c;
         bf16x8 kb[4];
-        e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
-        e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
+        if constexpr (F4) {
+            const uint32_t word = __builtin_bit_cast(uint32_t, cur.scale);
+            e2m1x32_to_operands(cur.lo, e8m0_scale((word >> (8 * g)) & 0xffu), kb);
+        } else {
+            e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
+            e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
+        }
         f32x4 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) {
@@ -146,9 +178,12 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++) part += hf[ht][i] * relu(acc[ht][i]);
         part = xor32_sum(xor16_sum(part));
-        if (g == 0 && s < nv)
-            a.scores[static_cast<int64_t>(t) * a.max_slots + s] =
-                cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
+        if (g == 0 && s < nv) {
+            float v;
+            if constexpr (F4) v = cur.scale == -INFINITY ? -INFINITY : part;   // scales applied in the dot
+            else v = cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
+            a.scores[static_cast<int64_t>(t) * a.max_slots + s] = v;
+        }
     };
 
     // ---- query operands and per-head factors (they depend on t only) ----
@@ -201,8 +236,9 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) {
         const uint8_t *qr = qlds + (16 * ht + c) * kQPitch;
-        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + 16 * g), qa[ht][0], qa[ht][1]);
-        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + 64 + 16 * g), qa[ht][2], qa[ht][3]);
+        const int q0 = F4 ? 32 * g : 16 * g, q1 = F4 ? 32 * g + 16 : 64 + 16 * g;   // the key's dims
+        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + q0), qa[ht][0], qa[ht][1]);
+        e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + q1), qa[ht][2], qa[ht][3]);
 #pragma unroll
         for (int i = 0; i < 4; i++) hf[ht][i] = qw[ht][i] * qs[ht][i];
     }
@@ -220,15 +256,15 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
     }
 }
 
-template <int WB>
+template <int WB, bool F4>
 static void launch_index(const IndexArgs &a, hipStream_t stream) {
     constexpr int tile = kSubTiles * kBlockSlots * WB;
     const dim3 grid(a.n_q, (a.max_slots + tile - 1) / tile), block(256 * WB);
     switch (a.h_idx / 16) {
-    case 1: hipLaunchKernelGGL((index_score_kernel<1, WB>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((index_score_kernel<2, WB>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((index_score_kernel<3, WB>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((index_score_kernel<4, WB>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((index_score_kernel<1, WB, F4>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((index_score_kernel<2, WB, F4>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((index_score_kernel<3, WB, F4>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((index_score_kernel<4, WB, F4>), grid, block, 0, stream, a); break;
     }
 }
 
@@ -237,8 +273,13 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     // workgroups per CU (256 CUs), four-wave 1024-slot tiles beyond
     constexpr int64_t kCUs = 256;
     const int64_t wide = static_cast<int64_t>(a.n_q) * ((a.max_slots + 2047) / 2048);
-    if (wide <= 2 * kCUs) launch_index<2>(a, stream);
-    else launch_index<1>(a, stream);
+    if (a.key_fp4) {
+        if (wide <= 2 * kCUs) launch_index<2, true>(a, stream);
+        else launch_index<1, true>(a, stream);
+    } else {
+        if (wide <= 2 * kCUs) launch_index<2, false>(a, stream);
+        else launch_index<1, false>(a, stream);
+    }
     return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ struct IndexArgs {
     const int32_t *n_slots;
     int max_slots;
     float *scores;
+    int key_fp4;            // keys: MXFP4 (KEY4 layout) instead of fp8 + fp32 scale
 };
 
 struct TopkArgs {

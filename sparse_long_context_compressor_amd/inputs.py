@@ -127,6 +127,10 @@ class Layer:
     swa_codes: Optional[torch.Tensor] = None   # [sum counts, 512] uint8
     swa_scales: Optional[torch.Tensor] = None  # [sum counts, 8] f32
     swa_rope: Optional[torch.Tensor] = None    # [sum counts, 64] bf16
+    # MXFP4 index keys (key_pool then has the KEY4 layout)
+    key_fp4: bool = False
+    key4_codes: Optional[torch.Tensor] = None  # [sum slots, 64] uint8
+    key4_e8m0: Optional[torch.Tensor] = None   # [sum slots, 4] uint8
     extra: dict = field(default_factory=dict)
 
     @property
@@ -141,6 +145,7 @@ class Layer:
 def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_slots: list,
                 W: int = 128, k: int = 0, H_I: int = 0, given_topk: bool = False,
                 permute: bool = True, compress_inputs: bool = False, swa_fp8: bool = False,
+                key_fp4: bool = False,
                 gamma_random: bool = False, sm_scale: Optional[float] = None,
                 device="cpu") -> Layer:
     """ctx[b]: context length of sequence b; queries: list of (seq, position);
@@ -262,6 +267,20 @@ def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_sl
         lay.key_table, lay.key_pool = key_table, key_pool
         lay.key_off = lay.cmp_off.clone()
         lay.key_codes, lay.key_scales = kcodes, kscales
+        if key_fp4:
+            # MXFP4 keys instead: random e2m1 pairs and E8M0 block scales
+            g4 = _gen(seed, "key4", "cpu")
+            lay.key4_codes = torch.randint(0, 256, (tot, DI // 2), generator=g4,
+                                           dtype=torch.uint8).to(dev)
+            lay.key4_e8m0 = torch.randint(120, 131, (tot, DI // 32), generator=g4,
+                                          dtype=torch.uint8).to(dev)
+            lay.key_fp4 = True
+            lay.key_pool = P.key4_pool_empty(nkb, dev)
+            for b in range(n_seq):
+                s0, n = cmp_off[b], n_slots[b]
+                if n:
+                    P.key4_pool_put(lay.key_pool, key_table[b], 0, lay.key4_codes[s0:s0 + n],
+                                    lay.key4_e8m0[s0:s0 + n])
         lay.qi = _fp8_codes((Q, H_I, DI), seed, "qi", dev)
         lay.qi_scale = _pow2((Q, H_I), seed, "qi_scale", dev)
         lay.qi_w = torch.rand((Q, H_I), generator=_gen(seed, "qi_w", dev), device=dev)
@@ -295,13 +314,14 @@ def swaonly_decode_b64(seed=1, device="cpu") -> Layer:
                        permute=False, device=device)
 
 
-def c4a_decode_64k(seed=2, device="cpu", batch=32, swa_fp8=False) -> Layer:
+def c4a_decode_64k(seed=2, device="cpu", batch=32, swa_fp8=False, key_fp4=False) -> Layer:
     """C4A decode, batch 32, H=64, context 65536 -> 16384 slots per sequence,
     indexer 64 heads x 128, top-k 512 + SWA 128, 64-row blocks, permuted tables
-    (swa_fp8: the SWA pool holds fp8 rows in the compressed-row layout)."""
+    (swa_fp8: the SWA pool holds fp8 rows in the compressed-row layout;
+    key_fp4: the index keys are MXFP4)."""
     return build_layer(seed, ratio=4, H=64, ctx=[65536] * batch,
                        queries=[(b, 65535) for b in range(batch)], n_slots=[16384] * batch,
-                       W=128, k=512, H_I=64, swa_fp8=swa_fp8, device=device)
+                       W=128, k=512, H_I=64, swa_fp8=swa_fp8, key_fp4=key_fp4, device=device)
 
 
 def c128a_decode_128k(seed=3, device="cpu", batch=32) -> Layer:

@@ -9,6 +9,9 @@ block's scales after all its rows) with this library's row widths:
   CMP pool   per block: 64 rows x (512 e4m3 codes | 64 bf16 rope) = 640 B,
              then 64 rows x 8 fp32 scales (one per 64 nope dims)  43008 B
   KEY pool   per block: 64 rows x 128 e4m3 codes, then 64 fp32   8448 B
+  KEY4 pool  MXFP4 keys, per block: 64 rows x 64 bytes of e2m1 pairs (even
+             element in the low nibble), then 64 rows x 4 E8M0 bytes  4352 B
+  fp8 SWA    the CMP layout, rows at positions instead of slots
 
 These helpers only move bytes (torch tensors, any device); they hold none of
 the method's arithmetic.
@@ -30,6 +33,8 @@ CMP_SCALE_OFF = BLOCK_ROWS * CMP_ROW_BYTES          # 40960
 CMP_BLOCK_BYTES = CMP_SCALE_OFF + BLOCK_ROWS * 4 * N_QBLK   # 43008
 KEY_SCALE_OFF = BLOCK_ROWS * D_INDEX                # 8192
 KEY_BLOCK_BYTES = KEY_SCALE_OFF + BLOCK_ROWS * 4    # 8448
+KEY4_SCALE_OFF = BLOCK_ROWS * D_INDEX // 2          # 4096
+KEY4_BLOCK_BYTES = KEY4_SCALE_OFF + BLOCK_ROWS * 4  # 4352
 
 
 def _u8(t: torch.Tensor) -> torch.Tensor:
@@ -128,3 +133,33 @@ def key_pool_get(pool, table_row, slot0, n):
     b, i = _phys_rows(table_row.to(pool.device), r)
     c, s = _key_views(pool)
     return c[b, i].contiguous(), s[b, i].contiguous().view(torch.float32).reshape(n)
+
+
+# -------------------------------------------------------------------- KEY4
+def key4_pool_empty(n_blocks: int, device="cpu") -> torch.Tensor:
+    return torch.zeros(n_blocks, KEY4_BLOCK_BYTES, dtype=torch.uint8, device=device)
+
+
+def _key4_views(pool):
+    nb = pool.shape[0]
+    codes = pool.as_strided((nb, BLOCK_ROWS, D_INDEX // 2), (KEY4_BLOCK_BYTES, D_INDEX // 2, 1))
+    scl = pool.as_strided((nb, BLOCK_ROWS, 4), (KEY4_BLOCK_BYTES, 4, 1), KEY4_SCALE_OFF)
+    return codes, scl
+
+
+def key4_pool_put(pool, table_row, slot0, codes4, e8m0):
+    """codes4 [n,64] uint8 (packed e2m1 pairs), e8m0 [n,4] uint8 for slots
+    slot0 .. slot0+n-1."""
+    n = codes4.shape[0]
+    r = _logical_rows(n, slot0, pool.device)
+    b, i = _phys_rows(table_row.to(pool.device), r)
+    c, s = _key4_views(pool)
+    c[b, i] = codes4.to(pool.device, torch.uint8)
+    s[b, i] = e8m0.to(pool.device, torch.uint8)
+
+
+def key4_pool_get(pool, table_row, slot0, n):
+    r = _logical_rows(n, slot0, pool.device)
+    b, i = _phys_rows(table_row.to(pool.device), r)
+    c, s = _key4_views(pool)
+    return c[b, i].contiguous(), s[b, i].contiguous()

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libslc.so")
 
 LAYER_SWAONLY, LAYER_C4A, LAYER_C128A = 1, 4, 128
 SWA_FP8 = 0x100     # OR'ed into a layer type (or the warm select's ratio): fp8 SWA pool
+KEY_MXFP4 = 0x200   # OR'ed into the ratio of index_scores / index_topk: MXFP4 keys
 SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED = [

@@ -70,6 +70,12 @@ def oracle_compress(O, lay):
 
 def oracle_index_topk(O, lay, queries=None, want_scores=True):
     qs = np.arange(lay.n_q) if queries is None else np.asarray(queries)
+    if getattr(lay, "key_fp4", False):
+        return O.index_topk_batch_mxfp4(
+            lay.k, np_u8(lay.qi)[qs], np_f32(lay.qi_scale)[qs], np_f32(lay.qi_w)[qs],
+            np_i32(lay.q_pos)[qs], np_i32(lay.q_seq)[qs], lay.ratio, lay.key_off.numpy(),
+            np_i32(lay.n_slots), np_u8(lay.key4_codes), np_u8(lay.key4_e8m0),
+            max_slots=lay.max_slots, want_scores=want_scores)
     res = O.index_topk_batch(
         lay.k, np_u8(lay.qi)[qs], np_f32(lay.qi_scale)[qs], np_f32(lay.qi_w)[qs],
         np_i32(lay.q_pos)[qs], np_i32(lay.q_seq)[qs], lay.ratio, lay.key_off.numpy(),
@@ -122,7 +128,8 @@ def gpu_index_topk(S, lay, scores=True):
     sc = torch.full((lay.n_q, ms), float("nan"), dtype=torch.float32, device=dev)
     idx = torch.empty((lay.n_q, lay.k), dtype=torch.int32, device=dev)
     ln = torch.empty(lay.n_q, dtype=torch.int32, device=dev)
-    S.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, lay.ratio,
+    kf = S.KEY_MXFP4 if getattr(lay, "key_fp4", False) else 0
+    S.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, lay.ratio | kf,
                    lay.key_pool, lay.key_table, lay.n_slots, ms, sc)
     S.topk_select(lay.k, sc, ms, lay.q_seq, lay.q_pos, lay.ratio, lay.n_slots, idx, ln)
     return sc, idx, ln

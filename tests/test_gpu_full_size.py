@@ -58,13 +58,15 @@ def test_swaonly_decode_b64_full(S, oracle):
     print(f"swaonly_decode_b64: max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
 
-@pytest.mark.parametrize("swa_fp8", [False, True], ids=["bf16_swa", "fp8_swa"])
-def test_c4a_decode_64k_full(S, oracle, swa_fp8):
+@pytest.mark.parametrize("swa_fp8,key_fp4", [(False, False), (True, False), (False, True)],
+                         ids=["bf16_swa", "fp8_swa", "mxfp4_keys"])
+def test_c4a_decode_64k_full(S, oracle, swa_fp8, key_fp4):
     """The whole decode step at B=32, every query checked: scores, top-k sets,
     the selection rule on the GPU's own scores, then attention over the GPU's
     own selection against the oracle's attention over the oracle's selection.
-    fp8_swa: the same step over an fp8 SWA pool (compressed-row layout)."""
-    lay = I.c4a_decode_64k(swa_fp8=swa_fp8)
+    fp8_swa: the same step over an fp8 SWA pool (compressed-row layout);
+    mxfp4_keys: with MXFP4 index keys."""
+    lay = I.c4a_decode_64k(swa_fp8=swa_fp8, key_fp4=key_fp4)
     t0 = time.perf_counter()
     idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay)
     out_ref, lse_ref = oracle_attention(oracle, lay, idx_ref)
@@ -95,7 +97,7 @@ def test_c4a_decode_64k_full(S, oracle, swa_fp8):
     keep = np.nonzero(same)[0]
     kt = torch.as_tensor(keep, device=out.device)
     e = check_attention(out[kt], lse[kt], out_ref[keep], lse_ref[keep])
-    print(f"c4a_decode_64k (fp8 SWA {swa_fp8}): near-tie slots {near}; "
+    print(f"c4a_decode_64k (fp8 SWA {swa_fp8}, MXFP4 keys {key_fp4}): near-tie slots {near}; "
           f"{len(keep)}/{lay.n_q} queries compared; "
           f"max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
