@@ -15,6 +15,7 @@ import numpy as np
 __all__ = [
     "build", "lib", "e4m3_decode", "e4m3_encode", "bf16_decode", "bf16_encode",
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
+    "compress_stream_seq",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
     "swa_insert", "swa_dequant", "e2m1_value", "e8m0_value", "index_scores_mxfp4",
     "index_topk_batch_mxfp4", "indexcache_skips", "num_threads",
@@ -74,6 +75,8 @@ def _declare(L):
         "oracle_sparse_mla_batch": (i32, [i32, i32, _P, _P, _P, i32, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, i32, _P, dbl, _P, _P, _P, _P]),
         "oracle_swa_insert": (i32, [i32, _P, _P, _P, i32, _P, _P, _P, _P]),
+        "oracle_compress_stream_seq": (i32, [i32, i32, _P, _P, _P, _P, dbl, _P, i32, _P, _P, _P,
+                                             _P]),
         "oracle_e2m1_value": (dbl, [C.c_uint8]),
         "oracle_e8m0_value": (dbl, [C.c_uint8]),
         "oracle_index_scores_mxfp4": (None, [i32, i32, _P, _P, _P, _P, _P, _P, _P]),
@@ -174,6 +177,28 @@ def compress_seq(r, kv_bits, score, gamma, eps, cos_sin):
     if rc:
         raise ValueError("slot anchor position outside the cos/sin table")
     return dict(codes=codes, scales=scales, rope=rope, pooled=pooled, prequant=pre)
+
+
+def compress_stream_seq(r, kv_bits, score, ape, gamma, eps, cos_sin):
+    """Streaming (two-block) compressor over one sequence's L tokens: kv
+    [L, coff*576] bf16 bits, score [L, coff*576] f32, ape [r, coff*576] f32.
+    Returns dict(codes, scales, rope, prequant) for the floor(L/r) slots."""
+    coff = 2 if r == 4 else 1
+    kv = _c(kv_bits, np.uint16).reshape(-1, coff * D)
+    L = kv.shape[0]
+    sc = _c(score, np.float32).reshape(L, coff * D)
+    ap = _c(ape, np.float32).reshape(r, coff * D)
+    g = _c(gamma, np.float32)
+    cs = _c(cos_sin, np.float32)
+    n = L // r
+    codes = np.zeros((n, DN), np.uint8)
+    scales = np.zeros((n, DN // QB), np.float32)
+    rope = np.zeros((n, DR), np.uint16)
+    pre = np.zeros((n, D), np.float32)
+    if lib().oracle_compress_stream_seq(r, L, _p(kv), _p(sc), _p(ap), _p(g), float(eps), _p(cs),
+                                        cs.shape[0], _p(codes), _p(scales), _p(rope), _p(pre)):
+        raise ValueError("slot anchor position outside the cos/sin table")
+    return dict(codes=codes, scales=scales, rope=rope, prequant=pre)
 
 
 def compress_batch(r, cu_seqlens, kv_bits, score, gamma, eps, cos_sin):

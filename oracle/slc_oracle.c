@@ -205,6 +205,38 @@ static void quantise_row(const float *y32, uint8_t *codes, float *scales, uint16
         rope[i] = oracle_bf16_encode((double)y32[OR_DN + i]);
 }
 
+/* The steps after the pool [P3 CSA compressor diagram; P5 6.2]: RMSNorm over
+ * the 576 dims, RoPE on the pairs (512+2i, 513+2i) at position pos, the row
+ * rounded to fp32, then the cache row format.  -1 if pos is past the table. */
+static int finish_slot(const double *pooled, int pos, const float *gamma, double eps,
+                       const float *cos_sin, int max_pos, uint8_t *codes, float *scales,
+                       uint16_t *rope, float *prequant_out)
+{
+    double y[OR_D], ms = 0.0, inv;
+    float y32[OR_D];
+    for (int d = 0; d < OR_D; d++)
+        ms += pooled[d] * pooled[d];
+    ms /= OR_D;
+    inv = 1.0 / sqrt(ms + eps);
+    for (int d = 0; d < OR_D; d++)
+        y[d] = pooled[d] * inv * (double)gamma[d];
+    if (pos >= max_pos)
+        return -1;
+    for (int i = 0; i < OR_DR / 2; i++) {
+        double c = cos_sin[(size_t)pos * OR_DR + i];
+        double s = cos_sin[(size_t)pos * OR_DR + OR_DR / 2 + i];
+        double a = y[OR_DN + 2 * i], b = y[OR_DN + 2 * i + 1];
+        y[OR_DN + 2 * i] = a * c - b * s;
+        y[OR_DN + 2 * i + 1] = a * s + b * c;
+    }
+    for (int d = 0; d < OR_D; d++)
+        y32[d] = (float)y[d];
+    if (prequant_out)
+        memcpy(prequant_out, y32, sizeof y32);
+    quantise_row(y32, codes, scales, rope);
+    return 0;
+}
+
 /*
  * One sequence of L tokens, ratio r in {4, 128}.
  *   kv    [L, 576] bf16 bits     per-token latent kv
@@ -233,10 +265,8 @@ int oracle_compress_seq(int r, int L, const uint16_t *kv, const float *score,
 {
     int n = oracle_n_slots(L, r);
     for (int j = 0; j < n; j++) {
-        double pooled[OR_D], y[OR_D];
-        float y32[OR_D];
-        int t_lo, t_hi, pos;
-        double ms = 0.0, inv;
+        double pooled[OR_D];
+        int t_lo, t_hi;
 
         oracle_window(j, r, L, &t_lo, &t_hi);
         for (int d = 0; d < OR_D; d++) {
@@ -253,31 +283,70 @@ int oracle_compress_seq(int r, int L, const uint16_t *kv, const float *score,
         }
         if (pooled_out)
             memcpy(pooled_out + (size_t)j * OR_D, pooled, sizeof pooled);
-
-        for (int d = 0; d < OR_D; d++)
-            ms += pooled[d] * pooled[d];
-        ms /= OR_D;
-        inv = 1.0 / sqrt(ms + eps);
-        for (int d = 0; d < OR_D; d++)
-            y[d] = pooled[d] * inv * (double)gamma[d];
-
-        pos = r * j;
-        if (pos >= max_pos)
+        if (finish_slot(pooled, r * j, gamma, eps, cos_sin, max_pos, codes + (size_t)j * OR_DN,
+                        scales + (size_t)j * (OR_DN / OR_QB), rope + (size_t)j * OR_DR,
+                        prequant_out ? prequant_out + (size_t)j * OR_D : NULL))
             return -1;
-        for (int i = 0; i < OR_DR / 2; i++) {
-            double c = cos_sin[(size_t)pos * OR_DR + i];
-            double s = cos_sin[(size_t)pos * OR_DR + OR_DR / 2 + i];
-            double a = y[OR_DN + 2 * i], b = y[OR_DN + 2 * i + 1];
-            y[OR_DN + 2 * i] = a * c - b * s;
-            y[OR_DN + 2 * i + 1] = a * s + b * c;
-        }
+    }
+    return 0;
+}
 
-        for (int d = 0; d < OR_D; d++)
-            y32[d] = (float)y[d];
-        if (prequant_out)
-            memcpy(prequant_out + (size_t)j * OR_D, y32, sizeof y32);
-        quantise_row(y32, codes + (size_t)j * OR_DN, scales + (size_t)j * (OR_DN / OR_QB),
-                     rope + (size_t)j * OR_DR);
+/*
+ * Streaming compressor, in its two-block form ["DeepseekV4Attention",
+ * DeepseekCompressor forward (save_partial_states adds the APE bias to the
+ * scores and keeps kv and score in an fp32 state cache) and "CSA compressor"
+ * (the C_a / C_b formula and the state layout table); "From MLA to CSA +
+ * HCA" 5.5 (a slot is compressed once its last token arrives)].
+ *   kv    [L, coff*576] bf16 bits: each token's coff kv blocks (r = 4: C_a
+ *         then C_b, coff = 2; r = 128: one block, coff = 1)
+ *   score [L, coff*576] fp32: the matching gate blocks (Z_a, Z_b)
+ *   ape   [r, coff*576] fp32: the positional bias (B_a, B_b), row pos % r
+ * Slot j is emitted when token r*j + r - 1 has arrived: slots j < floor(L/r).
+ * Its window entries, per channel d:
+ *   r = 4:   tokens 4j-4 .. 4j-1 (those >= 0) with their block 0 (C_a),
+ *            tokens 4j .. 4j+3 with their block 1 (C_b);
+ *   r = 128: tokens 128j .. 128j+127 with block 0.
+ * An entry's logit is the fp32 state value fp32(score + ape) and its value
+ * the kv block's; the pool is the per-channel softmax-weighted sum, then
+ * RMSNorm, RoPE at r*j and quantisation exactly as oracle_compress_seq.
+ * Outputs as oracle_compress_seq for the floor(L/r) emitted slots.
+ * Returns 0, or -1 when a slot's anchor is outside the cos/sin table.
+ */
+int oracle_compress_stream_seq(int r, int L, const uint16_t *kv, const float *score,
+                               const float *ape, const float *gamma, double eps,
+                               const float *cos_sin, int max_pos, uint8_t *codes,
+                               float *scales, uint16_t *rope, float *prequant_out)
+{
+    int coff = r == 4 ? 2 : 1, w = coff * OR_D;
+    int n = L / r;
+    for (int j = 0; j < n; j++) {
+        double pooled[OR_D];
+        int t_lo = r * j - (coff - 1) * r, t_hi = r * j + r - 1;
+        if (t_lo < 0)
+            t_lo = 0;
+        for (int d = 0; d < OR_D; d++) {
+            double m = -INFINITY, se = 0.0, acc = 0.0;
+            for (int pass = 0; pass < 2; pass++) {
+                for (int t = t_lo; t <= t_hi; t++) {
+                    int blk = (coff == 2 && t >= r * j) ? 1 : 0;
+                    size_t c = (size_t)t * w + (size_t)blk * OR_D + d;
+                    double logit = (float)(score[c] + ape[(size_t)(t % r) * w + blk * OR_D + d]);
+                    if (pass == 0) {
+                        if (logit > m)
+                            m = logit;
+                    } else {
+                        double e = exp(logit - m);
+                        se += e;
+                        acc += e * oracle_bf16_value(kv[c]);
+                    }
+                }
+            }
+            pooled[d] = acc / se;
+        }
+        if (finish_slot(pooled, r * j, gamma, eps, cos_sin, max_pos, codes + (size_t)j * OR_DN,
+                        scales + (size_t)j * (OR_DN / OR_QB), rope + (size_t)j * OR_DR,
+                        prequant_out ? prequant_out + (size_t)j * OR_D : NULL))
+            return -1;
     }
     return 0;
 }

@@ -720,3 +720,82 @@ def test_mxfp4_batch_respects_visibility(oracle):
         assert np.array_equal(sc[t, :nv], ref) and np.all(np.isnan(sc[t, nv:]))
         want, wl = oracle.topk(ref, 32)
         assert ln[t] == wl == min(32, nv) and np.array_equal(idx[t], want)
+
+
+# ------------------------------------------------- streaming (two-block) compress
+def _stream_case(g, r, L):
+    coff = 2 if r == 4 else 1
+    kvf = torch.from_numpy(g.normal(0, 1, (L, coff * 576)).astype(np.float32)).to(torch.bfloat16)
+    score = g.normal(0, 1, (L, coff * 576)).astype(np.float32)
+    ape = g.normal(0, 0.5, (r, coff * 576)).astype(np.float32)
+    gamma = g.uniform(0.5, 2.0, 576).astype(np.float32)
+    cs = np.zeros((L + 8, 64), np.float32)
+    ang = g.uniform(0, 6.28, (L + 8, 32))
+    cs[:, :32], cs[:, 32:] = np.cos(ang), np.sin(ang)
+    return kvf, score, ape, gamma, cs
+
+
+@pytest.mark.parametrize("r,L", [(4, 64), (4, 23), (128, 300)])
+def test_stream_equals_batch_compress_for_one_block_rows(oracle, r, L):
+    """Both kv blocks equal, both score blocks equal and no APE: every window
+    entry is the token's one row, so the streamed slots are the batch
+    compressor's complete slots, bit for bit."""
+    g = np.random.default_rng(50 + r)
+    kvf, score, _, gamma, cs = _stream_case(g, r, L)
+    one_kv, one_sc = kvf[:, :576], score[:, :576]
+    coff = 2 if r == 4 else 1
+    kv2 = bf16_bits(one_kv.repeat(1, coff))
+    sc2 = np.tile(one_sc, (1, coff))
+    st = oracle.compress_stream_seq(r, kv2, sc2, np.zeros((r, coff * 576), np.float32), gamma,
+                                    1e-6, cs)
+    bt = oracle.compress_seq(r, bf16_bits(one_kv), one_sc, gamma, 1e-6, cs)
+    n = L // r
+    assert st["codes"].shape[0] == n
+    for key in ("codes", "scales", "rope", "prequant"):
+        assert np.array_equal(st[key], bt[key][:n]), key
+
+
+def test_stream_blocks_and_bias_select_the_entries(oracle):
+    """A large APE entry at (row p % 4, block b) makes each slot's window pick
+    the one token with that residue in the block's token group: block 1 is
+    the slot's own four tokens 4j..4j+3, block 0 the four before them.  A
+    bias that is the same everywhere changes nothing."""
+    r, L = 4, 40
+    g = np.random.default_rng(60)
+    kvf, score, ape, gamma, cs = _stream_case(g, r, L)
+    kv = bf16_bits(kvf)
+    base = oracle.compress_stream_seq(r, kv, score, ape, gamma, 1e-6, cs)
+    same = oracle.compress_stream_seq(r, kv, score, ape + np.float32(2.5), gamma, 1e-6, cs)
+    assert np.allclose(same["prequant"], base["prequant"], rtol=1e-5, atol=1e-5)
+    kvd = kvf.double().numpy()
+    for row, blk in ((1, 1), (2, 0)):
+        a2 = np.zeros_like(ape)
+        a2[row, blk * 576: blk * 576 + 576] = 1e4
+        # compare pooled rows through RMSNorm: use unit gamma, identity RoPE
+        one = np.ones(576, np.float32)
+        ident = np.zeros_like(cs)
+        ident[:, :32] = 1.0
+        pre = oracle.compress_stream_seq(r, kv, score, a2, one, 0.0, ident)["prequant"]
+        for j in range(L // r):
+            t = 4 * j + row if blk == 1 else 4 * j - 4 + row
+            if t < 0:
+                continue
+            want = kvd[t, blk * 576: blk * 576 + 576]
+            want = want / np.sqrt(np.mean(want ** 2))
+            assert np.allclose(pre[j], want, rtol=1e-6, atol=1e-6), (row, blk, j)
+
+
+def test_stream_emits_only_complete_slots(oracle):
+    """floor(L/r) slots: the last slot of a sequence whose length is not a
+    multiple of r is not emitted, and earlier slots do not depend on the
+    tokens after their window."""
+    g = np.random.default_rng(61)
+    for r, L in ((4, 30), (128, 257)):
+        kvf, score, ape, gamma, cs = _stream_case(g, r, L)
+        full = oracle.compress_stream_seq(r, bf16_bits(kvf), score, ape, gamma, 1e-6, cs)
+        assert full["codes"].shape[0] == L // r
+        cut = (L // r) * r
+        part = oracle.compress_stream_seq(r, bf16_bits(kvf[:cut]), score[:cut], ape, gamma, 1e-6,
+                                          cs)
+        for key in ("codes", "scales", "rope", "prequant"):
+            assert np.array_equal(part[key], full[key])
