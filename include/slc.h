@@ -11,6 +11,9 @@
  *                           against the FP8 index keys of the visible slots.
  *   slc_topk_select         per-query global top-k over those scores.
  *   slc_index_topk          the two above in one call.
+ *   slc_compress_stream     the same compressor step by step: per-token state
+ *                           rows (two kv/score blocks, APE bias), slots
+ *                           emitted as they complete.
  *   slc_swa_insert          RoPE + fp8 quantisation + paged write of new tokens
  *                           into an fp8 sliding-window pool
  *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
@@ -175,6 +178,48 @@ slc_status_t slc_compress(int ratio, int n_seq, const int32_t *cu_seqlens, int m
                           const uint16_t *kv, const float *score, const float *gamma, float eps,
                           const float *cos_sin, int max_pos, slc_pool_t cmp_pool,
                           float *prequant, void *stream);
+
+/*
+ * slc_compress_stream -- the compressor as it runs step by step
+ * ("DeepseekV4Attention" (devpress): DeepseekCompressor forward, where
+ * save_partial_states adds the APE bias and keeps kv and score in an fp32
+ * state cache, then the fused compress kernel; "CSA compressor": the C_a /
+ * C_b formula and the state layout; "From MLA to CSA + HCA" 5.5: a slot is
+ * compressed once its ratio-th token has arrived).
+ *
+ * Each token t (sequence tok_seq[t], position p = tok_pos[t]) brings coff kv
+ * blocks and coff gate-score blocks of 576 dims (coff = 2 for ratio 4: C_a,
+ * C_b; 1 for ratio 128).  Step 1 writes its state row:
+ *   state[p] = [ kv blocks as fp32 | score blocks + ape[p % ratio] in fp32 ].
+ * Step 2: a token with (p + 1) % ratio == 0 emits slot j = p / ratio from
+ * the state rows of its window, per channel d:
+ *   ratio 4:   positions 4j-4 .. 4j-1 with block 0, 4j .. 4j+3 with block 1;
+ *   ratio 128: positions 128j .. 128j+127 with block 0;
+ *   pooled[d] = softmax-weighted sum of the entries' kv over their logits
+ *   (absent rows and positions < 0 are skipped),
+ * then RMSNorm, RoPE at r*j, quantisation and the store exactly as
+ * slc_compress.  The window's earlier rows come from earlier calls or from
+ * this one (step 1 completes before step 2).
+ *
+ *   ratio        4 or 128
+ *   n_tok        tokens in this call (>= 0); no two may share (sequence, position)
+ *   tok_seq, tok_pos  device int32 [n_tok]
+ *   kv           device bf16 [n_tok][coff*576], 16-byte aligned
+ *   score        device fp32 [n_tok][coff*576], 16-byte aligned
+ *   ape          device fp32 [ratio][coff*576]
+ *   state_pool   device fp32 rows of 2*coff*576 floats, state_block rows per
+ *                block, one table row per sequence (the pages use blocks of 4
+ *                rows for ratio 4 and 8 for ratio 128); a window of coff*ratio
+ *                positions must stay mapped until its slot is emitted
+ *   gamma, eps, cos_sin, max_pos, cmp_pool  as for slc_compress
+ *   prequant     nullable device fp32 [n_tok][576]: for an emitting token,
+ *                its slot's row after RMSNorm and RoPE (debug)
+ */
+slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
+                                 const int32_t *tok_pos, const uint16_t *kv, const float *score,
+                                 const float *ape, slc_pool_t state_pool, int state_block,
+                                 const float *gamma, float eps, const float *cos_sin, int max_pos,
+                                 slc_pool_t cmp_pool, float *prequant, void *stream);
 
 /*
  * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J

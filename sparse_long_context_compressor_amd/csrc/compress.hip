@@ -116,10 +116,11 @@ __device__ __forceinline__ void quant_store(const float (&y)[9], int lane, slc_p
 }
 
 // RMSNorm, RoPE, quantise and store one pooled slot held by one wave.
+// prequant rows: at the slot's physical row (pq_index < 0) or at pq_index.
 __device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, int seq, int slot,
                                             int ratio, const float *gamma, float eps,
                                             const float *cos_sin, int max_pos, slc_pool_t pool,
-                                            float *prequant) {
+                                            float *prequant, int64_t pq_index = -1) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 9; i++) ss += pooled[i] * pooled[i];
@@ -142,8 +143,38 @@ __device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, 
 
     int64_t row = pool_row(pool, seq, slot);
     if (row < 0) return;
-    if (prequant) store_prequant(prequant + row * kD, y, lane);
+    if (prequant) store_prequant(prequant + (pq_index < 0 ? row : pq_index) * kD, y, lane);
     quant_store(y, lane, pool, row);
+}
+
+// Streaming state rows: entry of (seq, pos) in a pool of `rows` rows per
+// block, each 2 * width floats (kv blocks, then score blocks); null if absent.
+__device__ __forceinline__ float *state_row(const slc_pool_t &p, int rows, int width, int seq,
+                                            int pos) {
+    if (pos < 0) return nullptr;
+    const int lb = pos / rows;
+    if (lb >= p.table_stride) return nullptr;
+    const int32_t pb = p.block_table[static_cast<int64_t>(seq) * p.table_stride + lb];
+    if (pb < 0 || pb >= p.n_blocks) return nullptr;
+    return reinterpret_cast<float *>(p.base) +
+           (static_cast<int64_t>(pb) * rows + pos % rows) * (2 * width);
+}
+
+// Fold one state entry's block `blk` into the lane's 9 channels (logits are
+// stored with the bias already added).
+__device__ __forceinline__ void pool_state(PoolState &s, const float *row, int width, int blk,
+                                           int lane) {
+    const float *kv = row + blk * kD, *sc = row + width + blk * kD;
+    const f32x4 k0 = *reinterpret_cast<const f32x4 *>(kv + 8 * lane);
+    const f32x4 k1 = *reinterpret_cast<const f32x4 *>(kv + 8 * lane + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + 8 * lane);
+    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + 8 * lane + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        state_add(s, i, s0[i], k0[i]);
+        state_add(s, 4 + i, s1[i], k1[i]);
+    }
+    state_add(s, 8, sc[kDN + lane], kv[kDN + lane]);
 }
 
 }  // namespace
@@ -250,6 +281,106 @@ __global__ __launch_bounds__(256) void swa_insert_kernel(SwaInsertArgs a) {
 hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream) {
     if (a.n_tok <= 0) return hipSuccess;
     hipLaunchKernelGGL(swa_insert_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Streaming compressor, step 1 ("DeepseekV4Attention", save_partial_states):
+// each token's kv blocks (as fp32) and score blocks plus the APE row
+// pos % ratio go to its state row.  One workgroup per token.
+__global__ __launch_bounds__(256) void stream_save_kernel(StreamArgs a) {
+    const int t = blockIdx.x;
+    const int width = (a.ratio == 4 ? 2 : 1) * kD;
+    const int pos = a.tok_pos[t];
+    float *row = state_row(a.state, a.state_block, width, a.tok_seq[t], pos);
+    if (!row) return;
+    const uint16_t *kv = a.kv + static_cast<int64_t>(t) * width;
+    const float *sc = a.score + static_cast<int64_t>(t) * width;
+    const float *ape = a.ape + static_cast<int64_t>(pos % a.ratio) * width;
+    for (int c = threadIdx.x; c < width; c += 256) {
+        row[c] = bf16_to_f32(kv[c]);
+        row[width + c] = sc[c] + ape[c];
+    }
+}
+
+// Step 2 (the fused compress -> RMSNorm -> RoPE -> quantise -> store): a
+// token at position r*j + r - 1 emits slot j from the state rows of its
+// window.  r = 4: one wave per token (four per workgroup); entries are the
+// block-0 halves of tokens 4j-4 .. 4j-1 and the block-1 halves of 4j ..
+// 4j+3 ("DeepseekV4Attention", CSA compressor: the older group brings C_a,
+// the newer C_b).  r = 128: one workgroup per token, four waves pooling 32
+// entries each, merged through LDS.  Absent state rows are skipped.
+__global__ __launch_bounds__(256) void stream_emit_r4_kernel(StreamArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+    const int slot = pos / 4;
+    PoolState st;
+    state_init(st);
+    for (int e = 0; e < 8; e++) {
+        const int p = 4 * slot - 4 + e;
+        const float *row = state_row(a.state, a.state_block, 2 * kD, seq, p);
+        if (row) pool_state(st, row, 2 * kD, e < 4 ? 0 : 1, lane);
+    }
+    float pooled[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) pooled[i] = st.l[i] > 0.f ? st.acc[i] / st.l[i] : 0.f;
+    finish_slot(pooled, lane, seq, slot, 4, a.gamma, a.eps, a.cos_sin, a.max_pos, a.pool,
+                a.prequant, t);
+}
+
+__global__ __launch_bounds__(256) void stream_emit_r128_kernel(StreamArgs a) {
+    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0 || (pos + 1) % 128 != 0) return;          // uniform over the workgroup
+    const int slot = pos / 128;
+    PoolState st;
+    state_init(st);
+    for (int e = 32 * w; e < 32 * w + 32; e++) {
+        const float *row = state_row(a.state, a.state_block, kD, seq, 128 * slot + e);
+        if (row) pool_state(st, row, kD, 0, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        part_m[w][8 * lane + i] = st.m[i];
+        part_l[w][8 * lane + i] = st.l[i];
+        part_acc[w][8 * lane + i] = st.acc[i];
+    }
+    part_m[w][kDN + lane] = st.m[8];
+    part_l[w][kDN + lane] = st.l[8];
+    part_acc[w][kDN + lane] = st.acc[8];
+    __syncthreads();
+    if (w != 0) return;
+    float pooled[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) {
+        const int d = i < 8 ? 8 * lane + i : kDN + lane;
+        float m = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) m = fmaxf(m, part_m[ww][d]);
+        float l = 0.f, acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const float sc = part_l[ww][d] > 0.f ? __expf(part_m[ww][d] - m) : 0.f;
+            l += part_l[ww][d] * sc;
+            acc += part_acc[ww][d] * sc;
+        }
+        pooled[i] = l > 0.f ? acc / l : 0.f;
+    }
+    finish_slot(pooled, lane, seq, slot, 128, a.gamma, a.eps, a.cos_sin, a.max_pos, a.pool,
+                a.prequant, t);
+}
+
+hipError_t launch_compress_stream(const StreamArgs &a, hipStream_t stream) {
+    if (a.n_tok <= 0) return hipSuccess;
+    hipLaunchKernelGGL(stream_save_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);
+    if (a.ratio == 4)
+        hipLaunchKernelGGL(stream_emit_r4_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(stream_emit_r128_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

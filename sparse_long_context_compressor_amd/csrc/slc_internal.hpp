@@ -34,6 +34,28 @@ struct SwaInsertArgs {
     float *prequant;
 };
 
+// Streaming compressor: token t (sequence tok_seq[t], position tok_pos[t])
+// brings coff kv / score blocks; its state row (fp32: coff kv blocks, then
+// coff score blocks with the APE bias added) lives in a paged state pool of
+// state_block rows per block; a token that completes a slot emits it.
+struct StreamArgs {
+    int ratio;
+    int n_tok;
+    const int32_t *tok_seq;
+    const int32_t *tok_pos;
+    const uint16_t *kv;         // [n_tok][coff*576] bf16
+    const float *score;         // [n_tok][coff*576]
+    const float *ape;           // [ratio][coff*576]
+    slc_pool_t state;
+    int state_block;
+    const float *gamma;
+    float eps;
+    const float *cos_sin;
+    int max_pos;
+    slc_pool_t pool;            // compressed pool (CMP layout)
+    float *prequant;            // nullable [n_tok][576], rows of emitting tokens
+};
+
 struct IndexArgs {
     int n_q;
     int h_idx;
@@ -97,6 +119,7 @@ struct AttnArgs {
 
 hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream);
 hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream);
+hipError_t launch_compress_stream(const StreamArgs &a, hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);

@@ -26,7 +26,7 @@ SLC_OK, SLC_ERR_INVALID_ARG, SLC_ERR_WORKSPACE, SLC_ERR_HIP = 0, 1, 2, 3
 EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
-    "slc_indexcache_skips", "slc_swa_insert",
+    "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -69,6 +69,9 @@ def lib():
         L.slc_topk_select_warm.restype = i32
         L.slc_topk_select_warm.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                            pool, vp]
+        L.slc_compress_stream.restype = i32
+        L.slc_compress_stream.argtypes = [i32, i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp,
+                                          i32, pool, vp, vp]
         L.slc_swa_insert.restype = i32
         L.slc_swa_insert.argtypes = [i32, vp, vp, vp, vp, i32, pool, vp, vp]
         L.slc_indexcache_skips.restype = i32
@@ -144,6 +147,33 @@ def compress(ratio: int, cu_seqlens: torch.Tensor, max_seqlen: int, kv: torch.Te
                               int(max_seqlen), _ptr(kv), _ptr(score), _ptr(gamma), float(eps),
                               _ptr(cos_sin), int(cos_sin.shape[0]), pool(cmp_pool, cmp_table),
                               _ptr(prequant), _stream()))
+
+
+def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv: torch.Tensor,
+                    score: torch.Tensor, ape: torch.Tensor, state_pool: torch.Tensor,
+                    state_table: torch.Tensor, state_block: int, gamma: torch.Tensor, eps: float,
+                    cos_sin: torch.Tensor, cmp_pool: torch.Tensor, cmp_table: torch.Tensor,
+                    prequant: Optional[torch.Tensor] = None) -> None:
+    """One step of the streaming compressor: state rows of the given tokens,
+    then the slots they complete (state_pool fp32 [n_blocks, state_block,
+    2*coff*576])."""
+    dev = kv.device
+    _need(kv, "kv", torch.bfloat16, dev)
+    _need(score, "score", torch.float32, dev)
+    _need(ape, "ape", torch.float32, dev)
+    _need(state_pool, "state_pool", torch.float32, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(cos_sin, "cos_sin", torch.float32, dev)
+    _need(tok_seq, "tok_seq", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(cmp_pool, "cmp_pool", torch.uint8, dev)
+    if prequant is not None:
+        _need(prequant, "prequant", torch.float32, dev)
+    _check(lib().slc_compress_stream(int(ratio), int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos),
+                                     _ptr(kv), _ptr(score), _ptr(ape),
+                                     pool(state_pool, state_table), int(state_block), _ptr(gamma),
+                                     float(eps), _ptr(cos_sin), int(cos_sin.shape[0]),
+                                     pool(cmp_pool, cmp_table), _ptr(prequant), _stream()))
 
 
 def swa_insert(kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,

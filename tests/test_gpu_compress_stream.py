@@ -1,0 +1,122 @@
+"""GPU parity of the streaming compressor ("DeepseekV4Attention": the
+compressor forward with its fp32 state cache and APE bias, the CSA formula
+with C_a / C_b blocks): sequences fed as a prefill chunk and then one token
+per step, in calls that mix sequences, against the oracle's two-block
+compressor over each whole sequence.  Rules as for the batch compressor:
+codes and scales equal except near an e4m3 rounding midpoint or a scale
+boundary (counted), rope within one bf16 step, the kernel's codes exactly the
+library casts of its own pre-quantisation rows, and no other byte written."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import bits16, near_midpoint, near_scale_boundary
+from sparse_long_context_compressor_amd import inputs as I
+from sparse_long_context_compressor_amd import pools as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    from sparse_long_context_compressor_amd import slc
+    slc.lib()
+    return slc
+
+
+def pow2_rule(amax):
+    if amax == 0:
+        return 1.0
+    e = int(np.ceil(np.log2(amax / 448.0)))
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    while amax <= 448.0 * 2.0 ** (e - 1):
+        e -= 1
+    return 2.0 ** e
+
+
+@pytest.mark.parametrize("r,lens,chunk,state_block", [(4, [37, 70, 4], 13, 4),
+                                                       (128, [300, 129], 140, 8)])
+def test_streamed_slots_match_oracle(S, oracle, r, lens, chunk, state_block):
+    coff = 2 if r == 4 else 1
+    g = torch.Generator().manual_seed(90 + r)
+    n_seq, T = len(lens), sum(lens)
+    kv = torch.randn((T, coff * 576), generator=g).to(torch.bfloat16)
+    score = torch.randn((T, coff * 576), generator=g)
+    ape = torch.randn((r, coff * 576), generator=g) * 0.5
+    gamma = torch.rand((576,), generator=g) + 0.5
+    cs = I.rope_table(max(lens) + 8)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+
+    ref = [oracle.compress_stream_seq(r, bits16(kv[offs[b]:offs[b + 1]]),
+                                      score[offs[b]:offs[b + 1]].numpy(), ape.numpy(),
+                                      gamma.numpy(), 1e-6, cs.numpy()) for b in range(n_seq)]
+
+    dev = "cuda"
+    st_blocks = [list(range(-(-L // state_block))) for L in lens]
+    st_table, n_st = I.block_table(st_blocks, max(len(b) for b in st_blocks), 91, "st", "cpu")
+    state = torch.zeros((n_st, state_block, 2 * coff * 576), dtype=torch.float32, device=dev)
+    c_blocks = [list(range(max(1, -(-(L // r) // 64)))) for L in lens]
+    c_table, n_cb = I.block_table(c_blocks, max(len(b) for b in c_blocks), 92, "ct", "cpu")
+    cmp_pool = P.cmp_pool_empty(n_cb, dev)
+    args = [t.to(dev) for t in (kv, score, ape, gamma, cs)]
+    st_table_d, c_table_d = st_table.to(dev), c_table.to(dev)
+
+    # calls: a prefill chunk of every sequence together, then one token of
+    # every unfinished sequence per step
+    calls = [[(b, p) for b in range(n_seq) for p in range(min(chunk, lens[b]))]]
+    for p in range(chunk, max(lens)):
+        calls.append([(b, p) for b in range(n_seq) if p < lens[b]])
+    pre = {}
+    for toks in calls:
+        rows = torch.tensor([offs[b] + p for b, p in toks], dtype=torch.long)
+        seq = torch.tensor([b for b, _ in toks], dtype=torch.int32, device=dev)
+        pos = torch.tensor([p for _, p in toks], dtype=torch.int32, device=dev)
+        pq = torch.full((len(toks), 576), float("nan"), device=dev)
+        S.compress_stream(r, seq, pos, args[0][rows.to(dev)].contiguous(),
+                          args[1][rows.to(dev)].contiguous(), args[2], state, st_table_d,
+                          state_block, args[3], 1e-6, args[4], cmp_pool, c_table_d, pq)
+        pq = pq.cpu().numpy()
+        for i, (b, p) in enumerate(toks):
+            if (p + 1) % r == 0:
+                pre[(b, p // r)] = pq[i]
+    torch.cuda.synchronize()
+    pool = cmp_pool.cpu()
+
+    written = np.zeros(n_cb * 64, bool)
+    excused = 0
+    for b, L in enumerate(lens):
+        n = L // r
+        assert sorted(j for bb, j in pre if bb == b) == list(range(n))
+        if n == 0:
+            continue
+        codes, scales, rope = P.cmp_pool_get(pool, c_table[b], 0, n)
+        codes, scales, rope = codes.numpy(), scales.numpy(), bits16(rope)
+        phys = (c_table[b].long()[torch.arange(n) // 64] * 64 + torch.arange(n) % 64).numpy()
+        written[phys] = True
+        g_pre = np.stack([pre[(b, j)] for j in range(n)])
+        o = ref[b]
+        assert np.max(np.abs(g_pre - o["prequant"])) <= 1e-4 * max(1.0, float(np.max(np.abs(o["prequant"]))))
+        for j in range(n):
+            for blk in range(8):
+                x = g_pre[j, 64 * blk:64 * blk + 64]
+                s = pow2_rule(float(np.max(np.abs(x.astype(np.float64)))))
+                assert scales[j, blk] == s
+                want = torch.from_numpy((x.astype(np.float64) / s).astype(np.float32)).to(
+                    torch.float8_e4m3fn).view(torch.uint8).numpy()
+                assert np.array_equal(codes[j, 64 * blk:64 * blk + 64], want)
+        assert np.array_equal(rope, bits16(torch.from_numpy(np.ascontiguousarray(g_pre[:, 512:]))))
+        o_amax = np.max(np.abs(o["prequant"][:, :512].reshape(n, 8, 64)), axis=2)
+        boundary = near_scale_boundary(o_amax)
+        assert np.all((scales == o["scales"]) | boundary)
+        v = o["prequant"][:, :512].reshape(n, 8, 64) / o["scales"][:, :, None]
+        ok_elem = near_midpoint(v) | boundary[:, :, None]
+        diff = codes.reshape(n, 8, 64) != o["codes"].reshape(n, 8, 64)
+        assert not np.any(diff & ~ok_elem), "fp8 code mismatch away from midpoints"
+        excused += int(np.sum(diff))
+        assert np.all(np.abs(rope.astype(np.int32) - o["rope"].astype(np.int32)) <= 1)
+    rows, scl = P._cmp_views(pool)
+    assert not rows.reshape(-1, 640)[torch.from_numpy(~written)].any()
+    assert not scl.reshape(-1, 32)[torch.from_numpy(~written)].any()
+    print(f"r={r}: {sum(L // r for L in lens)} slots streamed in {len(calls)} calls; "
+          f"codes excused near midpoints: {excused}")
