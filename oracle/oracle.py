@@ -15,7 +15,7 @@ import numpy as np
 __all__ = [
     "build", "lib", "e4m3_decode", "e4m3_encode", "bf16_decode", "bf16_encode",
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
-    "compress_stream_seq",
+    "compress_stream_seq", "compress_index_keys_stream_seq",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
     "swa_insert", "swa_dequant", "e2m1_value", "e8m0_value", "index_scores_mxfp4",
     "index_topk_batch_mxfp4", "indexcache_skips", "num_threads",
@@ -75,6 +75,8 @@ def _declare(L):
         "oracle_sparse_mla_batch": (i32, [i32, i32, _P, _P, _P, i32, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, i32, _P, dbl, _P, _P, _P, _P]),
         "oracle_swa_insert": (i32, [i32, _P, _P, _P, i32, _P, _P, _P, _P]),
+        "oracle_compress_index_keys_stream_seq": (i32, [i32, _P, _P, _P, _P, dbl, _P, i32, _P,
+                                                        _P, _P]),
         "oracle_compress_stream_seq": (i32, [i32, i32, _P, _P, _P, _P, dbl, _P, i32, _P, _P, _P,
                                              _P]),
         "oracle_e2m1_value": (dbl, [C.c_uint8]),
@@ -199,6 +201,27 @@ def compress_stream_seq(r, kv_bits, score, ape, gamma, eps, cos_sin):
                                         cs.shape[0], _p(codes), _p(scales), _p(rope), _p(pre)):
         raise ValueError("slot anchor position outside the cos/sin table")
     return dict(codes=codes, scales=scales, rope=rope, prequant=pre)
+
+
+def compress_index_keys_stream_seq(kv_bits, score, ape, gamma, eps, cos_sin):
+    """The indexer's 128-dim key compressor (ratio 4, two blocks) over one
+    sequence: kv [L, 256] bf16 bits, score [L, 256], ape [4, 256], gamma [128].
+    Returns dict(codes [n,128], scales [n], prequant [n,128]), n = L // 4."""
+    kv = _c(kv_bits, np.uint16).reshape(-1, 2 * DI)
+    L = kv.shape[0]
+    sc = _c(score, np.float32).reshape(L, 2 * DI)
+    ap = _c(ape, np.float32).reshape(4, 2 * DI)
+    g = _c(gamma, np.float32)
+    cs = _c(cos_sin, np.float32)
+    n = L // 4
+    codes = np.zeros((n, DI), np.uint8)
+    scales = np.zeros(n, np.float32)
+    pre = np.zeros((n, DI), np.float32)
+    if lib().oracle_compress_index_keys_stream_seq(L, _p(kv), _p(sc), _p(ap), _p(g), float(eps),
+                                                   _p(cs), cs.shape[0], _p(codes), _p(scales),
+                                                   _p(pre)):
+        raise ValueError("slot anchor position outside the cos/sin table")
+    return dict(codes=codes, scales=scales, prequant=pre)
 
 
 def compress_batch(r, cu_seqlens, kv_bits, score, gamma, eps, cos_sin):

@@ -457,6 +457,81 @@ void oracle_index_scores(int h_idx, int n, const uint8_t *q, const float *q_scal
     free(acc);
 }
 
+/*
+ * The indexer's own compressor ["DeepSeek-V4 attention layer types": the
+ * indexer holds a small compressor of head_dim 128 whose entries fill the
+ * indexer's K cache; "DeepseekV4Attention": the same compressor class (its
+ * RoPE on the last 64 dims, at (pos // r) * r) and the indexer cache entry
+ * of 128 fp8 values plus one fp32 scale].  Ratio 4, streamed in the
+ * two-block form of oracle_compress_stream_seq with rows of 128 dims:
+ *   kv, score [L, 2*128] (bf16 bits, fp32), ape [4, 2*128], gamma [128];
+ * slot j pools positions 4j-4 .. 4j-1 (block 0) and 4j .. 4j+3 (block 1)
+ * per channel, then RMSNorm over the 128 dims, RoPE on the pairs
+ * (64+2i, 65+2i) at position 4j, the row rounded to fp32, and one pow2 scale
+ * for all 128 dims (the compressed rows' rule) with e4m3 codes of y / scale.
+ * Outputs for the floor(L/4) emitted slots: codes [n,128], scales [n],
+ * prequant [n,128] (nullable).  Returns -1 if an anchor is past the table.
+ */
+int oracle_compress_index_keys_stream_seq(int L, const uint16_t *kv, const float *score,
+                                          const float *ape, const float *gamma, double eps,
+                                          const float *cos_sin, int max_pos, uint8_t *codes,
+                                          float *scales, float *prequant_out)
+{
+    const int r = 4, w = 2 * OR_DI;
+    int n = L / r;
+    for (int j = 0; j < n; j++) {
+        double pooled[OR_DI], y[OR_DI], ms = 0.0, inv, amax = 0.0, scale;
+        float y32[OR_DI];
+        int t_lo = r * j - r < 0 ? 0 : r * j - r, t_hi = r * j + r - 1, pos = r * j;
+        for (int d = 0; d < OR_DI; d++) {
+            double m = -INFINITY, se = 0.0, acc = 0.0;
+            for (int pass = 0; pass < 2; pass++) {
+                for (int t = t_lo; t <= t_hi; t++) {
+                    int blk = t >= r * j ? 1 : 0;
+                    size_t c = (size_t)t * w + (size_t)blk * OR_DI + d;
+                    double logit = (float)(score[c] + ape[(size_t)(t % r) * w + blk * OR_DI + d]);
+                    if (pass == 0) {
+                        if (logit > m)
+                            m = logit;
+                    } else {
+                        double e = exp(logit - m);
+                        se += e;
+                        acc += e * oracle_bf16_value(kv[c]);
+                    }
+                }
+            }
+            pooled[d] = acc / se;
+        }
+        for (int d = 0; d < OR_DI; d++)
+            ms += pooled[d] * pooled[d];
+        ms /= OR_DI;
+        inv = 1.0 / sqrt(ms + eps);
+        for (int d = 0; d < OR_DI; d++)
+            y[d] = pooled[d] * inv * (double)gamma[d];
+        if (pos >= max_pos)
+            return -1;
+        for (int i = 0; i < OR_DR / 2; i++) {
+            double c = cos_sin[(size_t)pos * OR_DR + i];
+            double s = cos_sin[(size_t)pos * OR_DR + OR_DR / 2 + i];
+            double a = y[OR_DI - OR_DR + 2 * i], b = y[OR_DI - OR_DR + 2 * i + 1];
+            y[OR_DI - OR_DR + 2 * i] = a * c - b * s;
+            y[OR_DI - OR_DR + 2 * i + 1] = a * s + b * c;
+        }
+        for (int d = 0; d < OR_DI; d++) {
+            y32[d] = (float)y[d];
+            if (fabs((double)y32[d]) > amax)
+                amax = fabs((double)y32[d]);
+        }
+        if (prequant_out)
+            memcpy(prequant_out + (size_t)j * OR_DI, y32, sizeof y32);
+        scale = ldexp(1.0, pow2_exponent_for(amax));
+        scales[j] = (float)scale;
+        for (int d = 0; d < OR_DI; d++)
+            codes[(size_t)j * OR_DI + d] = oracle_e4m3_encode((double)y32[d] / scale);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------- MXFP4 index keys */
 
 /* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no inf or NaN;

@@ -799,3 +799,43 @@ def test_stream_emits_only_complete_slots(oracle):
                                           cs)
         for key in ("codes", "scales", "rope", "prequant"):
             assert np.array_equal(part[key], full[key])
+
+
+def test_index_key_compressor_against_the_latent_compressor(oracle):
+    """Index-key rows placed in the last 128 dims of zero latent rows go through
+    the same pooling, and the latent compressor's RoPE dims (512..575) are the
+    index compressor's (64..127): the two prequant rows agree up to the RMSNorm
+    factor sqrt(576/128).  One scale covers all 128 dims (the exact pow2 rule)
+    and the codes are torch's e4m3 cast of prequant / scale."""
+    g = np.random.default_rng(70)
+    L = 45
+    kv128 = torch.from_numpy(g.normal(0, 1, (L, 2, 128)).astype(np.float32)).to(torch.bfloat16)
+    sc128 = g.normal(0, 1, (L, 2, 128)).astype(np.float32)
+    ape128 = g.normal(0, 0.5, (4, 2, 128)).astype(np.float32)
+    cs = np.zeros((L + 4, 64), np.float32)
+    ang = g.uniform(0, 6.28, (L + 4, 32))
+    cs[:, :32], cs[:, 32:] = np.cos(ang), np.sin(ang)
+    gam = np.ones(128, np.float32)
+    ix = oracle.compress_index_keys_stream_seq(bf16_bits(kv128.reshape(L, 256)),
+                                               sc128.reshape(L, 256), ape128.reshape(4, 256),
+                                               gam, 0.0, cs)
+    kv576 = torch.zeros((L, 2, 576), dtype=torch.bfloat16)
+    kv576[:, :, 448:] = kv128
+    sc576 = np.zeros((L, 2, 576), np.float32)
+    sc576[:, :, 448:] = sc128
+    ape576 = np.zeros((4, 2, 576), np.float32)
+    ape576[:, :, 448:] = ape128
+    lat = oracle.compress_stream_seq(4, bf16_bits(kv576.reshape(L, 1152)), sc576.reshape(L, 1152),
+                                     ape576.reshape(4, 1152), np.ones(576, np.float32), 0.0, cs)
+    n = L // 4
+    assert ix["codes"].shape == (n, 128)
+    ratio = lat["prequant"][:, 448:].astype(np.float64) / ix["prequant"].astype(np.float64)
+    assert np.allclose(ratio, math.sqrt(576 / 128), rtol=1e-6)
+    assert not lat["prequant"][:, :448].any()
+    for j in range(n):
+        x = ix["prequant"][j].astype(np.float64)
+        s = _scale_exact(float(np.max(np.abs(x))))
+        assert ix["scales"][j] == s
+        want = torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        assert np.array_equal(ix["codes"][j], want)
