@@ -14,6 +14,8 @@
  *   slc_compress_stream     the same compressor step by step: per-token state
  *                           rows (two kv/score blocks, APE bias), slots
  *                           emitted as they complete.
+ *   slc_compress_index_keys_stream  the indexer's 128-dim key compressor,
+ *                           step by step, into the index key pool.
  *   slc_swa_insert          RoPE + fp8 quantisation + paged write of new tokens
  *                           into an fp8 sliding-window pool
  *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
@@ -220,6 +222,35 @@ slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
                                  const float *ape, slc_pool_t state_pool, int state_block,
                                  const float *gamma, float eps, const float *cos_sin, int max_pos,
                                  slc_pool_t cmp_pool, float *prequant, void *stream);
+
+/*
+ * slc_compress_index_keys_stream -- the indexer's own compressor, step by
+ * step ("DeepSeek-V4 attention layer types": the indexer holds a small
+ * compressor of head_dim 128 whose entries fill its K cache;
+ * "DeepseekV4Attention": the compressor class's RoPE on the last 64 dims and
+ * the indexer cache entry of 128 fp8 values plus one fp32 scale).
+ *
+ * As slc_compress_stream with ratio 4 and rows of 128 dims: kv and score
+ * [n_tok][2*128] (blocks C_a, C_b), ape [4][2*128], state rows of 4*128
+ * floats.  An emitting token (p = 4j + 3) pools slot j's window, then
+ *   y = pooled * gamma / sqrt(mean(pooled^2) + eps) over the 128 dims,
+ *   RoPE on the pairs (64+2i, 65+2i) at position 4j (cos_sin[4j][i],
+ *   cos_sin[4j][32+i]),
+ *   one scale for the key (smallest 2^e with amax <= 448*2^e, 1 if amax = 0)
+ *   and e4m3 codes of y / scale,
+ * stored at slot j of its sequence in key_pool (KEY layout), the index keys
+ * slc_index_scores reads.
+ *   gamma        device fp32 [128], 16-byte aligned
+ *   prequant     nullable device fp32 [n_tok][128] (debug)
+ * Other arguments as for slc_compress_stream.
+ */
+slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
+                                            const int32_t *tok_pos, const uint16_t *kv,
+                                            const float *score, const float *ape,
+                                            slc_pool_t state_pool, int state_block,
+                                            const float *gamma, float eps, const float *cos_sin,
+                                            int max_pos, slc_pool_t key_pool, float *prequant,
+                                            void *stream);
 
 /*
  * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J

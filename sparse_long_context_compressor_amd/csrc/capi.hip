@@ -178,7 +178,38 @@ slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
     st = check_pool(cmp_pool, "compress_stream: cmp_pool");
     if (st != SLC_OK) return st;
     StreamArgs a{ratio, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool, state_block,
-                 gamma, eps, cos_sin, max_pos, cmp_pool, prequant};
+                 gamma, eps, cos_sin, max_pos, cmp_pool, prequant, kD};
+    return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
+}
+
+slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
+                                            const int32_t *tok_pos, const uint16_t *kv,
+                                            const float *score, const float *ape,
+                                            slc_pool_t state_pool, int state_block,
+                                            const float *gamma, float eps, const float *cos_sin,
+                                            int max_pos, slc_pool_t key_pool, float *prequant,
+                                            void *stream) {
+    if (n_tok < 0) return fail("compress_index_keys_stream: n_tok must be >= 0");
+    if (state_block < 1 || state_block > 1024)
+        return fail("compress_index_keys_stream: state_block must be in [1, 1024]");
+    if (!(eps >= 0.f) || !std::isfinite(eps))
+        return fail("compress_index_keys_stream: eps must be finite and >= 0");
+    if (max_pos < 1) return fail("compress_index_keys_stream: max_pos must be >= 1");
+    if (n_tok == 0) return SLC_OK;
+    if (!tok_seq || !tok_pos || !kv || !score || !ape || !gamma || !cos_sin)
+        return fail("compress_index_keys_stream: tok_seq, tok_pos, kv, score, ape, gamma and "
+                    "cos_sin are required");
+    if (!aligned(kv, 16) || !aligned(score, 16) || !aligned(gamma, 16) ||
+        (prequant && !aligned(prequant, 16)))
+        return fail("compress_index_keys_stream: kv, score, gamma and prequant must be 16-byte aligned");
+    slc_status_t st = check_pool(state_pool, "compress_index_keys_stream: state_pool");
+    if (st != SLC_OK) return st;
+    if (!aligned(state_pool.base, 16))
+        return fail("compress_index_keys_stream: state_pool must be 16-byte aligned");
+    st = check_pool(key_pool, "compress_index_keys_stream: key_pool");
+    if (st != SLC_OK) return st;
+    StreamArgs a{4, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool, state_block,
+                 gamma, eps, cos_sin, max_pos, key_pool, prequant, kDI};
     return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
 }
 

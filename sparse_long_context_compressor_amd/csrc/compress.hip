@@ -289,7 +289,7 @@ hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream) {
 // pos % ratio go to its state row.  One workgroup per token.
 __global__ __launch_bounds__(256) void stream_save_kernel(StreamArgs a) {
     const int t = blockIdx.x;
-    const int width = (a.ratio == 4 ? 2 : 1) * kD;
+    const int width = (a.ratio == 4 ? 2 : 1) * a.dim;
     const int pos = a.tok_pos[t];
     float *row = state_row(a.state, a.state_block, width, a.tok_seq[t], pos);
     if (!row) return;
@@ -374,10 +374,72 @@ __global__ __launch_bounds__(256) void stream_emit_r128_kernel(StreamArgs a) {
                 a.prequant, t);
 }
 
+// The indexer's key compressor (dim 128, ratio 4): one wave per token; lane
+// l holds dims 2l, 2l+1, so the RoPE pair (64+2i, 65+2i) is lane 32+i's own
+// two dims.  Pool as the latent r = 4 emit, RMSNorm over 128 dims, RoPE at
+// 4j, one pow2 scale for the key, e4m3 codes into the KEY pool.
+__global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+    const int slot = pos / 4;
+    constexpr int kW = 2 * kDI;                          // floats per half state row
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
+    for (int e = 0; e < 8; e++) {
+        const float *row = state_row(a.state, a.state_block, kW, seq, 4 * slot - 4 + e);
+        if (!row) continue;
+        const int blk = e < 4 ? 0 : 1;
+        const f32x2 kv = *reinterpret_cast<const f32x2 *>(row + blk * kDI + 2 * lane);
+        const f32x2 sc = *reinterpret_cast<const f32x2 *>(row + kW + blk * kDI + 2 * lane);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const float mn = fmaxf(m[i], sc[i]);
+            const float al = __expf(m[i] - mn), ex = __expf(sc[i] - mn);
+            l[i] = l[i] * al + ex;
+            acc[i] = acc[i] * al + ex * kv[i];
+            m[i] = mn;
+        }
+    }
+    float y[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) y[i] = l[i] > 0.f ? acc[i] / l[i] : 0.f;
+    const float ss = wave_sum(y[0] * y[0] + y[1] * y[1]);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kDI) + a.eps);
+    const f32x2 gm = *reinterpret_cast<const f32x2 *>(a.gamma + 2 * lane);
+    y[0] = y[0] * inv * gm[0];
+    y[1] = y[1] * inv * gm[1];
+    const int anchor = 4 * slot;
+    if (anchor >= a.max_pos) return;
+    if (lane >= 32) {
+        const int i = lane - 32;
+        const float c = a.cos_sin[static_cast<int64_t>(anchor) * kDR + i];
+        const float s = a.cos_sin[static_cast<int64_t>(anchor) * kDR + kDR / 2 + i];
+        const float y0 = y[0], y1 = y[1];
+        y[0] = y0 * c - y1 * s;
+        y[1] = y0 * s + y1 * c;
+    }
+    const int64_t row = pool_row(a.pool, seq, slot);
+    if (row < 0) return;
+    if (a.prequant)
+        *reinterpret_cast<f32x2 *>(a.prequant + static_cast<int64_t>(t) * kDI + 2 * lane) = f32x2{y[0], y[1]};
+    const float amax = wave_max(fmaxf(fabsf(y[0]), fabsf(y[1])));
+    const int e = pow2_exponent(amax);
+    const float inv_scale = ldexpf(1.f, -e);
+    const uint32_t code = f32_to_e4m3(y[0] * inv_scale) | (f32_to_e4m3(y[1] * inv_scale) << 8);
+    uint8_t *base = reinterpret_cast<uint8_t *>(a.pool.base) + (row / kBR) * SLC_KEY_BLOCK_BYTES;
+    reinterpret_cast<uint16_t *>(base + (row % kBR) * kDI)[lane] = static_cast<uint16_t>(code);
+    if (lane == 0)
+        reinterpret_cast<float *>(base + SLC_KEY_SCALE_OFFSET)[row % kBR] = ldexpf(1.f, e);
+}
+
 hipError_t launch_compress_stream(const StreamArgs &a, hipStream_t stream) {
     if (a.n_tok <= 0) return hipSuccess;
     hipLaunchKernelGGL(stream_save_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);
-    if (a.ratio == 4)
+    if (a.dim == kDI)
+        hipLaunchKernelGGL(stream_emit_keys_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);
+    else if (a.ratio == 4)
         hipLaunchKernelGGL(stream_emit_r4_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(stream_emit_r128_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);

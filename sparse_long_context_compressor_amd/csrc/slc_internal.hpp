@@ -52,8 +52,9 @@ struct StreamArgs {
     float eps;
     const float *cos_sin;
     int max_pos;
-    slc_pool_t pool;            // compressed pool (CMP layout)
-    float *prequant;            // nullable [n_tok][576], rows of emitting tokens
+    slc_pool_t pool;            // compressed pool (CMP layout; KEY layout for dim 128)
+    float *prequant;            // nullable [n_tok][dim], rows of emitting tokens
+    int dim;                    // 576 (latent rows) or 128 (index keys, ratio 4)
 };
 
 struct IndexArgs {

@@ -27,6 +27,7 @@ EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
+    "slc_compress_index_keys_stream",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -72,6 +73,9 @@ def lib():
         L.slc_compress_stream.restype = i32
         L.slc_compress_stream.argtypes = [i32, i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp,
                                           i32, pool, vp, vp]
+        L.slc_compress_index_keys_stream.restype = i32
+        L.slc_compress_index_keys_stream.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32,
+                                                     vp, i32, pool, vp, vp]
         L.slc_swa_insert.restype = i32
         L.slc_swa_insert.argtypes = [i32, vp, vp, vp, vp, i32, pool, vp, vp]
         L.slc_indexcache_skips.restype = i32
@@ -174,6 +178,29 @@ def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv
                                      pool(state_pool, state_table), int(state_block), _ptr(gamma),
                                      float(eps), _ptr(cos_sin), int(cos_sin.shape[0]),
                                      pool(cmp_pool, cmp_table), _ptr(prequant), _stream()))
+
+
+def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, state_table,
+                               state_block: int, gamma, eps: float, cos_sin, key_pool,
+                               key_table, prequant=None) -> None:
+    """One step of the indexer's 128-dim key compressor (ratio 4) into the
+    index key pool; state_pool fp32 [n_blocks, state_block, 512]."""
+    dev = kv.device
+    _need(kv, "kv", torch.bfloat16, dev)
+    _need(score, "score", torch.float32, dev)
+    _need(ape, "ape", torch.float32, dev)
+    _need(state_pool, "state_pool", torch.float32, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(cos_sin, "cos_sin", torch.float32, dev)
+    _need(tok_seq, "tok_seq", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(key_pool, "key_pool", torch.uint8, dev)
+    if prequant is not None:
+        _need(prequant, "prequant", torch.float32, dev)
+    _check(lib().slc_compress_index_keys_stream(
+        int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos), _ptr(kv), _ptr(score), _ptr(ape),
+        pool(state_pool, state_table), int(state_block), _ptr(gamma), float(eps), _ptr(cos_sin),
+        int(cos_sin.shape[0]), pool(key_pool, key_table), _ptr(prequant), _stream()))
 
 
 def swa_insert(kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,

@@ -120,3 +120,76 @@ def test_streamed_slots_match_oracle(S, oracle, r, lens, chunk, state_block):
     assert not scl.reshape(-1, 32)[torch.from_numpy(~written)].any()
     print(f"r={r}: {sum(L // r for L in lens)} slots streamed in {len(calls)} calls; "
           f"codes excused near midpoints: {excused}")
+
+
+def test_streamed_index_keys_match_oracle(S, oracle):
+    """The indexer's 128-dim key compressor, streamed as above into the index
+    key pool (KEY layout): per key one scale and 128 codes."""
+    lens, chunk, state_block = [45, 70, 3], 9, 4
+    g = torch.Generator().manual_seed(95)
+    n_seq, T = len(lens), sum(lens)
+    kv = torch.randn((T, 256), generator=g).to(torch.bfloat16)
+    score = torch.randn((T, 256), generator=g)
+    ape = torch.randn((4, 256), generator=g) * 0.5
+    gamma = torch.rand((128,), generator=g) + 0.5
+    cs = I.rope_table(max(lens) + 8)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    ref = [oracle.compress_index_keys_stream_seq(bits16(kv[offs[b]:offs[b + 1]]),
+                                                 score[offs[b]:offs[b + 1]].numpy(), ape.numpy(),
+                                                 gamma.numpy(), 1e-6, cs.numpy())
+           for b in range(n_seq)]
+    dev = "cuda"
+    st_blocks = [list(range(-(-L // state_block))) for L in lens]
+    st_table, n_st = I.block_table(st_blocks, max(len(b) for b in st_blocks), 96, "kst", "cpu")
+    state = torch.zeros((n_st, state_block, 512), dtype=torch.float32, device=dev)
+    k_blocks = [list(range(max(1, -(-(L // 4) // 64)))) for L in lens]
+    k_table, n_kb = I.block_table(k_blocks, max(len(b) for b in k_blocks), 97, "kt", "cpu")
+    key_pool = P.key_pool_empty(n_kb, dev)
+    kv_d, sc_d, ape_d, gm_d, cs_d = (t.to(dev) for t in (kv, score, ape, gamma, cs))
+    calls = [[(b, p) for b in range(n_seq) for p in range(min(chunk, lens[b]))]]
+    for p in range(chunk, max(lens)):
+        calls.append([(b, p) for b in range(n_seq) if p < lens[b]])
+    pre = {}
+    for toks in calls:
+        rows = torch.tensor([offs[b] + p for b, p in toks], dtype=torch.long, device=dev)
+        seq = torch.tensor([b for b, _ in toks], dtype=torch.int32, device=dev)
+        pos = torch.tensor([p for _, p in toks], dtype=torch.int32, device=dev)
+        pq = torch.full((len(toks), 128), float("nan"), device=dev)
+        S.compress_index_keys_stream(seq, pos, kv_d[rows].contiguous(), sc_d[rows].contiguous(),
+                                     ape_d, state, st_table.to(dev), state_block, gm_d, 1e-6,
+                                     cs_d, key_pool, k_table.to(dev), pq)
+        pq = pq.cpu().numpy()
+        for i, (b, p) in enumerate(toks):
+            if (p + 1) % 4 == 0:
+                pre[(b, p // 4)] = pq[i]
+    torch.cuda.synchronize()
+    pool = key_pool.cpu()
+    written = np.zeros(n_kb * 64, bool)
+    excused = 0
+    for b, L in enumerate(lens):
+        n = L // 4
+        if n == 0:
+            continue
+        codes, scales = P.key_pool_get(pool, k_table[b], 0, n)
+        codes, scales = codes.numpy(), scales.numpy()
+        written[(k_table[b].long()[torch.arange(n) // 64] * 64 + torch.arange(n) % 64).numpy()] = True
+        g_pre = np.stack([pre[(b, j)] for j in range(n)])
+        o = ref[b]
+        assert np.max(np.abs(g_pre - o["prequant"])) <= 1e-4 * max(1.0, float(np.max(np.abs(o["prequant"]))))
+        for j in range(n):
+            x = g_pre[j].astype(np.float64)
+            s = pow2_rule(float(np.max(np.abs(x))))
+            assert scales[j] == s
+            want = torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn).view(
+                torch.uint8).numpy()
+            assert np.array_equal(codes[j], want)
+        boundary = near_scale_boundary(np.max(np.abs(o["prequant"]), axis=1))
+        assert np.all((scales == o["scales"]) | boundary)
+        v = o["prequant"] / o["scales"][:, None]
+        diff = codes != o["codes"]
+        assert not np.any(diff & ~(near_midpoint(v) | boundary[:, None]))
+        excused += int(np.sum(diff))
+    c, s = P._key_views(pool)
+    assert not c.reshape(-1, 128)[torch.from_numpy(~written)].any()
+    assert not s.reshape(-1, 4)[torch.from_numpy(~written)].any()
+    print(f"index keys: {sum(L // 4 for L in lens)} streamed; codes excused: {excused}")
