@@ -449,6 +449,22 @@ def main():
         torch.neg(a, out=b)
         torch.cuda.synchronize()
 
+    # practical HBM peak of this GPU: a plain device-to-device copy of 1 GiB
+    # (read + write bytes), outside the timed step
+    src_ = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst_ = torch.empty_like(src_)
+    for _ in range(3):
+        dst_.copy_(src_)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst_.copy_(src_)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_GBps = 2.0 * src_.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src_, dst_
+
     log(f"timed: {ms_step * 1e3:.1f} us/step")
     achieved = INDEX_KERNEL_BYTES / (idx_ms * 1e-3) / 1e9
     rec = {
@@ -476,6 +492,9 @@ def main():
         "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profile(), "algorithmic_bytes": INDEX_KERNEL_BYTES},
+        "practical_peak": {"what": "1 GiB device copy, read + write bytes", "GBps": copy_GBps,
+                           "index_frac": achieved / copy_GBps,
+                           "step_frac": STEP_BYTES / (ms_step * 1e-3) / 1e9 / copy_GBps},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
