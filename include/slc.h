@@ -430,6 +430,18 @@ slc_status_t slc_sparse_mla_prefill(int layer_type, int n_q, int n_heads, const 
                                     float sm_scale, uint16_t *out, float *lse, void *workspace,
                                     size_t ws_bytes, void *stream);
 
+/*
+ * slc_stream_read_probe -- measurement only, not part of the layer: reads
+ * every byte of buf once (16-byte loads, grid-stride over `blocks`
+ * workgroups of 256 threads) and writes one folded word per workgroup to
+ * sink [blocks], so that a caller can time the GPU's practical streaming
+ * read bandwidth beside the published HBM peak.
+ *   buf    device, 16-byte aligned, bytes a multiple of 16
+ *   sink   device uint32 [blocks]
+ */
+slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

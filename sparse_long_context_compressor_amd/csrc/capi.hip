@@ -213,6 +213,17 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
     return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
 }
 
+slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,
+                                   void *stream) {
+    if (!buf || !sink) return fail("stream_read_probe: buf and sink are required");
+    if (bytes % 16 != 0 || !aligned(buf, 16))
+        return fail("stream_read_probe: buf must be 16-byte aligned and bytes a multiple of 16");
+    if (blocks < 1 || blocks > 65536) return fail("stream_read_probe: blocks must be in [1, 65536]");
+    if (bytes == 0) return SLC_OK;
+    return hip_status(launch_stream_read(buf, static_cast<int64_t>(bytes / 16), sink, blocks,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 slc_status_t slc_swa_insert(int n_tok, const uint16_t *kv, const int32_t *tok_seq,
                             const int32_t *tok_pos, const float *cos_sin, int max_pos,
                             slc_pool_t swa_pool, float *prequant_debug, void *stream) {

@@ -27,7 +27,7 @@ EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
-    "slc_compress_index_keys_stream",
+    "slc_compress_index_keys_stream", "slc_stream_read_probe",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -76,6 +76,8 @@ def lib():
         L.slc_compress_index_keys_stream.restype = i32
         L.slc_compress_index_keys_stream.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32,
                                                      vp, i32, pool, vp, vp]
+        L.slc_stream_read_probe.restype = i32
+        L.slc_stream_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.slc_swa_insert.restype = i32
         L.slc_swa_insert.argtypes = [i32, vp, vp, vp, vp, i32, pool, vp, vp]
         L.slc_indexcache_skips.restype = i32
@@ -201,6 +203,13 @@ def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, sta
         int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos), _ptr(kv), _ptr(score), _ptr(ape),
         pool(state_pool, state_table), int(state_block), _ptr(gamma), float(eps), _ptr(cos_sin),
         int(cos_sin.shape[0]), pool(key_pool, key_table), _ptr(prequant), _stream()))
+
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of buf once (measurement of the streaming read rate);
+    sink: uint32-sized int32 [blocks] on the same device."""
+    _check(lib().slc_stream_read_probe(_ptr(buf), int(buf.numel() * buf.element_size()),
+                                       _ptr(sink), int(sink.numel()), _stream()))
 
 
 def swa_insert(kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
