@@ -165,6 +165,23 @@ def test_index_scores_and_topk_match_oracle(S, oracle, h_idx):
     print(f"h_idx={h_idx}: near-tie slots excluded: {near}")
 
 
+def test_index_topk_at_the_maxima(S, oracle):
+    """64 index heads and k = 4096 (the ABI's maxima), with lists longer and
+    shorter than k."""
+    lay = I.build_layer(21, ratio=4, H=16, ctx=[40000, 12000],
+                        queries=[(0, 39999), (1, 11999), (0, 16383)], n_slots=[10000, 3000],
+                        W=16, k=4096, H_I=64)
+    idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay)
+    to_device(lay)
+    sc, idx, ln = gpu_index_topk(S, lay)
+    torch.cuda.synchronize()
+    sc, idx, ln = sc.cpu().numpy(), idx.cpu().numpy(), ln.cpu().numpy()
+    nv = nvis_of(lay, 4)
+    assert np.array_equal(ln, len_ref) and list(ln) == [4096, 3000, 4096]
+    check_topk_sets(idx, ln, sc_ref, nv, lay.k)
+    assert np.array_equal(idx, exact_topk_of(sc, nv, lay.k))
+
+
 @pytest.mark.parametrize("H", [16, 48])
 def test_topk_select_warm_equals_select(S, oracle, H):
     """The select with the decode's L2 warm-up (extra read-only workgroups) gives
@@ -300,6 +317,10 @@ ATTN_CASES = {
                           W=128, k=256, given_topk=True),
     "c4a_given_h48": dict(ratio=4, H=48, ctx=[4000], queries=[(0, 3999)], n_slots=[1000], W=64,
                           k=77, given_topk=True),
+    # the ABI's maxima: 128 heads, a 1024-row window, a 4096-entry list
+    "c4a_max_h128_w1024_k4096": dict(ratio=4, H=128, ctx=[20000, 1500],
+                                     queries=[(0, 19999), (1, 1499)], n_slots=[5000, 375],
+                                     W=1024, k=4096, given_topk=True),
 }
 
 
