@@ -54,3 +54,76 @@ def test_graph_replays_match_eager():
         for a, b in zip(ref, got):
             assert torch.equal(a, b), f"replay {r} differs"
         assert torch.isfinite(junk)
+
+
+def test_graph_of_a_serving_step_with_the_streaming_calls():
+    """A decode step with the per-step writers captured too: the new tokens'
+    SWA rows inserted into an fp8 pool, the streaming compressor's state save
+    and emission, then index, warm select and decode over the fp8 pool.  The
+    writers rewrite the same rows on every replay, so each replay must give
+    the eager results bit for bit."""
+    from sparse_long_context_compressor_amd import slc
+    from sparse_long_context_compressor_amd import pools as P
+    lay = I.build_layer(22, ratio=4, H=64, ctx=[8000] * 4, queries=[(b, 7999) for b in range(4)],
+                        n_slots=[2000] * 4, W=128, k=256, H_I=32, swa_fp8=True)
+    to_device(lay)
+    dev = lay.q.device
+    g = torch.Generator(device="cpu").manual_seed(5)
+    n = lay.n_q
+    new_kv = torch.randn((n, 576), generator=g).to(torch.bfloat16).to(dev)
+    kv2 = torch.randn((n, 1152), generator=g).to(torch.bfloat16).to(dev)
+    sc2 = torch.randn((n, 1152), generator=g).to(dev)
+    ape = (torch.randn((4, 1152), generator=g) * 0.5).to(dev)
+    gamma = torch.ones(576, device=dev)
+    cs = I.rope_table(8000, device=dev)
+    # state rows for positions 7992..7999 of every sequence (block of 4 rows)
+    st_table = torch.full((n, 2000), -1, dtype=torch.int32)
+    for b in range(n):
+        st_table[b, 1998], st_table[b, 1999] = 2 * b, 2 * b + 1
+    st_table = st_table.to(dev)
+    state = torch.zeros((2 * n, 4, 2304), dtype=torch.float32, device=dev)
+    c_pool = P.cmp_pool_empty(lay.cmp_blocks, dev)
+    pos = lay.q_pos.clone()
+    ms = lay.max_slots
+    sc = torch.empty((n, ms), dtype=torch.float32, device=dev)
+    idx = torch.empty((n, lay.k), dtype=torch.int32, device=dev)
+    ln = torch.empty(n, dtype=torch.int32, device=dev)
+    out = torch.empty((n, lay.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n, lay.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(slc.sparse_mla_workspace_size(True, n, lay.H, lay.W, lay.k), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        slc.swa_insert(new_kv, lay.q_seq, pos, cs, lay.swa_pool, lay.swa_table)
+        slc.compress_stream(4, lay.q_seq, pos, kv2, sc2, ape, state, st_table, 4, gamma, 1e-6, cs,
+                            c_pool, lay.cmp_table)
+        slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
+                         lay.key_table, lay.n_slots, ms, sc)
+        slc.topk_select_warm(lay.k, sc, ms, lay.q_seq, lay.q_pos, 4 | slc.SWA_FP8, lay.n_slots,
+                             idx, ln, lay.q, lay.W, lay.swa_pool, lay.swa_table)
+        slc.sparse_mla_decode(4 | slc.SWA_FP8, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool,
+                              lay.swa_table, lay.cmp_pool, lay.cmp_table, idx, lay.n_slots,
+                              lay.sm_scale, out, lse, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, ln, out.view(torch.int16), lse, c_pool, lay.swa_pool)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        for t in (idx, ln, out, lse, c_pool):
+            t.zero_()
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (idx, ln, out.view(torch.int16), lse, c_pool, lay.swa_pool)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {r} differs"
+        assert torch.isfinite(junk)
+    assert c_pool.any()                     # the emitting tokens (p = 7999) wrote their slots
