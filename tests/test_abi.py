@@ -133,3 +133,43 @@ def test_indexcache_skips_match_the_oracle(S, oracle):
         S.indexcache_skips([4, 4], 2, "SF")
     with pytest.raises(S.SlcError):
         S.indexcache_skips([4, 4], 2, "FX")
+
+
+def test_invalid_arguments_of_the_next_rows_are_rejected(S):
+    """The fp8 SWA insert, the streaming compressors, the MXFP4 flag and the
+    read probe validate on the host, before any launch."""
+    L = S.lib()
+    P = _null_pool(S)
+    fake = C.c_void_p(256)
+    pool = S.Pool(C.c_void_p(256), C.c_void_p(256), 4, 4)
+    # SWA insert: no destination pool; misaligned kv; nothing to do is fine
+    assert L.slc_swa_insert(2, fake, fake, fake, fake, 16, P, None, None) == 1
+    assert L.slc_swa_insert(2, C.c_void_p(258), fake, fake, fake, 16, pool, None, None) == 1
+    assert L.slc_swa_insert(0, None, None, None, None, 16, P, None, None) == 0
+    # streaming compressor: ratio, state block size, missing pools
+    a = [1, fake, fake, fake, fake, fake, pool, 4, fake, 1e-6, fake, 16, pool, None, None]
+    assert L.slc_compress_stream(3, *a) == 1 and b"ratio" in L.slc_last_error()
+    b = list(a)
+    b[7] = 0
+    assert L.slc_compress_stream(4, *b) == 1 and b"state_block" in L.slc_last_error()
+    c = list(a)
+    c[6] = P
+    assert L.slc_compress_stream(4, *c) == 1 and b"state_pool" in L.slc_last_error()
+    d = list(a)
+    d[12] = P
+    assert L.slc_compress_stream(128, *d) == 1 and b"cmp_pool" in L.slc_last_error()
+    e = [1, fake, fake, fake, fake, fake, pool, 4, fake, 1e-6, fake, 16, P, None, None]
+    assert L.slc_compress_index_keys_stream(*e) == 1 and b"key_pool" in L.slc_last_error()
+    f = list(e)
+    f[9] = -1.0
+    assert L.slc_compress_index_keys_stream(*f) == 1 and b"eps" in L.slc_last_error()
+    # the MXFP4 flag does not make an invalid ratio valid; the SWA flag on a
+    # layer type that does not exist is rejected
+    assert L.slc_index_scores(1, 16, fake, fake, fake, fake, fake, 3 | S.KEY_MXFP4, P, fake, 16,
+                              fake, None) == 1
+    args = [1, 64, fake, fake, fake, 128, P, P, None, 0, None, 0.1, fake, None, None, 0, None]
+    assert L.slc_sparse_mla_decode(2 | S.SWA_FP8, *args) == 1
+    # the probe: misaligned buffer, odd size, no sink
+    assert L.slc_stream_read_probe(C.c_void_p(258), 16, fake, 4, None) == 1
+    assert L.slc_stream_read_probe(fake, 17, fake, 4, None) == 1
+    assert L.slc_stream_read_probe(fake, 16, None, 4, None) == 1
