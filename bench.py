@@ -100,11 +100,11 @@ def _short(name: str) -> str:
     return name.replace("void ", "").strip()
 
 
-def report_stats(trace_dir: str, out_md: str, cmds):
+def report_stats(trace_dir: str, out_md: str, cmds, workload: str = "c4a_decode_64k"):
     """Kernel-time summary of one rocprofv3 --kernel-trace --stats run."""
     rows = _csv_rows(trace_dir, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = ["# Kernel time, c4a_decode_64k benchmark (rocprofv3 kernel trace)", "",
+    lines = [f"# Kernel time, {workload} benchmark (rocprofv3 kernel trace)", "",
              "Made by:", ""] + [f"    {c}" for c in cmds] + [
         "", "| kernel | calls | avg us | min us | max us | share of GPU time |",
         "|---|---:|---:|---:|---:|---:|"]
@@ -328,7 +328,7 @@ def other_workload(args):
 def main():
     args = parse()
     if args.report_stats:
-        return report_stats(*args.report_stats, args.cmd)
+        return report_stats(*args.report_stats, args.cmd, args.workload)
     if args.report_counters:
         return report_counters(*args.report_counters, args.calib_copy_mib, args.cmd)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
