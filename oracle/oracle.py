@@ -17,7 +17,7 @@ __all__ = [
     "pow2_scale", "n_slots", "n_visible", "window", "compress_seq", "compress_batch",
     "compress_stream_seq", "compress_index_keys_stream_seq",
     "index_scores", "topk", "index_topk_batch", "sparse_mla", "sparse_mla_batch",
-    "swa_insert", "swa_dequant", "e2m1_value", "e8m0_value", "index_scores_mxfp4",
+    "swa_insert", "swa_dequant", "e2m1_value", "e8m0_value", "mxfp4_quantise", "index_scores_mxfp4",
     "index_topk_batch_mxfp4", "indexcache_skips", "num_threads",
 ]
 
@@ -80,6 +80,7 @@ def _declare(L):
         "oracle_compress_stream_seq": (i32, [i32, i32, _P, _P, _P, _P, dbl, _P, i32, _P, _P, _P,
                                              _P]),
         "oracle_e2m1_value": (dbl, [C.c_uint8]),
+        "oracle_mxfp4_quantise": (None, [i32, _P, _P, _P]),
         "oracle_e8m0_value": (dbl, [C.c_uint8]),
         "oracle_index_scores_mxfp4": (None, [i32, i32, _P, _P, _P, _P, _P, _P, _P]),
         "oracle_index_topk_batch_mxfp4": (None, [i32, i32, i32, _P, _P, _P, _P, _P, i32, _P,
@@ -293,6 +294,17 @@ def e2m1_value(nibble: int) -> float:
 
 def e8m0_value(b: int) -> float:
     return lib().oracle_e8m0_value(int(b))
+
+
+def mxfp4_quantise(y):
+    """y [n,128] f32 -> (codes4 [n,64] u8, e8m0 [n,4] u8): per 32-dim block the
+    smallest 2^e with amax <= 6 * 2^e, nearest e2m1 codes (ties to even)."""
+    v = _c(y, np.float32).reshape(-1, DI)
+    n = v.shape[0]
+    c4 = np.zeros((n, DI // 2), np.uint8)
+    e8 = np.zeros((n, DI // 32), np.uint8)
+    lib().oracle_mxfp4_quantise(n, _p(v), _p(c4), _p(e8))
+    return c4, e8
 
 
 def index_scores_mxfp4(q_codes, q_scale, w, keys4, key_e8m0):

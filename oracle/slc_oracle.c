@@ -544,6 +544,58 @@ double oracle_e2m1_value(uint8_t nibble)
     return sign ? -mag : mag;
 }
 
+/* Nearest e2m1 code of x, ties to the even code; magnitudes above 6 take 6. */
+static uint8_t e2m1_encode(double x)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double a = fabs(x);
+    int best = 0;
+    for (int c = 1; c < 8; c++) {
+        double dc = fabs(a - mag[c]), db = fabs(a - mag[best]);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return (uint8_t)(best | (x < 0.0 ? 8 : 0));
+}
+
+/*
+ * MXFP4 quantisation of index keys [P5 6.1: the FP4 / MXFP4 indexer K cache;
+ * the OCP MX element and scale formats]: per 32-dim block, the scale is the
+ * smallest 2^e with amax <= 6 * 2^e (1 if amax = 0; the same rule as the
+ * fp8 rows with e2m1's largest magnitude 6), stored as the E8M0 byte e + 127,
+ * and each element becomes the nearest e2m1 code of y / 2^e (ties to even),
+ * two per byte with the even element in the low nibble.
+ *   y [n, 128] fp32 -> codes4 [n, 64], e8m0 [n, 4].
+ */
+void oracle_mxfp4_quantise(int n, const float *y, uint8_t *codes4, uint8_t *e8m0)
+{
+    for (int s = 0; s < n; s++) {
+        for (int b = 0; b < OR_DI / 32; b++) {
+            double amax = 0.0, scale;
+            int e = 0;
+            for (int i = 0; i < 32; i++) {
+                double a = fabs((double)y[(size_t)s * OR_DI + 32 * b + i]);
+                if (a > amax)
+                    amax = a;
+            }
+            if (amax > 0.0) {
+                frexp(amax / 6.0, &e);
+                while (amax <= ldexp(6.0, e - 1))
+                    e--;
+                while (amax > ldexp(6.0, e))
+                    e++;
+            }
+            scale = ldexp(1.0, e);
+            e8m0[(size_t)s * 4 + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; i += 2) {
+                uint8_t lo = e2m1_encode((double)y[(size_t)s * OR_DI + 32 * b + i] / scale);
+                uint8_t hi = e2m1_encode((double)y[(size_t)s * OR_DI + 32 * b + i + 1] / scale);
+                codes4[(size_t)s * (OR_DI / 2) + 16 * b + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
 /* OCP E8M0 block scale: 2^(byte - 127); 255 is NaN. */
 double oracle_e8m0_value(uint8_t b)
 {

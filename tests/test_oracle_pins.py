@@ -839,3 +839,53 @@ def test_index_key_compressor_against_the_latent_compressor(oracle):
         want = torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn).view(
             torch.uint8).numpy()
         assert np.array_equal(ix["codes"][j], want)
+
+
+def _scale6_exact(amax):
+    """Smallest power of two s with amax <= 6 s (exact rational search)."""
+    a = Fraction(amax)
+    if a == 0:
+        return 0
+    e = 0
+    while a > 6 * Fraction(2) ** e:
+        e += 1
+    while a <= 6 * Fraction(2) ** (e - 1):
+        e -= 1
+    return e
+
+
+def test_mxfp4_quantiser(oracle):
+    """Per 32-dim block: the exact scale rule (amax <= 6 * 2^e, smallest e),
+    the nearest e2m1 magnitude by brute force with ties to the even code,
+    the even element in the low nibble, and exact round trips of values that
+    are already e2m1 * 2^e."""
+    g = np.random.default_rng(80)
+    y = (g.normal(0, 1, (40, 128)) * np.repeat(np.exp(g.normal(0, 2, (40, 4))), 32, axis=1)).astype(np.float32)
+    c4, e8 = oracle.mxfp4_quantise(y)
+    mags = np.array(E2M1_MAGNITUDES)
+    for s in range(40):
+        for b in range(4):
+            blk = y[s, 32 * b: 32 * b + 32].astype(np.float64)
+            e = _scale6_exact(float(np.max(np.abs(blk))))
+            assert e8[s, b] == e + 127
+    vals = _unpack_e2m1(c4)
+    deq = vals * np.repeat(np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=1)
+    for s in range(40):
+        for b in range(4):
+            blk = y[s, 32 * b: 32 * b + 32].astype(np.float64)
+            e = int(e8[s, b]) - 127
+            v = blk / 2.0 ** e
+            d = np.abs(np.abs(v)[:, None] - mags[None, :])
+            best = np.argmin(d + 1e-12 * (np.arange(8) % 2)[None, :], axis=1)   # ties -> even code
+            assert np.array_equal(np.abs(vals[s, 32 * b: 32 * b + 32]), mags[best])
+            assert np.all((vals[s, 32 * b: 32 * b + 32] < 0) <= (blk < 0))
+    assert np.all(np.abs(deq - y) <= np.repeat(np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=1))
+    # exact representatives round-trip, and the midpoints go to the even code
+    ex = np.zeros((2, 128), np.float32)
+    ex[0] = np.resize(np.array([6, -4, 3, 1.5, -0.5, 0, 2, 1], np.float32), 128) * 0.125
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    ex[1] = np.resize(mids, 128)
+    c, e = oracle.mxfp4_quantise(ex)
+    assert np.array_equal(_unpack_e2m1(c)[0] * 0.125, ex[0]) and np.all(e[0] == 127 - 3)
+    assert np.all(e[1] == 127)
+    assert np.array_equal(_unpack_e2m1(c)[1][:8], np.array([0, 1, 1, 2, 2, 4, 4, 6], np.float64))
