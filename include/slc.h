@@ -239,7 +239,11 @@ slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
  *   one scale for the key (smallest 2^e with amax <= 448*2^e, 1 if amax = 0)
  *   and e4m3 codes of y / scale,
  * stored at slot j of its sequence in key_pool (KEY layout), the index keys
- * slc_index_scores reads.
+ * slc_index_scores reads.  With key_flags = SLC_KEY_MXFP4 the key is written
+ * as MXFP4 into a KEY4 pool instead: per 32-dim block the smallest 2^e with
+ * amax <= 6 * 2^e (E8M0 byte e + 127) and the nearest e2m1 code of y / 2^e,
+ * ties to the even code.
+ *   key_flags    0 (fp8 keys) or SLC_KEY_MXFP4
  *   gamma        device fp32 [128], 16-byte aligned
  *   prequant     nullable device fp32 [n_tok][128] (debug)
  * Other arguments as for slc_compress_stream.
@@ -249,8 +253,8 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
                                             const float *score, const float *ape,
                                             slc_pool_t state_pool, int state_block,
                                             const float *gamma, float eps, const float *cos_sin,
-                                            int max_pos, slc_pool_t key_pool, float *prequant,
-                                            void *stream);
+                                            int max_pos, int key_flags, slc_pool_t key_pool,
+                                            float *prequant, void *stream);
 
 /*
  * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J

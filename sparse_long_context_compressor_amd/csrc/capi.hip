@@ -187,9 +187,11 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
                                             const float *score, const float *ape,
                                             slc_pool_t state_pool, int state_block,
                                             const float *gamma, float eps, const float *cos_sin,
-                                            int max_pos, slc_pool_t key_pool, float *prequant,
-                                            void *stream) {
+                                            int max_pos, int key_flags, slc_pool_t key_pool,
+                                            float *prequant, void *stream) {
     if (n_tok < 0) return fail("compress_index_keys_stream: n_tok must be >= 0");
+    if (key_flags != 0 && key_flags != SLC_KEY_MXFP4)
+        return fail("compress_index_keys_stream: key_flags must be 0 or SLC_KEY_MXFP4");
     if (state_block < 1 || state_block > 1024)
         return fail("compress_index_keys_stream: state_block must be in [1, 1024]");
     if (!(eps >= 0.f) || !std::isfinite(eps))
@@ -209,7 +211,8 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
     st = check_pool(key_pool, "compress_index_keys_stream: key_pool");
     if (st != SLC_OK) return st;
     StreamArgs a{4, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool, state_block,
-                 gamma, eps, cos_sin, max_pos, key_pool, prequant, kDI};
+                 gamma, eps, cos_sin, max_pos, key_pool, prequant, kDI,
+                 key_flags == SLC_KEY_MXFP4 ? 1 : 0};
     return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
 }
 

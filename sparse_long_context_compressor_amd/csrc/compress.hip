@@ -115,6 +115,27 @@ __device__ __forceinline__ void quant_store(const float (&y)[9], int lane, slc_p
     if ((lane & 7) == 0) cmp_scale_ptr(pool, row)[lane >> 3] = ldexpf(1.f, e);
 }
 
+// Smallest e with amax <= 6 * 2^e (e2m1's largest magnitude); 0 for amax == 0.
+__device__ __forceinline__ int pow2_exponent_e2m1(float amax) {
+    if (!(amax > 0.f)) return 0;
+    int ex;
+    frexpf(amax, &ex);            // amax = f * 2^ex, f in [0.5, 1); 6 = 0.75 * 2^3
+    int e = ex - 3;
+    while (amax > ldexpf(6.f, e)) e++;
+    while (amax <= ldexpf(6.f, e - 1)) e--;
+    return e;
+}
+
+// Nearest e2m1 code of x (|x| <= 6 by the caller's scale), ties to the even
+// code: the thresholds are the midpoints between adjacent magnitudes 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6, taken with > where the lower code is even.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+    const float m = fabsf(x);
+    const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                       (m >= 3.5f) + (m > 5.f);
+    return c | (x < 0.f ? 8u : 0u);
+}
+
 // RMSNorm, RoPE, quantise and store one pooled slot held by one wave.
 // prequant rows: at the slot's physical row (pq_index < 0) or at pq_index.
 __device__ __forceinline__ void finish_slot(const float (&pooled)[9], int lane, int seq, int slot,
@@ -424,6 +445,23 @@ __global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
     if (row < 0) return;
     if (a.prequant)
         *reinterpret_cast<f32x2 *>(a.prequant + static_cast<int64_t>(t) * kDI + 2 * lane) = f32x2{y[0], y[1]};
+    if (a.key_fp4) {
+        // MXFP4: block b = lanes 16b .. 16b+15 (dims 32b .. 32b+31); byte l of
+        // the key holds dims 2l (low nibble) and 2l+1
+        float bmax = fmaxf(fabsf(y[0]), fabsf(y[1]));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 1, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 2, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 4, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 8, 64));
+        const int e = pow2_exponent_e2m1(bmax);
+        const float inv_scale = ldexpf(1.f, -e);
+        const uint32_t byte = e2m1_code(y[0] * inv_scale) | (e2m1_code(y[1] * inv_scale) << 4);
+        uint8_t *base = reinterpret_cast<uint8_t *>(a.pool.base) + (row / kBR) * SLC_KEY4_BLOCK_BYTES;
+        base[(row % kBR) * (kDI / 2) + lane] = static_cast<uint8_t>(byte);
+        if ((lane & 15) == 0)
+            base[SLC_KEY4_SCALE_OFFSET + (row % kBR) * 4 + (lane >> 4)] = static_cast<uint8_t>(e + 127);
+        return;
+    }
     const float amax = wave_max(fmaxf(fabsf(y[0]), fabsf(y[1])));
     const int e = pow2_exponent(amax);
     const float inv_scale = ldexpf(1.f, -e);

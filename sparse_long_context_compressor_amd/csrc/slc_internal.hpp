@@ -55,6 +55,7 @@ struct StreamArgs {
     slc_pool_t pool;            // compressed pool (CMP layout; KEY layout for dim 128)
     float *prequant;            // nullable [n_tok][dim], rows of emitting tokens
     int dim;                    // 576 (latent rows) or 128 (index keys, ratio 4)
+    int key_fp4;                // index keys: MXFP4 into a KEY4 pool instead of fp8
 };
 
 struct IndexArgs {

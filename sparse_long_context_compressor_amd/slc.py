@@ -75,7 +75,7 @@ def lib():
                                           i32, pool, vp, vp]
         L.slc_compress_index_keys_stream.restype = i32
         L.slc_compress_index_keys_stream.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32,
-                                                     vp, i32, pool, vp, vp]
+                                                     vp, i32, i32, pool, vp, vp]
         L.slc_stream_read_probe.restype = i32
         L.slc_stream_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.slc_swa_insert.restype = i32
@@ -184,9 +184,10 @@ def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv
 
 def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, state_table,
                                state_block: int, gamma, eps: float, cos_sin, key_pool,
-                               key_table, prequant=None) -> None:
+                               key_table, prequant=None, mxfp4: bool = False) -> None:
     """One step of the indexer's 128-dim key compressor (ratio 4) into the
-    index key pool; state_pool fp32 [n_blocks, state_block, 512]."""
+    index key pool (a KEY4 pool of MXFP4 keys with mxfp4=True); state_pool
+    fp32 [n_blocks, state_block, 512]."""
     dev = kv.device
     _need(kv, "kv", torch.bfloat16, dev)
     _need(score, "score", torch.float32, dev)
@@ -202,7 +203,8 @@ def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, sta
     _check(lib().slc_compress_index_keys_stream(
         int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos), _ptr(kv), _ptr(score), _ptr(ape),
         pool(state_pool, state_table), int(state_block), _ptr(gamma), float(eps), _ptr(cos_sin),
-        int(cos_sin.shape[0]), pool(key_pool, key_table), _ptr(prequant), _stream()))
+        int(cos_sin.shape[0]), KEY_MXFP4 if mxfp4 else 0, pool(key_pool, key_table),
+        _ptr(prequant), _stream()))
 
 
 def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:

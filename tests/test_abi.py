@@ -158,11 +158,14 @@ def test_invalid_arguments_of_the_next_rows_are_rejected(S):
     d = list(a)
     d[12] = P
     assert L.slc_compress_stream(128, *d) == 1 and b"cmp_pool" in L.slc_last_error()
-    e = [1, fake, fake, fake, fake, fake, pool, 4, fake, 1e-6, fake, 16, P, None, None]
+    e = [1, fake, fake, fake, fake, fake, pool, 4, fake, 1e-6, fake, 16, 0, P, None, None]
     assert L.slc_compress_index_keys_stream(*e) == 1 and b"key_pool" in L.slc_last_error()
     f = list(e)
     f[9] = -1.0
     assert L.slc_compress_index_keys_stream(*f) == 1 and b"eps" in L.slc_last_error()
+    h = list(e)
+    h[12] = 3
+    assert L.slc_compress_index_keys_stream(*h) == 1 and b"key_flags" in L.slc_last_error()
     # the MXFP4 flag does not make an invalid ratio valid; the SWA flag on a
     # layer type that does not exist is rejected
     assert L.slc_index_scores(1, 16, fake, fake, fake, fake, fake, 3 | S.KEY_MXFP4, P, fake, 16,

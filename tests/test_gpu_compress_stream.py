@@ -122,9 +122,16 @@ def test_streamed_slots_match_oracle(S, oracle, r, lens, chunk, state_block):
           f"codes excused near midpoints: {excused}")
 
 
-def test_streamed_index_keys_match_oracle(S, oracle):
+E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+@pytest.mark.parametrize("mxfp4", [False, True], ids=["fp8_keys", "mxfp4_keys"])
+def test_streamed_index_keys_match_oracle(S, oracle, mxfp4):
     """The indexer's 128-dim key compressor, streamed as above into the index
-    key pool (KEY layout): per key one scale and 128 codes."""
+    key pool: fp8 keys (KEY layout: one scale and 128 codes per key) or MXFP4
+    keys (KEY4 layout), the latter judged like the fp8 codes: the kernel's
+    codes are the oracle quantiser applied to its own rows, and equal to the
+    oracle's except near an e2m1 midpoint or a scale boundary."""
     lens, chunk, state_block = [45, 70, 3], 9, 4
     g = torch.Generator().manual_seed(95)
     n_seq, T = len(lens), sum(lens)
@@ -144,7 +151,7 @@ def test_streamed_index_keys_match_oracle(S, oracle):
     state = torch.zeros((n_st, state_block, 512), dtype=torch.float32, device=dev)
     k_blocks = [list(range(max(1, -(-(L // 4) // 64)))) for L in lens]
     k_table, n_kb = I.block_table(k_blocks, max(len(b) for b in k_blocks), 97, "kt", "cpu")
-    key_pool = P.key_pool_empty(n_kb, dev)
+    key_pool = (P.key4_pool_empty if mxfp4 else P.key_pool_empty)(n_kb, dev)
     kv_d, sc_d, ape_d, gm_d, cs_d = (t.to(dev) for t in (kv, score, ape, gamma, cs))
     calls = [[(b, p) for b in range(n_seq) for p in range(min(chunk, lens[b]))]]
     for p in range(chunk, max(lens)):
@@ -157,7 +164,7 @@ def test_streamed_index_keys_match_oracle(S, oracle):
         pq = torch.full((len(toks), 128), float("nan"), device=dev)
         S.compress_index_keys_stream(seq, pos, kv_d[rows].contiguous(), sc_d[rows].contiguous(),
                                      ape_d, state, st_table.to(dev), state_block, gm_d, 1e-6,
-                                     cs_d, key_pool, k_table.to(dev), pq)
+                                     cs_d, key_pool, k_table.to(dev), pq, mxfp4=mxfp4)
         pq = pq.cpu().numpy()
         for i, (b, p) in enumerate(toks):
             if (p + 1) % 4 == 0:
@@ -169,6 +176,29 @@ def test_streamed_index_keys_match_oracle(S, oracle):
     for b, L in enumerate(lens):
         n = L // 4
         if n == 0:
+            continue
+        if mxfp4:
+            c4, e8 = P.key4_pool_get(pool, k_table[b], 0, n)
+            c4, e8 = c4.numpy(), e8.numpy()
+            written[(k_table[b].long()[torch.arange(n) // 64] * 64 + torch.arange(n) % 64).numpy()] = True
+            g_pre = np.stack([pre[(b, j)] for j in range(n)])
+            o = ref[b]
+            assert np.max(np.abs(g_pre - o["prequant"])) <= 1e-4 * max(1.0, float(np.max(np.abs(o["prequant"]))))
+            own_c4, own_e8 = oracle.mxfp4_quantise(g_pre)
+            assert np.array_equal(c4, own_c4) and np.array_equal(e8, own_e8)
+            ref_c4, ref_e8 = oracle.mxfp4_quantise(o["prequant"])
+            bmax = np.max(np.abs(o["prequant"].reshape(n, 4, 32)), axis=2).astype(np.float64)
+            eb = np.round(np.log2(np.maximum(bmax, 1e-300) / 6.0))
+            boundary = np.abs(bmax - 6.0 * np.exp2(eb)) <= 1e-5 * bmax
+            assert np.all((e8 == ref_e8) | boundary)
+            v = np.abs(o["prequant"].reshape(n, 4, 32).astype(np.float64)) / \
+                np.exp2(ref_e8.astype(np.float64) - 127)[:, :, None]
+            near = np.min(np.abs(v[..., None] - E2M1_MIDS), axis=-1) <= 1e-5 * np.maximum(v, 1e-30)
+            lo = np.stack([c4 & 15, c4 >> 4], -1).reshape(n, 4, 32)
+            rlo = np.stack([ref_c4 & 15, ref_c4 >> 4], -1).reshape(n, 4, 32)
+            diff = lo != rlo
+            assert not np.any(diff & ~(near | boundary[:, :, None]))
+            excused += int(np.sum(diff))
             continue
         codes, scales = P.key_pool_get(pool, k_table[b], 0, n)
         codes, scales = codes.numpy(), scales.numpy()
@@ -189,7 +219,7 @@ def test_streamed_index_keys_match_oracle(S, oracle):
         diff = codes != o["codes"]
         assert not np.any(diff & ~(near_midpoint(v) | boundary[:, None]))
         excused += int(np.sum(diff))
-    c, s = P._key_views(pool)
-    assert not c.reshape(-1, 128)[torch.from_numpy(~written)].any()
+    c, s = (P._key4_views if mxfp4 else P._key_views)(pool)
+    assert not c.reshape(-1, c.shape[-1])[torch.from_numpy(~written)].any()
     assert not s.reshape(-1, 4)[torch.from_numpy(~written)].any()
     print(f"index keys: {sum(L // 4 for L in lens)} streamed; codes excused: {excused}")
