@@ -184,8 +184,16 @@ def cpu_baseline(n_q: int):
         oracle_attention(O, lay, idx)
         passes += 1
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": passes * n_q / dt, "unit": "queries/s", "cores": int(O.num_threads()),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{passes} passes over {n_q} of the 32 sequences (one query each, same "
                       f"shapes: 16384 slots, H_I=64, k=512, H=64, SWA 128), index top-k + "
                       f"attention, {dt:.2f} s wall"}
