@@ -340,8 +340,9 @@ def main():
     if args.report_counters:
         return report_counters(*args.report_counters, args.calib_copy_mib, args.cmd)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU (the decode path shards by sequence with "
-              "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path shards by sequence with no exchange "
+              "between GPUs, so one GPU's share at the real shape is the measurement. "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.workload != "c4a_decode_64k":
