@@ -28,12 +28,15 @@
  *       mapping: valid iff (pos+1) % r == 0, slot = pos // r), Ch.2 MLA
  *       (absorbed MQA over the 576-wide latent, values = first 512 dims).
  *
- * Readings taken where the pages are silent or disagree (each is listed in
- * the design notes): slots are ceil(L/r) with a trailing partial slot pooled
+ * Readings taken where the pages are silent or disagree: slots are
+ * ceil(L/r) with a trailing partial slot pooled
  * over the tokens present; softmax is per channel over the window's tokens;
  * RMSNorm runs over all 576 latent dims; the pow2 scale is the smallest 2^e
  * with amax <= 448 * 2^e (exact comparison), stored as fp32; fp8 is OCP
- * E4M3FN with round-to-nearest-even; top-k ties go to the lower slot index.
+ * E4M3FN with round-to-nearest-even; top-k ties go to the lower slot index;
+ * the streaming compressor's older token group brings block 0 (C_a) and the
+ * newer block 1 (C_b); MXFP4 keys put the even element in the low nibble and
+ * scale each 32-dim block by the smallest 2^e with amax <= 6 * 2^e.
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py
  * (closed forms, worked examples from the pages, library routines for the
