@@ -53,7 +53,8 @@ def parse():
                     choices=["c4a_decode_64k", "c4a_prefill_2k", "c128a_decode_128k",
                              "swaonly_decode_b64", "c4a_single_layer_4k",
                              "c4a_decode_64k_stages", "c4a_decode_64k_fp8swa",
-                             "c4a_decode_64k_fp4keys", "c4a_decode_64k_fp8swa_fp4keys"],
+                             "c4a_decode_64k_fp4keys", "c4a_decode_64k_fp8swa_fp4keys",
+                             "c4a_compress_stream_b32"],
                     help="c4a_decode_64k is the headline; the others print supplementary "
                          "per-stage timings of the same kernels on the other workloads")
     ap.add_argument("--report-stats", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
@@ -333,6 +334,83 @@ def other_workload(args):
     print(json.dumps(rec), flush=True)
 
 
+def compress_stream_workload(args):
+    """The streaming compressor in a C4A decode: 32 sequences at 64K context,
+    one new token each per step (positions 65532..65535 cycle, so one step in
+    four emits a slot); per step the latent compressor and the indexer's key
+    compressor, both with 4-row state blocks, one launch each (one token per
+    sequence per call).  One JSON line."""
+    import torch
+    from sparse_long_context_compressor_amd import inputs as I
+    from sparse_long_context_compressor_amd import pools as P
+    from sparse_long_context_compressor_amd import slc
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    slc.lib()
+    n, ctx = 32, 65536
+    g = torch.Generator().manual_seed(7)
+    kv = torch.randn((4, n, 1152), generator=g).to(torch.bfloat16).to(dev)
+    sc = torch.randn((4, n, 1152), generator=g).to(dev)
+    kv_i = torch.randn((4, n, 256), generator=g).to(torch.bfloat16).to(dev)
+    sc_i = torch.randn((4, n, 256), generator=g).to(dev)
+    ape = torch.randn((4, 1152), generator=g).to(dev)
+    ape_i = torch.randn((4, 256), generator=g).to(dev)
+    gamma, gamma_i = torch.ones(576, device=dev), torch.ones(128, device=dev)
+    cs = I.rope_table(ctx, device=dev)
+    blocks = ctx // 4
+    st_table, n_st = I.block_table([list(range(blocks - 2, blocks))] * n, blocks, 8, "st", dev)
+    state = torch.zeros((n_st, 4, 2304), device=dev)
+    state_i = torch.zeros((n_st, 4, 512), device=dev)
+    c_table, n_cb = I.block_table([list(range(256))] * n, 256, 9, "ct", dev)
+    cmp_pool = P.cmp_pool_empty(n_cb, dev)
+    key_pool = P.key_pool_empty(n_cb, dev)
+    seq = torch.arange(n, dtype=torch.int32, device=dev)
+    pos = [torch.full((n,), ctx - 4 + i, dtype=torch.int32, device=dev) for i in range(4)]
+
+    def step(i):
+        j = i % 4
+        slc.compress_stream(4, seq, pos[j], kv[j], sc[j], ape, state, st_table, 4, gamma, 1e-6,
+                            cs, cmp_pool, c_table, one_per_seq=True)
+        slc.compress_index_keys_stream(seq, pos[j], kv_i[j], sc_i[j], ape_i, state_i, st_table, 4,
+                                       gamma_i, 1e-6, cs, key_pool, c_table, one_per_seq=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = 4 * max(1, args.steps // 4)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    # the same four steps captured once and replayed (no host work per call)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(4):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(4):
+            step(i)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps // 4):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"workload": "c4a_compress_stream_b32", "sequences": n, "context": ctx,
+                      "us_per_step": us, "graph_us_per_step": us_graph, "steps": steps,
+                      "emitting_steps": "1 in 4", "calls_per_step": 2, "kernels_per_step": 2,
+                      "data": "synthetic"}), flush=True)
+
+
 def main():
     args = parse()
     if args.report_stats:
@@ -345,6 +423,8 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "c4a_compress_stream_b32":
+        return compress_stream_workload(args)
     if args.workload != "c4a_decode_64k":
         return other_workload(args)
 

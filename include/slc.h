@@ -224,6 +224,22 @@ slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
                                  slc_pool_t cmp_pool, float *prequant, void *stream);
 
 /*
+ * slc_compress_stream_step -- slc_compress_stream in one launch for calls
+ * that bring at most one token per sequence (a decode step): each token's
+ * workgroup writes its state row and, if it completes a slot, pools the
+ * window from the rows saved by earlier calls plus its own row, which it
+ * keeps on chip.  Arguments and results as slc_compress_stream; a call with
+ * two tokens of one sequence gives unspecified slots (never an access out of
+ * bounds).
+ */
+slc_status_t slc_compress_stream_step(int ratio, int n_tok, const int32_t *tok_seq,
+                                      const int32_t *tok_pos, const uint16_t *kv,
+                                      const float *score, const float *ape,
+                                      slc_pool_t state_pool, int state_block, const float *gamma,
+                                      float eps, const float *cos_sin, int max_pos,
+                                      slc_pool_t cmp_pool, float *prequant, void *stream);
+
+/*
  * slc_compress_index_keys_stream -- the indexer's own compressor, step by
  * step ("DeepSeek-V4 attention layer types": the indexer holds a small
  * compressor of head_dim 128 whose entries fill its K cache;
@@ -255,6 +271,20 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
                                             const float *gamma, float eps, const float *cos_sin,
                                             int max_pos, int key_flags, slc_pool_t key_pool,
                                             float *prequant, void *stream);
+
+/*
+ * slc_compress_index_keys_stream_step -- slc_compress_index_keys_stream in
+ * one launch, under slc_compress_stream_step's condition (at most one token
+ * per sequence per call).
+ */
+slc_status_t slc_compress_index_keys_stream_step(int n_tok, const int32_t *tok_seq,
+                                                 const int32_t *tok_pos, const uint16_t *kv,
+                                                 const float *score, const float *ape,
+                                                 slc_pool_t state_pool, int state_block,
+                                                 const float *gamma, float eps,
+                                                 const float *cos_sin, int max_pos, int key_flags,
+                                                 slc_pool_t key_pool, float *prequant,
+                                                 void *stream);
 
 /*
  * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J

@@ -155,11 +155,11 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
     return hip_status(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
-slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
-                                 const int32_t *tok_pos, const uint16_t *kv, const float *score,
-                                 const float *ape, slc_pool_t state_pool, int state_block,
-                                 const float *gamma, float eps, const float *cos_sin, int max_pos,
-                                 slc_pool_t cmp_pool, float *prequant, void *stream) {
+static slc_status_t compress_stream(bool one_per_seq, int ratio, int n_tok, const int32_t *tok_seq,
+                                    const int32_t *tok_pos, const uint16_t *kv, const float *score,
+                                    const float *ape, slc_pool_t state_pool, int state_block,
+                                    const float *gamma, float eps, const float *cos_sin, int max_pos,
+                                    slc_pool_t cmp_pool, float *prequant, void *stream) {
     if (ratio != 4 && ratio != 128) return fail("compress_stream: ratio must be 4 or 128");
     if (n_tok < 0) return fail("compress_stream: n_tok must be >= 0");
     if (state_block < 1 || state_block > 1024)
@@ -179,16 +179,35 @@ slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
     if (st != SLC_OK) return st;
     StreamArgs a{ratio, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool, state_block,
                  gamma, eps, cos_sin, max_pos, cmp_pool, prequant, kD};
-    return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_compress_stream(a, one_per_seq, static_cast<hipStream_t>(stream)));
 }
 
-slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
-                                            const int32_t *tok_pos, const uint16_t *kv,
-                                            const float *score, const float *ape,
-                                            slc_pool_t state_pool, int state_block,
-                                            const float *gamma, float eps, const float *cos_sin,
-                                            int max_pos, int key_flags, slc_pool_t key_pool,
-                                            float *prequant, void *stream) {
+slc_status_t slc_compress_stream(int ratio, int n_tok, const int32_t *tok_seq,
+                                 const int32_t *tok_pos, const uint16_t *kv, const float *score,
+                                 const float *ape, slc_pool_t state_pool, int state_block,
+                                 const float *gamma, float eps, const float *cos_sin, int max_pos,
+                                 slc_pool_t cmp_pool, float *prequant, void *stream) {
+    return compress_stream(false, ratio, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool,
+                           state_block, gamma, eps, cos_sin, max_pos, cmp_pool, prequant, stream);
+}
+
+slc_status_t slc_compress_stream_step(int ratio, int n_tok, const int32_t *tok_seq,
+                                      const int32_t *tok_pos, const uint16_t *kv,
+                                      const float *score, const float *ape,
+                                      slc_pool_t state_pool, int state_block, const float *gamma,
+                                      float eps, const float *cos_sin, int max_pos,
+                                      slc_pool_t cmp_pool, float *prequant, void *stream) {
+    return compress_stream(true, ratio, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool,
+                           state_block, gamma, eps, cos_sin, max_pos, cmp_pool, prequant, stream);
+}
+
+static slc_status_t index_keys_stream(bool one_per_seq, int n_tok, const int32_t *tok_seq,
+                                      const int32_t *tok_pos, const uint16_t *kv,
+                                      const float *score, const float *ape,
+                                      slc_pool_t state_pool, int state_block,
+                                      const float *gamma, float eps, const float *cos_sin,
+                                      int max_pos, int key_flags, slc_pool_t key_pool,
+                                      float *prequant, void *stream) {
     if (n_tok < 0) return fail("compress_index_keys_stream: n_tok must be >= 0");
     if (key_flags != 0 && key_flags != SLC_KEY_MXFP4)
         return fail("compress_index_keys_stream: key_flags must be 0 or SLC_KEY_MXFP4");
@@ -213,7 +232,32 @@ slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
     StreamArgs a{4, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool, state_block,
                  gamma, eps, cos_sin, max_pos, key_pool, prequant, kDI,
                  key_flags == SLC_KEY_MXFP4 ? 1 : 0};
-    return hip_status(launch_compress_stream(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_compress_stream(a, one_per_seq, static_cast<hipStream_t>(stream)));
+}
+
+slc_status_t slc_compress_index_keys_stream(int n_tok, const int32_t *tok_seq,
+                                            const int32_t *tok_pos, const uint16_t *kv,
+                                            const float *score, const float *ape,
+                                            slc_pool_t state_pool, int state_block,
+                                            const float *gamma, float eps, const float *cos_sin,
+                                            int max_pos, int key_flags, slc_pool_t key_pool,
+                                            float *prequant, void *stream) {
+    return index_keys_stream(false, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool,
+                             state_block, gamma, eps, cos_sin, max_pos, key_flags, key_pool,
+                             prequant, stream);
+}
+
+slc_status_t slc_compress_index_keys_stream_step(int n_tok, const int32_t *tok_seq,
+                                                 const int32_t *tok_pos, const uint16_t *kv,
+                                                 const float *score, const float *ape,
+                                                 slc_pool_t state_pool, int state_block,
+                                                 const float *gamma, float eps,
+                                                 const float *cos_sin, int max_pos, int key_flags,
+                                                 slc_pool_t key_pool, float *prequant,
+                                                 void *stream) {
+    return index_keys_stream(true, n_tok, tok_seq, tok_pos, kv, score, ape, state_pool,
+                             state_block, gamma, eps, cos_sin, max_pos, key_flags, key_pool,
+                             prequant, stream);
 }
 
 slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,

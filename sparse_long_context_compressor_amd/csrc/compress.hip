@@ -330,18 +330,16 @@ __global__ __launch_bounds__(256) void stream_save_kernel(StreamArgs a) {
 // 4j+3 ("DeepseekV4Attention", CSA compressor: the older group brings C_a,
 // the newer C_b).  r = 128: one workgroup per token, four waves pooling 32
 // entries each, merged through LDS.  Absent state rows are skipped.
-__global__ __launch_bounds__(256) void stream_emit_r4_kernel(StreamArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.n_tok) return;
-    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
-    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+// own: the emitting token's own state row (in LDS) when the caller has it,
+// else null (read from the state pool like the others).
+__device__ __forceinline__ void emit_r4(const StreamArgs &a, int t, int seq, int pos,
+                                        const float *own, int lane) {
     const int slot = pos / 4;
     PoolState st;
     state_init(st);
     for (int e = 0; e < 8; e++) {
         const int p = 4 * slot - 4 + e;
-        const float *row = state_row(a.state, a.state_block, 2 * kD, seq, p);
+        const float *row = (own && p == pos) ? own : state_row(a.state, a.state_block, 2 * kD, seq, p);
         if (row) pool_state(st, row, 2 * kD, e < 4 ? 0 : 1, lane);
     }
     float pooled[9];
@@ -351,17 +349,26 @@ __global__ __launch_bounds__(256) void stream_emit_r4_kernel(StreamArgs a) {
                 a.prequant, t);
 }
 
-__global__ __launch_bounds__(256) void stream_emit_r128_kernel(StreamArgs a) {
-    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = blockIdx.x;
+__global__ __launch_bounds__(256) void stream_emit_r4_kernel(StreamArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
     const int pos = a.tok_pos[t], seq = a.tok_seq[t];
-    if (pos < 0 || (pos + 1) % 128 != 0) return;          // uniform over the workgroup
+    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+    emit_r4(a, t, seq, pos, nullptr, lane);
+}
+
+// r = 128: the workgroup's four waves pool 32 positions each, merged in LDS.
+__device__ __forceinline__ void emit_r128(const StreamArgs &a, int t, int seq, int pos,
+                                          const float *own, int lane, int w,
+                                          float (*part_m)[kD], float (*part_l)[kD],
+                                          float (*part_acc)[kD]) {
     const int slot = pos / 128;
     PoolState st;
     state_init(st);
     for (int e = 32 * w; e < 32 * w + 32; e++) {
-        const float *row = state_row(a.state, a.state_block, kD, seq, 128 * slot + e);
+        const int p = 128 * slot + e;
+        const float *row = (own && p == pos) ? own : state_row(a.state, a.state_block, kD, seq, p);
         if (row) pool_state(st, row, kD, 0, lane);
     }
 #pragma unroll
@@ -395,21 +402,27 @@ __global__ __launch_bounds__(256) void stream_emit_r128_kernel(StreamArgs a) {
                 a.prequant, t);
 }
 
+__global__ __launch_bounds__(256) void stream_emit_r128_kernel(StreamArgs a) {
+    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0 || (pos + 1) % 128 != 0) return;          // uniform over the workgroup
+    emit_r128(a, t, seq, pos, nullptr, lane, w, part_m, part_l, part_acc);
+}
+
 // The indexer's key compressor (dim 128, ratio 4): one wave per token; lane
 // l holds dims 2l, 2l+1, so the RoPE pair (64+2i, 65+2i) is lane 32+i's own
 // two dims.  Pool as the latent r = 4 emit, RMSNorm over 128 dims, RoPE at
 // 4j, one pow2 scale for the key, e4m3 codes into the KEY pool.
-__global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.n_tok) return;
-    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
-    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+__device__ __forceinline__ void emit_keys(const StreamArgs &a, int t, int seq, int pos,
+                                          const float *own, int lane) {
     const int slot = pos / 4;
     constexpr int kW = 2 * kDI;                          // floats per half state row
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
     for (int e = 0; e < 8; e++) {
-        const float *row = state_row(a.state, a.state_block, kW, seq, 4 * slot - 4 + e);
+        const int p = 4 * slot - 4 + e;
+        const float *row = (own && p == pos) ? own : state_row(a.state, a.state_block, kW, seq, p);
         if (!row) continue;
         const int blk = e < 4 ? 0 : 1;
         const f32x2 kv = *reinterpret_cast<const f32x2 *>(row + blk * kDI + 2 * lane);
@@ -472,8 +485,58 @@ __global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
         reinterpret_cast<float *>(base + SLC_KEY_SCALE_OFFSET)[row % kBR] = ldexpf(1.f, e);
 }
 
-hipError_t launch_compress_stream(const StreamArgs &a, hipStream_t stream) {
+__global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0 || (pos + 1) % 4 != 0) return;           // uniform over the wave
+    emit_keys(a, t, seq, pos, nullptr, lane);
+}
+
+// Both steps in one launch, for calls that bring at most one token per
+// sequence (a decode step): the window's other positions were saved by
+// earlier calls, and the token's own row is pooled from LDS.  One workgroup
+// per token.
+__global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a) {
+    __shared__ __attribute__((aligned(16))) float own[4 * kD];
+    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int pos = a.tok_pos[t], seq = a.tok_seq[t];
+    if (pos < 0) return;                                  // uniform over the workgroup
+    const int width = (a.ratio == 4 ? 2 : 1) * a.dim;
+    float *row = state_row(a.state, a.state_block, width, seq, pos);
+    const uint16_t *kv = a.kv + static_cast<int64_t>(t) * width;
+    const float *sc = a.score + static_cast<int64_t>(t) * width;
+    const float *ape = a.ape + static_cast<int64_t>(pos % a.ratio) * width;
+    for (int c = threadIdx.x; c < width; c += 256) {
+        const float k = bf16_to_f32(kv[c]), v = sc[c] + ape[c];
+        own[c] = k;
+        own[width + c] = v;
+        if (row) {
+            row[c] = k;
+            row[width + c] = v;
+        }
+    }
+    __syncthreads();
+    if ((pos + 1) % a.ratio != 0) return;
+    const float *mine = row ? own : nullptr;              // an unmapped row is skipped, as in the pool
+    if (a.dim == kDI) {
+        if (w == 0) emit_keys(a, t, seq, pos, mine, lane);
+    } else if (a.ratio == 4) {
+        if (w == 0) emit_r4(a, t, seq, pos, mine, lane);
+    } else {
+        emit_r128(a, t, seq, pos, mine, lane, w, part_m, part_l, part_acc);
+    }
+}
+
+hipError_t launch_compress_stream(const StreamArgs &a, bool one_per_seq, hipStream_t stream) {
     if (a.n_tok <= 0) return hipSuccess;
+    if (one_per_seq) {
+        hipLaunchKernelGGL(stream_step_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(stream_save_kernel, dim3(a.n_tok), dim3(256), 0, stream, a);
     if (a.dim == kDI)
         hipLaunchKernelGGL(stream_emit_keys_kernel, dim3((a.n_tok + 3) / 4), dim3(256), 0, stream, a);

@@ -27,7 +27,8 @@ EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
-    "slc_compress_index_keys_stream", "slc_stream_read_probe",
+    "slc_compress_index_keys_stream", "slc_stream_read_probe", "slc_compress_stream_step",
+    "slc_compress_index_keys_stream_step",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -70,12 +71,14 @@ def lib():
         L.slc_topk_select_warm.restype = i32
         L.slc_topk_select_warm.argtypes = [i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, i32,
                                            pool, vp]
-        L.slc_compress_stream.restype = i32
-        L.slc_compress_stream.argtypes = [i32, i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp,
-                                          i32, pool, vp, vp]
-        L.slc_compress_index_keys_stream.restype = i32
-        L.slc_compress_index_keys_stream.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32,
-                                                     vp, i32, i32, pool, vp, vp]
+        for name in ("slc_compress_stream", "slc_compress_stream_step"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp, i32, pool, vp, vp]
+        for name in ("slc_compress_index_keys_stream", "slc_compress_index_keys_stream_step"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp, i32, i32, pool, vp, vp]
         L.slc_stream_read_probe.restype = i32
         L.slc_stream_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.slc_swa_insert.restype = i32
@@ -159,10 +162,10 @@ def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv
                     score: torch.Tensor, ape: torch.Tensor, state_pool: torch.Tensor,
                     state_table: torch.Tensor, state_block: int, gamma: torch.Tensor, eps: float,
                     cos_sin: torch.Tensor, cmp_pool: torch.Tensor, cmp_table: torch.Tensor,
-                    prequant: Optional[torch.Tensor] = None) -> None:
+                    prequant: Optional[torch.Tensor] = None, one_per_seq: bool = False) -> None:
     """One step of the streaming compressor: state rows of the given tokens,
     then the slots they complete (state_pool fp32 [n_blocks, state_block,
-    2*coff*576])."""
+    2*coff*576]).  one_per_seq: at most one token per sequence, one launch."""
     dev = kv.device
     _need(kv, "kv", torch.bfloat16, dev)
     _need(score, "score", torch.float32, dev)
@@ -175,7 +178,8 @@ def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv
     _need(cmp_pool, "cmp_pool", torch.uint8, dev)
     if prequant is not None:
         _need(prequant, "prequant", torch.float32, dev)
-    _check(lib().slc_compress_stream(int(ratio), int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos),
+    f = lib().slc_compress_stream_step if one_per_seq else lib().slc_compress_stream
+    _check(f(int(ratio), int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos),
                                      _ptr(kv), _ptr(score), _ptr(ape),
                                      pool(state_pool, state_table), int(state_block), _ptr(gamma),
                                      float(eps), _ptr(cos_sin), int(cos_sin.shape[0]),
@@ -184,7 +188,8 @@ def compress_stream(ratio: int, tok_seq: torch.Tensor, tok_pos: torch.Tensor, kv
 
 def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, state_table,
                                state_block: int, gamma, eps: float, cos_sin, key_pool,
-                               key_table, prequant=None, mxfp4: bool = False) -> None:
+                               key_table, prequant=None, mxfp4: bool = False,
+                               one_per_seq: bool = False) -> None:
     """One step of the indexer's 128-dim key compressor (ratio 4) into the
     index key pool (a KEY4 pool of MXFP4 keys with mxfp4=True); state_pool
     fp32 [n_blocks, state_block, 512]."""
@@ -200,7 +205,9 @@ def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, sta
     _need(key_pool, "key_pool", torch.uint8, dev)
     if prequant is not None:
         _need(prequant, "prequant", torch.float32, dev)
-    _check(lib().slc_compress_index_keys_stream(
+    f = (lib().slc_compress_index_keys_stream_step if one_per_seq
+         else lib().slc_compress_index_keys_stream)
+    _check(f(
         int(kv.shape[0]), _ptr(tok_seq), _ptr(tok_pos), _ptr(kv), _ptr(score), _ptr(ape),
         pool(state_pool, state_table), int(state_block), _ptr(gamma), float(eps), _ptr(cos_sin),
         int(cos_sin.shape[0]), KEY_MXFP4 if mxfp4 else 0, pool(key_pool, key_table),

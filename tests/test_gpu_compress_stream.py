@@ -223,3 +223,62 @@ def test_streamed_index_keys_match_oracle(S, oracle, mxfp4):
     assert not c.reshape(-1, c.shape[-1])[torch.from_numpy(~written)].any()
     assert not s.reshape(-1, 4)[torch.from_numpy(~written)].any()
     print(f"index keys: {sum(L // 4 for L in lens)} streamed; codes excused: {excused}")
+
+
+@pytest.mark.parametrize("kind", ["r4", "r128", "keys_fp8", "keys_mxfp4"])
+def test_one_launch_step_equals_two_launch_path(S, kind):
+    """slc_compress_stream_step / slc_compress_index_keys_stream_step (one
+    launch per call, at most one token per sequence) write exactly the bytes
+    the two-launch path writes: same state rows, same slots, same prequant."""
+    r = 128 if kind == "r128" else 4
+    keys = kind.startswith("keys")
+    dim = 128 if keys else 576
+    coff = 2 if r == 4 else 1
+    lens, chunk, sb = ([300, 200] if r == 128 else [45, 30]), (130 if r == 128 else 9), 4
+    g = torch.Generator().manual_seed(99)
+    T = sum(lens)
+    kv = torch.randn((T, coff * dim), generator=g).to(torch.bfloat16).cuda()
+    score = torch.randn((T, coff * dim), generator=g).cuda()
+    ape = (torch.randn((r, coff * dim), generator=g) * 0.5).cuda()
+    gamma = (torch.rand((dim,), generator=g) + 0.5).cuda()
+    cs = I.rope_table(max(lens) + 8, device="cuda")
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    st_blocks = [list(range(-(-L // sb))) for L in lens]
+    st_table, n_st = I.block_table(st_blocks, max(len(b) for b in st_blocks), 98, "s1", "cuda")
+    c_blocks = [list(range(max(1, -(-(L // r) // 64)))) for L in lens]
+    c_table, n_cb = I.block_table(c_blocks, max(len(b) for b in c_blocks), 99, "c1", "cuda")
+
+    def run(one_per_seq):
+        state = torch.zeros((n_st, sb, 2 * coff * dim), dtype=torch.float32, device="cuda")
+        if keys:
+            pool = (P.key4_pool_empty if kind == "keys_mxfp4" else P.key_pool_empty)(n_cb, "cuda")
+        else:
+            pool = P.cmp_pool_empty(n_cb, "cuda")
+        calls = [[(b, p) for b in range(len(lens)) for p in range(min(chunk, lens[b]))]]
+        for p in range(chunk, max(lens)):
+            calls.append([(b, p) for b in range(len(lens)) if p < lens[b]])
+        pres = []
+        for i, toks in enumerate(calls):
+            rows = torch.tensor([offs[b] + p for b, p in toks], dtype=torch.long, device="cuda")
+            seq = torch.tensor([b for b, _ in toks], dtype=torch.int32, device="cuda")
+            pos = torch.tensor([p for _, p in toks], dtype=torch.int32, device="cuda")
+            pq = torch.zeros((len(toks), dim), device="cuda")
+            step = one_per_seq and i > 0               # the chunk has several tokens per sequence
+            if keys:
+                S.compress_index_keys_stream(seq, pos, kv[rows].contiguous(), score[rows].contiguous(),
+                                             ape, state, st_table, sb, gamma, 1e-6, cs, pool,
+                                             c_table, pq, mxfp4=kind == "keys_mxfp4",
+                                             one_per_seq=step)
+            else:
+                S.compress_stream(r, seq, pos, kv[rows].contiguous(), score[rows].contiguous(), ape,
+                                  state, st_table, sb, gamma, 1e-6, cs, pool, c_table, pq,
+                                  one_per_seq=step)
+            pres.append(pq)
+        torch.cuda.synchronize()
+        return state, pool, torch.cat(pres)
+
+    s2, p2, q2 = run(False)
+    s1, p1, q1 = run(True)
+    assert torch.equal(s1, s2)
+    assert torch.equal(p1, p2) and p1.any()
+    assert torch.equal(q1, q2)
