@@ -405,9 +405,47 @@ def compress_stream_workload(args):
     e1.record()
     torch.cuda.synchronize()
     us_graph = e0.elapsed_time(e1) * 1e3 / steps
+
+    # all of a step's writers in one launch: the new tokens' rows into an fp8
+    # SWA pool plus both compressors (slc_decode_step_writers)
+    swa_kv = torch.randn((4, n, 576), generator=g).to(torch.bfloat16).to(dev)
+    swa_table, n_sb = I.block_table([[ctx // 64 - 1]] * n, ctx // 64, 10, "swa", dev)
+    swa_pool = P.cmp_pool_empty(n_sb, dev)
+
+    def writers(i):
+        j = i % 4
+        slc.decode_step_writers(
+            seq, pos[j], cs, swa=dict(kv=swa_kv[j], pool=swa_pool, table=swa_table),
+            latent=dict(ratio=4, kv=kv[j], score=sc[j], ape=ape, gamma=gamma, eps=1e-6,
+                        state=state, state_table=st_table, state_block=4, pool=cmp_pool,
+                        table=c_table),
+            keys=dict(kv=kv_i[j], score=sc_i[j], ape=ape_i, gamma=gamma_i, eps=1e-6,
+                      state=state_i, state_table=st_table, state_block=4, pool=key_pool,
+                      table=c_table))
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(4):
+            writers(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph2):
+        for i in range(4):
+            writers(i)
+    for _ in range(3):
+        graph2.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps // 4):
+        graph2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_writers = e0.elapsed_time(e1) * 1e3 / steps
     print(json.dumps({"workload": "c4a_compress_stream_b32", "sequences": n, "context": ctx,
                       "us_per_step": us, "graph_us_per_step": us_graph, "steps": steps,
                       "emitting_steps": "1 in 4", "calls_per_step": 2, "kernels_per_step": 2,
+                      "writers_one_launch_graph_us_per_step": us_writers,
+                      "writers_note": "SWA insert (fp8 pool) + both compressors, one launch",
                       "data": "synthetic"}), flush=True)
 
 

@@ -16,6 +16,8 @@
  *                           emitted as they complete.
  *   slc_compress_index_keys_stream  the indexer's 128-dim key compressor,
  *                           step by step, into the index key pool.
+ *   slc_decode_step_writers the per-token writers of a decode step (SWA insert
+ *                           and both streaming compressors) in one launch.
  *   slc_swa_insert          RoPE + fp8 quantisation + paged write of new tokens
  *                           into an fp8 sliding-window pool
  *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
@@ -285,6 +287,42 @@ slc_status_t slc_compress_index_keys_stream_step(int n_tok, const int32_t *tok_s
                                                  const float *cos_sin, int max_pos, int key_flags,
                                                  slc_pool_t key_pool, float *prequant,
                                                  void *stream);
+
+/*
+ * slc_decode_step_writers -- a decode step's per-token writers in one launch:
+ * slc_swa_insert, slc_compress_stream_step and
+ * slc_compress_index_keys_stream_step for the same n_tok tokens (at most one
+ * per sequence), each part skipped when its input is NULL (swa_kv, kv,
+ * key_kv).  Every part computes exactly what its own call computes; the
+ * three write disjoint pools.  Arguments as in those calls.
+ */
+typedef struct slc_step_writers {
+    int n_tok;
+    const int32_t *tok_seq, *tok_pos;   /* device int32 [n_tok]               */
+    const float *cos_sin;               /* device fp32 [max_pos][64]          */
+    int max_pos;
+    /* SWA insert: fp8 SWA pool (CMP layout) */
+    const uint16_t *swa_kv;             /* [n_tok][576] bf16, or NULL         */
+    slc_pool_t swa_pool;
+    /* latent compressor step */
+    int ratio;                          /* 4 or 128                           */
+    const uint16_t *kv;                 /* [n_tok][coff*576] bf16, or NULL    */
+    const float *score, *ape, *gamma;
+    float eps;
+    slc_pool_t state_pool;
+    int state_block;
+    slc_pool_t cmp_pool;
+    /* index-key compressor step (ratio 4) */
+    const uint16_t *key_kv;             /* [n_tok][256] bf16, or NULL         */
+    const float *key_score, *key_ape, *key_gamma;
+    float key_eps;
+    slc_pool_t key_state_pool;
+    int key_state_block;
+    int key_flags;                      /* 0 or SLC_KEY_MXFP4                 */
+    slc_pool_t key_pool;
+} slc_step_writers_t;
+
+slc_status_t slc_decode_step_writers(const slc_step_writers_t *w, void *stream);
 
 /*
  * slc_swa_insert -- "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J

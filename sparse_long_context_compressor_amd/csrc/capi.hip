@@ -260,6 +260,61 @@ slc_status_t slc_compress_index_keys_stream_step(int n_tok, const int32_t *tok_s
                              prequant, stream);
 }
 
+slc_status_t slc_decode_step_writers(const slc_step_writers_t *w, void *stream) {
+    if (!w) return fail("decode_step_writers: w is required");
+    const int n = w->n_tok;
+    if (n < 0) return fail("decode_step_writers: n_tok must be >= 0");
+    if (n == 0) return SLC_OK;
+    if (!w->tok_seq || !w->tok_pos || !w->cos_sin || w->max_pos < 1)
+        return fail("decode_step_writers: tok_seq, tok_pos and cos_sin (max_pos >= 1) are required");
+    slc_status_t st;
+    SwaInsertArgs swa{};
+    if (w->swa_kv) {
+        if (!aligned(w->swa_kv, 16)) return fail("decode_step_writers: swa_kv must be 16-byte aligned");
+        if ((st = check_pool(w->swa_pool, "decode_step_writers: swa_pool")) != SLC_OK) return st;
+        swa = SwaInsertArgs{n, w->swa_kv, w->tok_seq, w->tok_pos, w->cos_sin, w->max_pos,
+                            w->swa_pool, nullptr};
+    }
+    auto check_stream = [&](const uint16_t *kv, const float *score, const float *ape,
+                            const float *gamma, float eps, slc_pool_t state, int block,
+                            slc_pool_t dst, const char *what) -> slc_status_t {
+        if (!score || !ape || !gamma)
+            return fail("decode_step_writers: score, ape and gamma of each compressor are required");
+        if (!aligned(kv, 16) || !aligned(score, 16) || !aligned(gamma, 16) || !aligned(state.base, 16))
+            return fail("decode_step_writers: kv, score, gamma and state pools must be 16-byte aligned");
+        if (block < 1 || block > 1024) return fail("decode_step_writers: state_block must be in [1, 1024]");
+        if (!(eps >= 0.f) || !std::isfinite(eps)) return fail("decode_step_writers: eps must be finite and >= 0");
+        slc_status_t r = check_pool(state, "decode_step_writers: state_pool");
+        if (r != SLC_OK) return r;
+        return check_pool(dst, what);
+    };
+    StreamArgs lat{}, keys{};
+    if (w->kv) {
+        if (w->ratio != 4 && w->ratio != 128) return fail("decode_step_writers: ratio must be 4 or 128");
+        if ((st = check_stream(w->kv, w->score, w->ape, w->gamma, w->eps, w->state_pool,
+                               w->state_block, w->cmp_pool, "decode_step_writers: cmp_pool")) != SLC_OK)
+            return st;
+        lat = StreamArgs{w->ratio, n, w->tok_seq, w->tok_pos, w->kv, w->score, w->ape,
+                         w->state_pool, w->state_block, w->gamma, w->eps, w->cos_sin, w->max_pos,
+                         w->cmp_pool, nullptr, kD};
+    }
+    if (w->key_kv) {
+        if (w->key_flags != 0 && w->key_flags != SLC_KEY_MXFP4)
+            return fail("decode_step_writers: key_flags must be 0 or SLC_KEY_MXFP4");
+        if ((st = check_stream(w->key_kv, w->key_score, w->key_ape, w->key_gamma, w->key_eps,
+                               w->key_state_pool, w->key_state_block, w->key_pool,
+                               "decode_step_writers: key_pool")) != SLC_OK)
+            return st;
+        keys = StreamArgs{4, n, w->tok_seq, w->tok_pos, w->key_kv, w->key_score, w->key_ape,
+                          w->key_state_pool, w->key_state_block, w->key_gamma, w->key_eps,
+                          w->cos_sin, w->max_pos, w->key_pool, nullptr, kDI,
+                          w->key_flags == SLC_KEY_MXFP4 ? 1 : 0};
+    }
+    return hip_status(launch_step_writers(w->kv ? &lat : nullptr, w->key_kv ? &keys : nullptr,
+                                          w->swa_kv ? &swa : nullptr,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,
                                    void *stream) {
     if (!buf || !sink) return fail("stream_read_probe: buf and sink are required");

@@ -278,10 +278,7 @@ __global__ __launch_bounds__(256) void compress_r128_kernel(CompressArgs a) {
 // the cache row format, written at the position's row of its sequence.
 // "From MLA to CSA + HCA" 6.2 (the fused KV insert: GPT-J RoPE, fp8
 // quantisation, paged write) and 5.5 (the SWA cache's fp8 row).
-__global__ __launch_bounds__(256) void swa_insert_kernel(SwaInsertArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.n_tok) return;
+__device__ __forceinline__ void swa_insert_token(const SwaInsertArgs &a, int t, int lane) {
     const int seq = a.tok_seq[t], pos = a.tok_pos[t];
     if (pos < 0 || pos >= a.max_pos) return;        // uniform over the wave
     const uint16_t *kr = a.kv + static_cast<int64_t>(t) * kD;
@@ -297,6 +294,13 @@ __global__ __launch_bounds__(256) void swa_insert_kernel(SwaInsertArgs a) {
     const int64_t row = pool_row(a.pool, seq, pos);
     if (row < 0) return;
     quant_store(y, lane, a.pool, row);
+}
+
+__global__ __launch_bounds__(256) void swa_insert_kernel(SwaInsertArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_tok) return;
+    swa_insert_token(a, t, lane);
 }
 
 hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream) {
@@ -498,11 +502,14 @@ __global__ __launch_bounds__(256) void stream_emit_keys_kernel(StreamArgs a) {
 // sequence (a decode step): the window's other positions were saved by
 // earlier calls, and the token's own row is pooled from LDS.  One workgroup
 // per token.
-__global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a) {
-    __shared__ __attribute__((aligned(16))) float own[4 * kD];
-    __shared__ float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+struct StepLds {
+    float own[4 * kD];
+    float part_m[4][kD], part_l[4][kD], part_acc[4][kD];
+};
+
+__device__ __forceinline__ void stream_step(const StreamArgs &a, int t, StepLds &lds) {
+    float *own = lds.own;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = blockIdx.x;
     const int pos = a.tok_pos[t], seq = a.tok_seq[t];
     if (pos < 0) return;                                  // uniform over the workgroup
     const int width = (a.ratio == 4 ? 2 : 1) * a.dim;
@@ -527,8 +534,43 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a) {
     } else if (a.ratio == 4) {
         if (w == 0) emit_r4(a, t, seq, pos, mine, lane);
     } else {
-        emit_r128(a, t, seq, pos, mine, lane, w, part_m, part_l, part_acc);
+        emit_r128(a, t, seq, pos, mine, lane, w, lds.part_m, lds.part_l, lds.part_acc);
     }
+}
+
+__global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a) {
+    __shared__ __attribute__((aligned(16))) StepLds lds;
+    stream_step(a, blockIdx.x, lds);
+}
+
+// A decode step's per-token writers in one launch: workgroups [0, nl) run
+// the latent compressor's step for token b, [nl, nl + nk) the index-key
+// compressor's, and the rest insert the tokens' SWA rows, four per
+// workgroup.  The three write disjoint pools.
+__global__ __launch_bounds__(256) void step_writers_kernel(StreamArgs lat, StreamArgs keys,
+                                                           SwaInsertArgs swa, int nl, int nk) {
+    __shared__ __attribute__((aligned(16))) StepLds lds;
+    const int b = blockIdx.x;
+    if (b < nl) {
+        stream_step(lat, b, lds);
+    } else if (b < nl + nk) {
+        stream_step(keys, b - nl, lds);
+    } else {
+        const int t = (b - nl - nk) * 4 + (threadIdx.x >> 6);
+        if (t < swa.n_tok) swa_insert_token(swa, t, threadIdx.x & 63);
+    }
+}
+
+hipError_t launch_step_writers(const StreamArgs *lat, const StreamArgs *keys,
+                               const SwaInsertArgs *swa, hipStream_t stream) {
+    const int nl = lat ? lat->n_tok : 0, nk = keys ? keys->n_tok : 0;
+    const int ns = swa ? (swa->n_tok + 3) / 4 : 0;
+    if (nl + nk + ns == 0) return hipSuccess;
+    const StreamArgs none{};
+    const SwaInsertArgs no_swa{};
+    hipLaunchKernelGGL(step_writers_kernel, dim3(nl + nk + ns), dim3(256), 0, stream,
+                       lat ? *lat : none, keys ? *keys : none, swa ? *swa : no_swa, nl, nk);
+    return hipGetLastError();
 }
 
 hipError_t launch_compress_stream(const StreamArgs &a, bool one_per_seq, hipStream_t stream) {

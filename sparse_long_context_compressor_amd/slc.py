@@ -28,7 +28,7 @@ EXPORTED = [
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
     "slc_compress_index_keys_stream", "slc_stream_read_probe", "slc_compress_stream_step",
-    "slc_compress_index_keys_stream_step",
+    "slc_compress_index_keys_stream_step", "slc_decode_step_writers",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
 ]
@@ -37,6 +37,18 @@ EXPORTED = [
 class Pool(C.Structure):
     _fields_ = [("base", C.c_void_p), ("block_table", C.c_void_p),
                 ("table_stride", C.c_int32), ("n_blocks", C.c_int64)]
+
+
+class StepWriters(C.Structure):
+    _fields_ = [("n_tok", C.c_int), ("tok_seq", C.c_void_p), ("tok_pos", C.c_void_p),
+                ("cos_sin", C.c_void_p), ("max_pos", C.c_int),
+                ("swa_kv", C.c_void_p), ("swa_pool", Pool),
+                ("ratio", C.c_int), ("kv", C.c_void_p), ("score", C.c_void_p),
+                ("ape", C.c_void_p), ("gamma", C.c_void_p), ("eps", C.c_float),
+                ("state_pool", Pool), ("state_block", C.c_int), ("cmp_pool", Pool),
+                ("key_kv", C.c_void_p), ("key_score", C.c_void_p), ("key_ape", C.c_void_p),
+                ("key_gamma", C.c_void_p), ("key_eps", C.c_float), ("key_state_pool", Pool),
+                ("key_state_block", C.c_int), ("key_flags", C.c_int), ("key_pool", Pool)]
 
 
 class SlcError(RuntimeError):
@@ -79,6 +91,8 @@ def lib():
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp, i32, i32, pool, vp, vp]
+        L.slc_decode_step_writers.restype = i32
+        L.slc_decode_step_writers.argtypes = [C.POINTER(StepWriters), vp]
         L.slc_stream_read_probe.restype = i32
         L.slc_stream_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.slc_swa_insert.restype = i32
@@ -212,6 +226,35 @@ def compress_index_keys_stream(tok_seq, tok_pos, kv, score, ape, state_pool, sta
         pool(state_pool, state_table), int(state_block), _ptr(gamma), float(eps), _ptr(cos_sin),
         int(cos_sin.shape[0]), KEY_MXFP4 if mxfp4 else 0, pool(key_pool, key_table),
         _ptr(prequant), _stream()))
+
+
+def decode_step_writers(tok_seq, tok_pos, cos_sin, swa=None, latent=None, keys=None) -> None:
+    """A decode step's writers in one launch (at most one token per sequence).
+    swa = dict(kv, pool, table); latent = dict(ratio, kv, score, ape, gamma,
+    eps, state, state_table, state_block, pool, table); keys = the same
+    without ratio, plus mxfp4 (bool).  Omitted parts are skipped."""
+    w = StepWriters()
+    w.n_tok = int(tok_seq.numel())
+    w.tok_seq, w.tok_pos, w.cos_sin = _ptr(tok_seq), _ptr(tok_pos), _ptr(cos_sin)
+    w.max_pos = int(cos_sin.shape[0])
+    if swa is not None:
+        _need(swa["kv"], "swa kv", torch.bfloat16, swa["kv"].device)
+        w.swa_kv, w.swa_pool = _ptr(swa["kv"]), pool(swa["pool"], swa["table"])
+    if latent is not None:
+        w.ratio = int(latent["ratio"])
+        w.kv, w.score, w.ape = _ptr(latent["kv"]), _ptr(latent["score"]), _ptr(latent["ape"])
+        w.gamma, w.eps = _ptr(latent["gamma"]), float(latent["eps"])
+        w.state_pool = pool(latent["state"], latent["state_table"])
+        w.state_block = int(latent["state_block"])
+        w.cmp_pool = pool(latent["pool"], latent["table"])
+    if keys is not None:
+        w.key_kv, w.key_score, w.key_ape = _ptr(keys["kv"]), _ptr(keys["score"]), _ptr(keys["ape"])
+        w.key_gamma, w.key_eps = _ptr(keys["gamma"]), float(keys["eps"])
+        w.key_state_pool = pool(keys["state"], keys["state_table"])
+        w.key_state_block = int(keys["state_block"])
+        w.key_flags = KEY_MXFP4 if keys.get("mxfp4") else 0
+        w.key_pool = pool(keys["pool"], keys["table"])
+    _check(lib().slc_decode_step_writers(C.byref(w), _stream()))
 
 
 def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -282,3 +282,57 @@ def test_one_launch_step_equals_two_launch_path(S, kind):
     assert torch.equal(s1, s2)
     assert torch.equal(p1, p2) and p1.any()
     assert torch.equal(q1, q2)
+
+
+@pytest.mark.parametrize("mxfp4", [False, True], ids=["fp8_keys", "mxfp4_keys"])
+def test_decode_step_writers_equal_the_separate_calls(S, mxfp4):
+    """slc_decode_step_writers (SWA insert + both compressor steps in one
+    launch) writes exactly what the three separate calls write, over steps
+    that do and do not complete a slot."""
+    n, ctx = 6, 2048
+    g = torch.Generator().manual_seed(123)
+    cs = I.rope_table(ctx, device="cuda")
+    blocks = [list(range(ctx // 64))] * n
+    swa_table, nsb = I.block_table(blocks, ctx // 64, 1, "w", "cuda")
+    st_table, nst = I.block_table([list(range(ctx // 4))] * n, ctx // 4, 2, "s", "cuda")
+    c_table, ncb = I.block_table([list(range(ctx // 4 // 64))] * n, ctx // 4 // 64, 3, "c", "cuda")
+    seq = torch.arange(n, dtype=torch.int32, device="cuda")
+    ape = (torch.randn((4, 1152), generator=g) * 0.5).cuda()
+    ape_k = (torch.randn((4, 256), generator=g) * 0.5).cuda()
+    gamma, gamma_k = (torch.rand(576, generator=g) + 0.5).cuda(), (torch.rand(128, generator=g) + 0.5).cuda()
+    steps = []
+    for p in range(1990, 2000):
+        steps.append(dict(pos=torch.full((n,), p, dtype=torch.int32, device="cuda"),
+                          swa=torch.randn((n, 576), generator=g).to(torch.bfloat16).cuda(),
+                          kv=torch.randn((n, 1152), generator=g).to(torch.bfloat16).cuda(),
+                          sc=torch.randn((n, 1152), generator=g).cuda(),
+                          kvk=torch.randn((n, 256), generator=g).to(torch.bfloat16).cuda(),
+                          sck=torch.randn((n, 256), generator=g).cuda()))
+
+    def pools():
+        return dict(swa=P.cmp_pool_empty(nsb, "cuda"), cmp=P.cmp_pool_empty(ncb, "cuda"),
+                    key=(P.key4_pool_empty if mxfp4 else P.key_pool_empty)(ncb, "cuda"),
+                    st=torch.zeros((nst, 4, 2304), device="cuda"),
+                    stk=torch.zeros((nst, 4, 512), device="cuda"))
+
+    a, b = pools(), pools()
+    for st in steps:
+        S.swa_insert(st["swa"], seq, st["pos"], cs, a["swa"], swa_table)
+        S.compress_stream(4, seq, st["pos"], st["kv"], st["sc"], ape, a["st"], st_table, 4, gamma,
+                          1e-6, cs, a["cmp"], c_table, one_per_seq=True)
+        S.compress_index_keys_stream(seq, st["pos"], st["kvk"], st["sck"], ape_k, a["stk"],
+                                     st_table, 4, gamma_k, 1e-6, cs, a["key"], c_table,
+                                     mxfp4=mxfp4, one_per_seq=True)
+        S.decode_step_writers(
+            seq, st["pos"], cs,
+            swa=dict(kv=st["swa"], pool=b["swa"], table=swa_table),
+            latent=dict(ratio=4, kv=st["kv"], score=st["sc"], ape=ape, gamma=gamma, eps=1e-6,
+                        state=b["st"], state_table=st_table, state_block=4, pool=b["cmp"],
+                        table=c_table),
+            keys=dict(kv=st["kvk"], score=st["sck"], ape=ape_k, gamma=gamma_k, eps=1e-6,
+                      state=b["stk"], state_table=st_table, state_block=4, pool=b["key"],
+                      table=c_table, mxfp4=mxfp4))
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    assert a["cmp"].any() and a["key"].any() and a["swa"].any()
