@@ -176,3 +176,23 @@ def test_invalid_arguments_of_the_next_rows_are_rejected(S):
     assert L.slc_stream_read_probe(C.c_void_p(258), 16, fake, 4, None) == 1
     assert L.slc_stream_read_probe(fake, 17, fake, 4, None) == 1
     assert L.slc_stream_read_probe(fake, 16, None, 4, None) == 1
+
+
+def test_decode_step_writers_validate_on_the_host(S):
+    L = S.lib()
+    assert L.slc_decode_step_writers(None, None) == 1
+    w = S.StepWriters()
+    w.n_tok = 0
+    assert L.slc_decode_step_writers(C.byref(w), None) == 0            # nothing to do
+    fake = 256
+    w.n_tok, w.tok_seq, w.tok_pos, w.cos_sin, w.max_pos = 4, fake, fake, fake, 16
+    w.kv, w.score, w.ape, w.gamma, w.ratio = fake, fake, fake, fake, 3
+    assert L.slc_decode_step_writers(C.byref(w), None) == 1 and b"ratio" in L.slc_last_error()
+    w.kv = None
+    w.key_kv, w.key_score, w.key_ape, w.key_gamma, w.key_flags = fake, fake, fake, fake, 7
+    assert L.slc_decode_step_writers(C.byref(w), None) == 1 and b"key_flags" in L.slc_last_error()
+    w.key_flags = 0
+    assert L.slc_decode_step_writers(C.byref(w), None) == 1 and b"state" in L.slc_last_error()
+    w.key_kv = None
+    w.swa_kv = 258                                                        # misaligned
+    assert L.slc_decode_step_writers(C.byref(w), None) == 1 and b"swa_kv" in L.slc_last_error()
