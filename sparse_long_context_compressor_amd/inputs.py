@@ -332,12 +332,13 @@ def c128a_decode_128k(seed=3, device="cpu", batch=32) -> Layer:
                        W=128, k=512, given_topk=True, device=device)
 
 
-def c4a_prefill_2k(seed=4, device="cpu") -> Layer:
+def c4a_prefill_2k(seed=4, device="cpu", swa_fp8=False, key_fp4=False) -> Layer:
     """C4A prefill chunk: 2048 causal query tokens at positions 129024..131071,
-    H=64, context 131072 -> 32768 slots, indexer 64 heads, top-k 2048 + SWA 128."""
+    H=64, context 131072 -> 32768 slots, indexer 64 heads, top-k 2048 + SWA 128
+    (swa_fp8 / key_fp4: the fp8 SWA pool and MXFP4 index keys)."""
     return build_layer(seed, ratio=4, H=64, ctx=[131072],
                        queries=[(0, p) for p in range(129024, 131072)], n_slots=[32768],
-                       W=128, k=2048, H_I=64, device=device)
+                       W=128, k=2048, H_I=64, swa_fp8=swa_fp8, key_fp4=key_fp4, device=device)
 
 
 CONFIGS = {

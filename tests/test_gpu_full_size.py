@@ -115,11 +115,14 @@ def test_c128a_decode_128k_full(S, oracle):
 PREFILL_SAMPLE = [0, 1, 2, 3, 4, 511, 1024, 1535, 2043, 2044, 2045, 2046, 2047]
 
 
-def test_c4a_prefill_2k_full(S, oracle):
+@pytest.mark.parametrize("fmt", ["bf16_swa", "fp8_swa_mxfp4_keys"])
+def test_c4a_prefill_2k_full(S, oracle, fmt):
     """All 2048 tokens run on the GPU (index scores, top-k 2048, prefill
     attention); the oracle checks a sample of tokens that includes the
-    chunk's ends and tokens on both sides of a visibility step."""
-    lay = I.c4a_prefill_2k()
+    chunk's ends and tokens on both sides of a visibility step.  The second
+    case runs the same chunk over an fp8 SWA pool with MXFP4 index keys."""
+    alt = fmt != "bf16_swa"
+    lay = I.c4a_prefill_2k(swa_fp8=alt, key_fp4=alt)
     qs = np.array(PREFILL_SAMPLE)
     t0 = time.perf_counter()
     idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay, queries=qs)
@@ -147,5 +150,5 @@ def test_c4a_prefill_2k_full(S, oracle):
     e = check_attention(out[kt], lse[kt], out_ref[keep], lse_ref[keep])
     # every token's output is finite and its lse is finite (each list is non-empty)
     assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
-    print(f"c4a_prefill_2k: near-tie slots {near}; {len(keep)}/{len(qs)} sampled tokens "
+    print(f"c4a_prefill_2k ({fmt}): near-tie slots {near}; {len(keep)}/{len(qs)} sampled tokens "
           f"compared; max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
