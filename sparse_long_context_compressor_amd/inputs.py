@@ -195,11 +195,13 @@ def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_sl
     swa_table, nsb = block_table(swa_blocks, width, seed, "swa_table", dev, permute)
     swa_codes = swa_scales = swa_rope = None
     if swa_fp8:
-        # fp8 SWA rows in the compressed-row layout: random codes, pow2 scales
-        # and bf16 rope dims (swa_rows is then left unset)
+        # fp8 SWA rows in the compressed-row layout: random codes (N(0, 64)
+        # before the e4m3 cast) with the scale 2^-6, so that the rows are
+        # unit-scale like the bf16 SWA rows, and bf16 rope dims (swa_rows is
+        # then left unset)
         nrow = swa_rows.shape[0]
         swa_codes = _fp8_codes((nrow, DN), seed, "swa_codes", dev)
-        swa_scales = _pow2((nrow, DN // 64), seed, "swa_scales", dev)
+        swa_scales = _pow2((nrow, DN // 64), seed, "swa_scales", dev, lo=-6, hi=-6)
         swa_rope = _randn((nrow, DR), seed, "swa_rope", dev, torch.bfloat16)
         swa_rows = None
         swa_pool = P.cmp_pool_empty(nsb, dev)
@@ -306,12 +308,12 @@ def c4a_single_layer_4k(seed=0, device="cpu") -> Layer:
                        W=128, k=256, H_I=16, compress_inputs=True, device=device)
 
 
-def swaonly_decode_b64(seed=1, device="cpu") -> Layer:
+def swaonly_decode_b64(seed=1, device="cpu", swa_fp8=False) -> Layer:
     """swaonly decode, batch 64, H=64, context 8192, only the last 128 tokens
-    attended; blocks laid out contiguously."""
+    attended; blocks laid out contiguously (swa_fp8: an fp8 SWA pool)."""
     return build_layer(seed, ratio=1, H=64, ctx=[8192] * 64,
                        queries=[(b, 8191) for b in range(64)], n_slots=[0] * 64, W=128,
-                       permute=False, device=device)
+                       permute=False, swa_fp8=swa_fp8, device=device)
 
 
 def c4a_decode_64k(seed=2, device="cpu", batch=32, swa_fp8=False, key_fp4=False) -> Layer:
@@ -324,12 +326,12 @@ def c4a_decode_64k(seed=2, device="cpu", batch=32, swa_fp8=False, key_fp4=False)
                        W=128, k=512, H_I=64, swa_fp8=swa_fp8, key_fp4=key_fp4, device=device)
 
 
-def c128a_decode_128k(seed=3, device="cpu", batch=32) -> Layer:
+def c128a_decode_128k(seed=3, device="cpu", batch=32, swa_fp8=False) -> Layer:
     """C128A decode, batch 32, H=64, context 131072 -> 1024 slots, given top-k
-    512 distinct uniform samples per query, SWA 128."""
+    512 distinct uniform samples per query, SWA 128 (swa_fp8: an fp8 SWA pool)."""
     return build_layer(seed, ratio=128, H=64, ctx=[131072] * batch,
                        queries=[(b, 131071) for b in range(batch)], n_slots=[1024] * batch,
-                       W=128, k=512, given_topk=True, device=device)
+                       W=128, k=512, given_topk=True, swa_fp8=swa_fp8, device=device)
 
 
 def c4a_prefill_2k(seed=4, device="cpu", swa_fp8=False, key_fp4=False) -> Layer:

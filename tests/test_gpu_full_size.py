@@ -48,8 +48,9 @@ def sets_equal(a, b):
     return [set(x[x >= 0].tolist()) == set(y[y >= 0].tolist()) for x, y in zip(a, b)]
 
 
-def test_swaonly_decode_b64_full(S, oracle):
-    lay = I.swaonly_decode_b64()
+@pytest.mark.parametrize("swa_fp8", [False, True], ids=["bf16_swa", "fp8_swa"])
+def test_swaonly_decode_b64_full(S, oracle, swa_fp8):
+    lay = I.swaonly_decode_b64(swa_fp8=swa_fp8)
     out_ref, lse_ref = oracle_attention(oracle, lay, None)
     to_device(lay)
     out, lse = gpu_attention(S, lay, None)
@@ -102,8 +103,9 @@ def test_c4a_decode_64k_full(S, oracle, swa_fp8, key_fp4):
           f"max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
 
-def test_c128a_decode_128k_full(S, oracle):
-    lay = I.c128a_decode_128k()
+@pytest.mark.parametrize("swa_fp8", [False, True], ids=["bf16_swa", "fp8_swa"])
+def test_c128a_decode_128k_full(S, oracle, swa_fp8):
+    lay = I.c128a_decode_128k(swa_fp8=swa_fp8)
     out_ref, lse_ref = oracle_attention(oracle, lay, lay.given_idx.numpy())
     to_device(lay)
     out, lse = gpu_attention(S, lay, lay.given_idx)
