@@ -416,7 +416,12 @@ slc_status_t slc_topk_select_warm(int n_q, int k, const float *scores, int max_s
                                   const uint16_t *q, int n_heads, int window, slc_pool_t swa_pool,
                                   void *stream);
 
-/* Bytes of workspace slc_index_topk needs (scores of every visible slot). */
+/* Bytes of workspace slc_index_topk needs: the fp32 scores of every visible
+ * slot, [n_q][max_slots], which the select reads back.  Host arithmetic only;
+ * 0 when n_q or max_slots is not positive.  The pages size such scratch on the
+ * host before any real call ("DeepseekV4Attention" (devpress), forward_mqa:
+ * the warm-up dummy run only allocates the workspace) and hand it to the
+ * kernels from a workspace manager (_forward_prefill, step 3). */
 size_t slc_index_topk_workspace_size(int n_q, int max_slots);
 
 /* slc_index_scores followed by slc_topk_select, scores kept in `workspace`
@@ -486,6 +491,13 @@ slc_status_t slc_indexcache_skips(int n_layers, const int32_t *compress_ratios, 
  * softmax states; prefill gives each query token its own workgroup.  Both
  * compute the same function.
  */
+/* Workspace sizes of the two attention calls (host arithmetic only, the
+ * same sizing passages as slc_index_topk_workspace_size: "DeepseekV4Attention"
+ * (devpress), forward_mqa's dummy run and _forward_prefill's workspace
+ * manager).  Decode: the partial (O, max, sum) states of the list splits the
+ * call's split plan forms for these shapes, 0 when it forms one split;
+ * prefill: always 0 (one workgroup per query token, nothing to merge).
+ * k is the compressed list length the call will pass (0 for SWAONLY). */
 size_t slc_sparse_mla_decode_workspace_size(int n_q, int n_heads, int window, int k);
 slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,
                                    const int32_t *q_seq, const int32_t *q_pos, int window,
@@ -503,16 +515,38 @@ slc_status_t slc_sparse_mla_prefill(int layer_type, int n_q, int n_heads, const 
                                     size_t ws_bytes, void *stream);
 
 /*
- * slc_stream_read_probe -- measurement only, not part of the layer: reads
- * every byte of buf once (16-byte loads, grid-stride over `blocks`
- * workgroups of 256 threads) and writes one folded word per workgroup to
- * sink [blocks], so that a caller can time the GPU's practical streaming
- * read bandwidth beside the published HBM peak.
- *   buf    device, 16-byte aligned, bytes a multiple of 16
- *   sink   device uint32 [blocks]
+ * slc_workspace_size -- one sizer for every call that takes a workspace.
+ * "DeepseekV4Attention" (devpress), forward_mqa: the warm-up dummy run does
+ * nothing but allocate the workspace, so the size must follow from the
+ * shapes alone, before any real call; _forward_prefill (step 3) then takes
+ * its scratch from the workspace manager rather than allocating per call.
+ * This library keeps the same split: the caller sizes and owns the
+ * workspace, the calls only use it.
+ *
+ *   op      SLC_OP_INDEX_TOPK          slc_index_topk (uses n_q, max_slots)
+ *           SLC_OP_SPARSE_MLA_DECODE   slc_sparse_mla_decode (n_q, n_heads,
+ *                                      window, k)
+ *           SLC_OP_SPARSE_MLA_PREFILL  slc_sparse_mla_prefill (the same)
+ *   shape   HOST pointer; fields an op does not use are ignored
+ * Returns the bytes the call needs (0: it needs none; pass NULL), equal to
+ * the matching per-op sizer's result.  An unknown op or a NULL shape returns
+ * SIZE_MAX, which no allocation satisfies.  Host arithmetic only.
  */
-slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,
-                                   void *stream);
+typedef enum {
+    SLC_OP_INDEX_TOPK = 1,
+    SLC_OP_SPARSE_MLA_DECODE = 2,
+    SLC_OP_SPARSE_MLA_PREFILL = 3
+} slc_op_t;
+
+typedef struct slc_shape {
+    int n_q;         /* queries: sequences (decode) or tokens (prefill, index) */
+    int n_heads;     /* query heads (attention)                               */
+    int window;      /* sliding-window length (attention)                     */
+    int k;           /* top-k / compressed list length                        */
+    int max_slots;   /* index: row stride of the scores                       */
+} slc_shape_t;
+
+size_t slc_workspace_size(slc_op_t op, const slc_shape_t *shape);
 
 #ifdef __cplusplus
 }

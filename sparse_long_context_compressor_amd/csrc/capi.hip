@@ -3,6 +3,7 @@
 // here allocates, synchronises or reads device memory.
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 
@@ -315,17 +316,6 @@ slc_status_t slc_decode_step_writers(const slc_step_writers_t *w, void *stream) 
                                           static_cast<hipStream_t>(stream)));
 }
 
-slc_status_t slc_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int blocks,
-                                   void *stream) {
-    if (!buf || !sink) return fail("stream_read_probe: buf and sink are required");
-    if (bytes % 16 != 0 || !aligned(buf, 16))
-        return fail("stream_read_probe: buf must be 16-byte aligned and bytes a multiple of 16");
-    if (blocks < 1 || blocks > 65536) return fail("stream_read_probe: blocks must be in [1, 65536]");
-    if (bytes == 0) return SLC_OK;
-    return hip_status(launch_stream_read(buf, static_cast<int64_t>(bytes / 16), sink, blocks,
-                                         static_cast<hipStream_t>(stream)));
-}
-
 slc_status_t slc_swa_insert(int n_tok, const uint16_t *kv, const int32_t *tok_seq,
                             const int32_t *tok_pos, const float *cos_sin, int max_pos,
                             slc_pool_t swa_pool, float *prequant_debug, void *stream) {
@@ -422,6 +412,18 @@ size_t slc_sparse_mla_decode_workspace_size(int n_q, int n_heads, int window, in
 
 size_t slc_sparse_mla_prefill_workspace_size(int n_q, int n_heads, int window, int k) {
     return attn_ws(n_q, n_heads, window, k, false);
+}
+
+size_t slc_workspace_size(slc_op_t op, const slc_shape_t *shape) {
+    if (!shape) return SIZE_MAX;
+    switch (op) {
+    case SLC_OP_INDEX_TOPK: return slc_index_topk_workspace_size(shape->n_q, shape->max_slots);
+    case SLC_OP_SPARSE_MLA_DECODE:
+        return attn_ws(shape->n_q, shape->n_heads, shape->window, shape->k, true);
+    case SLC_OP_SPARSE_MLA_PREFILL:
+        return attn_ws(shape->n_q, shape->n_heads, shape->window, shape->k, false);
+    }
+    return SIZE_MAX;
 }
 
 static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads,

@@ -27,11 +27,13 @@ EXPORTED = [
     "slc_status_string", "slc_last_error", "slc_compress", "slc_index_scores",
     "slc_topk_select", "slc_topk_select_warm", "slc_index_topk_workspace_size", "slc_index_topk",
     "slc_indexcache_skips", "slc_swa_insert", "slc_compress_stream",
-    "slc_compress_index_keys_stream", "slc_stream_read_probe", "slc_compress_stream_step",
+    "slc_compress_index_keys_stream", "slc_compress_stream_step",
     "slc_compress_index_keys_stream_step", "slc_decode_step_writers",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
-    "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill",
+    "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill", "slc_workspace_size",
 ]
+
+OP_INDEX_TOPK, OP_SPARSE_MLA_DECODE, OP_SPARSE_MLA_PREFILL = 1, 2, 3
 
 
 class Pool(C.Structure):
@@ -49,6 +51,11 @@ class StepWriters(C.Structure):
                 ("key_kv", C.c_void_p), ("key_score", C.c_void_p), ("key_ape", C.c_void_p),
                 ("key_gamma", C.c_void_p), ("key_eps", C.c_float), ("key_state_pool", Pool),
                 ("key_state_block", C.c_int), ("key_flags", C.c_int), ("key_pool", Pool)]
+
+
+class Shape(C.Structure):
+    _fields_ = [("n_q", C.c_int), ("n_heads", C.c_int), ("window", C.c_int), ("k", C.c_int),
+                ("max_slots", C.c_int)]
 
 
 class SlcError(RuntimeError):
@@ -93,8 +100,6 @@ def lib():
             f.argtypes = [i32, vp, vp, vp, vp, vp, pool, i32, vp, f32, vp, i32, i32, pool, vp, vp]
         L.slc_decode_step_writers.restype = i32
         L.slc_decode_step_writers.argtypes = [C.POINTER(StepWriters), vp]
-        L.slc_stream_read_probe.restype = i32
-        L.slc_stream_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.slc_swa_insert.restype = i32
         L.slc_swa_insert.argtypes = [i32, vp, vp, vp, vp, i32, pool, vp, vp]
         L.slc_indexcache_skips.restype = i32
@@ -112,6 +117,8 @@ def lib():
             g = getattr(L, name + "_workspace_size")
             g.restype = sz
             g.argtypes = [i32, i32, i32, i32]
+        L.slc_workspace_size.restype = sz
+        L.slc_workspace_size.argtypes = [i32, C.POINTER(Shape)]
         _lib = L
     return _lib
 
@@ -257,13 +264,6 @@ def decode_step_writers(tok_seq, tok_pos, cos_sin, swa=None, latent=None, keys=N
     _check(lib().slc_decode_step_writers(C.byref(w), _stream()))
 
 
-def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
-    """Read every byte of buf once (measurement of the streaming read rate);
-    sink: uint32-sized int32 [blocks] on the same device."""
-    _check(lib().slc_stream_read_probe(_ptr(buf), int(buf.numel() * buf.element_size()),
-                                       _ptr(sink), int(sink.numel()), _stream()))
-
-
 def swa_insert(kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
                cos_sin: torch.Tensor, swa_pool: torch.Tensor, swa_table: torch.Tensor,
                prequant: Optional[torch.Tensor] = None) -> None:
@@ -316,6 +316,14 @@ def indexcache_skips(compress_ratios, freq: int, pattern: str = "") -> list:
     _check(lib().slc_indexcache_skips(int(r.shape[0]), r.ctypes.data, int(freq),
                                       pattern.encode() if pattern else None, out.ctypes.data))
     return out.tolist()
+
+
+def workspace_size(op: int, n_q: int = 0, n_heads: int = 0, window: int = 0, k: int = 0,
+                   max_slots: int = 0) -> int:
+    """slc_workspace_size: bytes of workspace the call `op` needs for these
+    shapes (OP_INDEX_TOPK, OP_SPARSE_MLA_DECODE, OP_SPARSE_MLA_PREFILL)."""
+    sh = Shape(int(n_q), int(n_heads), int(window), int(k), int(max_slots))
+    return int(lib().slc_workspace_size(int(op), C.byref(sh)))
 
 
 def index_topk_workspace_size(n_q: int, max_slots: int) -> int:

@@ -95,6 +95,34 @@ def test_invalid_arguments_are_rejected_before_launch(S):
     assert L.slc_topk_select(0, 8, None, 16, None, None, 4, None, None, None, None) == 0
 
 
+def test_workspace_size_dispatches_to_the_per_op_sizers(S):
+    """slc_workspace_size (host arithmetic) equals the matching per-op sizer on
+    every workload shape and on edge shapes, and flags misuse with SIZE_MAX."""
+    L = S.lib()
+    size_max = C.c_size_t(-1).value
+    shapes = [(32, 64, 128, 512, 16384), (64, 64, 128, 0, 1), (32, 64, 128, 512, 1024),
+              (2048, 64, 128, 2048, 32768), (1, 16, 128, 256, 1024), (1, 128, 1024, 4096, 5000),
+              (0, 64, 128, 512, 16384), (3, 48, 64, 77, 1000), (5, 16, 0, 0, 1)]
+    for n_q, h, w, k, ms in shapes:
+        sh = S.Shape(n_q, h, w, k, ms)
+        assert L.slc_workspace_size(S.OP_INDEX_TOPK, C.byref(sh)) == \
+            L.slc_index_topk_workspace_size(n_q, ms)
+        assert L.slc_workspace_size(S.OP_SPARSE_MLA_DECODE, C.byref(sh)) == \
+            L.slc_sparse_mla_decode_workspace_size(n_q, h, w, k)
+        assert L.slc_workspace_size(S.OP_SPARSE_MLA_PREFILL, C.byref(sh)) == \
+            L.slc_sparse_mla_prefill_workspace_size(n_q, h, w, k)
+        assert S.workspace_size(S.OP_SPARSE_MLA_DECODE, n_q, h, w, k, ms) == \
+            L.slc_sparse_mla_decode_workspace_size(n_q, h, w, k)
+    # the index scores of 32 queries over 16384 slots, 256-byte rounded
+    sh = S.Shape(32, 64, 128, 512, 16384)
+    assert L.slc_workspace_size(S.OP_INDEX_TOPK, C.byref(sh)) == 32 * 16384 * 4
+    assert L.slc_workspace_size(S.OP_SPARSE_MLA_DECODE, C.byref(sh)) > 0
+    assert L.slc_workspace_size(S.OP_SPARSE_MLA_PREFILL, C.byref(sh)) == 0
+    # an unknown op or no shape: SIZE_MAX, which no allocation satisfies
+    assert L.slc_workspace_size(9, C.byref(sh)) == size_max
+    assert L.slc_workspace_size(S.OP_INDEX_TOPK, None) == size_max
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from sparse_long_context_compressor_amd import slc
     monkeypatch.setattr(slc, "LIB_PATH", str(tmp_path / "missing.so"))
@@ -136,8 +164,8 @@ def test_indexcache_skips_match_the_oracle(S, oracle):
 
 
 def test_invalid_arguments_of_the_next_rows_are_rejected(S):
-    """The fp8 SWA insert, the streaming compressors, the MXFP4 flag and the
-    read probe validate on the host, before any launch."""
+    """The fp8 SWA insert, the streaming compressors and the MXFP4 flag
+    validate on the host, before any launch."""
     L = S.lib()
     P = _null_pool(S)
     fake = C.c_void_p(256)
@@ -172,10 +200,6 @@ def test_invalid_arguments_of_the_next_rows_are_rejected(S):
                               fake, None) == 1
     args = [1, 64, fake, fake, fake, 128, P, P, None, 0, None, 0.1, fake, None, None, 0, None]
     assert L.slc_sparse_mla_decode(2 | S.SWA_FP8, *args) == 1
-    # the probe: misaligned buffer, odd size, no sink
-    assert L.slc_stream_read_probe(C.c_void_p(258), 16, fake, 4, None) == 1
-    assert L.slc_stream_read_probe(fake, 17, fake, 4, None) == 1
-    assert L.slc_stream_read_probe(fake, 16, None, 4, None) == 1
 
 
 def test_decode_step_writers_validate_on_the_host(S):
