@@ -124,8 +124,6 @@ hipError_t launch_swa_insert(const SwaInsertArgs &a, hipStream_t stream);
 hipError_t launch_compress_stream(const StreamArgs &a, bool one_per_seq, hipStream_t stream);
 hipError_t launch_step_writers(const StreamArgs *lat, const StreamArgs *keys,
                                const SwaInsertArgs *swa, hipStream_t stream);
-hipError_t launch_stream_read(const void *buf, int64_t units, uint32_t *sink, int blocks,
-                              hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);

@@ -145,12 +145,14 @@ class Layer:
 def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_slots: list,
                 W: int = 128, k: int = 0, H_I: int = 0, given_topk: bool = False,
                 permute: bool = True, compress_inputs: bool = False, swa_fp8: bool = False,
-                key_fp4: bool = False,
+                key_fp4: bool = False, swa_scale_exp: tuple = (-6, -6),
                 gamma_random: bool = False, sm_scale: Optional[float] = None,
                 device="cpu") -> Layer:
     """ctx[b]: context length of sequence b; queries: list of (seq, position);
     n_slots[b]: compressed slots of sequence b (stated by the caller).
-    SWA rows are drawn for positions [min_q max(0, p-W+1), max_q p] per sequence."""
+    SWA rows are drawn for positions [min_q max(0, p-W+1), max_q p] per sequence.
+    swa_scale_exp: with swa_fp8, each 64-dim block of an SWA row takes the scale
+    2^e, e uniform on [lo, hi] (the default (-6, -6) gives unit-scale rows)."""
     n_seq = len(ctx)
     dev = device
     q_seq = torch.tensor([s for s, _ in queries], dtype=torch.int32)
@@ -196,12 +198,13 @@ def build_layer(seed: int, *, ratio: int, H: int, ctx: list, queries: list, n_sl
     swa_codes = swa_scales = swa_rope = None
     if swa_fp8:
         # fp8 SWA rows in the compressed-row layout: random codes (N(0, 64)
-        # before the e4m3 cast) with the scale 2^-6, so that the rows are
-        # unit-scale like the bf16 SWA rows, and bf16 rope dims (swa_rows is
-        # then left unset)
+        # before the e4m3 cast) with per-block scales 2^U{lo..hi} (by default
+        # 2^-6, so that the rows are unit-scale like the bf16 SWA rows), and
+        # bf16 rope dims (swa_rows is then left unset)
         nrow = swa_rows.shape[0]
         swa_codes = _fp8_codes((nrow, DN), seed, "swa_codes", dev)
-        swa_scales = _pow2((nrow, DN // 64), seed, "swa_scales", dev, lo=-6, hi=-6)
+        swa_scales = _pow2((nrow, DN // 64), seed, "swa_scales", dev, lo=swa_scale_exp[0],
+                           hi=swa_scale_exp[1])
         swa_rope = _randn((nrow, DR), seed, "swa_rope", dev, torch.bfloat16)
         swa_rows = None
         swa_pool = P.cmp_pool_empty(nsb, dev)
