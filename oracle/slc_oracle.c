@@ -183,7 +183,10 @@ static int pow2_exponent_for(double amax)
         e--;
     while (amax > ldexp(OR_E4M3_MAX, e))
         e++;
-    return e;
+    /* the scale is stored as an fp32 power of two: below 2^-126 it would no
+     * longer be a normal fp32, so tinier blocks share that scale (their codes
+     * round toward zero) */
+    return e < -126 ? -126 : e;
 }
 
 /* The cache row format ["DeepseekV4Attention", cache block layout; "From
@@ -587,6 +590,8 @@ void oracle_mxfp4_quantise(int n, const float *y, uint8_t *codes4, uint8_t *e8m0
                     e--;
                 while (amax > ldexp(6.0, e))
                     e++;
+                if (e < -127)
+                    e = -127;      /* E8M0's smallest scale, byte 0 = 2^-127 */
             }
             scale = ldexp(1.0, e);
             e8m0[(size_t)s * 4 + b] = (uint8_t)(e + 127);

@@ -63,7 +63,8 @@ __device__ __forceinline__ void pool_token(PoolState &s, const uint16_t *kv, con
     state_add(s, 8, s_rope, bf16_to_f32(kr_rope));
 }
 
-// Smallest e with amax <= 448 * 2^e (exact comparisons); 0 for amax == 0.
+// Smallest e with amax <= 448 * 2^e (exact comparisons), at least -126; 0 for
+// amax == 0.
 __device__ __forceinline__ int pow2_exponent(float amax) {
     if (!(amax > 0.f)) return 0;
     int ex;
@@ -71,7 +72,9 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
     int e = ex - 9;
     while (amax > ldexpf(448.f, e)) e++;
     while (amax <= ldexpf(448.f, e - 1)) e--;
-    return e;
+    // the scale is stored as an fp32 power of two, normal down to 2^-126:
+    // tinier blocks share that scale (their codes round toward zero)
+    return e < -126 ? -126 : e;
 }
 
 // GPT-J RoPE of the lane's rope channel at position pos: the pair
@@ -115,7 +118,8 @@ __device__ __forceinline__ void quant_store(const float (&y)[9], int lane, slc_p
     if ((lane & 7) == 0) cmp_scale_ptr(pool, row)[lane >> 3] = ldexpf(1.f, e);
 }
 
-// Smallest e with amax <= 6 * 2^e (e2m1's largest magnitude); 0 for amax == 0.
+// Smallest e with amax <= 6 * 2^e (e2m1's largest magnitude), at least -127;
+// 0 for amax == 0.
 __device__ __forceinline__ int pow2_exponent_e2m1(float amax) {
     if (!(amax > 0.f)) return 0;
     int ex;
@@ -123,7 +127,7 @@ __device__ __forceinline__ int pow2_exponent_e2m1(float amax) {
     int e = ex - 3;
     while (amax > ldexpf(6.f, e)) e++;
     while (amax <= ldexpf(6.f, e - 1)) e--;
-    return e;
+    return e < -127 ? -127 : e;   // E8M0's smallest scale (byte 0 = 2^-127)
 }
 
 // Nearest e2m1 code of x (|x| <= 6 by the caller's scale), ties to the even

@@ -9,8 +9,9 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (bits16, check_attention, check_topk_sets, gpu_attention, gpu_index_topk,
-                     np_f32, np_i32, np_u8, oracle_attention, oracle_index_topk, to_device)
+from helpers import (bits16, check_attention, check_attention_scaled, check_topk_sets,
+                     gpu_attention, gpu_index_topk, np_f32, np_i32, np_u8, oracle_attention,
+                     oracle_index_topk, to_device, value_absmax)
 from sparse_long_context_compressor_amd import inputs as I
 from sparse_long_context_compressor_amd import pools as P
 
@@ -49,7 +50,11 @@ def _insert_case(seed=5):
     table[0, 2] = -1                         # positions 128..191 of sequence 0 have no block
     seq = torch.tensor([s for s, _ in toks], dtype=torch.int32)
     pos = torch.tensor([p for _, p in toks], dtype=torch.int32)
-    return toks, table, nb, seq, pos, _kv(len(toks), seed)
+    kv = _kv(len(toks), seed)
+    # one token's first 64-dim block is denormal-sized: its scale stops at
+    # 2^-126, the smallest normal fp32 power of two
+    kv[2, :64] = (kv[2, :64].float() * 2.0 ** -132).to(torch.bfloat16)
+    return toks, table, nb, seq, pos, kv
 
 
 def test_swa_insert_matches_oracle(S, oracle):
@@ -126,7 +131,30 @@ def test_attention_over_fp8_swa_matches_oracle(S, oracle, case, decode):
     check_attention(out, lse, out_ref, lse_ref)
 
 
-def test_insert_then_decode_chain(S, oracle):
+@pytest.mark.parametrize("decode", [True, False], ids=["decode", "prefill"])
+@pytest.mark.parametrize("case", list(SWA8_CASES))
+def test_attention_over_wide_scale_fp8_swa(S, oracle, case, decode):
+    """fp8 SWA rows whose 64-dim blocks take scales 2^-8 .. 2^-5 (so that a
+    per-block scale addressing slip changes the result), judged by the bar
+    that scales with the rows' values (check_attention_scaled): |g - o| <=
+    2e-2 + 2^-8 max|V_d| + one bf16 step at |o|, relative L2 <= 1e-2, lse
+    within 2e-2."""
+    lay = I.build_layer(64, swa_fp8=True, swa_scale_exp=(-8, -5), **SWA8_CASES[case])
+    sc = np_f32(lay.swa_scales)
+    assert len(np.unique(sc)) == 4 and np.any(sc[:, :, None] != sc[:, None, :])
+    idx = _list_of(lay)
+    out_ref, lse_ref = oracle_attention(oracle, lay, None if idx is None else idx.numpy())
+    vmax = value_absmax(oracle, lay, None if idx is None else idx.numpy())
+    to_device(lay)
+    out, lse = gpu_attention(S, lay, None if idx is None else idx.to("cuda"), decode=decode)
+    torch.cuda.synchronize()
+    e = check_attention_scaled(out, lse, out_ref, lse_ref, vmax)
+    print(f"{case} wide scales: max abs {e[0]:.3g} (max |o| {e[3]:.3g}, max |V| {e[4]:.3g}), "
+          f"rel L2 {e[1]:.3g}")
+
+
+@pytest.mark.parametrize("spread", [0.25, 2.0], ids=["unit_scale", "wide_scale"])
+def test_insert_then_decode_chain(S, oracle, spread):
     """New tokens' rows go through the insert into an fp8 pool and the decode
     attends to them: the oracle's insert feeds the oracle's attention, the
     kernel's insert feeds the kernel's decode."""
@@ -138,19 +166,27 @@ def test_insert_then_decode_chain(S, oracle):
     seq = np.repeat(np.arange(lay.n_seq, dtype=np.int32), counts)
     pos = np.concatenate([np.arange(b, b + c, dtype=np.int32)
                           for b, c in zip(np_i32(lay.swa_base), counts)])
-    kv = _kv(len(pos), 62, spread=0.25)     # unit-scale rows, as a normed latent is
+    # unit-scale rows, as a normed latent is; and rows whose 64-dim blocks
+    # span magnitudes e^(2 N(0,1)), judged by the bar that scales with |o|
+    kv = _kv(len(pos), 62, spread=spread)
     codes, scales, rope, _ = oracle.swa_insert(bits16(kv), pos, cs.numpy())
     lay.swa_codes = torch.from_numpy(codes)
     lay.swa_scales = torch.from_numpy(scales)
     lay.swa_rope = torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16)
     out_ref, lse_ref = oracle_attention(oracle, lay, idx.numpy())
+    vmax = value_absmax(oracle, lay, idx.numpy())
     to_device(lay)
     lay.swa_pool.zero_()
     S.swa_insert(kv.cuda(), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), cs.cuda(),
                  lay.swa_pool, lay.swa_table)
     out, lse = gpu_attention(S, lay, idx.cuda())
     torch.cuda.synchronize()
-    check_attention(out, lse, out_ref, lse_ref)
+    if spread < 1.0:
+        check_attention(out, lse, out_ref, lse_ref)
+    else:
+        e = check_attention_scaled(out, lse, out_ref, lse_ref, vmax)
+        print(f"wide-scale chain: max abs {e[0]:.3g} (max |o| {e[3]:.3g}, max |V| {e[4]:.3g}), "
+              f"rel L2 {e[1]:.3g}")
 
 
 def test_warm_select_over_fp8_swa_equals_select(S, oracle):

@@ -889,3 +889,34 @@ def test_mxfp4_quantiser(oracle):
     assert np.array_equal(_unpack_e2m1(c)[0] * 0.125, ex[0]) and np.all(e[0] == 127 - 3)
     assert np.all(e[1] == 127)
     assert np.array_equal(_unpack_e2m1(c)[1][:8], np.array([0, 1, 1, 2, 2, 4, 4, 6], np.float64))
+
+
+def test_scales_of_tiny_blocks_stay_in_range(oracle):
+    """Blocks of denormal-sized values: the fp8 row scale stops at 2^-126 (the
+    smallest normal fp32 power of two) and the MXFP4 block scale at E8M0's
+    byte 0 (2^-127), instead of leaving the stored format's range; codes then
+    follow from y / scale by the usual rounding."""
+    tiny = np.float32(3.0 * 2.0 ** -130)                   # a denormal fp32
+    assert oracle.pow2_scale(float(tiny)) == 2.0 ** -126
+    assert oracle.pow2_scale(448.0 * 2.0 ** -127) == 2.0 ** -126
+    assert oracle.pow2_scale(448.0 * 2.0 ** -125) == 2.0 ** -125
+    assert oracle.pow2_scale(448.0 * 2.0 ** -125 * (1 + 2.0 ** -20)) == 2.0 ** -124
+    # an fp8 SWA row whose first 64-dim block is tiny: scale 2^-126, codes of y * 2^126
+    kv = np.zeros((1, 576), np.float32)
+    kv[0, :64] = np.float32(2.0 ** -127) * np.resize(np.array([1, -3, 0.5, 2], np.float32), 64)
+    kv[0, 64:512] = 1.0
+    codes, scales, _, pre = oracle.swa_insert(oracle.bf16_encode(kv), np.array([0], np.int32),
+                                              np.tile(np.r_[np.ones(32), np.zeros(32)], (1, 1)).astype(np.float32))
+    assert scales[0, 0] == np.float32(2.0 ** -126) and scales[0, 1] == np.float32(2.0 ** -8)
+    assert np.array_equal(oracle.e4m3_decode(codes[0, :4]),
+                          np.array([0.5, -1.5, 0.25, 1.0]))
+    # MXFP4: amax 6 * 2^-127 needs no clamp; 3 * 2^-128 and smaller take byte 0
+    y = np.zeros((1, 128), np.float32)
+    y[0, :32] = np.float32(6.0 * 2.0 ** -127)
+    y[0, 32:64] = np.float32(3.0 * 2.0 ** -128)
+    y[0, 64:96] = np.float32(2.0 ** -140)
+    y[0, 96:] = 1.0
+    c4, e8 = oracle.mxfp4_quantise(y)
+    assert list(e8[0]) == [0, 0, 0, 127 - 2]          # amax 1 <= 6 * 2^-2
+    v = _unpack_e2m1(c4)[0]
+    assert np.all(v[:32] == 6.0) and np.all(v[32:64] == 1.5) and np.all(v[64:96] == 0.0)
