@@ -53,12 +53,76 @@ def near_midpoint(x: np.ndarray, rel=1e-5) -> np.ndarray:
     return d <= rel * np.maximum(a, 1e-30)
 
 
-def near_scale_boundary(amax: np.ndarray, rel=1e-5) -> np.ndarray:
-    """True where amax lies within rel of some 448 * 2^e."""
+def near_scale_boundary(amax: np.ndarray, rel=1e-5, win=None) -> np.ndarray:
+    """True where amax lies within rel (relative) plus win (absolute, same
+    shape, optional) of some 448 * 2^e."""
     a = np.maximum(amax.astype(np.float64), 1e-300)
     e = np.round(np.log2(a / 448.0))
     b = 448.0 * np.exp2(e)
-    return np.abs(a - b) <= rel * a
+    return np.abs(a - b) <= rel * a + (0.0 if win is None else win)
+
+
+def near_midpoint_within(v: np.ndarray, win: np.ndarray) -> np.ndarray:
+    """True where |v| lies within win (absolute, same shape) of an e4m3
+    rounding midpoint."""
+    mids = e4m3_midpoints()
+    a = np.abs(v.astype(np.float64))
+    j = np.clip(np.searchsorted(mids, a), 1, len(mids) - 1)
+    d = np.minimum(np.abs(a - mids[j - 1]), np.abs(a - mids[j]))
+    return d <= win
+
+
+# Relative size of the fp32 rounding in a compressed row before quantisation,
+# against the size of the terms it sums (see pool_magnitude): the window
+# weights' exponent arguments and exp (a few ulp of |s - m| <= ~10), the
+# window sum and the RMSNorm divisor over 576 dims come to a few 1e-6 at most;
+# 2^-16 (1.5e-5) leaves a margin over that.
+POOL_FP32_REL = 2.0 ** -16
+
+
+def pool_magnitude(kv: np.ndarray, score: np.ndarray, gamma: np.ndarray, eps: float, r: int,
+                   chunk: int = 128) -> np.ndarray:
+    """Per slot of one sequence (kv [L,576] values, score [L,576]) and dim:
+    M = gamma * (sum_t w_t |kv_t|) / (sum_t w_t) / rms, with w_t the window's
+    per-channel softmax weights and rms the slot's RMSNorm divisor, so that
+    |y| <= M (for the rope dims, the sum over the rotated pair).  The fp32 rounding of a pooled value is bounded relative to M,
+    not to |y|: the weights' rounding scales every term, and the terms can
+    cancel.  Windows as the compressor's (r = 4: [4j-4, 4j+3]; r = 128:
+    [128j, 128j+127]; clipped to [0, L))."""
+    L = kv.shape[0]
+    n = -(-L // r)
+    coff = 2 if r == 4 else 1
+    out = np.empty((n, 576))
+    for j0 in range(0, n, chunk):
+        j = np.arange(j0, min(n, j0 + chunk))
+        t = (r * j - (coff - 1) * r)[:, None] + np.arange(coff * r)[None, :]
+        ok = (t >= 0) & (t < L)
+        tc = np.clip(t, 0, L - 1)
+        x = kv[tc].astype(np.float64)
+        sc = np.where(ok[:, :, None], score[tc].astype(np.float64), -np.inf)
+        w = np.exp(sc - sc.max(axis=1, keepdims=True))
+        den = w.sum(axis=1)
+        pooled = (w * x).sum(axis=1) / den
+        absum = (w * np.abs(x)).sum(axis=1) / den
+        rms = np.sqrt(np.mean(pooled * pooled, axis=1) + eps)
+        out[j] = gamma[None, :] * absum / rms[:, None]
+    # RoPE mixes each pair (512+2i, 513+2i): either output sums terms of both
+    rp = out[:, 512::2] + out[:, 513::2]
+    out[:, 512::2] = rp
+    out[:, 513::2] = rp
+    return out
+
+
+def near_bf16_midpoint_within(x: np.ndarray, win: np.ndarray) -> np.ndarray:
+    """True where the fp32 value x lies within win (absolute) of a bf16
+    rounding midpoint (the fp32 patterns ending in 0x8000 around it)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    lower = u & np.uint32(0xFFFF0000)
+    mid_hi = (lower | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    mid_lo = np.where(lower & np.uint32(0x7FFF0000), (lower - np.uint32(0x8000)), lower).astype(
+        np.uint32).view(np.float32).astype(np.float64)
+    a = x.astype(np.float64)
+    return np.minimum(np.abs(a - mid_hi), np.abs(a - mid_lo)) <= win
 
 
 # ------------------------------------------------------------------ oracle side
@@ -166,6 +230,64 @@ def check_attention(out_gpu, lse_gpu, out_ref_bits, lse_ref, atol=2e-2, rel=1e-2
     assert rl2 <= rel, f"relative L2 err {rl2:.3g}"
     assert lerr <= atol, f"lse err {lerr:.3g}"
     return float(err.max()), rl2, lerr
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """One bf16 step at |x| (8 significant bits): 2^(floor(log2|x|) - 7); 0 at 0."""
+    m, e = np.frexp(np.abs(x.astype(np.float64)))
+    return np.where(m > 0, np.ldexp(1.0, e - 8), 0.0)
+
+
+def value_absmax(O, lay, idx):
+    """Per query and value dim d: the largest |V_d| over the rows the query
+    attends (its window and its valid compressed entries), [Q, 512]."""
+    swa = (oracle_swa_rows(O, lay).astype(np.uint32) << 16).view(np.float32)[:, :512]
+    qs, qp = np_i32(lay.q_seq), np_i32(lay.q_pos)
+    base, off = np_i32(lay.swa_base), lay.swa_off.cpu().numpy()
+    ns = np_i32(lay.n_slots)
+    out = np.zeros((lay.n_q, 512))
+    for t in range(lay.n_q):
+        b, p = int(qs[t]), int(qp[t])
+        lo = max(0, p - lay.W + 1)
+        rows = swa[off[b] + lo - base[b]: off[b] + p - base[b] + 1]
+        m = np.abs(rows).max(axis=0) if len(rows) else np.zeros(512)
+        if idx is not None and lay.ratio > 1:
+            sel = np.asarray(idx[t])
+            sel = sel[(sel >= 0) & (sel < ns[b])]
+            if len(sel):
+                r0 = int(lay.cmp_off[b]) + sel
+                v = fp8_values(np_u8(lay.cmp_codes)[r0]) * \
+                    np.repeat(np_f32(lay.cmp_scales)[r0].astype(np.float64), 64, axis=1)
+                m = np.maximum(m, np.abs(v).max(axis=0))
+        out[t] = m
+    return out
+
+
+def check_attention_scaled(out_gpu, lse_gpu, out_ref_bits, lse_ref, vmax, atol=2e-2, rel=1e-2):
+    """The attention bar for rows of any dynamic range.  The probabilities
+    enter the value product as bf16 (a relative rounding of 2^-9 each), so
+    output dim d of a query is off by up to 2^-9 times the weighted mean of
+    |V_d|, which is at most vmax[q, d] (value_absmax); the output's own
+    rounding to bf16 adds one step at |o|.  Per element:
+        |g - o| <= atol + 2^-8 vmax[q, d] + one bf16 step at |o|,
+    with the relative L2 error <= rel over all outputs and lse within atol.
+    For unit-scale rows (|V| of a few units) this is within 2e-2 of the plain
+    bar; it grows only where the rows' values do."""
+    g = out_gpu.float().cpu().numpy().astype(np.float64)
+    o = (out_ref_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(g - o)
+    fin = np.isfinite(lse_ref)
+    lg = lse_gpu.cpu().numpy()
+    assert np.array_equal(np.isfinite(lg), fin), "lse finiteness differs"
+    lerr = float(np.max(np.abs(lg[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    rl2 = float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30))
+    bar = atol + 2.0 ** -8 * np.asarray(vmax)[:, None, :] + bf16_ulp(o)
+    worst = int(np.argmax(err - bar))
+    assert np.all(err <= bar), \
+        f"abs err {err.flat[worst]:.3g} above {bar.flat[worst]:.3g} at |o| = {abs(o.flat[worst]):.3g}"
+    assert rl2 <= rel, f"relative L2 err {rl2:.3g}"
+    assert lerr <= atol, f"lse err {lerr:.3g}"
+    return float(err.max()), rl2, lerr, float(np.max(np.abs(o))), float(np.max(vmax))
 
 
 def check_topk_sets(gpu_idx, gpu_len, ref_scores_rows, nvis, k, rel=1e-6):

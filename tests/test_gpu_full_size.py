@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes, launched exactly as the benchmark
 launches them (same shapes, same split plan, same workspace); the oracle
 checks every query where it finishes in seconds, else a sample of queries
-chosen to include the first, the last and visibility-boundary positions.
+chosen to include the first, the last and visibility-boundary positions,
+with properties that hold at any size checked on every query.
 
 Workloads (synthetic, seeded): swaonly decode B=64 H=64 SWA 128; C4A decode
 B=32 H=64 64K context (16384 slots, indexer 64x128, top-k 512); C128A decode
@@ -114,43 +115,69 @@ def test_c128a_decode_128k_full(S, oracle, swa_fp8):
     print(f"c128a_decode_128k: max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
 
 
-PREFILL_SAMPLE = [0, 1, 2, 3, 4, 511, 1024, 1535, 2043, 2044, 2045, 2046, 2047]
+# the chunk's first and last 64 tokens (16 visibility steps at each end) and
+# 128 tokens at a stride of 15 through the middle (every residue mod 4)
+PREFILL_GROUPS = {
+    "head": list(range(0, 64)),
+    "mid_a": [64 + 15 * i for i in range(64)],
+    "mid_b": [64 + 15 * i for i in range(64, 128)],
+    "tail": list(range(1984, 2048)),
+}
 
 
-@pytest.mark.parametrize("fmt", ["bf16_swa", "fp8_swa_mxfp4_keys"])
-def test_c4a_prefill_2k_full(S, oracle, fmt):
-    """All 2048 tokens run on the GPU (index scores, top-k 2048, prefill
-    attention); the oracle checks a sample of tokens that includes the
-    chunk's ends and tokens on both sides of a visibility step.  The second
-    case runs the same chunk over an fp8 SWA pool with MXFP4 index keys."""
-    alt = fmt != "bf16_swa"
+@pytest.fixture(scope="module", params=["bf16_swa", "fp8_swa_mxfp4_keys"])
+def prefill_run(request):
+    """All 2048 tokens on the GPU once per format (index scores, top-k 2048,
+    prefill attention); the second format runs the same chunk over an fp8 SWA
+    pool with MXFP4 index keys.  Results are kept on the host."""
+    from sparse_long_context_compressor_amd import slc as S
+    alt = request.param != "bf16_swa"
     lay = I.c4a_prefill_2k(swa_fp8=alt, key_fp4=alt)
-    qs = np.array(PREFILL_SAMPLE)
-    t0 = time.perf_counter()
-    idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay, queries=qs)
-    out_ref, lse_ref = oracle_attention(oracle, lay, idx_ref, queries=qs)
-    print(f"oracle {time.perf_counter() - t0:.1f} s", flush=True)
+    host = I.c4a_prefill_2k(swa_fp8=alt, key_fp4=alt)      # the oracle's copy
     to_device(lay)
     sc, idx, ln = gpu_index_topk(S, lay)
     out, lse = gpu_attention(S, lay, idx, decode=False)
     torch.cuda.synchronize()
-    nv_all = nvis_of(lay, 4)
-    ln_h = ln.cpu().numpy()
-    assert np.array_equal(ln_h, np.minimum(nv_all, lay.k))
-    qt = torch.as_tensor(qs, device=sc.device)
-    sc_s = sc[qt].cpu().numpy()
-    idx_s = idx[qt].cpu().numpy()
-    nv = nv_all[qs]
+    res = dict(fmt=request.param, lay=host, sc=sc.cpu().numpy(), idx=idx.cpu().numpy(),
+               ln=ln.cpu().numpy(), out=out.cpu(), lse=lse.cpu())
+    del lay, sc, idx, ln, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def test_c4a_prefill_2k_all_tokens(prefill_run):
+    """Every token: list length min(k, n_vis), the list is exactly the top-k
+    of the GPU's own scores (ties to the lower slot), and the attention
+    output and lse are finite (each list is non-empty)."""
+    r = prefill_run
+    lay = r["lay"]
+    nv = nvis_of(lay, 4)
     assert nv[0] == 32256 and nv[3] == 32257 and nv[-1] == 32768
+    assert np.array_equal(r["ln"], np.minimum(nv, lay.k))
+    assert np.array_equal(r["idx"], exact_topk_of(r["sc"], nv, lay.k))
+    assert torch.isfinite(r["lse"]).all() and torch.isfinite(r["out"].float()).all()
+
+
+@pytest.mark.parametrize("group", list(PREFILL_GROUPS))
+def test_c4a_prefill_2k_against_oracle(prefill_run, oracle, group):
+    """The oracle on 64 of the chunk's tokens per group (256 in all): scores,
+    top-k sets with the near-tie rule, and attention where the GPU's and the
+    oracle's selections are the same set."""
+    r = prefill_run
+    lay = r["lay"]
+    qs = np.array(PREFILL_GROUPS[group])
+    t0 = time.perf_counter()
+    idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay, queries=qs)
+    out_ref, lse_ref = oracle_attention(oracle, lay, idx_ref, queries=qs)
+    print(f"oracle {time.perf_counter() - t0:.1f} s", flush=True)
+    nv = nvis_of(lay, 4)[qs]
+    sc_s, idx_s = r["sc"][qs], r["idx"][qs]
     check_scores(sc_s, sc_ref, nv)
-    near = check_topk_sets(idx_s, ln_h[qs], sc_ref, nv, lay.k)
-    assert np.array_equal(idx_s, exact_topk_of(sc_s, nv, lay.k))
+    near = check_topk_sets(idx_s, r["ln"][qs], sc_ref, nv, lay.k)
     same = sets_equal(idx_s, idx_ref)
     assert sum(same) >= len(qs) - near
     keep = np.nonzero(same)[0]
-    kt = qt[torch.as_tensor(keep, device=sc.device)]
-    e = check_attention(out[kt], lse[kt], out_ref[keep], lse_ref[keep])
-    # every token's output is finite and its lse is finite (each list is non-empty)
-    assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
-    print(f"c4a_prefill_2k ({fmt}): near-tie slots {near}; {len(keep)}/{len(qs)} sampled tokens "
-          f"compared; max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
+    kt = torch.as_tensor(qs[keep])
+    e = check_attention(r["out"][kt], r["lse"][kt], out_ref[keep], lse_ref[keep])
+    print(f"c4a_prefill_2k ({r['fmt']}, {group}): near-tie slots {near}; {len(keep)}/{len(qs)} "
+          f"tokens compared; max abs {e[0]:.3g} rel L2 {e[1]:.3g} lse {e[2]:.3g}")
