@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 
@@ -498,6 +499,73 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
                                               ((per * kDN * sizeof(uint16_t) + 15) & ~static_cast<size_t>(15)));
     }
     return hip_status(launch_attention(a, decode, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- no-allocation decode
+// The decode's split partials in a library-owned device array instead of a
+// caller workspace.  In host code `scratch` names a host-side stand-in, not
+// device memory: only the address hipGetSymbolAddress returns for the
+// current device may reach a kernel or a copy.  Each GPU holds its own copy
+// until the process ends.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, resolved once per device.
+slc_status_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return fail("sparse_mla_decode_noalloc: device id out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!ptr) return fail("sparse_mla_decode_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SLC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t slc_sparse_mla_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+slc_status_t slc_sparse_mla_decode_noalloc(int layer_type, int n_q, int n_heads,
+                                           const uint16_t *q, const int32_t *q_seq,
+                                           const int32_t *q_pos, int window, slc_pool_t swa_pool,
+                                           slc_pool_t cmp_pool, const int32_t *cmp_idx, int k,
+                                           const int32_t *n_slots, float sm_scale, uint16_t *out,
+                                           float *lse, void *stream) {
+    // the size check is host arithmetic and comes before any device call
+    const int kk = (layer_type & ~SLC_SWA_FP8) == SLC_LAYER_SWAONLY ? 0 : k;
+    const size_t need = n_q > 0 && n_heads > 0 && kk >= 0 && window >= 0
+                            ? attn_ws(n_q, n_heads, window, kk, true) : 0;
+    if (need > kScratchBytes) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "sparse_mla_decode_noalloc: these shapes need %zu bytes of split partials, "
+                      "above the %zu-byte static scratch; use slc_sparse_mla_decode with a workspace",
+                      need, kScratchBytes);
+        return SLC_ERR_WORKSPACE;
+    }
+    void *ws = nullptr;
+    if (need > 0) {
+        slc_status_t st = scratch_of_current_device(&ws);
+        if (st != SLC_OK) return st;
+    }
+    return sparse_mla(true, layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool, cmp_pool,
+                      cmp_idx, k, n_slots, sm_scale, out, lse, ws, need, stream);
 }
 
 slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,

@@ -31,6 +31,7 @@ EXPORTED = [
     "slc_compress_index_keys_stream_step", "slc_decode_step_writers",
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill", "slc_workspace_size",
+    "slc_sparse_mla_decode_noalloc", "slc_sparse_mla_decode_noalloc_max_bytes",
 ]
 
 OP_INDEX_TOPK, OP_SPARSE_MLA_DECODE, OP_SPARSE_MLA_PREFILL = 1, 2, 3
@@ -117,6 +118,11 @@ def lib():
             g = getattr(L, name + "_workspace_size")
             g.restype = sz
             g.argtypes = [i32, i32, i32, i32]
+        L.slc_sparse_mla_decode_noalloc.restype = i32
+        L.slc_sparse_mla_decode_noalloc.argtypes = [i32, i32, i32, vp, vp, vp, i32, pool, pool, vp,
+                                                    i32, vp, f32, vp, vp, vp]
+        L.slc_sparse_mla_decode_noalloc_max_bytes.restype = sz
+        L.slc_sparse_mla_decode_noalloc_max_bytes.argtypes = []
         L.slc_workspace_size.restype = sz
         L.slc_workspace_size.argtypes = [i32, C.POINTER(Shape)]
         _lib = L
@@ -375,3 +381,20 @@ def sparse_mla_prefill(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table,
                        lse=None, workspace=None):
     _sparse_mla(False, layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
                 cmp_table, cmp_idx, n_slots, sm_scale, out, lse, workspace)
+
+
+def sparse_mla_decode_noalloc(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table,
+                              cmp_pool=None, cmp_table=None, cmp_idx=None, n_slots=None,
+                              sm_scale=1.0, out=None, lse=None):
+    """slc_sparse_mla_decode_noalloc: the decode with its split partials in the
+    library's static device array (no workspace, no allocation)."""
+    n_q, H = int(q.shape[0]), int(q.shape[1])
+    k = 0 if cmp_idx is None else int(cmp_idx.shape[1])
+    _check(lib().slc_sparse_mla_decode_noalloc(
+        int(layer_type), n_q, H, _ptr(q), _ptr(q_seq), _ptr(q_pos), int(window),
+        pool(swa_pool, swa_table), pool(cmp_pool, cmp_table), _ptr(cmp_idx), k, _ptr(n_slots),
+        float(sm_scale), _ptr(out), _ptr(lse), _stream()))
+
+
+def sparse_mla_decode_noalloc_max_bytes() -> int:
+    return int(lib().slc_sparse_mla_decode_noalloc_max_bytes())

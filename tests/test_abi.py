@@ -123,6 +123,22 @@ def test_workspace_size_dispatches_to_the_per_op_sizers(S):
     assert L.slc_workspace_size(S.OP_INDEX_TOPK, None) == size_max
 
 
+def test_noalloc_decode_rejects_oversized_shapes_before_any_device_call(S):
+    """The no-allocation decode checks its partials' size against its static
+    array on the host (SLC_ERR_WORKSPACE), before it touches a device."""
+    L = S.lib()
+    assert L.slc_sparse_mla_decode_noalloc_max_bytes() == 32 << 20
+    fake = C.c_void_p(256)
+    pool = S.Pool(C.c_void_p(256), C.c_void_p(256), 4, 4)
+    assert L.slc_sparse_mla_decode_workspace_size(4096, 128, 1024, 4096) > (32 << 20)
+    st = L.slc_sparse_mla_decode_noalloc(4, 4096, 128, fake, fake, fake, 1024, pool, pool, fake,
+                                         4096, fake, 0.1, fake, None, None)
+    assert st == 2 and b"static scratch" in L.slc_last_error()
+    # argument errors come first, as for the workspace form
+    assert L.slc_sparse_mla_decode_noalloc(2, 1, 64, fake, fake, fake, 128, pool, pool, None, 0,
+                                           None, 0.1, fake, None, None) == 1
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from sparse_long_context_compressor_amd import slc
     monkeypatch.setattr(slc, "LIB_PATH", str(tmp_path / "missing.so"))
