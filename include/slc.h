@@ -511,14 +511,15 @@ slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const u
  * cannot allocate device memory or pass a workspace: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  The same
  * kernels and results; the split partials go to a static device array of
- * slc_sparse_mla_decode_noalloc_max_bytes() bytes (32 MiB) that the library
+ * slc_sparse_mla_decode_noalloc_max_bytes() bytes (12 MiB) that the library
  * holds on each GPU it runs on until the process ends.  Its device address
  * is resolved on the first call on each device (with that device current).
  * The call allocates nothing (no hipMalloc, no library allocation).
  *   Arguments and results as slc_sparse_mla_decode, without the workspace.
  *   Shapes whose partials exceed the array (slc_sparse_mla_decode_workspace_size
  *   above the maximum) return SLC_ERR_WORKSPACE before any launch; the 64K
- *   decode (32 queries, 64 heads, window 128, top-k 512) needs about 8.5 MB.
+ *   decode (32 queries, 64 heads, window 128, top-k 512) needs about 8.5 MB;
+ *   the split plan bounds any shape's partials by about 17 MB.
  *   Nothing in the array needs to start cleared: every partial is written
  *   before it is merged.  All calls on one GPU share the array, so calls that
  *   may overlap on one GPU (other streams, other host threads) race.

@@ -427,13 +427,12 @@ size_t slc_workspace_size(slc_op_t op, const slc_shape_t *shape) {
     return SIZE_MAX;
 }
 
-static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads,
-                               const uint16_t *q, const int32_t *q_seq, const int32_t *q_pos,
-                               int window, slc_pool_t swa_pool, slc_pool_t cmp_pool,
-                               const int32_t *cmp_idx, int k, const int32_t *n_slots,
-                               float sm_scale, uint16_t *out, float *lse, void *workspace,
-                               size_t ws_bytes, void *stream) {
-    const bool swa_fp8 = (layer_type & SLC_SWA_FP8) != 0;
+// The attention calls' argument checks (everything but the workspace).
+static slc_status_t mla_args_check(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                   const int32_t *q_seq, const int32_t *q_pos, int window,
+                                   slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                                   const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                                   float sm_scale, uint16_t *out) {
     layer_type &= ~SLC_SWA_FP8;
     if (layer_type != SLC_LAYER_SWAONLY && layer_type != SLC_LAYER_C4A &&
         layer_type != SLC_LAYER_C128A)
@@ -463,6 +462,20 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
         if (k > 0 && (!cmp_idx || !n_slots))
             return fail("sparse_mla: cmp_idx and n_slots are required for C4A / C128A");
     }
+    return SLC_OK;
+}
+
+static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads,
+                               const uint16_t *q, const int32_t *q_seq, const int32_t *q_pos,
+                               int window, slc_pool_t swa_pool, slc_pool_t cmp_pool,
+                               const int32_t *cmp_idx, int k, const int32_t *n_slots,
+                               float sm_scale, uint16_t *out, float *lse, void *workspace,
+                               size_t ws_bytes, void *stream) {
+    slc_status_t st = mla_args_check(layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool,
+                                     cmp_pool, cmp_idx, k, n_slots, sm_scale, out);
+    if (st != SLC_OK || n_q == 0) return st;
+    const bool swa_fp8 = (layer_type & SLC_SWA_FP8) != 0;
+    layer_type &= ~SLC_SWA_FP8;
     int kk = layer_type == SLC_LAYER_SWAONLY ? 0 : k;
     int splits, cps, groups;
     attention_plan(n_q, n_heads, window, kk, decode, &splits, &cps, &groups);
@@ -511,7 +524,7 @@ static slc_status_t sparse_mla(bool decode, int layer_type, int n_q, int n_heads
 // until the process ends.
 namespace {
 
-constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchBytes = size_t(12) << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -548,7 +561,11 @@ slc_status_t slc_sparse_mla_decode_noalloc(int layer_type, int n_q, int n_heads,
                                            slc_pool_t cmp_pool, const int32_t *cmp_idx, int k,
                                            const int32_t *n_slots, float sm_scale, uint16_t *out,
                                            float *lse, void *stream) {
-    // the size check is host arithmetic and comes before any device call
+    // the argument and size checks are host arithmetic and come before any
+    // device call
+    slc_status_t st0 = mla_args_check(layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool,
+                                      cmp_pool, cmp_idx, k, n_slots, sm_scale, out);
+    if (st0 != SLC_OK || n_q == 0) return st0;
     const int kk = (layer_type & ~SLC_SWA_FP8) == SLC_LAYER_SWAONLY ? 0 : k;
     const size_t need = n_q > 0 && n_heads > 0 && kk >= 0 && window >= 0
                             ? attn_ws(n_q, n_heads, window, kk, true) : 0;

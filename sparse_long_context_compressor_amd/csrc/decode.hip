@@ -1,0 +1,553 @@
+// decode.hip -- sparse MLA decode in absorbed (MQA) form: H query heads
+// against one shared 576-wide latent row per attended entry, values from the
+// row's first 512 dims ("From MLA to CSA + HCA", Ch.2), over the sliding
+// window plus the compressed slots of the query's list ("DeepSeek-V4
+// attention layer types", Indexer / C4A / C128A: the attention takes the SWA
+// indices together with the compressed top-k indices; "DeepseekV4Attention"
+// (devpress), _forward_decode).
+//
+// One workgroup of eight waves per (query, block of 16*HG heads, list split).
+// A split takes a contiguous share of the window entries and of the
+// compressed entries, and loads all of its rows into LDS at once with
+// gfx950's direct global->LDS 16-byte loads, as they are stored: window rows
+// as bf16 (or fp8 rows with their scales, for an fp8 window pool), compressed
+// rows as e4m3 codes + bf16 rope + 8 fp32 scales.  Nothing is dequantised
+// into LDS:
+//   S^T = K . Q^T  v_mfma_f32_16x16x32_bf16; a lane's K operand is 16 bytes
+//                  of one row that lie in one 64-dim scale block, converted
+//                  exactly to bf16 with that block's scale on the way
+//                  (v_cvt_scalef32_pk_bf16_fp8).  The MFMA k-order is a fixed
+//                  permutation of the 576 dims, the same for K and Q.
+//   O^T += V^T . P^T  the V^T operand comes straight from the row-major rows
+//                  with the transposing LDS reads (ds_read_b64_tr_b8 for fp8
+//                  codes, ds_read_b64_tr_b16 for bf16 rows); within one
+//                  64-dim block of the output each compressed row has
+//                  exactly one scale, which is folded into that row's
+//                  probability (a power of two: exact).
+// Lists longer than one LDS load of rows are taken in passes with an online
+// softmax between them.  Splits of one query write normalised partial
+// states; mla_combine_kernel merges them (attention.hip).
+
+#include "slc_internal.hpp"
+
+namespace slc {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kB16Pitch = 2 * kD + 16;          // bytes per bf16 row in LDS (1168)
+constexpr int kF8Pitch = 688;                   // 512 codes | 64 bf16 rope | 8 fp32 scales | pad
+constexpr int kF8Data = SLC_CMP_ROW_BYTES;      // 640: codes + rope, then the scales
+constexpr int kRowBytes = 133 * 1024;           // LDS for one pass's rows
+constexpr int kMaxPassRows = 192;               // rows of one pass (a multiple of 32)
+constexpr int kMaxKsteps = kMaxPassRows / 32;
+constexpr int kOutPitch = 144;                  // bytes per head in the output stage (64 dims + pad)
+// Q of one head group is staged here, later the P^T operands (both fit)
+constexpr int kQpBytes = kMaxKsteps * 2 * 2 * 64 * 16;
+static_assert(16 * kB16Pitch <= kQpBytes, "one head group of Q fits the P^T region");
+static_assert(kWaves * 32 * kOutPitch <= kRowBytes, "the output is staged in the row region");
+
+static_assert(kF8Pitch % 16 == 0 && (kF8Pitch / 16) % 2 == 1, "16-byte reads of 8 rows hit distinct banks");
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Rows of skipped or padding entries are loaded from here (never written),
+// so every row in LDS holds finite values.
+__device__ __attribute__((aligned(256))) uint8_t kDecZeroPage[2048];
+
+// One direct global->LDS load of 16 bytes per active lane: lane l's bytes
+// land at dst + off + 16 l (dst wave-uniform); off is added to src as well.
+template <int OFF>
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, OFF, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint8_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 times a power-of-two scale, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1, float scale) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), scale, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), scale, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), scale, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), scale, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+}  // namespace
+
+// Wait until at most n (wave-uniform, clamped to 31) of this wave's vector
+// memory operations are outstanding; a larger n waits as for 31, which is
+// never too short.
+__device__ __forceinline__ void wait_vmem_at_most(int n) {
+#define SLC_VM_CASE(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | 0x70 | 0xF00 | (((k) >> 4) << 14)); break;
+    switch (n < 31 ? (n < 0 ? 0 : n) : 31) {
+        SLC_VM_CASE(0) SLC_VM_CASE(1) SLC_VM_CASE(2) SLC_VM_CASE(3) SLC_VM_CASE(4) SLC_VM_CASE(5)
+        SLC_VM_CASE(6) SLC_VM_CASE(7) SLC_VM_CASE(8) SLC_VM_CASE(9) SLC_VM_CASE(10) SLC_VM_CASE(11)
+        SLC_VM_CASE(12) SLC_VM_CASE(13) SLC_VM_CASE(14) SLC_VM_CASE(15) SLC_VM_CASE(16)
+        SLC_VM_CASE(17) SLC_VM_CASE(18) SLC_VM_CASE(19) SLC_VM_CASE(20) SLC_VM_CASE(21)
+        SLC_VM_CASE(22) SLC_VM_CASE(23) SLC_VM_CASE(24) SLC_VM_CASE(25) SLC_VM_CASE(26)
+        SLC_VM_CASE(27) SLC_VM_CASE(28) SLC_VM_CASE(29) SLC_VM_CASE(30)
+        default: __builtin_amdgcn_s_waitcnt((31 & 15) | 0x70 | 0xF00 | (1 << 14)); break;
+    }
+#undef SLC_VM_CASE
+}
+
+// Grid: ceil(n_q / 8) * 8 * HB * S workgroups of 512 threads, HB = n_heads /
+// (16 HG).  Blocks of one query share blockIdx % 8 (one XCD, one L2).
+// F8: the window pool holds fp8 rows in the compressed-row layout.
+//
+// A workgroup: resolve the pass's rows, issue all their loads, then take the
+// pass in stages of k-steps (32 rows): each stage waits only for its own
+// rows, so its scores and value products run while later rows land.  A
+// 16-row tile's scores are computed for 16 heads by a wave of that head
+// group; a wave's value products cover one 64-dim output block (one scale
+// per row) of every head.
+template <int HG, bool F8>
+__global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t rows[kRowBytes];
+    // Q staging (one head group at a time) and, after, the P^T operands
+    __shared__ __attribute__((aligned(16))) uint8_t qp[kQpBytes];
+    __shared__ __attribute__((aligned(16))) int32_t rid[kMaxPassRows];            // physical rows
+    __shared__ float cm[kWaves][1][16];                                           // wave maxima
+    __shared__ float lp[kWaves][16];                                              // wave sums
+    f32x4 (*pfrag)[HG][2][64] = reinterpret_cast<f32x4 (*)[HG][2][64]>(qp);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+
+    // the prologue's kernel arguments in one round of loads
+    const int32_t *q_seq_p = a.q_seq, *q_pos_p = a.q_pos, *n_slots_p = a.n_slots;
+    const int32_t *cmp_idx_p = a.cmp_idx, *swa_tab = a.swa.block_table, *cmp_tab = a.cmp.block_table;
+    const int swa_stride = a.swa.table_stride, cmp_stride = a.cmp.table_stride;
+    const int64_t swa_nb = a.swa.n_blocks, cmp_nb = a.cmp.n_blocks;
+    const int window = a.window, kk = a.k, n_q = a.n_q, S = a.n_splits;
+    const int HB = a.n_heads / (16 * HG);
+    __asm__ volatile("" ::"s"(q_seq_p), "s"(q_pos_p), "s"(n_slots_p), "s"(cmp_idx_p), "s"(swa_tab),
+                     "s"(cmp_tab), "s"(swa_stride), "s"(cmp_stride), "s"(swa_nb), "s"(cmp_nb),
+                     "s"(window), "s"(kk), "s"(n_q), "s"(S), "s"(HB));
+
+    const int per_group = 8 * HB * S;
+    const int grp = blockIdx.x / per_group, rem = blockIdx.x % per_group;
+    const int t = 8 * grp + (rem & 7);
+    const int hb = (rem >> 3) % HB, split = (rem >> 3) / HB;
+    if (t >= n_q) return;                                         // uniform per workgroup
+
+    // ---- Q loads first (they depend on nothing): the block's heads are one
+    // contiguous run, 16-byte units u -> head u / 72, bytes 16 (u % 72)
+    constexpr int kQUnits = 16 * HG * kD / 8;
+    constexpr int kQIt = (kQUnits + kThreads - 1) / kThreads;
+    u32x4 qv[kQIt];
+    {
+        const uint16_t *qsrc = a.q + (static_cast<int64_t>(t) * a.n_heads + 16 * HG * hb) * kD;
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = tid + kThreads * i;
+            if (u < kQUnits) qv[i] = *reinterpret_cast<const u32x4 *>(qsrc + 8 * u);
+        }
+    }
+    const int seq = q_seq_p[t], p = q_pos_p[t];
+    const int ns = kk > 0 ? n_slots_p[seq] : 0;
+
+    // this split's shares of the window and of the compressed list
+    const int sw0 = split * a.sw_per, sw1 = min(window, sw0 + a.sw_per);
+    const int cm0 = split * a.cm_per, cm1 = min(kk, cm0 + a.cm_per);
+    const int n_sw = max(0, sw1 - sw0), n_cm = max(0, cm1 - cm0);
+    const int sw_cap = a.sw_cap, cm_cap = a.cm_cap;
+    const int passes = max(n_sw > 0 ? (n_sw + sw_cap - 1) / sw_cap : 0,
+                           n_cm > 0 ? (n_cm + cm_cap - 1) / cm_cap : 0);
+
+    f32x4 o[4][HG];
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int hg = 0; hg < HG; hg++) o[dt][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; hg++) m_run[hg] = -INFINITY;
+    float l_part = 0.f;                                           // the wave's rows' share of its head group's sums
+    const float sm2 = a.sm_scale_log2;
+    const int hgw = HG == 2 ? (w & 1) : 0;                         // the wave's head group (scores)
+    bf16x8 qb[9][2];                                              // its Q^T operands
+
+    for (int pass = 0; pass < passes; pass++) {
+        // ---- this pass's rows: window rows first (padded to 32), then
+        // compressed rows (padded to 32)
+        const int e_sw = sw0 + pass * sw_cap, e_cm = cm0 + pass * cm_cap;
+        const int nsw = max(0, min(sw_cap, sw1 - e_sw)), ncm = max(0, min(cm_cap, cm1 - e_cm));
+        const int nsw_pad = (nsw + 31) & ~31, ncm_pad = (ncm + 31) & ~31;
+        const int R = nsw_pad + ncm_pad;
+        const int f8base = F8 ? 0 : nsw_pad * kB16Pitch;          // byte offset of the fp8 rows
+        const int f8first = F8 ? 0 : nsw_pad;                     // first row kept as fp8
+
+        // resolve: thread j -> physical row of pass row j (-1: skipped/padding)
+        if (tid < R) {
+            int32_t phys = -1;
+            if (tid < nsw_pad) {
+                const int pos = p - window + 1 + e_sw + tid;
+                const int64_t lb = pos >> 6;
+                if (tid < nsw && pos >= 0 && lb < swa_stride) {
+                    const int32_t pb = swa_tab[static_cast<int64_t>(seq) * swa_stride + lb];
+                    if (pb >= 0 && pb < swa_nb) phys = pb * kBR + (pos & (kBR - 1));
+                }
+            } else {
+                const int j = tid - nsw_pad;
+                if (j < ncm) {
+                    const int s = cmp_idx_p[static_cast<int64_t>(t) * kk + e_cm + j];
+                    const int64_t lb = s >> 6;
+                    if (s >= 0 && s < ns && lb < cmp_stride) {
+                        const int32_t pb = cmp_tab[static_cast<int64_t>(seq) * cmp_stride + lb];
+                        if (pb >= 0 && pb < cmp_nb) phys = pb * kBR + (s & (kBR - 1));
+                    }
+                }
+            }
+            rid[tid] = phys;
+        }
+        if (pass == 0) {
+            // head group 0 of Q into the staging region
+#pragma unroll
+            for (int i = 0; i < kQIt; i++) {
+                const int u = tid + kThreads * i;
+                if (u < 16 * kD / 8)
+                    *reinterpret_cast<u32x4 *>(qp + (u / (kD / 8)) * kB16Pitch + 16 * (u % (kD / 8))) = qv[i];
+            }
+        }
+        __syncthreads();                                          // rid (and Q group 0) ready
+
+        // ---- issue every load of the pass: wave w takes pass rows w, w+8,
+        // ...; all their ids are read first, so that no LDS access sits
+        // between the loads.  Stages: k-steps [0, KA) first, then the rest.
+        const int K = R / 32;
+        const int KA = K <= 1 ? K : (K + 1) / 2;
+        const int rowsA = 32 * KA;
+        int later = 0;                                            // this wave's loads of stage 2
+        {
+            const int myr = w + kWaves * lane;
+            const int32_t my_id = myr < R ? rid[myr] : -1;
+            const int nr = (R - w + kWaves - 1) / kWaves;
+            const uint8_t *swa_b = reinterpret_cast<const uint8_t *>(a.swa.base);
+            const uint8_t *cmp_b = reinterpret_cast<const uint8_t *>(a.cmp.base);
+            for (int i = 0; i < nr; i++) {
+                const int r = w + kWaves * i;
+                const int32_t id = __builtin_amdgcn_readlane(my_id, i);
+                const bool f8row = F8 || r >= nsw_pad;
+                const bool from_swa = r < nsw_pad;
+                if (f8row) {
+                    // 40 lanes: 640 bytes of codes and rope; 2 lanes: the 32 bytes of scales
+                    const uint8_t *blk = (from_swa ? swa_b : cmp_b) +
+                                         static_cast<int64_t>(id >> 6) * SLC_CMP_BLOCK_BYTES;
+                    const uint8_t *src = lane < 40 ? blk + (id & 63) * SLC_CMP_ROW_BYTES + 16 * lane
+                                                   : blk + SLC_CMP_SCALE_OFFSET + (id & 63) * 32 + 16 * (lane - 40);
+                    if (id < 0) src = kDecZeroPage + 16 * lane;
+                    if (lane < 42) dma16<0>(src, rows + f8base + (r - f8first) * kF8Pitch);
+                    later += r >= rowsA ? 1 : 0;
+                } else {
+                    const uint8_t *src = id >= 0 ? swa_b + static_cast<int64_t>(id) * (2 * kD) + 16 * lane
+                                                 : kDecZeroPage + 16 * lane;
+                    uint8_t *dst = rows + r * kB16Pitch;
+                    dma16<0>(src, dst);
+                    if (lane < 8) dma16<1024>(src, dst);
+                    later += r >= rowsA ? 2 : 0;
+                }
+            }
+        }
+
+        if (pass == 0) {
+            // the wave's head group's Q^T operands, in the k-order of the K
+            // operand: k-step (s, h), lane (g, c) -> head c, dims 64 s + 16 g +
+            // 8 h + 0..7.  Group 0 is staged; group 1 replaces it once every
+            // wave has read group 0.
+#pragma unroll
+            for (int hg = 0; hg < HG; hg++) {
+                if (hg > 0) {
+                    __syncthreads();                              // group hg-1 read
+#pragma unroll
+                    for (int i = 0; i < kQIt; i++) {
+                        const int u = tid + kThreads * i - hg * (16 * kD / 8);
+                        if (u >= 0 && u < 16 * kD / 8)
+                            *reinterpret_cast<u32x4 *>(qp + (u / (kD / 8)) * kB16Pitch + 16 * (u % (kD / 8))) = qv[i];
+                    }
+                    __syncthreads();                              // group hg staged
+                }
+                if (hg == hgw) {
+                    const uint8_t *qr = qp + c * kB16Pitch + 32 * g;
+#pragma unroll
+                    for (int s = 0; s < 9; s++)
+#pragma unroll
+                        for (int h = 0; h < 2; h++) qb[s][h] = ld_bf16x8(qr + 128 * s + 16 * h);
+                }
+            }
+        }
+
+        for (int stage = 0; stage < 2; stage++) {
+            const int k0 = stage == 0 ? 0 : KA, k1 = stage == 0 ? KA : K;
+            if (k0 >= k1) break;                                  // uniform
+            if (stage == 0) wait_vmem_at_most(later);
+            else __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                                      // the stage's rows are in LDS
+
+            // ---- scores: tile tau (rows 16 tau .. +15) of the stage for head
+            // group hgw, by waves of that group in turn
+            constexpr int kPerGroup = kWaves / HG;                // waves per head group
+            constexpr int kTilesPerWave = kMaxPassRows / 32 / kPerGroup + 1;
+            const int T0 = 2 * k0, T1 = 2 * k1;
+            const int wq = w / HG;                                // rank within the group
+            float x[kTilesPerWave][4];
+            float wmax = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kTilesPerWave; j++) {
+                const int tau = T0 + wq + kPerGroup * j;
+                if (tau < T1) {                                   // wave-uniform
+                    const int r0 = 16 * tau;
+                    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+                    if (F8 || r0 >= nsw_pad) {
+                        const uint8_t *kr = rows + f8base + (r0 - f8first + c) * kF8Pitch;
+                        const f32x4 sc0 = *reinterpret_cast<const f32x4 *>(kr + kF8Data);
+                        const f32x4 sc1 = *reinterpret_cast<const f32x4 *>(kr + kF8Data + 16);
+                        const float scl[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+#pragma unroll
+                        for (int s = 0; s < 8; s++) {
+                            const u32x4 v = *reinterpret_cast<const u32x4 *>(kr + 64 * s + 16 * g);
+                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(v[0], v[1], scl[s]), qb[s][0], acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(v[2], v[3], scl[s]), qb[s][1], acc1, 0, 0, 0);
+                        }
+                        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(kr + kDN + 32 * g), qb[8][0], acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(kr + kDN + 32 * g + 16), qb[8][1], acc1, 0, 0, 0);
+                    } else {
+                        const uint8_t *kr = rows + (r0 + c) * kB16Pitch + 32 * g;
+#pragma unroll
+                        for (int s = 0; s < 9; s++) {
+                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(kr + 128 * s), qb[s][0], acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_bf16x8(kr + 128 * s + 16), qb[s][1], acc1, 0, 0, 0);
+                        }
+                    }
+                    const u32x4 valid = *reinterpret_cast<const u32x4 *>(rid + r0 + 4 * g);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        x[j][i] = static_cast<int32_t>(valid[i]) >= 0 ? (acc0[i] + acc1[i]) * sm2 : -INFINITY;
+                        wmax = fmaxf(wmax, x[j][i]);
+                    }
+                }
+            }
+            wmax = xor32_max(xor16_max(wmax));
+            if (g == 0) cm[w][0][c] = wmax;
+            __syncthreads();                                      // every wave's maxima
+
+            // the same lazy reference update in every wave: it moves only
+            // when a stage's maximum exceeds it by more than 2^8
+            float alpha[HG];
+#pragma unroll
+            for (int hg = 0; hg < HG; hg++) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int ww = 0; ww < kPerGroup; ww++) mx = fmaxf(mx, cm[HG * ww + hg][0][c]);
+                alpha[hg] = 1.f;
+                if (mx > m_run[hg] + 8.0f) {
+                    alpha[hg] = m_run[hg] == -INFINITY ? 0.f : exp2f(m_run[hg] - mx);
+                    m_run[hg] = mx;
+                }
+            }
+            // probabilities of this wave's tiles -> P^T operands (k-step
+            // tau/2, half tau%2: rows 4g+i, then 16+4g+i)
+            {
+                const float mr = m_run[hgw];
+                float psum = 0.f;
+#pragma unroll
+                for (int j = 0; j < kTilesPerWave; j++) {
+                    const int tau = T0 + wq + kPerGroup * j;
+                    if (tau < T1) {
+                        f32x4 pv;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            pv[i] = mr == -INFINITY ? 0.f : exp2f(x[j][i] - mr);
+                            psum += pv[i];
+                        }
+                        pfrag[tau >> 1][hgw][tau & 1][lane] = pv;
+                    }
+                }
+                psum = xor32_sum(xor16_sum(psum));
+                l_part = l_part * alpha[hgw] + psum;
+            }
+#pragma unroll
+            for (int hg = 0; hg < HG; hg++)
+                if (alpha[hg] != 1.f) {                           // uniform across the workgroup
+#pragma unroll
+                    for (int dt = 0; dt < 4; dt++) o[dt][hg] *= alpha[hg];
+                }
+            __syncthreads();                                      // the P^T operands
+
+            // ---- values: wave w owns output dims 64w .. 64w+63 (scale block
+            // w) for every head of the block; k-step kap covers pass rows
+            // 32 kap + {4g+j, 16+4g+j}, j = 0..3, in the P^T operands' order
+            for (int kap = k0; kap < k1; kap++) {
+                const int rb = 32 * kap;
+                const bool f8 = F8 || rb >= nsw_pad;              // uniform
+                bf16x8 pb[HG];
+                bf16x8 va[4];
+                if (f8) {
+                    // the rows' scales of block w, folded into the probabilities
+                    const uint8_t *f8r = rows + f8base + (rb - f8first) * kF8Pitch;
+                    float sc[8];
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        const int rr = (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+                        sc[j] = *reinterpret_cast<const float *>(f8r + rr * kF8Pitch + kF8Data + 4 * w);
+                    }
+#pragma unroll
+                    for (int hg = 0; hg < HG; hg++) {
+                        const f32x4 p0 = pfrag[kap][hg][0][lane], p1 = pfrag[kap][hg][1][lane];
+                        pb[hg] = __builtin_bit_cast(
+                            bf16x8, u32x4{f32x2_to_bf16x2(p0[0] * sc[0], p0[1] * sc[1]),
+                                          f32x2_to_bf16x2(p0[2] * sc[2], p0[3] * sc[3]),
+                                          f32x2_to_bf16x2(p1[0] * sc[4], p1[1] * sc[5]),
+                                          f32x2_to_bf16x2(p1[2] * sc[6], p1[3] * sc[7])});
+                    }
+                    // V^T: lane (g, c) addresses row R(kap, g, c/2), bytes 8 (c%2)
+                    // of each 16-dim tile of block w; it receives dim 16 dt + c of
+                    // the group's 8 rows
+                    const int jr = c >> 1;
+                    const int rr = jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4);
+                    const uint8_t *vr = f8r + rr * kF8Pitch + 64 * w + 8 * (c & 1);
+#pragma unroll
+                    for (int dt = 0; dt < 4; dt++) {
+                        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (__attribute__((address_space(3))) i32x2 *)(vr + 16 * dt));
+                        va[dt] = e4m3x8_to_bf16(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), 1.0f);
+                    }
+                } else {
+#pragma unroll
+                    for (int hg = 0; hg < HG; hg++) {
+                        const f32x4 p0 = pfrag[kap][hg][0][lane], p1 = pfrag[kap][hg][1][lane];
+                        pb[hg] = __builtin_bit_cast(
+                            bf16x8, u32x4{f32x2_to_bf16x2(p0[0], p0[1]), f32x2_to_bf16x2(p0[2], p0[3]),
+                                          f32x2_to_bf16x2(p1[0], p1[1]), f32x2_to_bf16x2(p1[2], p1[3])});
+                    }
+                    // lane (g, c) addresses rows rb + 4g + c/4 and rb + 16 + 4g + c/4,
+                    // elements 4 (c%4) of each 16-dim tile; it receives element c
+                    const uint8_t *v1 = rows + (rb + 4 * g + (c >> 2)) * kB16Pitch + 2 * (64 * w + 4 * (c & 3));
+                    const uint8_t *v2 = v1 + 16 * kB16Pitch;
+#pragma unroll
+                    for (int dt = 0; dt < 4; dt++) {
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(v1 + 32 * dt));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(v2 + 32 * dt));
+                        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                        va[dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+                    for (int hg = 0; hg < HG; hg++)
+                        o[dt][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pb[hg], o[dt][hg], 0, 0, 0);
+            }
+        }
+        __syncthreads();                                          // rows, rid and P^T free for the next pass
+    }
+    if (passes == 0) __syncthreads();                             // (nothing staged; keep the barrier count)
+
+    // ---- the heads' sums, then this wave's 64 output dims of every head
+    if (g == 0) lp[w][c] = l_part;
+    __syncthreads();
+    float L[HG], inv[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; hg++) {
+        L[hg] = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves / HG; ww++) L[hg] += lp[HG * ww + hg][c];
+        inv[hg] = L[hg] > 0.f ? 1.f / L[hg] : 0.f;
+    }
+    // O / L as bf16 through a per-wave LDS stage ([head][64 dims], pitch
+    // kOutPitch), so that each store writes 128 contiguous bytes of a head
+    uint8_t *stg = rows + w * (32 * kOutPitch);
+#pragma unroll
+    for (int hg = 0; hg < HG; hg++)
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+            *reinterpret_cast<u32x2 *>(stg + (16 * hg + c) * kOutPitch + 2 * (16 * dt + 4 * g)) =
+                u32x2{f32x2_to_bf16x2(o[dt][hg][0] * inv[hg], o[dt][hg][1] * inv[hg]),
+                      f32x2_to_bf16x2(o[dt][hg][2] * inv[hg], o[dt][hg][3] * inv[hg])};
+    __asm__ volatile("" ::: "memory");
+    const int h0 = 16 * HG * hb;
+    const int64_t row0_out = S == 1 ? static_cast<int64_t>(t) * a.n_heads + h0
+                                    : (static_cast<int64_t>(t) * S + split) * a.n_heads + h0;
+    uint16_t *dst = (S == 1 ? a.out : a.part_o) + row0_out * kDN + 64 * w;
+#pragma unroll
+    for (int it = 0; it < 2 * HG; it++) {
+        const int u = lane + 64 * it;                             // 16 * HG heads x 8 units
+        const int hh = u >> 3, part = u & 7;
+        *reinterpret_cast<u32x4 *>(dst + static_cast<int64_t>(hh) * kDN + 8 * part) =
+            *reinterpret_cast<const u32x4 *>(stg + hh * kOutPitch + 16 * part);
+    }
+    if (w == 0 && g == 0) {
+#pragma unroll
+        for (int hg = 0; hg < HG; hg++) {
+            const int64_t hrow = row0_out + 16 * hg + c;
+            if (S == 1) {
+                if (a.lse) a.lse[hrow] = L[hg] > 0.f ? (m_run[hg] + log2f(L[hg])) * kLn2 : -INFINITY;
+            } else {
+                a.part_ml[2 * hrow] = m_run[hg];
+                a.part_ml[2 * hrow + 1] = L[hg];
+            }
+        }
+    }
+}
+
+// Pass capacities of a decode launch (host arithmetic): each split takes
+// ceil(W / S) window entries and ceil(k / S) compressed entries; a pass holds
+// up to sw_cap window rows and cm_cap compressed rows (multiples of 32, at
+// most kMaxPassRows in all) within kRowBytes of LDS.  Of the capacities that
+// fit, those with the fewest passes are taken.
+void decode_pass_caps(AttnArgs &a) {
+    const int S = a.n_splits > 0 ? a.n_splits : 1;
+    a.sw_per = (a.window + S - 1) / S;
+    a.cm_per = (a.k + S - 1) / S;
+    const int sw_row = a.swa_fp8 ? kF8Pitch : kB16Pitch;
+    const int sw_max = (a.sw_per + 31) & ~31, cm_max = (a.cm_per + 31) & ~31;
+    int best = -1, best_sw = 32, best_cm = 32;
+    for (int sw = sw_max > 0 ? 32 : 0; sw <= sw_max; sw += 32) {
+        const int left_b = kRowBytes - sw * sw_row, left_r = kMaxPassRows - sw;
+        if (left_b < 0 || left_r < 0) break;
+        int cm = 0;
+        if (cm_max > 0) {
+            cm = cm_max;
+            cm = cm < (left_b / kF8Pitch) / 32 * 32 ? cm : (left_b / kF8Pitch) / 32 * 32;
+            cm = cm < left_r / 32 * 32 ? cm : left_r / 32 * 32;
+            if (cm < 32) continue;
+        }
+        const int ps = sw > 0 ? (a.sw_per + sw - 1) / sw : 0;
+        const int pc = cm > 0 ? (a.cm_per + cm - 1) / cm : 0;
+        const int passes = ps > pc ? ps : pc;
+        if (best < 0 || passes < best) {
+            best = passes;
+            best_sw = sw;
+            best_cm = cm;
+        }
+        if (sw == 0) break;
+    }
+    a.sw_cap = best_sw > 0 ? best_sw : 32;
+    a.cm_cap = best_cm > 0 ? best_cm : 32;
+}
+
+hipError_t launch_decode(const AttnArgs &a0, hipStream_t stream) {
+    AttnArgs a = a0;
+    decode_pass_caps(a);
+    const int hg = a.head_groups;
+    const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
+    const dim3 grid(groups * 8u * (a.n_heads / (16 * hg)) * a.n_splits);
+    if (a.swa_fp8) {
+        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, true>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((mla_decode_kernel<1, true>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, false>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((mla_decode_kernel<1, false>), grid, dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace slc

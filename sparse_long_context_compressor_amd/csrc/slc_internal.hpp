@@ -113,8 +113,10 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     int n_splits;           // decode: workgroups per (query, head block) along the list
-    int rows_per_split;     // list entries each split covers (a multiple of 16)
-    int head_groups;        // decode: 16-head groups per workgroup (1, 2 or 4)
+    int rows_per_split;     // prefill: list entries of its one split
+    int head_groups;        // decode: 16-head groups per workgroup (1 or 2)
+    int sw_per, cm_per;     // decode: window / compressed entries per split
+    int sw_cap, cm_cap;     // decode: window / compressed rows per LDS pass
     uint16_t *part_o;       // bf16 [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
 };
@@ -127,9 +129,11 @@ hipError_t launch_step_writers(const StreamArgs *lat, const StreamArgs *keys,
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);
+hipError_t launch_decode(const AttnArgs &a, hipStream_t stream);   // decode.hip (no combine)
+hipError_t launch_combine(const AttnArgs &a, hipStream_t stream);  // merge of the decode's splits
 
 // split plan (host arithmetic only): decode splits each (query, head block)'s
-// list so that about one workgroup per CU runs; prefill never splits.
+// lists so that about one workgroup per CU runs; prefill never splits.
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
                     int *rows_per_split, int *head_groups);
 // 16-head groups one decode workgroup serves (2 when n_heads allows, else 1)

@@ -127,12 +127,14 @@ def test_noalloc_decode_rejects_oversized_shapes_before_any_device_call(S):
     """The no-allocation decode checks its partials' size against its static
     array on the host (SLC_ERR_WORKSPACE), before it touches a device."""
     L = S.lib()
-    assert L.slc_sparse_mla_decode_noalloc_max_bytes() == 32 << 20
+    assert L.slc_sparse_mla_decode_noalloc_max_bytes() == 12 << 20
     fake = C.c_void_p(256)
     pool = S.Pool(C.c_void_p(256), C.c_void_p(256), 4, 4)
-    assert L.slc_sparse_mla_decode_workspace_size(4096, 128, 1024, 4096) > (32 << 20)
-    st = L.slc_sparse_mla_decode_noalloc(4, 4096, 128, fake, fake, fake, 1024, pool, pool, fake,
-                                         4096, fake, 0.1, fake, None, None)
+    # 100 queries x 2 head blocks split in two: 13 MB of partials
+    assert L.slc_sparse_mla_decode_workspace_size(100, 64, 128, 512) > (12 << 20)
+    assert L.slc_sparse_mla_decode_workspace_size(32, 64, 128, 512) <= (12 << 20)
+    st = L.slc_sparse_mla_decode_noalloc(4, 100, 64, fake, fake, fake, 128, pool, pool, fake,
+                                         512, fake, 0.1, fake, None, None)
     assert st == 2 and b"static scratch" in L.slc_last_error()
     # argument errors come first, as for the workspace form
     assert L.slc_sparse_mla_decode_noalloc(2, 1, 64, fake, fake, fake, 128, pool, pool, None, 0,

@@ -52,15 +52,15 @@ def test_noalloc_decode_rejects_shapes_beyond_its_array():
     S.lib()
     lay = I.build_layer(11, ratio=4, H=16, ctx=[600], queries=[(0, 599)], n_slots=[150], W=16,
                         k=32, given_topk=True, device="cuda")
-    big_q = 4096        # 4096 queries x 128 heads of partials exceed the array
-    assert S.sparse_mla_workspace_size(True, big_q, 128, 1024, 4096) > \
+    n_q = 100           # 100 queries x 64 heads in two splits: 13 MB of partials
+    assert S.sparse_mla_workspace_size(True, n_q, 64, 128, 512) > \
         S.sparse_mla_decode_noalloc_max_bytes()
-    q = torch.zeros((big_q, 128, 576), dtype=torch.bfloat16, device="cuda")
-    z = torch.zeros(big_q, dtype=torch.int32, device="cuda")
-    idx = torch.zeros((big_q, 4096), dtype=torch.int32, device="cuda")
-    out = torch.zeros((big_q, 128, 512), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((n_q, 64, 576), dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    idx = torch.zeros((n_q, 512), dtype=torch.int32, device="cuda")
+    out = torch.zeros((n_q, 64, 512), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S.SlcError) as e:
-        S.sparse_mla_decode_noalloc(4, q, z, z, 1024, lay.swa_pool, lay.swa_table, lay.cmp_pool,
+        S.sparse_mla_decode_noalloc(4, q, z, z, 128, lay.swa_pool, lay.swa_table, lay.cmp_pool,
                                     lay.cmp_table, idx, lay.n_slots, 0.1, out, None)
     assert e.value.status == S.SLC_ERR_WORKSPACE
     assert not out.any()
