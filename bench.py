@@ -33,6 +33,9 @@ TOPK_BYTES_PER_QUERY = SLOTS * 4 + K * 4 + 4
 ATTN_BYTES_PER_QUERY = (H * 576 * 2 + W * 1152 + K * 672 + K * 4 + H * 512 * 2 + H * 4)
 STEP_BYTES = B * (SLOTS * 132 + IDX_BYTES_PER_QUERY + K * 4 + ATTN_BYTES_PER_QUERY)
 INDEX_KERNEL_BYTES = B * (SLOTS * IDX_BYTES_PER_SLOT + IDX_BYTES_PER_QUERY)
+# ratio-4 compress of 4096 tokens: each token's kv (bf16) and score (fp32)
+# rows of 576 read once, each of the 1024 slots written once (672 B)
+COMPRESS_4K_BYTES = 4096 * (576 * 2 + 576 * 4) + 1024 * 672
 
 
 def parse():
@@ -61,6 +64,9 @@ def parse():
                     help="summarise a rocprofv3 --stats csv directory into OUT_MD and exit")
     ap.add_argument("--report-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_STEM"),
                     help="turn FETCH_SIZE / WRITE_SIZE csv runs into OUT_STEM.json/.md and exit")
+    ap.add_argument("--report-mfma", nargs=2, metavar=("PMC_DIR", "OUT_STEM"),
+                    help="turn an MFMA counter run (MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) into OUT_STEM.json/.md and exit")
     ap.add_argument("--cmd", action="append", default=[],
                     help="a command recorded verbatim in a report (repeatable)")
     return ap.parse_args()
@@ -108,9 +114,24 @@ def stream_read(buf, sink) -> None:
         raise RuntimeError(f"bench_stream_read failed ({rc})")
 
 
-def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "sparse_long_context_compressor_amd", "csrc", "index.hip")
+def kernel_source_hash(name: str = "index.hip") -> str:
+    p = os.path.join(ROOT, "sparse_long_context_compressor_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+# the source file each library kernel is built from (for tying counter
+# summaries to the code they were taken on)
+KERNEL_SOURCES = {"index_score_kernel": "index.hip", "topk_kernel": "topk.hip",
+                  "topk_warm_kernel": "topk.hip", "topk_small_kernel": "topk.hip",
+                  "topk_long_kernel": "topk.hip", "mla_decode_kernel": "decode.hip",
+                  "mla_combine_kernel": "attention.hip", "mla_prefill_kernel": "attention.hip",
+                  "compress_r4_kernel": "compress.hip", "compress_r128_kernel": "compress.hip"}
+
+
+def _kernel_key(name: str) -> str:
+    """slc::mla_decode_kernel<2, false>(slc::AttnArgs) -> mla_decode_kernel"""
+    base = name.split("(")[0].replace("void ", "").strip()
+    return base.split("::")[-1].split("<")[0]
 
 
 def traffic_from_profile():
@@ -163,53 +184,155 @@ def report_stats(trace_dir: str, out_md: str, cmds, workload: str = "c4a_decode_
     print("\n".join(lines))
 
 
-def report_counters(fetch_dir: str, write_dir: str, stem: str, calib_mib: int, cmds):
-    """HBM bytes per index-score launch: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch) of the kernel, each scaled by the same counter's reading for a
-    plain fp32 elementwise copy that reads and writes calib_mib MiB."""
+def report_counters(fetch_dir: str, write_dir: str, stem: str, calib_mib: int, cmds,
+                    workload: str = "c4a_decode_64k"):
+    """HBM bytes per launch of every library kernel in a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by the same counter's
+    reading for a plain fp32 elementwise copy that reads and writes calib_mib
+    MiB.  Writes OUT_STEM.json / .md; for the headline workload the index
+    kernel's record (the bench line's `traffic`) keeps its own file."""
     if calib_mib <= 0:
         raise SystemExit("--calib-copy-mib must give the calibration copy's size")
 
-    def per_dispatch(d, counter, match):
+    def per_kernel(d, counter):
         vals = {}
         for r in _csv_rows(d, "counter_collection.csv"):
-            if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
-                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-        if not vals:
-            raise SystemExit(f"no {counter} rows for the kernel in {d}")
-        v = sorted(vals.values())
-        return sum(v) / len(v), len(v), v[0], v[-1]
+            if r["Counter_Name"] == counter:
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (name, _), v in vals.items():
+            out.setdefault(name, []).append(v)
+        return {n: (sum(v) / len(v), len(v), min(v), max(v)) for n, v in out.items()}
 
-    is_index = lambda n: "index_score_kernel" in n  # noqa: E731
-    is_copy = lambda n: "neg_kernel" in n           # noqa: E731
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cp = [n for n in fetch if "neg_kernel" in n]
+    cpw = [n for n in write if "neg_kernel" in n]
+    if not cp or not cpw:
+        raise SystemExit("no calibration copy (neg_kernel) in the counter runs")
     known = calib_mib * 1024.0                      # KiB read = KiB written by the copy
-    f_idx = per_dispatch(fetch_dir, "FETCH_SIZE", is_index)
-    w_idx = per_dispatch(write_dir, "WRITE_SIZE", is_index)
-    f_cp = per_dispatch(fetch_dir, "FETCH_SIZE", is_copy)
-    w_cp = per_dispatch(write_dir, "WRITE_SIZE", is_copy)
-    kf, kw = known / f_cp[0], known / w_cp[0]
-    traffic = (f_idx[0] * kf + w_idx[0] * kw) * 1024.0
-    rec = {"kernel": "index_score_kernel", "workload": "c4a_decode_64k",
-           "fetch_kib_per_dispatch": f_idx[0], "write_kib_per_dispatch": w_idx[0],
-           "dispatches": [f_idx[1], w_idx[1]],
-           "calibration": {"copy_mib": calib_mib, "fetch_kib": f_cp[0], "write_kib": w_cp[0],
-                           "fetch_factor": kf, "write_factor": kw},
-           "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": INDEX_KERNEL_BYTES,
-           "traffic_over_algorithmic": traffic / INDEX_KERNEL_BYTES,
-           "index_hip_sha256_16": kernel_source_hash(), "commands": cmds}
-    json.dump(rec, open(stem + ".json", "w"), indent=1)
-    md = ["# HBM traffic of index_score_kernel, c4a_decode_64k (rocprofv3 counters)", "",
+    f_cp, w_cp = fetch[cp[0]][0], write[cpw[0]][0]
+    kf, kw = known / f_cp, known / w_cp
+    # algorithmic bytes per launch where this file states them
+    algo = {}
+    if workload == "c4a_decode_64k":
+        algo = {"index_score_kernel": INDEX_KERNEL_BYTES,
+                "mla_decode_kernel + mla_combine_kernel": B * ATTN_BYTES_PER_QUERY}
+    elif workload == "c4a_single_layer_4k":
+        algo = {"compress_r4_kernel": COMPRESS_4K_BYTES}
+    kernels = {}
+    for name in sorted(fetch):
+        if "slc::" not in name or name not in write:
+            continue
+        key = _kernel_key(name)
+        f, w = fetch[name], write[name]
+        kernels[key] = {"name": _short(name), "fetch_kib": f[0], "write_kib": w[0],
+                        "dispatches": [f[1], w[1]], "fetch_range_kib": [f[2], f[3]],
+                        "hbm_read_bytes": f[0] * kf * 1024.0,
+                        "hbm_write_bytes": w[0] * kw * 1024.0,
+                        "source": KERNEL_SOURCES.get(key),
+                        "source_sha256_16": kernel_source_hash(KERNEL_SOURCES[key])
+                        if key in KERNEL_SOURCES else None}
+        kernels[key]["hbm_bytes"] = kernels[key]["hbm_read_bytes"] + kernels[key]["hbm_write_bytes"]
+    groups = {}
+    for label, ab in algo.items():
+        parts = [k.strip() for k in label.split("+")]
+        if all(p_ in kernels for p_ in parts):
+            t = sum(kernels[p_]["hbm_bytes"] for p_ in parts)
+            groups[label] = {"hbm_bytes": t, "algorithmic_bytes": ab, "ratio": t / ab}
+    calib = {"copy_mib": calib_mib, "fetch_kib": f_cp, "write_kib": w_cp,
+             "fetch_factor": kf, "write_factor": kw}
+    json.dump({"workload": workload, "kernels": kernels, "vs_algorithmic": groups,
+               "calibration": calib, "commands": cmds}, open(stem + ".json", "w"), indent=1)
+    md = [f"# HBM traffic per launch, {workload} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
           "Made by:", ""] + [f"    {c}" for c in cmds] + [
-        "", f"- FETCH_SIZE: {f_idx[0]:.0f} KiB per dispatch (mean of {f_idx[1]}, "
-            f"range {f_idx[2]:.0f}..{f_idx[3]:.0f})",
-        f"- WRITE_SIZE: {w_idx[0]:.0f} KiB per dispatch (mean of {w_idx[1]})",
-        f"- calibration copy of {calib_mib} MiB: FETCH_SIZE {f_cp[0]:.0f} KiB, WRITE_SIZE "
-        f"{w_cp[0]:.0f} KiB -> factors {kf:.4f} (read), {kw:.4f} (write)",
-        f"- scaled HBM traffic per launch: {traffic / 1e6:.2f} MB; algorithmic "
-        f"{INDEX_KERNEL_BYTES / 1e6:.2f} MB; ratio {traffic / INDEX_KERNEL_BYTES:.3f}",
-        f"- index.hip sha256[:16] at the time: {kernel_source_hash()}"]
+        "", f"Calibration: a plain fp32 copy of {calib_mib} MiB reads FETCH_SIZE {f_cp:.0f} KiB "
+            f"and WRITE_SIZE {w_cp:.0f} KiB, so the counters are scaled by {kf:.4f} (read) and "
+            f"{kw:.4f} (write).", "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | source sha256[:16] |",
+        "|---|---:|---:|---:|---:|---:|---|"]
+    for key, k in kernels.items():
+        md.append(f"| `{k['name']}` | {k['dispatches'][0]} | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | "
+                  f"{k['hbm_read_bytes'] / 1e6:.2f} | {k['hbm_write_bytes'] / 1e6:.2f} | "
+                  f"{k['source']} {k['source_sha256_16']} |")
+    if groups:
+        md += ["", "| against the algorithmic bytes | HBM MB | algorithmic MB | ratio |",
+               "|---|---:|---:|---:|"]
+        for label, gr in groups.items():
+            md.append(f"| {label} | {gr['hbm_bytes'] / 1e6:.2f} | {gr['algorithmic_bytes'] / 1e6:.2f} | "
+                      f"{gr['ratio']:.3f} |")
     open(stem + ".md", "w").write("\n".join(md) + "\n")
     print("\n".join(md))
+    if workload == "c4a_decode_64k" and "index_score_kernel" in kernels:
+        k = kernels["index_score_kernel"]
+        rec = {"kernel": "index_score_kernel", "workload": workload,
+               "fetch_kib_per_dispatch": k["fetch_kib"], "write_kib_per_dispatch": k["write_kib"],
+               "dispatches": k["dispatches"], "calibration": calib,
+               "hbm_bytes_per_launch": k["hbm_bytes"], "algorithmic_bytes_per_launch": INDEX_KERNEL_BYTES,
+               "traffic_over_algorithmic": k["hbm_bytes"] / INDEX_KERNEL_BYTES,
+               "index_hip_sha256_16": kernel_source_hash(), "commands": cmds}
+        d = os.path.dirname(stem) or "."
+        json.dump(rec, open(os.path.join(d, "index_score_c4a_decode_64k_counters.json"), "w"), indent=1)
+
+
+def report_mfma(pmc_dir: str, stem: str, cmds, workload: str):
+    """MFMA use per library kernel from one counter run: MfmaUtil (rocprofv3's
+    derived percentage: MFMA-busy SIMD cycles over active cycles times SIMDs),
+    the bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16, in units of 512 FLOP),
+    means per dispatch.  Writes OUT_STEM.json / .md."""
+    vals = {}
+    for r in _csv_rows(pmc_dir, "counter_collection.csv"):
+        key = (r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"])
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (name, disp, ctr), v in vals.items():
+        if "slc::" in name:
+            per.setdefault(name, {}).setdefault(ctr, []).append(v)
+    kernels = {}
+    for name, ctrs in per.items():
+        key = _kernel_key(name)
+        mean = {c: sum(v) / len(v) for c, v in ctrs.items()}
+        kernels[key] = {"name": _short(name), "dispatches": max(len(v) for v in ctrs.values()),
+                        "mfma_util_pct": mean.get("MfmaUtil"),
+                        "bf16_mfma_flop": mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512.0,
+                        "mfma_busy_cycles_sum": mean.get("SQ_VALU_MFMA_BUSY_CYCLES"),
+                        "grbm_gui_active": mean.get("GRBM_GUI_ACTIVE"),
+                        "source": KERNEL_SOURCES.get(key),
+                        "source_sha256_16": kernel_source_hash(KERNEL_SOURCES[key])
+                        if key in KERNEL_SOURCES else None}
+    json.dump({"workload": workload, "kernels": kernels, "commands": cmds},
+              open(stem + ".json", "w"), indent=1)
+    md = [f"# MFMA use per launch, {workload} (rocprofv3 counters)", "", "Made by:", ""] + \
+         [f"    {c}" for c in cmds] + [
+        "", "MfmaUtil is rocprofv3's derived counter: the SIMDs' summed MFMA-busy cycles "
+            "(SQ_VALU_MFMA_BUSY_CYCLES) over the kernel's active cycles (GRBM_GUI_ACTIVE, "
+            "largest over the XCDs) times the 1024 SIMDs, in per cent. The bf16 MFMA work is "
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP.", "",
+        "| kernel | dispatches | MfmaUtil % | bf16 MFMA GFLOP per launch | source sha256[:16] |",
+        "|---|---:|---:|---:|---|"]
+    for key, k in kernels.items():
+        u = k["mfma_util_pct"]
+        md.append(f"| `{k['name']}` | {k['dispatches']} | {u:.1f} | {k['bf16_mfma_flop'] / 1e9:.1f} | "
+                  f"{k['source']} {k['source_sha256_16']} |" if u is not None else
+                  f"| `{k['name']}` | {k['dispatches']} | - | {k['bf16_mfma_flop'] / 1e9:.1f} | "
+                  f"{k['source']} {k['source_sha256_16']} |")
+    open(stem + ".md", "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def mfma_from_profile(workload: str):
+    """MfmaUtil per kernel from the committed counter summary of a workload,
+    for kernels whose source is unchanged since it was taken; else None."""
+    p = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    out = {}
+    for key, k in d.get("kernels", {}).items():
+        src = k.get("source")
+        if src and k.get("source_sha256_16") == kernel_source_hash(src) and k.get("mfma_util_pct") is not None:
+            out[key] = k["mfma_util_pct"] / 100.0
+    return out or None
 
 
 def cpu_baseline(n_q: int):
@@ -373,6 +496,15 @@ def other_workload(args):
             iflops = 2.0 * float(nv.sum()) * HIi * 128
             rec["index_TFLOPs"] = iflops / (per["index_scores"] * 1e-6) / 1e12
             rec["index_mfma_frac_bf16"] = rec["index_TFLOPs"] / BF16_PEAK_TFLOPS
+        # MFMA busy share per kernel from the committed counter run (null once
+        # a kernel's source has changed since)
+        rec["mfma_util"] = mfma_from_profile(name)
+    if args.calib_copy_mib:
+        # the known-size copy the HBM byte counters are scaled by
+        a_ = torch.ones((args.calib_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
+        b_ = torch.empty_like(a_)
+        torch.neg(a_, out=b_)
+        torch.cuda.synchronize()
     print(json.dumps(rec), flush=True)
 
 
@@ -496,7 +628,9 @@ def main():
     if args.report_stats:
         return report_stats(*args.report_stats, args.cmd, args.workload)
     if args.report_counters:
-        return report_counters(*args.report_counters, args.calib_copy_mib, args.cmd)
+        return report_counters(*args.report_counters, args.calib_copy_mib, args.cmd, args.workload)
+    if args.report_mfma:
+        return report_mfma(*args.report_mfma, args.cmd, args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path shards by sequence with no exchange "
               "between GPUs, so one GPU's share at the real shape is the measurement. "
