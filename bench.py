@@ -676,7 +676,20 @@ def main():
                               lay.cmp_pool, lay.cmp_table, idx, lay.n_slots, lay.sm_scale, out,
                               lse, ws)
 
+    def topk_decode(lay):
+        # the select and the decode over its list in one call (one launch
+        # plus the merge of the splits)
+        slc.sparse_mla_decode_topk(4, lay.q, lay.q_seq, lay.q_pos, W, lay.swa_pool, lay.swa_table,
+                                   lay.cmp_pool, lay.cmp_table, K, scores, SLOTS, lay.n_slots, idx,
+                                   ln, lay.sm_scale, out, lse, ws)
+
     def step(lay):
+        index_scores(lay)
+        topk_decode(lay)
+
+    def step_separate(lay):
+        # the same step as three calls: index, select (with the decode's L2
+        # warm-up), decode
         index_scores(lay)
         topk(lay)
         decode(lay)
@@ -728,6 +741,13 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step_separate(reps[i % len(reps)])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step_separate = t_start.elapsed_time(t_end) / args.steps
 
     # ---- the same steps as replays of the captured graph (reported alongside) ----
     graph_ms = None
@@ -771,6 +791,7 @@ def main():
         return e0.elapsed_time(e1) / (reps_n * per_graph)
 
     idx_ms = graph_timed(index_scores, args.steps)
+    topk_decode_ms = graph_timed(topk_decode, args.steps)
     topk_ms = graph_timed(topk, args.steps)
     attn_ms = graph_timed(decode, args.steps)
 
@@ -822,9 +843,12 @@ def main():
         "achieved_step_GBps": STEP_BYTES / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": STEP_BYTES / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "timing": "eager_launches",
+        "ms_per_step_three_calls": ms_step_separate,
         "graph_ms_per_step": graph_ms,
-        "kernels_us": {"index_scores": idx_ms * 1e3, "topk_select": topk_ms * 1e3,
-                       "sparse_mla_decode": attn_ms * 1e3},
+        "kernels_us": {"index_scores": idx_ms * 1e3,
+                       "sparse_mla_decode_topk": topk_decode_ms * 1e3,
+                       "topk_select_separate": topk_ms * 1e3,
+                       "sparse_mla_decode_separate": attn_ms * 1e3},
         "kernels_timing": "graph_replay" if args.graph else "eager_launches",
         "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -20,6 +20,8 @@
  *                           and both streaming compressors) in one launch.
  *   slc_swa_insert          RoPE + fp8 quantisation + paged write of new tokens
  *                           into an fp8 sliding-window pool
+ *   slc_sparse_mla_decode_topk  the C4A top-k select and the decode over its
+ *                           list in one call.
  *   slc_sparse_mla_decode   absorbed-MQA sparse MLA attention over the sliding
  *   slc_sparse_mla_prefill  window plus the selected compressed slots.
  *
@@ -505,6 +507,37 @@ slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const u
                                    const int32_t *cmp_idx, int k, const int32_t *n_slots,
                                    float sm_scale, uint16_t *out, float *lse, void *workspace,
                                    size_t ws_bytes, void *stream);
+
+/*
+ * slc_sparse_mla_decode_topk -- the C4A branch's top-k select and the decode
+ * over its list in one call: "DeepSeek-V4 attention layer types", Indexer /
+ * C4A branch (the indexer's global top-k per query feeds the compressed
+ * indices of the attention) with "DeepseekV4Attention" (devpress),
+ * _forward_decode (the SWA and the compressed indices go to one attention
+ * kernel).  Results are those of slc_topk_select(k, scores, ...) followed by
+ * slc_sparse_mla_decode(layer_type, ..., topk_idx, k, ...): the same list,
+ * written to topk_idx / topk_len, and the same out / lse, bit for bit.
+ * Where the shapes allow (scores 16-byte aligned, 4 <= max_slots <= 16384,
+ * max_slots a multiple of 4, and the split plan's compressed share of a
+ * split at most 512 entries) the decode's workgroups select the list
+ * themselves in the same launch; otherwise the call runs the two steps.
+ *
+ *   layer_type   SLC_LAYER_C4A, optionally OR'ed with SLC_SWA_FP8
+ *   k            1 .. SLC_MAX_TOPK; scores / max_slots as slc_topk_select
+ *                (the visible count of query t is min(n_slots[q_seq[t]],
+ *                (q_pos[t] + 1) / 4), at most max_slots)
+ *   topk_idx     device int32 [n_q][k];  topk_len  device int32 [n_q]
+ *   other arguments, the workspace and its size as slc_sparse_mla_decode
+ *   (slc_sparse_mla_decode_workspace_size(n_q, n_heads, window, k)).
+ */
+slc_status_t slc_sparse_mla_decode_topk(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                        const int32_t *q_seq, const int32_t *q_pos, int window,
+                                        slc_pool_t swa_pool, slc_pool_t cmp_pool, int k,
+                                        const float *scores, int max_slots,
+                                        const int32_t *n_slots, int32_t *topk_idx,
+                                        int32_t *topk_len, float sm_scale, uint16_t *out,
+                                        float *lse, void *workspace, size_t ws_bytes,
+                                        void *stream);
 
 /*
  * slc_sparse_mla_decode_noalloc -- slc_sparse_mla_decode for callers that

@@ -585,6 +585,72 @@ slc_status_t slc_sparse_mla_decode_noalloc(int layer_type, int n_q, int n_heads,
                       cmp_idx, k, n_slots, sm_scale, out, lse, ws, need, stream);
 }
 
+slc_status_t slc_sparse_mla_decode_topk(int layer_type, int n_q, int n_heads, const uint16_t *q,
+                                        const int32_t *q_seq, const int32_t *q_pos, int window,
+                                        slc_pool_t swa_pool, slc_pool_t cmp_pool, int k,
+                                        const float *scores, int max_slots,
+                                        const int32_t *n_slots, int32_t *topk_idx,
+                                        int32_t *topk_len, float sm_scale, uint16_t *out,
+                                        float *lse, void *workspace, size_t ws_bytes,
+                                        void *stream) {
+    if ((layer_type & ~SLC_SWA_FP8) != SLC_LAYER_C4A)
+        return fail("sparse_mla_decode_topk: layer_type must be SLC_LAYER_C4A (optionally | SLC_SWA_FP8)");
+    if (k < 1 || k > SLC_MAX_TOPK) return fail("sparse_mla_decode_topk: k must be in [1, SLC_MAX_TOPK]");
+    slc_status_t st = check_index_common(n_q, q_seq, q_pos, SLC_LAYER_C4A, n_slots, max_slots);
+    if (st != SLC_OK) return st;
+    st = mla_args_check(layer_type, n_q, n_heads, q, q_seq, q_pos, window, swa_pool, cmp_pool,
+                        topk_idx, k, n_slots, sm_scale, out);
+    if (st != SLC_OK || n_q == 0) return st;
+    if (!scores || !topk_len) return fail("sparse_mla_decode_topk: scores and topk_len are required");
+    const size_t need = attn_ws(n_q, n_heads, window, k, true);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256))) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "sparse_mla_decode_topk: workspace needs %zu bytes, 256-byte aligned", need);
+        return SLC_ERR_WORKSPACE;
+    }
+    AttnArgs a{};
+    a.layer_type = SLC_LAYER_C4A;
+    a.n_q = n_q;
+    a.n_heads = n_heads;
+    a.q = q;
+    a.q_seq = q_seq;
+    a.q_pos = q_pos;
+    a.window = window;
+    a.swa_fp8 = (layer_type & SLC_SWA_FP8) ? 1 : 0;
+    a.swa = swa_pool;
+    a.cmp = cmp_pool;
+    a.cmp_idx = topk_idx;
+    a.k = k;
+    a.n_slots = n_slots;
+    a.sm_scale_log2 = sm_scale * kLog2e;
+    a.out = out;
+    a.lse = lse;
+    int splits, cps, groups;
+    attention_plan(n_q, n_heads, window, k, true, &splits, &cps, &groups);
+    a.n_splits = splits;
+    a.rows_per_split = cps;
+    a.head_groups = groups;
+    if (splits > 1) {
+        size_t per = static_cast<size_t>(n_q) * splits * n_heads;
+        a.part_o = static_cast<uint16_t *>(workspace);
+        a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                              ((per * kDN * sizeof(uint16_t) + 15) & ~static_cast<size_t>(15)));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (decode_can_select(a, scores, max_slots)) {
+        a.sel_scores = scores;
+        a.sel_max_slots = max_slots;
+        a.sel_ratio = SLC_LAYER_C4A;
+        a.sel_idx = topk_idx;
+        a.sel_len = topk_len;
+        return hip_status(launch_attention(a, true, s));
+    }
+    TopkArgs ta{n_q, k, scores, max_slots, q_seq, q_pos, SLC_LAYER_C4A, n_slots, topk_idx, topk_len};
+    hipError_t e = launch_topk(ta, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_attention(a, true, s));
+}
+
 slc_status_t slc_sparse_mla_decode(int layer_type, int n_q, int n_heads, const uint16_t *q,
                                    const int32_t *q_seq, const int32_t *q_pos, int window,
                                    slc_pool_t swa_pool, slc_pool_t cmp_pool,

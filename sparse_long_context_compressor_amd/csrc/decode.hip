@@ -29,6 +29,7 @@
 // states; mla_combine_kernel merges them (attention.hip).
 
 #include "slc_internal.hpp"
+#include "select.hpp"
 
 namespace slc {
 
@@ -39,7 +40,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kB16Pitch = 2 * kD + 16;          // bytes per bf16 row in LDS (1168)
 constexpr int kF8Pitch = 688;                   // 512 codes | 64 bf16 rope | 8 fp32 scales | pad
 constexpr int kF8Data = SLC_CMP_ROW_BYTES;      // 640: codes + rope, then the scales
-constexpr int kRowBytes = 133 * 1024;           // LDS for one pass's rows
+constexpr int kRowBytes = 132 * 1024;           // LDS for one pass's rows
 constexpr int kMaxPassRows = 192;               // rows of one pass (a multiple of 32)
 constexpr int kMaxKsteps = kMaxPassRows / 32;
 constexpr int kOutPitch = 144;                  // bytes per head in the output stage (64 dims + pad)
@@ -49,6 +50,15 @@ static_assert(16 * kB16Pitch <= kQpBytes, "one head group of Q fits the P^T regi
 static_assert(kWaves * 32 * kOutPitch <= kRowBytes, "the output is staged in the row region");
 
 static_assert(kF8Pitch % 16 == 0 && (kF8Pitch / 16) % 2 == 1, "16-byte reads of 8 rows hit distinct banks");
+
+// The select of a workgroup's own list: 32 scores per thread (rows up to
+// 16384 slots), up to 2048 prefiltered candidates; its histogram and
+// candidates live in the Q / P^T region (free until the list is known).
+constexpr int kSelR = 32;
+constexpr int kSelMaxSlots = kThreads * kSelR;
+constexpr int kSelCand = 2048;
+constexpr int kMaxListShare = 512;              // list entries of one split
+static_assert(hist_words<kThreads>() * 4 + 8 * kSelCand <= kQpBytes, "select scratch fits");
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -99,6 +109,9 @@ __device__ __forceinline__ void wait_vmem_at_most(int n) {
 // Grid: ceil(n_q / 8) * 8 * HB * S workgroups of 512 threads, HB = n_heads /
 // (16 HG).  Blocks of one query share blockIdx % 8 (one XCD, one L2).
 // F8: the window pool holds fp8 rows in the compressed-row layout.
+// SEL: the workgroup selects the query's top-k list from its index scores
+// itself (every workgroup of the query the same list; head block 0 writes
+// its split's share of it out) before it resolves its rows.
 //
 // A workgroup: resolve the pass's rows, issue all their loads, then take the
 // pass in stages of k-steps (32 rows): each stage waits only for its own
@@ -106,7 +119,7 @@ __device__ __forceinline__ void wait_vmem_at_most(int n) {
 // 16-row tile's scores are computed for 16 heads by a wave of that head
 // group; a wave's value products cover one 64-dim output block (one scale
 // per row) of every head.
-template <int HG, bool F8>
+template <int HG, bool F8, bool SEL>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t rows[kRowBytes];
     // Q staging (one head group at a time) and, after, the P^T operands
@@ -114,6 +127,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) int32_t rid[kMaxPassRows];            // physical rows
     __shared__ float cm[kWaves][1][16];                                           // wave maxima
     __shared__ float lp[kWaves][16];                                              // wave sums
+    __shared__ int32_t lst[SEL ? kMaxListShare : 1];                              // the split's list share
+    __shared__ int sel_red[SEL ? 3 * kWaves : 1];
+    __shared__ int sel_sh[SEL ? 8 : 1];
     f32x4 (*pfrag)[HG][2][64] = reinterpret_cast<f32x4 (*)[HG][2][64]>(qp);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -137,22 +153,37 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
     const int hb = (rem >> 3) % HB, split = (rem >> 3) / HB;
     if (t >= n_q) return;                                         // uniform per workgroup
 
-    // ---- Q loads first (they depend on nothing): the block's heads are one
+    // SEL: the query's score row (the select needs it before anything else),
+    // 16-byte loads in the select's layout (units past the row re-read
+    // its last unit; their slots lie past the visible count and are masked)
+    f32x4 raw[SEL ? kSelR / 4 : 1];
+    if constexpr (SEL) {
+        const int msl = a.sel_max_slots;
+        const float *sc = a.sel_scores + static_cast<int64_t>(t) * msl;
+#pragma unroll
+        for (int q = 0; q < kSelR / 4; q++) {
+            const int s0 = w * 64 * kSelR + 256 * q + 4 * lane;
+            raw[q] = *reinterpret_cast<const f32x4 *>(sc + (s0 < msl ? s0 : msl - 4));
+        }
+    }
+
+    // ---- Q loads (they depend on nothing): the block's heads are one
     // contiguous run, 16-byte units u -> head u / 72, bytes 16 (u % 72)
     constexpr int kQUnits = 16 * HG * kD / 8;
     constexpr int kQIt = (kQUnits + kThreads - 1) / kThreads;
     u32x4 qv[kQIt];
-    {
+    auto load_q = [&]() {
         const uint16_t *qsrc = a.q + (static_cast<int64_t>(t) * a.n_heads + 16 * HG * hb) * kD;
 #pragma unroll
         for (int i = 0; i < kQIt; i++) {
             const int u = tid + kThreads * i;
             if (u < kQUnits) qv[i] = *reinterpret_cast<const u32x4 *>(qsrc + 8 * u);
         }
-    }
+    };
+    // SEL: after the select, so that its scores have the CU's loads to themselves
+    if constexpr (!SEL) load_q();
     const int seq = q_seq_p[t], p = q_pos_p[t];
     const int ns = kk > 0 ? n_slots_p[seq] : 0;
-
     // this split's shares of the window and of the compressed list
     const int sw0 = split * a.sw_per, sw1 = min(window, sw0 + a.sw_per);
     const int cm0 = split * a.cm_per, cm1 = min(kk, cm0 + a.cm_per);
@@ -160,6 +191,125 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
     const int sw_cap = a.sw_cap, cm_cap = a.cm_cap;
     const int passes = max(n_sw > 0 ? (n_sw + sw_cap - 1) / sw_cap : 0,
                            n_cm > 0 ? (n_cm + cm_cap - 1) / cm_cap : 0);
+
+
+    // ---- pass geometry: a pass holds window rows first (padded to 32), then
+    // compressed rows (padded to 32); stages: k-steps [0, KA), then the rest
+    struct Geo {
+        int e_sw, e_cm, nsw, ncm, nsw_pad, R, f8base, f8first, K, KA, rowsA;
+    };
+    auto geo = [&](int pass) {
+        Geo G;
+        G.e_sw = sw0 + pass * sw_cap;
+        G.e_cm = cm0 + pass * cm_cap;
+        G.nsw = max(0, min(sw_cap, sw1 - G.e_sw));
+        G.ncm = max(0, min(cm_cap, cm1 - G.e_cm));
+        G.nsw_pad = (G.nsw + 31) & ~31;
+        G.R = G.nsw_pad + ((G.ncm + 31) & ~31);
+        G.f8base = F8 ? 0 : G.nsw_pad * kB16Pitch;                // byte offset of the fp8 rows
+        G.f8first = F8 ? 0 : G.nsw_pad;                           // first row kept as fp8
+        G.K = G.R / 32;
+        G.KA = G.K <= 1 ? G.K : (G.K + 1) / 2;
+        G.rowsA = 32 * G.KA;
+        return G;
+    };
+    // resolve: thread j in [lo, hi) -> physical row of pass row j (-1:
+    // skipped or padding)
+    auto resolve = [&](const Geo &G, int lo, int hi) {
+        if (tid >= lo && tid < hi) {
+            int32_t phys = -1;
+            if (tid < G.nsw_pad) {
+                const int pos = p - window + 1 + G.e_sw + tid;
+                const int64_t lb = pos >> 6;
+                if (tid < G.nsw && pos >= 0 && lb < swa_stride) {
+                    const int32_t pb = swa_tab[static_cast<int64_t>(seq) * swa_stride + lb];
+                    if (pb >= 0 && pb < swa_nb) phys = pb * kBR + (pos & (kBR - 1));
+                }
+            } else {
+                const int j = tid - G.nsw_pad;
+                if (j < G.ncm) {
+                    const int s = SEL ? lst[G.e_cm - cm0 + j] : cmp_idx_p[static_cast<int64_t>(t) * kk + G.e_cm + j];
+                    const int64_t lb = s >> 6;
+                    if (s >= 0 && s < ns && lb < cmp_stride) {
+                        const int32_t pb = cmp_tab[static_cast<int64_t>(seq) * cmp_stride + lb];
+                        if (pb >= 0 && pb < cmp_nb) phys = pb * kBR + (s & (kBR - 1));
+                    }
+                }
+            }
+            rid[tid] = phys;
+        }
+    };
+    // issue the loads of this wave's pass rows w + 8 i, i in [i0, i1); all
+    // their ids are read first, so that no LDS access sits between the loads.
+    // Returns the count of those loads that belong to the second stage.
+    auto issue = [&](const Geo &G, int i0, int i1) {
+        int n2 = 0;
+        const int32_t my_id = w + kWaves * lane < G.R ? rid[w + kWaves * lane] : -1;
+        const uint8_t *swa_b = reinterpret_cast<const uint8_t *>(a.swa.base);
+        const uint8_t *cmp_b = reinterpret_cast<const uint8_t *>(a.cmp.base);
+        for (int i = i0; i < i1; i++) {
+            const int r = w + kWaves * i;
+            const int32_t id = __builtin_amdgcn_readlane(my_id, i);
+            const bool f8row = F8 || r >= G.nsw_pad;
+            const bool from_swa = r < G.nsw_pad;
+            if (f8row) {
+                // 40 lanes: 640 bytes of codes and rope; 2 lanes: the 32 bytes of scales
+                const uint8_t *blk = (from_swa ? swa_b : cmp_b) +
+                                     static_cast<int64_t>(id >> 6) * SLC_CMP_BLOCK_BYTES;
+                const uint8_t *src = lane < 40 ? blk + (id & 63) * SLC_CMP_ROW_BYTES + 16 * lane
+                                               : blk + SLC_CMP_SCALE_OFFSET + (id & 63) * 32 + 16 * (lane - 40);
+                if (id < 0) src = kDecZeroPage + 16 * lane;
+                if (lane < 42) dma16<0>(src, rows + G.f8base + (r - G.f8first) * kF8Pitch);
+                n2 += r >= G.rowsA ? 1 : 0;
+            } else {
+                const uint8_t *src = id >= 0 ? swa_b + static_cast<int64_t>(id) * (2 * kD) + 16 * lane
+                                             : kDecZeroPage + 16 * lane;
+                uint8_t *dst = rows + r * kB16Pitch;
+                dma16<0>(src, dst);
+                if (lane < 8) dma16<1024>(src, dst);
+                n2 += r >= G.rowsA ? 2 : 0;
+            }
+        }
+        return n2;
+    };
+
+    // SEL: the select, before anything that depends on the list.  (Issuing
+    // pass 0's window rows ahead of it measured slower: the select then waits
+    // for their table lookups, and their loads queue with the scores'.)
+    if constexpr (SEL) {
+        // list entries [cm0, cm1) into lst; head block 0 also writes them out
+        const int msl = a.sel_max_slots;
+        int n = visible_slots(p, a.sel_ratio, ns);
+        n = n < msl ? n : msl;
+        const bool writer = hb == 0;
+        int32_t *gl = a.sel_idx + static_cast<int64_t>(t) * kk;
+        if (writer && split == 0 && tid == 0) a.sel_len[t] = n < kk ? n : kk;
+        if (n <= kk) {                                            // everything visible is selected
+            for (int i = cm0 + tid; i < cm1; i += kThreads) {
+                const int32_t v = i < n ? i : -1;
+                lst[i - cm0] = v;
+                if (writer) gl[i] = v;
+            }
+        } else {
+            uint32_t *hist = reinterpret_cast<uint32_t *>(qp);
+            uint32_t *cand_key = hist + hist_words<kThreads>();
+            int32_t *cand_slot = reinterpret_cast<int32_t *>(cand_key + kSelCand);
+            select_row<kThreads, kSelR, kSelCand>(
+                raw, a.sel_scores + static_cast<int64_t>(t) * msl, n, kk,
+                [&](int pos, int32_t slot) {
+                    if (pos >= cm0 && pos < cm1) {
+                        lst[pos - cm0] = slot;
+                        if (writer) gl[pos] = slot;
+                    }
+                },
+                hist, cand_key, cand_slot, sel_red, sel_sh);
+        }
+        __syncthreads();                                          // lst ready, qp free again
+        // the list's stores are complete before the rows' loads go out: the
+        // stage waits below count only those loads
+        wait_vmem_at_most(0);
+        load_q();
+    }
 
     f32x4 o[4][HG];
 #pragma unroll
@@ -175,38 +325,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
     bf16x8 qb[9][2];                                              // its Q^T operands
 
     for (int pass = 0; pass < passes; pass++) {
-        // ---- this pass's rows: window rows first (padded to 32), then
-        // compressed rows (padded to 32)
-        const int e_sw = sw0 + pass * sw_cap, e_cm = cm0 + pass * cm_cap;
-        const int nsw = max(0, min(sw_cap, sw1 - e_sw)), ncm = max(0, min(cm_cap, cm1 - e_cm));
-        const int nsw_pad = (nsw + 31) & ~31, ncm_pad = (ncm + 31) & ~31;
-        const int R = nsw_pad + ncm_pad;
-        const int f8base = F8 ? 0 : nsw_pad * kB16Pitch;          // byte offset of the fp8 rows
-        const int f8first = F8 ? 0 : nsw_pad;                     // first row kept as fp8
-
-        // resolve: thread j -> physical row of pass row j (-1: skipped/padding)
-        if (tid < R) {
-            int32_t phys = -1;
-            if (tid < nsw_pad) {
-                const int pos = p - window + 1 + e_sw + tid;
-                const int64_t lb = pos >> 6;
-                if (tid < nsw && pos >= 0 && lb < swa_stride) {
-                    const int32_t pb = swa_tab[static_cast<int64_t>(seq) * swa_stride + lb];
-                    if (pb >= 0 && pb < swa_nb) phys = pb * kBR + (pos & (kBR - 1));
-                }
-            } else {
-                const int j = tid - nsw_pad;
-                if (j < ncm) {
-                    const int s = cmp_idx_p[static_cast<int64_t>(t) * kk + e_cm + j];
-                    const int64_t lb = s >> 6;
-                    if (s >= 0 && s < ns && lb < cmp_stride) {
-                        const int32_t pb = cmp_tab[static_cast<int64_t>(seq) * cmp_stride + lb];
-                        if (pb >= 0 && pb < cmp_nb) phys = pb * kBR + (s & (kBR - 1));
-                    }
-                }
-            }
-            rid[tid] = phys;
-        }
+        const Geo G = geo(pass);
+        const int nsw_pad = G.nsw_pad, R = G.R, f8base = G.f8base, f8first = G.f8first;
+        const int K = G.K, KA = G.KA;
+        resolve(G, 0, R);
         if (pass == 0) {
             // head group 0 of Q into the staging region
 #pragma unroll
@@ -217,44 +339,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(AttnArgs a) {
             }
         }
         __syncthreads();                                          // rid (and Q group 0) ready
-
-        // ---- issue every load of the pass: wave w takes pass rows w, w+8,
-        // ...; all their ids are read first, so that no LDS access sits
-        // between the loads.  Stages: k-steps [0, KA) first, then the rest.
-        const int K = R / 32;
-        const int KA = K <= 1 ? K : (K + 1) / 2;
-        const int rowsA = 32 * KA;
-        int later = 0;                                            // this wave's loads of stage 2
-        {
-            const int myr = w + kWaves * lane;
-            const int32_t my_id = myr < R ? rid[myr] : -1;
-            const int nr = (R - w + kWaves - 1) / kWaves;
-            const uint8_t *swa_b = reinterpret_cast<const uint8_t *>(a.swa.base);
-            const uint8_t *cmp_b = reinterpret_cast<const uint8_t *>(a.cmp.base);
-            for (int i = 0; i < nr; i++) {
-                const int r = w + kWaves * i;
-                const int32_t id = __builtin_amdgcn_readlane(my_id, i);
-                const bool f8row = F8 || r >= nsw_pad;
-                const bool from_swa = r < nsw_pad;
-                if (f8row) {
-                    // 40 lanes: 640 bytes of codes and rope; 2 lanes: the 32 bytes of scales
-                    const uint8_t *blk = (from_swa ? swa_b : cmp_b) +
-                                         static_cast<int64_t>(id >> 6) * SLC_CMP_BLOCK_BYTES;
-                    const uint8_t *src = lane < 40 ? blk + (id & 63) * SLC_CMP_ROW_BYTES + 16 * lane
-                                                   : blk + SLC_CMP_SCALE_OFFSET + (id & 63) * 32 + 16 * (lane - 40);
-                    if (id < 0) src = kDecZeroPage + 16 * lane;
-                    if (lane < 42) dma16<0>(src, rows + f8base + (r - f8first) * kF8Pitch);
-                    later += r >= rowsA ? 1 : 0;
-                } else {
-                    const uint8_t *src = id >= 0 ? swa_b + static_cast<int64_t>(id) * (2 * kD) + 16 * lane
-                                                 : kDecZeroPage + 16 * lane;
-                    uint8_t *dst = rows + r * kB16Pitch;
-                    dma16<0>(src, dst);
-                    if (lane < 8) dma16<1024>(src, dst);
-                    later += r >= rowsA ? 2 : 0;
-                }
-            }
-        }
+        const int later = issue(G, 0, (R - w + kWaves - 1) / kWaves);   // this wave's loads of stage 2
 
         if (pass == 0) {
             // the wave's head group's Q^T operands, in the k-order of the K
@@ -534,19 +619,33 @@ void decode_pass_caps(AttnArgs &a) {
     a.cm_cap = best_cm > 0 ? best_cm : 32;
 }
 
+bool decode_can_select(const AttnArgs &a0, const float *scores, int max_slots) {
+    AttnArgs a = a0;
+    decode_pass_caps(a);
+    return scores && (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && max_slots >= 4 &&
+           max_slots % 4 == 0 && max_slots <= kSelMaxSlots && a.cm_per <= kMaxListShare;
+}
+
+template <bool SEL>
+static void launch_decode_as(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    const int hg = a.head_groups;
+    if (a.swa_fp8) {
+        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, true, SEL>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((mla_decode_kernel<1, true, SEL>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, false, SEL>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((mla_decode_kernel<1, false, SEL>), grid, dim3(kThreads), 0, stream, a);
+    }
+}
+
 hipError_t launch_decode(const AttnArgs &a0, hipStream_t stream) {
     AttnArgs a = a0;
     decode_pass_caps(a);
     const int hg = a.head_groups;
     const unsigned groups = static_cast<unsigned>((a.n_q + 7) / 8);
     const dim3 grid(groups * 8u * (a.n_heads / (16 * hg)) * a.n_splits);
-    if (a.swa_fp8) {
-        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, true>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((mla_decode_kernel<1, true>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-        if (hg == 2) hipLaunchKernelGGL((mla_decode_kernel<2, false>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((mla_decode_kernel<1, false>), grid, dim3(kThreads), 0, stream, a);
-    }
+    if (a.sel_scores) launch_decode_as<true>(a, grid, stream);
+    else launch_decode_as<false>(a, grid, stream);
     return hipGetLastError();
 }
 

@@ -119,6 +119,14 @@ struct AttnArgs {
     int sw_cap, cm_cap;     // decode: window / compressed rows per LDS pass
     uint16_t *part_o;       // bf16 [n_q][n_splits][H][512] (decode, n_splits > 1)
     float *part_ml;         // [n_q][n_splits][H][2]
+    // decode that selects its own compressed list (sel_scores non-null):
+    // index scores [n_q][sel_max_slots], visible counts by sel_ratio; the
+    // list goes to sel_idx [n_q][k] and its length to sel_len [n_q]
+    const float *sel_scores;
+    int sel_max_slots;
+    int sel_ratio;
+    int32_t *sel_idx;
+    int32_t *sel_len;
 };
 
 hipError_t launch_compress(const CompressArgs &a, int n_seq, hipStream_t stream);
@@ -130,6 +138,9 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs &a, hipStream_t stream);   // decode.hip (no combine)
+// whether launch_decode selects the list itself for these shapes (else the
+// caller runs the top-k select first)
+bool decode_can_select(const AttnArgs &a, const float *scores, int max_slots);
 hipError_t launch_combine(const AttnArgs &a, hipStream_t stream);  // merge of the decode's splits
 
 // split plan (host arithmetic only): decode splits each (query, head block)'s

@@ -32,6 +32,7 @@ EXPORTED = [
     "slc_sparse_mla_decode_workspace_size", "slc_sparse_mla_decode",
     "slc_sparse_mla_prefill_workspace_size", "slc_sparse_mla_prefill", "slc_workspace_size",
     "slc_sparse_mla_decode_noalloc", "slc_sparse_mla_decode_noalloc_max_bytes",
+    "slc_sparse_mla_decode_topk",
 ]
 
 OP_INDEX_TOPK, OP_SPARSE_MLA_DECODE, OP_SPARSE_MLA_PREFILL = 1, 2, 3
@@ -125,6 +126,9 @@ def lib():
         L.slc_sparse_mla_decode_noalloc_max_bytes.argtypes = []
         L.slc_workspace_size.restype = sz
         L.slc_workspace_size.argtypes = [i32, C.POINTER(Shape)]
+        L.slc_sparse_mla_decode_topk.restype = i32
+        L.slc_sparse_mla_decode_topk.argtypes = [i32, i32, i32, vp, vp, vp, i32, pool, pool, i32,
+                                                 vp, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -381,6 +385,22 @@ def sparse_mla_prefill(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table,
                        lse=None, workspace=None):
     _sparse_mla(False, layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
                 cmp_table, cmp_idx, n_slots, sm_scale, out, lse, workspace)
+
+
+def sparse_mla_decode_topk(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table, cmp_pool,
+                           cmp_table, k, scores, max_slots, n_slots, topk_idx, topk_len,
+                           sm_scale=1.0, out=None, lse=None, workspace=None):
+    """slc_sparse_mla_decode_topk: the C4A top-k select of scores and the decode
+    over its list in one call (the list also written to topk_idx / topk_len)."""
+    n_q, H = int(q.shape[0]), int(q.shape[1])
+    need = sparse_mla_workspace_size(True, n_q, H, window, int(k))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().slc_sparse_mla_decode_topk(
+        int(layer_type), n_q, H, _ptr(q), _ptr(q_seq), _ptr(q_pos), int(window),
+        pool(swa_pool, swa_table), pool(cmp_pool, cmp_table), int(k), _ptr(scores),
+        int(max_slots), _ptr(n_slots), _ptr(topk_idx), _ptr(topk_len), float(sm_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), 0 if workspace is None else int(workspace.numel()), _stream()))
 
 
 def sparse_mla_decode_noalloc(layer_type, q, q_seq, q_pos, window, swa_pool, swa_table,

@@ -95,6 +95,29 @@ def test_invalid_arguments_are_rejected_before_launch(S):
     assert L.slc_topk_select(0, 8, None, 16, None, None, 4, None, None, None, None) == 0
 
 
+def test_decode_topk_validates_on_the_host(S):
+    """slc_sparse_mla_decode_topk: argument and workspace errors come back
+    before any launch (no device here)."""
+    L = S.lib()
+    fake = C.c_void_p(256)
+    pool = S.Pool(C.c_void_p(256), C.c_void_p(256), 4, 4)
+
+    def call(layer, k, ws=None, ws_bytes=0, scores=fake, max_slots=16384, topk_len=fake):
+        return L.slc_sparse_mla_decode_topk(layer, 32, 64, fake, fake, fake, 128, pool, pool, k,
+                                            scores, max_slots, fake, fake, topk_len, 0.1, fake,
+                                            None, ws, ws_bytes, None)
+    assert call(128, 512) == 1 and b"C4A" in L.slc_last_error()      # C128A takes a given list
+    assert call(1, 512) == 1                                           # SWAONLY has no list
+    assert call(4, 0) == 1 and call(4, 5000) == 1                      # k outside 1..SLC_MAX_TOPK
+    assert call(4, 512, max_slots=0) == 1                              # no slots
+    assert call(4, 512, scores=None) == 1 and b"scores" in L.slc_last_error()
+    assert call(4, 512, topk_len=None) == 1
+    assert call(4, 512) == 2                                           # the decode's workspace is missing
+    assert L.slc_sparse_mla_decode_topk(4, 0, 64, None, None, None, 128, pool, pool, 512, None,
+                                        16384, None, None, None, 0.1, None, None, None, 0,
+                                        None) == 0                     # nothing to do is not an error
+
+
 def test_workspace_size_dispatches_to_the_per_op_sizers(S):
     """slc_workspace_size (host arithmetic) equals the matching per-op sizer on
     every workload shape and on edge shapes, and flags misuse with SIZE_MAX."""
