@@ -60,6 +60,9 @@ constexpr int kSubTiles = 16;                       // 16-key sub-tiles per wave
 constexpr int kBlockSlots = 64;                     // slots per key block (one table entry)
 constexpr int kRing = 4;                            // sub-tiles per load group (2 groups in flight)
 constexpr int kQPitch = kDI + 16;                   // LDS bytes per staged query head
+// queries per workgroup on large grids (a prefill chunk): consecutive
+// queries of one sequence share every key load and key conversion
+constexpr int kPrefillQT = 2;
 
 // ReLU on the bit pattern: non-negative floats compare as non-negative ints,
 // negative ones as negative ints, so one integer max does it (-0 -> +0).
@@ -256,6 +259,222 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
     }
 }
 
+// Several consecutive queries per workgroup (large grids: a prefill chunk):
+// the same 1024-slot tiles as index_score_kernel<HT, 1, F4>, with the
+// workgroup's QT queries of one sequence sharing every key load and key
+// conversion (their operands held side by side); queries of different
+// sequences take a pass each.
+template <int HT, bool F4, int QT>
+__global__ __launch_bounds__(256) void index_score_mq_kernel(IndexArgs a) {
+    constexpr int WB = 1;
+    constexpr int RG = 2;                                        // sub-tiles per load group (registers: QT queries' operands)
+    constexpr int kThreads = 256 * WB, kTile = kSubTiles * kBlockSlots * WB;
+    const int t0 = blockIdx.x * QT;                              // the workgroup's queries t0 .. t0+QT-1
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int wq = w & 3;                                        // 16-slot quarter of a block
+    const int wb = __builtin_amdgcn_readfirstlane(w >> 2);       // block within a sub-tile
+    const int s0 = blockIdx.y * kTile;
+
+    // The kernel arguments of the start-up chain in one round of loads
+    // (left alone, the compiler spreads them over several dependent rounds,
+    // each a full load latency before the first key is requested).
+    const int32_t *q_seq_p = a.q_seq, *q_pos_p = a.q_pos, *n_slots_p = a.n_slots;
+    const int32_t *table_p = a.keys.block_table;
+    const int stride = a.keys.table_stride;
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.keys.base);
+    const uint8_t *zpage = kIndexZeroPage;
+    const int64_t n_blocks = a.keys.n_blocks;
+    const int n_q = a.n_q;
+    __asm__ volatile("" ::"s"(q_seq_p), "s"(q_pos_p), "s"(n_slots_p), "s"(table_p), "s"(stride), "s"(kbase),
+                     "s"(zpage), "s"(n_blocks), "s"(n_q));
+
+    // QT > 1: queries of one sequence share every key load (one pass); else
+    // (or when their sequences differ) each query takes a pass of its own
+    const int nq = min(QT, n_q - t0);
+    int seqs[QT];
+#pragma unroll
+    for (int qi = 0; qi < QT; qi++) seqs[qi] = q_seq_p[min(t0 + qi, n_q - 1)];
+    bool same = true;
+#pragma unroll
+    for (int qi = 1; qi < QT; qi++) same = same && seqs[qi] == seqs[0];
+    const int passes = same ? 1 : nq;
+
+    // The pass's 32 block-table entries first, in one load (lane j % 32
+    // takes entry j; entries past the table read entry 0 and are discarded):
+    // the first key loads wait on them, and a wave's loads complete in issue
+    // order.  Each sub-tile later moves its entry to a scalar register, so no
+    // key load waits on a table lookup of its own.
+    int32_t my_pb;
+    auto lookup = [&](int seq) {
+        const int64_t table_row = static_cast<int64_t>(seq) * stride;
+        const int64_t lb = (s0 >> 6) + (lane & (kSubTiles * WB - 1));
+        const bool in = lb < stride;
+        my_pb = table_p[table_row + (in ? lb : 0)];
+        my_pb = in ? my_pb : -1;
+    };
+    lookup(seqs[0]);
+
+    int nv[QT];                                  // visible slots: read after the first key loads
+    bf16x8 qa[QT][HT][4];                        // filled after the first key loads are issued
+    float hf[QT][HT][4];
+
+    constexpr uint32_t kKeyBytes = F4 ? kDI / 2 : kDI;
+    constexpr uint32_t kBlkBytes = F4 ? SLC_KEY4_BLOCK_BYTES : SLC_KEY_BLOCK_BYTES;
+    constexpr uint32_t kScaleOff = F4 ? SLC_KEY4_SCALE_OFFSET : SLC_KEY_SCALE_OFFSET;
+    const uint32_t lane_off = static_cast<uint32_t>((16 * wq + c) * kKeyBytes + 16 * g);
+    const uint32_t scale_off = static_cast<uint32_t>(kScaleOff + 4 * (16 * wq + c));
+
+    // sub-tile j reads through a buffer resource on its (wave-uniform) block;
+    // an absent block gets a zero-size resource, whose loads return zeros
+    auto stage = [&](int j, KeyStage &st) {
+        const int32_t pb = __builtin_amdgcn_readlane(my_pb, WB * j + wb);
+        const bool ok = pb >= 0 && pb < n_blocks;
+        const uint8_t *bp = ok ? kbase + static_cast<int64_t>(pb) * kBlkBytes : zpage;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(bp), 0, ok ? kBlkBytes : 0, kBufferWord3);
+        st.lo = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0);
+        if constexpr (!F4) st.hi = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 64u, 0, 0);
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, scale_off, 0, 0));
+        st.scale = ok ? sc : -INFINITY;
+    };
+    // the keys of sub-tile j against the pass's queries (every query of the
+    // workgroup in a shared pass, query `pass` alone otherwise)
+    auto compute = [&](int j, const KeyStage &cur, int pass) {
+        const int s = s0 + kBlockSlots * (WB * j + wb) + 16 * wq + c;
+        bf16x8 kb[4];
+        if constexpr (F4) {
+            const uint32_t word = __builtin_bit_cast(uint32_t, cur.scale);
+            e2m1x32_to_operands(cur.lo, e8m0_scale((word >> (8 * g)) & 0xffu), kb);
+        } else {
+            e4m3x16_to_operands(cur.lo, kb[0], kb[1]);
+            e4m3x16_to_operands(cur.hi, kb[2], kb[3]);
+        }
+#pragma unroll
+        for (int qi = 0; qi < QT; qi++) {
+            if (!(same ? qi < nq : qi == pass)) continue;         // uniform
+            f32x4 acc[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) {
+                acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; st++)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qi][ht][st], kb[st], acc[ht], 0,
+                                                                       0, 0);
+            }
+            float part = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) part += hf[qi][ht][i] * relu(acc[ht][i]);
+            part = xor32_sum(xor16_sum(part));
+            if (g == 0 && s < nv[qi]) {
+                float v;
+                if constexpr (F4) v = cur.scale == -INFINITY ? -INFINITY : part;   // scales applied in the dot
+                else v = cur.scale == -INFINITY ? -INFINITY : part * cur.scale;
+                a.scores[static_cast<int64_t>(t0 + qi) * a.max_slots + s] = v;
+            }
+        }
+    };
+
+    // ---- query operands and per-head factors (they depend on t only) ----
+    // A query's 16*HT heads x 128 codes are one contiguous run (and the
+    // workgroup's queries are consecutive) that the workgroup loads once,
+    // coalesced (per-wave operand loads would fetch it four times, in
+    // half-line pieces), and stages through LDS.  With one workgroup per CU
+    // (WB = 2) these loads follow the first key loads, which wait only on the
+    // table; with several four-wave workgroups per CU (WB = 1) they come
+    // first (measured 4% faster there), and the key loads' wait on the table,
+    // issued before them, does not cover them.  The visible counts decide
+    // the early exit after the first key loads either way: those read
+    // in-range blocks or the zero page.
+    constexpr int kQUnits = QT * 16 * HT * kDI / 16;     // 16-byte units
+    constexpr int kQIt = (kQUnits + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[QT * 16 * HT * kQPitch];
+    u32x4 qraw[kQIt];
+    f32x4 qw[QT][HT], qs[QT][HT];
+    auto load_query = [&]() {
+        // units past the last query re-read the last query's (and are dropped)
+        const int64_t last = static_cast<int64_t>(n_q) * a.h_idx * kDI / 16 - 1;
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(a.q) + static_cast<int64_t>(t0) * a.h_idx * kDI / 16;
+#pragma unroll
+        for (int i = 0; i < kQIt; i++) {
+            const int u = threadIdx.x + kThreads * i;
+            const int64_t gu = static_cast<int64_t>(t0) * a.h_idx * kDI / 16 + u;
+            if (u < kQUnits) qraw[i] = qp[gu <= last ? u : last - static_cast<int64_t>(t0) * a.h_idx * kDI / 16];
+        }
+#pragma unroll
+        for (int qi = 0; qi < QT; qi++) {
+            const int tq = min(t0 + qi, n_q - 1);
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) {
+                const int64_t o = static_cast<int64_t>(tq) * a.h_idx + 16 * ht + 4 * g;   // heads 4g..4g+3
+                qw[qi][ht] = *reinterpret_cast<const f32x4 *>(a.w + o);
+                qs[qi][ht] = *reinterpret_cast<const f32x4 *>(a.q_scale + o);
+            }
+        }
+    };
+
+    // two explicit buffers of RG sub-tiles: load group q+1 while computing q
+    KeyStage buf0[RG], buf1[RG];
+    if constexpr (WB == 1) load_query();
+#pragma unroll
+    for (int j = 0; j < RG; j++) stage(j, buf0[j]);
+    if constexpr (WB != 1) load_query();
+    int nv_any = 0;
+#pragma unroll
+    for (int qi = 0; qi < QT; qi++) {
+        const int tq = min(t0 + qi, n_q - 1);
+        int v = visible_slots(q_pos_p[tq], a.ratio, n_slots_p[seqs[qi]]);
+        v = v < a.max_slots ? v : a.max_slots;
+        nv[qi] = qi < nq ? v : 0;
+        nv_any = max(nv_any, nv[qi]);
+    }
+    if (s0 >= nv_any) return;
+
+#pragma unroll
+    for (int i = 0; i < kQIt; i++) {
+        const int u = threadIdx.x + kThreads * i;
+        if (u < kQUnits)
+            *reinterpret_cast<u32x4 *>(qlds + (u / (kDI / 16)) * kQPitch + 16 * (u % (kDI / 16))) = qraw[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qi = 0; qi < QT; qi++)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            const uint8_t *qr = qlds + ((qi * HT + ht) * 16 + c) * kQPitch;
+            const int q0 = F4 ? 32 * g : 16 * g, q1 = F4 ? 32 * g + 16 : 64 + 16 * g;   // the key's dims
+            e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + q0), qa[qi][ht][0], qa[qi][ht][1]);
+            e4m3x16_to_operands(*reinterpret_cast<const u32x4 *>(qr + q1), qa[qi][ht][2], qa[qi][ht][3]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) hf[qi][ht][i] = qw[qi][ht][i] * qs[qi][ht][i];
+        }
+    for (int pass = 0; pass < passes; pass++) {
+        int nvp = nv_any;                                        // this pass's largest visible count
+        if (pass > 0) {                                          // (queries of different sequences)
+            lookup(seqs[pass]);
+            nvp = nv[pass];
+#pragma unroll
+            for (int j = 0; j < RG; j++) stage(j, buf0[j]);
+        } else if (!same) {
+            nvp = nv[0];
+        }
+#pragma unroll
+        for (int q = 0; q < kSubTiles / RG; q++) {
+            KeyStage (&cur)[RG] = (q & 1) ? buf1 : buf0;
+            KeyStage (&nxt)[RG] = (q & 1) ? buf0 : buf1;
+            if (q + 1 < kSubTiles / RG) {
+#pragma unroll
+                for (int j = 0; j < RG; j++) stage((q + 1) * RG + j, nxt[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < RG; j++)
+                if (s0 + kBlockSlots * (WB * (q * RG + j) + wb) < nvp) compute(q * RG + j, cur[j], pass);   // wave-uniform
+        }
+    }
+}
+
 template <int WB, bool F4>
 static void launch_index(const IndexArgs &a, hipStream_t stream) {
     constexpr int tile = kSubTiles * kBlockSlots * WB;
@@ -268,6 +487,18 @@ static void launch_index(const IndexArgs &a, hipStream_t stream) {
     }
 }
 
+template <bool F4>
+static void launch_index_mq(const IndexArgs &a, hipStream_t stream) {
+    constexpr int tile = kSubTiles * kBlockSlots;
+    const dim3 grid((a.n_q + kPrefillQT - 1) / kPrefillQT, (a.max_slots + tile - 1) / tile), block(256);
+    switch (a.h_idx / 16) {
+    case 1: hipLaunchKernelGGL((index_score_mq_kernel<1, F4, kPrefillQT>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((index_score_mq_kernel<2, F4, kPrefillQT>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((index_score_mq_kernel<3, F4, kPrefillQT>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((index_score_mq_kernel<4, F4, kPrefillQT>), grid, block, 0, stream, a); break;
+    }
+}
+
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     // eight-wave 2048-slot tiles while the grid stays within about two
     // workgroups per CU (256 CUs), four-wave 1024-slot tiles beyond
@@ -275,10 +506,10 @@ hipError_t launch_index_scores(const IndexArgs &a, hipStream_t stream) {
     const int64_t wide = static_cast<int64_t>(a.n_q) * ((a.max_slots + 2047) / 2048);
     if (a.key_fp4) {
         if (wide <= 2 * kCUs) launch_index<2, true>(a, stream);
-        else launch_index<1, true>(a, stream);
+        else launch_index_mq<true>(a, stream);
     } else {
         if (wide <= 2 * kCUs) launch_index<2, false>(a, stream);
-        else launch_index<1, false>(a, stream);
+        else launch_index_mq<false>(a, stream);
     }
     return hipGetLastError();
 }
