@@ -121,7 +121,8 @@ def kernel_source_hash(name: str = "index.hip") -> str:
 
 # the source file each library kernel is built from (for tying counter
 # summaries to the code they were taken on)
-KERNEL_SOURCES = {"index_score_kernel": "index.hip", "topk_kernel": "topk.hip",
+KERNEL_SOURCES = {"index_score_kernel": "index.hip", "index_score_mq_kernel": "index.hip",
+                  "topk_kernel": "topk.hip",
                   "topk_warm_kernel": "topk.hip", "topk_small_kernel": "topk.hip",
                   "topk_long_kernel": "topk.hip", "mla_decode_kernel": "decode.hip",
                   "mla_combine_kernel": "attention.hip", "mla_prefill_kernel": "attention.hip",
@@ -216,23 +217,29 @@ def report_counters(fetch_dir: str, write_dir: str, stem: str, calib_mib: int, c
     # algorithmic bytes per launch where this file states them
     algo = {}
     if workload == "c4a_decode_64k":
-        algo = {"index_score_kernel": INDEX_KERNEL_BYTES,
-                "mla_decode_kernel + mla_combine_kernel": B * ATTN_BYTES_PER_QUERY}
+        algo = {"slc::index_score_kernel<4, 2, false>": INDEX_KERNEL_BYTES,
+                # the step's select + decode call: the attention's bytes plus
+                # the score rows it selects from
+                "slc::mla_decode_kernel<2, false, true> + slc::mla_combine_kernel<4>":
+                    B * (ATTN_BYTES_PER_QUERY + SLOTS * 4 + 4),
+                "slc::mla_decode_kernel<2, false, false> + slc::mla_combine_kernel<4>":
+                    B * ATTN_BYTES_PER_QUERY}
     elif workload == "c4a_single_layer_4k":
-        algo = {"compress_r4_kernel": COMPRESS_4K_BYTES}
+        algo = {"slc::compress_r4_kernel": COMPRESS_4K_BYTES}
     kernels = {}
     for name in sorted(fetch):
         if "slc::" not in name or name not in write:
             continue
-        key = _kernel_key(name)
+        key = _short(name)
+        base = _kernel_key(name)
         f, w = fetch[name], write[name]
         kernels[key] = {"name": _short(name), "fetch_kib": f[0], "write_kib": w[0],
                         "dispatches": [f[1], w[1]], "fetch_range_kib": [f[2], f[3]],
                         "hbm_read_bytes": f[0] * kf * 1024.0,
                         "hbm_write_bytes": w[0] * kw * 1024.0,
-                        "source": KERNEL_SOURCES.get(key),
-                        "source_sha256_16": kernel_source_hash(KERNEL_SOURCES[key])
-                        if key in KERNEL_SOURCES else None}
+                        "source": KERNEL_SOURCES.get(base),
+                        "source_sha256_16": kernel_source_hash(KERNEL_SOURCES[base])
+                        if base in KERNEL_SOURCES else None}
         kernels[key]["hbm_bytes"] = kernels[key]["hbm_read_bytes"] + kernels[key]["hbm_write_bytes"]
     groups = {}
     for label, ab in algo.items():
@@ -263,8 +270,8 @@ def report_counters(fetch_dir: str, write_dir: str, stem: str, calib_mib: int, c
                       f"{gr['ratio']:.3f} |")
     open(stem + ".md", "w").write("\n".join(md) + "\n")
     print("\n".join(md))
-    if workload == "c4a_decode_64k" and "index_score_kernel" in kernels:
-        k = kernels["index_score_kernel"]
+    if workload == "c4a_decode_64k" and "slc::index_score_kernel<4, 2, false>" in kernels:
+        k = kernels["slc::index_score_kernel<4, 2, false>"]
         rec = {"kernel": "index_score_kernel", "workload": workload,
                "fetch_kib_per_dispatch": k["fetch_kib"], "write_kib_per_dispatch": k["write_kib"],
                "dispatches": k["dispatches"], "calibration": calib,
