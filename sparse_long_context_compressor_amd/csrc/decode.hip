@@ -29,6 +29,7 @@
 // states; mla_combine_kernel merges them (attention.hip).
 
 #include "slc_internal.hpp"
+#include "rows.hpp"
 #include "select.hpp"
 
 namespace slc {
@@ -37,9 +38,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kB16Pitch = 2 * kD + 16;          // bytes per bf16 row in LDS (1168)
-constexpr int kF8Pitch = 688;                   // 512 codes | 64 bf16 rope | 8 fp32 scales | pad
-constexpr int kF8Data = SLC_CMP_ROW_BYTES;      // 640: codes + rope, then the scales
 constexpr int kRowBytes = 132 * 1024;           // LDS for one pass's rows
 constexpr int kMaxPassRows = 192;               // rows of one pass (a multiple of 32)
 constexpr int kMaxKsteps = kMaxPassRows / 32;
@@ -48,8 +46,6 @@ constexpr int kOutPitch = 144;                  // bytes per head in the output 
 constexpr int kQpBytes = kMaxKsteps * 2 * 2 * 64 * 16;
 static_assert(16 * kB16Pitch <= kQpBytes, "one head group of Q fits the P^T region");
 static_assert(kWaves * 32 * kOutPitch <= kRowBytes, "the output is staged in the row region");
-
-static_assert(kF8Pitch % 16 == 0 && (kF8Pitch / 16) % 2 == 1, "16-byte reads of 8 rows hit distinct banks");
 
 // The select of a workgroup's own list: 32 scores per thread (rows up to
 // 16384 slots), up to 2048 prefiltered candidates; its histogram and
@@ -60,51 +56,7 @@ constexpr int kSelCand = 2048;
 constexpr int kMaxListShare = 512;              // list entries of one split
 static_assert(hist_words<kThreads>() * 4 + 8 * kSelCand <= kQpBytes, "select scratch fits");
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Rows of skipped or padding entries are loaded from here (never written),
-// so every row in LDS holds finite values.
-__device__ __attribute__((aligned(256))) uint8_t kDecZeroPage[2048];
-
-// One direct global->LDS load of 16 bytes per active lane: lane l's bytes
-// land at dst + off + 16 l (dst wave-uniform); off is added to src as well.
-template <int OFF>
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, OFF, 0);
-}
-
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint8_t *p) {
-    return *reinterpret_cast<const bf16x8 *>(p);
-}
-
-// 8 e4m3 codes (two dwords) -> 8 bf16 times a power-of-two scale, exactly.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1, float scale) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), scale, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), scale, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), scale, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), scale, true);
-    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 }  // namespace
-
-// Wait until at most n (wave-uniform, clamped to 31) of this wave's vector
-// memory operations are outstanding; a larger n waits as for 31, which is
-// never too short.
-__device__ __forceinline__ void wait_vmem_at_most(int n) {
-#define SLC_VM_CASE(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | 0x70 | 0xF00 | (((k) >> 4) << 14)); break;
-    switch (n < 31 ? (n < 0 ? 0 : n) : 31) {
-        SLC_VM_CASE(0) SLC_VM_CASE(1) SLC_VM_CASE(2) SLC_VM_CASE(3) SLC_VM_CASE(4) SLC_VM_CASE(5)
-        SLC_VM_CASE(6) SLC_VM_CASE(7) SLC_VM_CASE(8) SLC_VM_CASE(9) SLC_VM_CASE(10) SLC_VM_CASE(11)
-        SLC_VM_CASE(12) SLC_VM_CASE(13) SLC_VM_CASE(14) SLC_VM_CASE(15) SLC_VM_CASE(16)
-        SLC_VM_CASE(17) SLC_VM_CASE(18) SLC_VM_CASE(19) SLC_VM_CASE(20) SLC_VM_CASE(21)
-        SLC_VM_CASE(22) SLC_VM_CASE(23) SLC_VM_CASE(24) SLC_VM_CASE(25) SLC_VM_CASE(26)
-        SLC_VM_CASE(27) SLC_VM_CASE(28) SLC_VM_CASE(29) SLC_VM_CASE(30)
-        default: __builtin_amdgcn_s_waitcnt((31 & 15) | 0x70 | 0xF00 | (1 << 14)); break;
-    }
-#undef SLC_VM_CASE
-}
 
 // Grid: ceil(n_q / 8) * 8 * HB * S workgroups of 512 threads, HB = n_heads /
 // (16 HG).  Blocks of one query share blockIdx % 8 (one XCD, one L2).
