@@ -446,10 +446,30 @@ def other_workload(args):
             f(r | fl, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool, lay.swa_table, lay.cmp_pool,
               lay.cmp_table, get_idx(lay), lay.n_slots, lay.sm_scale, out, lse, ws)
     stages["sparse_mla_decode" if decode else "sparse_mla_prefill"] = attention
+    fused = decode and r == 4 and HIi > 0
+
+    def topk_decode(lay):
+        # the select and the decode over its list in one call
+        slc.sparse_mla_decode_topk(4 | fl, lay.q, lay.q_seq, lay.q_pos, Ww, lay.swa_pool,
+                                   lay.swa_table, lay.cmp_pool, lay.cmp_table, Kk, sc, ms_,
+                                   lay.n_slots, idx, ln, lay.sm_scale, out, lse, ws)
+    if fused:
+        stages["sparse_mla_decode_topk"] = topk_decode
+
+    def step_calls(lay):
+        for k_, fn in stages.items():
+            if k_ != "sparse_mla_decode_topk":
+                fn(lay)
 
     def step(lay):
-        for fn in stages.values():
-            fn(lay)
+        if fused:
+            # the step as the library's fastest form: (compress,) index, then
+            # the select and decode in one call
+            for k_, fn in stages.items():
+                if k_ not in ("topk_select", "sparse_mla_decode"):
+                    fn(lay)
+        else:
+            step_calls(lay)
 
     def timed(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -462,15 +482,47 @@ def other_workload(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def graph_timed(fn, n):
+        """ms per call of fn as replays of a graph of back-to-back calls over the
+        replicas (an eager loop of one short op is bound by the host)."""
+        per_graph = len(reps) * 4
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for rr in reps:
+                fn(rr)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                fn(reps[i % len(reps)])
+        g.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, n // per_graph)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_rep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_rep * per_graph)
+
     steps = max(10, args.steps // (10 if name == "c4a_prefill_2k" else 1))
     for i in range(args.warmup):
         step(reps[i % len(reps)])
     torch.cuda.synchronize()
     ms_step = timed(step, steps)
-    per = {k: timed(fn, steps) * 1e3 for k, fn in stages.items()}
+    long_ops = name == "c4a_prefill_2k"     # milliseconds per op: eager launches suffice
+    per = {k: (timed if long_ops else graph_timed)(fn, steps) * 1e3 for k, fn in stages.items()}
     rec = {"workload": name, "queries": Q, "heads": Hh, "window": Ww, "topk": Kk,
            "ms_per_pass": ms_step, "queries_per_s": Q / (ms_step * 1e-3), "stages_us": per,
+           "stages_timing": "eager_launches" if long_ops else "graph_replay",
            "steps": steps, "data": "synthetic"}
+    if fused:
+        rec["ms_per_pass_three_calls"] = timed(step_calls, steps)
+        rec["graph_ms_per_pass"] = graph_timed(step, steps)
     # algorithmic bytes / flops of the attention stage
     n_cmp = Kk if r > 1 else 0
     att_us = per["sparse_mla_decode" if decode else "sparse_mla_prefill"]

@@ -397,7 +397,12 @@ void mla_prefill_kernel(AttnArgs a) {
 // into LDS at once and is bound by how fast the compute units pull bytes, so
 // the lists are split until about one workgroup runs per CU (256): S =
 // ceil(256 / (queries x head blocks)), at most kMaxCombineSplits, and fewer
-// while a split would hold under 32 entries.  Prefill never splits.
+// while a split would hold under 32 entries.  No split at all when splitting
+// would take fewer than kMergeRows entries off each workgroup: the merge (a
+// second launch over the partial states) costs more than that saves (the
+// 128-row window of 64 queries measured 13.5 us unsplit against 16.5 us in
+// two splits plus the merge; one query's 384 entries 16.5 us in 8 splits
+// against 18.4 us in 4).  Prefill never splits.
 void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n_splits,
                     int *rows_per_split, int *head_groups) {
     const int entries = window + k;
@@ -413,6 +418,8 @@ void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n
     int sp = (kCUs + blocks - 1) / blocks;
     sp = sp < kMaxCombineSplits ? sp : kMaxCombineSplits;
     while (sp > 1 && entries / sp < 32) sp--;
+    constexpr int kMergeRows = 80;
+    if (sp > 1 && entries * (sp - 1) < kMergeRows * sp) sp = 1;
     *n_splits = sp;
     *rows_per_split = (entries + sp - 1) / sp;
     *head_groups = ng;
