@@ -913,7 +913,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profile(), "algorithmic_bytes": INDEX_KERNEL_BYTES},
         "practical_peak": {"read_GBps": read_GBps, "copy_GBps": copy_GBps,
-                           "what": "2 GiB streaming read (bench_probe.hip, 8 loads in flight per thread); 1 GiB torch device copy, read + write",
+                           "what": "2 GiB streaming read (bench_probe.hip: one contiguous 512 KB region per workgroup, 8 non-temporal loads in flight per thread); 1 GiB torch device copy, read + write",
                            "index_frac_of_read": achieved / read_GBps,
                            "step_frac_of_read": STEP_BYTES / (ms_step * 1e-3) / 1e9 / read_GBps},
     }
