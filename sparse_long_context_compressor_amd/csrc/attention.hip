@@ -189,7 +189,7 @@ __device__ __forceinline__ float softmax_update(float (&x)[N], float &m_run, flo
     cmax = xor32_max(xor16_max(cmax));
     float alpha = 1.f;
     if (cmax > m_run + kLazyLog2) {      // also taken when m_run = -inf and cmax is finite
-        alpha = exp2f(m_run - cmax);
+        alpha = __builtin_amdgcn_exp2f(m_run - cmax);
         m_run = cmax;
     }
     float psum = 0.f;
@@ -199,7 +199,7 @@ __device__ __forceinline__ float softmax_update(float (&x)[N], float &m_run, flo
     } else {
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            p[i] = exp2f(x[i] - m_run);
+            p[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
             psum += p[i];
         }
     }
@@ -294,102 +294,169 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------- prefill
-// NW + 4 waves: waves 0..NW-1 compute (wave w: heads 16w..16w+15 of the block,
-// all rows of each 32-row chunk), four more waves gather the next chunk.
+// Eight waves: four compute, four gather.  Two LDS tiles alternate: while the
+// compute waves work on chunk c (32 rows) in one, the gather waves write
+// chunk c + 1 into the other (its loads were issued two chunks ahead).
+// Per chunk:
+//   scores   compute wave w < NW owns heads 16w..16w+15 of the block: S^T for
+//            the chunk's rows, its heads' online softmax, and publishes the
+//            P^T operands and rescale factors of its heads in LDS;
+//   values   compute wave w owns output dims 128w..128w+127 of every head:
+//            each V^T operand, read once with ds_read_tr16_b64, serves the
+//            NW head groups' P^T operands (a quarter of the transposing reads
+//            that one wave per head group over all 512 dims would need).
+// Barriers: one before chunk 0, one between a chunk's scores and its values,
+// one between chunks, one before the output (both roles take all of them).
 template <int NW, bool F8>
-__global__ __launch_bounds__((NW + 4) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ktile[kPreRows * kKPitch];
-    __shared__ int32_t src[kMaxEntries];
+    __shared__ __attribute__((aligned(16))) uint16_t ktile[2][kPreRows * kKPitch];
+    __shared__ __attribute__((aligned(16))) int32_t src[kMaxEntries + kPreRows];   // -1 past the list
+    __shared__ u32x4 pshare[4][64];                 // P^T operands per head group
+    __shared__ float ashare[4][16];                 // rescale factor per head
+    __shared__ float lshare[4][16];                 // final sum per head
 
-    constexpr int NT = (NW + 4) * 64;
+    constexpr int NT = 512;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int t = blockIdx.x;
-    const int h0 = 64 * blockIdx.y;                 // head block (up to 64 heads)
+    const int h0 = 16 * NW * blockIdx.y;            // head block (NW groups of 16)
     const int seq = a.q_seq[t], p = a.q_pos[t];
     const int E = a.window + a.k;
     const int ns = a.k > 0 ? a.n_slots[seq] : 0;
 
-    for (int e = tid; e < E; e += NT) src[e] = resolve_entry(a, t, seq, p, ns, e);
+    const int nchunks = (E + kPreRows - 1) / kPreRows;
+    for (int e = tid; e < nchunks * kPreRows; e += NT) src[e] = e < E ? resolve_entry(a, t, seq, p, ns, e) : -1;
     __syncthreads();
 
-    if (w >= NW) {
-        RowGather<kPreRows / 4, F8> ga, gb;
-        const int pw = __builtin_amdgcn_readfirstlane(w - NW);
+    if (w >= 4) {
+        RowGather<kPreRows / 4, F8> ga, gb;     // chunks 0, 2, 4, ... and 1, 3, 5, ...
+        const int pw = __builtin_amdgcn_readfirstlane(w - 4);
         // unconditional loads (past the list: the zero page), so that a
         // buffer's store waits for its own loads only
         ga.load(a, src, 0, 0, E, pw, lane);
         gb.load(a, src, 0, kPreRows, E, pw, lane);
-        for (int e0 = 0; e0 < E; e0 += 2 * kPreRows) {
-            if (e0 != 0) __syncthreads();
-            ga.store(ktile, a, e0, pw, lane);
-            __syncthreads();
-            ga.load(a, src, 0, e0 + 2 * kPreRows, E, pw, lane);
-            if (e0 + kPreRows < E) {
-                __syncthreads();
-                gb.store(ktile, a, e0 + kPreRows, pw, lane);
-                __syncthreads();
+        ga.store(ktile[0], a, 0, pw, lane);
+        ga.load(a, src, 0, 2 * kPreRows, E, pw, lane);
+        __syncthreads();                                  // chunk 0 in tile 0
+        for (int cc = 0; cc < nchunks; cc += 2) {
+            // chunk cc + 1 into tile 1 (chunk cc - 1's values are done)
+            if (cc + 1 < nchunks) {
+                gb.store(ktile[1], a, (cc + 1) * kPreRows, pw, lane);
+                gb.load(a, src, 0, (cc + 3) * kPreRows, E, pw, lane);
             }
-            gb.load(a, src, 0, e0 + 3 * kPreRows, E, pw, lane);
+            __syncthreads();                              // chunk cc: scores -> values
+            if (cc + 1 >= nchunks) break;
+            __syncthreads();                              // chunk cc done, cc + 1 in tile 1
+            if (cc + 2 < nchunks) {
+                ga.store(ktile[0], a, (cc + 2) * kPreRows, pw, lane);
+                ga.load(a, src, 0, (cc + 4) * kPreRows, E, pw, lane);
+            }
+            __syncthreads();                              // chunk cc + 1: scores -> values
+            if (cc + 2 >= nchunks) break;
+            __syncthreads();                              // chunk cc + 1 done, cc + 2 in tile 0
         }
+        __syncthreads();                                  // the final sums
         return;
     }
 
-    const int h = h0 + 16 * w + c;
+    const bool owner = w < NW;                            // a head group's scores
     bf16x8 qb[kD / 32];
-    load_q(a, t, h, g, qb);
-    f32x4 o[kDN / 16];
+    if (owner) load_q(a, t, h0 + 16 * w + c, g, qb);
+    f32x4 o[NW][8];                                       // dims 128w + 16 ct + 4g.., head 16 hg + c
 #pragma unroll
-    for (int ct = 0; ct < kDN / 16; ct++) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hg = 0; hg < NW; hg++)
+#pragma unroll
+        for (int ct = 0; ct < 8; ct++) o[hg][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int e0 = 0; e0 < E; e0 += kPreRows) {
-        if (e0 != 0) __syncthreads();
-        __syncthreads();
+    __syncthreads();                                      // chunk 0 in tile 0
+    for (int cc = 0; cc < nchunks; cc++) {
+        const int e0 = cc * kPreRows;
+        const uint16_t *kt = ktile[cc & 1];
+        if (owner) {
+            // the rows' ids (-1: skipped or past the list), read ahead of the products
+            i32x4 sv[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) sv[mt] = *reinterpret_cast<const i32x4 *>(src + e0 + 16 * mt + 4 * g);
+            // per row tile, two accumulators (even and odd k-steps), so that
+            // consecutive products do not wait for each other
+            f32x4 sacc[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) {
+                f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                const uint16_t *kr = kt + (16 * mt + c) * kKPitch + 8 * g;
+#pragma unroll
+                for (int s = 0; s < kD / 32; s += 2) {
+                    bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * s));
+                    bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * s + 32));
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[s + 1], s1, 0, 0, 0);
+                }
+                sacc[mt] = s0 + s1;
+            }
+            float x[8], pv[8];
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) x[4 * mt + i] = sv[mt][i] >= 0 ? sacc[mt][i] * a.sm_scale_log2 : -INFINITY;
+            const float alpha = softmax_update<8>(x, m_run, l_run, pv);
+            // k = 32 rows: 4g+0..3 then 16+4g+0..3 (same order as the V^T reads)
+            pshare[w][lane] = u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
+                                    bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])};
+            if (g == 0) ashare[w][c] = alpha;
+        }
+        __syncthreads();                                  // the chunk's P^T and factors
 
-        f32x4 sacc[2];
+        bf16x8 pb[NW];
+        float al[NW];
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
-            sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t *kr = ktile + (16 * mt + c) * kKPitch + 8 * g;
+        for (int hg = 0; hg < NW; hg++) {
+            pb[hg] = __builtin_bit_cast(bf16x8, pshare[hg][lane]);
+            al[hg] = ashare[hg][c];
+        }
 #pragma unroll
-            for (int s = 0; s < kD / 32; s++) {
-                bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 32 * s));
-                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
+        for (int hg = 0; hg < NW; hg++) {
+            if (__ballot(al[hg] != 1.f)) {
+#pragma unroll
+                for (int ct = 0; ct < 8; ct++) o[hg][ct] *= al[hg];
             }
         }
-        float x[8], pv[8];
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                int e = e0 + 16 * mt + 4 * g + i;
-                x[4 * mt + i] = (e < E && src[e] >= 0) ? sacc[mt][i] * a.sm_scale_log2 : -INFINITY;
-            }
-        const bool had = m_run != -INFINITY;
-        const float alpha = softmax_update<8>(x, m_run, l_run, pv);
-        if (__ballot(had && alpha != 1.f)) {
-#pragma unroll
-            for (int ct = 0; ct < kDN / 16; ct++) o[ct] *= alpha;
-        }
-
-        // k = 32 rows: 4g+0..3 then 16+4g+0..3 (same order as pv)
-        bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{bf16_pair_rne(pv[0], pv[1]), bf16_pair_rne(pv[2], pv[3]),
-                          bf16_pair_rne(pv[4], pv[5]), bf16_pair_rne(pv[6], pv[7])});
-        const uint16_t *v1 = ktile + (4 * g + (c >> 2)) * kKPitch + 4 * (c & 3);
+        const uint16_t *v1 = kt + (4 * g + (c >> 2)) * kKPitch + 4 * (c & 3) + 128 * w;
         const uint16_t *v2 = v1 + 16 * kKPitch;
 #pragma unroll
-        for (int ct = 0; ct < kDN / 16; ct++) {
+        for (int ct = 0; ct < 8; ct++) {
             i16x4 lo = lds_read_tr16(v1 + 16 * ct);
             i16x4 hi = lds_read_tr16(v2 + 16 * ct);
             u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
             bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-            o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[ct], 0, 0, 0);
+#pragma unroll
+            for (int hg = 0; hg < NW; hg++)
+                o[hg][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hg], o[hg][ct], 0, 0, 0);
         }
+        if (cc + 1 < nchunks) __syncthreads();           // chunk cc done, cc + 1 in the other tile
     }
-    store_out(a, t, h, g, o, m_run, l_run);
+
+    // the owners' sums (and log-sum-exp) of their heads, then every wave
+    // normalises and writes its dims of every head
+    if (owner && g == 0) {
+        lshare[w][c] = l_run;
+        if (a.lse)
+            a.lse[static_cast<int64_t>(t) * a.n_heads + h0 + 16 * w + c] =
+                l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hg = 0; hg < NW; hg++) {
+        const float l = lshare[hg][c];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *op = a.out + (static_cast<int64_t>(t) * a.n_heads + h0 + 16 * hg + c) * kDN + 128 * w + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < 8; ct++)
+            *reinterpret_cast<u32x2 *>(op + 16 * ct) =
+                u32x2{bf16_pair_rne(o[hg][ct][0] * inv, o[hg][ct][1] * inv),
+                      bf16_pair_rne(o[hg][ct][2] * inv, o[hg][ct][3] * inv)};
+    }
 }
 
 // Decode split plan (host arithmetic only).  Head groups per workgroup: 2
@@ -447,21 +514,25 @@ hipError_t launch_attention(const AttnArgs &a, bool decode, hipStream_t stream) 
         if (e != hipSuccess || a.n_splits == 1) return e;
         return launch_combine(a, stream);
     }
-    const int hb = (a.n_heads + 63) / 64;          // head blocks of up to 64 heads
-    const int nw = a.n_heads / hb / 16;            // 16-head groups per block (uniform)
+    // head blocks of up to four 16-head groups, all blocks alike: the fewest
+    // blocks that divide the groups evenly (80 heads: five blocks of 16)
+    const int groups = a.n_heads / 16;
+    int hb = (groups + 3) / 4;
+    while (groups % hb != 0) hb++;
+    const int nw = groups / hb;
     dim3 grid(a.n_q, hb);
     if (a.swa_fp8) {
         switch (nw) {
-        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, true>), grid, dim3(320), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, true>), grid, dim3(384), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, true>), grid, dim3(448), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, true>), grid, dim3(512), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, true>), grid, dim3(512), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, true>), grid, dim3(512), 0, stream, a); break;
         default: hipLaunchKernelGGL((mla_prefill_kernel<4, true>), grid, dim3(512), 0, stream, a); break;
         }
     } else {
         switch (nw) {
-        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, false>), grid, dim3(320), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, false>), grid, dim3(384), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, false>), grid, dim3(448), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((mla_prefill_kernel<1, false>), grid, dim3(512), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mla_prefill_kernel<2, false>), grid, dim3(512), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((mla_prefill_kernel<3, false>), grid, dim3(512), 0, stream, a); break;
         default: hipLaunchKernelGGL((mla_prefill_kernel<4, false>), grid, dim3(512), 0, stream, a); break;
         }
     }

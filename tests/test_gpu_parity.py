@@ -402,6 +402,12 @@ ATTN_CASES = {
                           W=128, k=256, given_topk=True),
     "c4a_given_h48": dict(ratio=4, H=48, ctx=[4000], queries=[(0, 3999)], n_slots=[1000], W=64,
                           k=77, given_topk=True),
+    # head counts whose 16-head groups split into uneven blocks of four:
+    # 80 heads run as five blocks of 16, 96 as two blocks of 48
+    "c4a_given_h80": dict(ratio=4, H=80, ctx=[3000, 900], queries=[(0, 2999), (1, 899)],
+                          n_slots=[750, 225], W=96, k=130, given_topk=True),
+    "c4a_given_h96": dict(ratio=4, H=96, ctx=[2500], queries=[(0, 2499)], n_slots=[625], W=128,
+                          k=200, given_topk=True),
     # the ABI's maxima: 128 heads, a 1024-row window, a 4096-entry list
     "c4a_max_h128_w1024_k4096": dict(ratio=4, H=128, ctx=[20000, 1500],
                                      queries=[(0, 19999), (1, 1499)], n_slots=[5000, 375],
