@@ -63,6 +63,9 @@ constexpr int kQPitch = kDI + 16;                   // LDS bytes per staged quer
 // queries per workgroup on large grids (a prefill chunk): consecutive
 // queries of one sequence share every key load and key conversion
 constexpr int kPrefillQT = 2;
+// 64-slot blocks per such workgroup (its queries are staged once for all)
+constexpr int kPrefillST = 64;
+constexpr int kPrefillNS = 2;                       // spans of kPrefillST blocks per workgroup
 
 // ReLU on the bit pattern: non-negative floats compare as non-negative ints,
 // negative ones as negative ints, so one integer max does it (-0 -> +0).
@@ -260,21 +263,24 @@ __global__ __launch_bounds__(256 * WB) void index_score_kernel(IndexArgs a) {
 }
 
 // Several consecutive queries per workgroup (large grids: a prefill chunk):
-// the same 1024-slot tiles as index_score_kernel<HT, 1, F4>, with the
-// workgroup's QT queries of one sequence sharing every key load and key
-// conversion (their operands held side by side); queries of different
-// sequences take a pass each.
-template <int HT, bool F4, int QT>
+// four waves as in index_score_kernel<HT, 1, F4>, each taking ST 16-slot
+// sub-tiles (ST 64-slot blocks per workgroup), with the workgroup's QT
+// queries of one sequence sharing every key load and key conversion (their
+// operands held side by side); queries of different sequences take a pass
+// each.  A workgroup takes NS spans of ST blocks in turn and stages its
+// queries once for all of them.
+template <int HT, bool F4, int QT, int ST, int NS>
 __global__ __launch_bounds__(256) void index_score_mq_kernel(IndexArgs a) {
+    static_assert(ST <= 64 && (ST & (ST - 1)) == 0 && ST % 4 == 0, "one table entry per lane");
     constexpr int WB = 1;
     constexpr int RG = 2;                                        // sub-tiles per load group (registers: QT queries' operands)
-    constexpr int kThreads = 256 * WB, kTile = kSubTiles * kBlockSlots * WB;
+    constexpr int kThreads = 256 * WB, kTile = ST * kBlockSlots * WB;
     const int t0 = blockIdx.x * QT;                              // the workgroup's queries t0 .. t0+QT-1
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int wq = w & 3;                                        // 16-slot quarter of a block
     const int wb = __builtin_amdgcn_readfirstlane(w >> 2);       // block within a sub-tile
-    const int s0 = blockIdx.y * kTile;
+    int s0 = blockIdx.y * NS * kTile;                            // the current span's first slot
 
     // The kernel arguments of the start-up chain in one round of loads
     // (left alone, the compiler spreads them over several dependent rounds,
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(256) void index_score_mq_kernel(IndexArgs a) {
     int32_t my_pb;
     auto lookup = [&](int seq) {
         const int64_t table_row = static_cast<int64_t>(seq) * stride;
-        const int64_t lb = (s0 >> 6) + (lane & (kSubTiles * WB - 1));
+        const int64_t lb = (s0 >> 6) + (lane & (ST * WB - 1));
         const bool in = lb < stride;
         my_pb = table_p[table_row + (in ? lb : 0)];
         my_pb = in ? my_pb : -1;
@@ -450,7 +456,15 @@ __global__ __launch_bounds__(256) void index_score_mq_kernel(IndexArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++) hf[qi][ht][i] = qw[qi][ht][i] * qs[qi][ht][i];
         }
-    for (int pass = 0; pass < passes; pass++) {
+    for (int span = 0; span < NS; span++) {
+      if (span > 0) {                                            // the next ST blocks
+        s0 += kTile;
+        if (s0 >= nv_any) break;
+        lookup(seqs[0]);
+#pragma unroll
+        for (int j = 0; j < RG; j++) stage(j, buf0[j]);
+      }
+      for (int pass = 0; pass < passes; pass++) {
         int nvp = nv_any;                                        // this pass's largest visible count
         if (pass > 0) {                                          // (queries of different sequences)
             lookup(seqs[pass]);
@@ -460,18 +474,23 @@ __global__ __launch_bounds__(256) void index_score_mq_kernel(IndexArgs a) {
         } else if (!same) {
             nvp = nv[0];
         }
-#pragma unroll
-        for (int q = 0; q < kSubTiles / RG; q++) {
-            KeyStage (&cur)[RG] = (q & 1) ? buf1 : buf0;
-            KeyStage (&nxt)[RG] = (q & 1) ? buf0 : buf1;
-            if (q + 1 < kSubTiles / RG) {
+        // load groups alternate between the two buffers: group q + 1 loads
+        // while group q is computed
+        constexpr int NG = ST / RG;
+        auto group = [&](int q, KeyStage (&cur)[RG], KeyStage (&nxt)[RG]) {
+            if (q + 1 < NG) {
 #pragma unroll
                 for (int j = 0; j < RG; j++) stage((q + 1) * RG + j, nxt[j]);
             }
 #pragma unroll
             for (int j = 0; j < RG; j++)
                 if (s0 + kBlockSlots * (WB * (q * RG + j) + wb) < nvp) compute(q * RG + j, cur[j], pass);   // wave-uniform
+        };
+        for (int q = 0; q < NG; q += 2) {
+            group(q, buf0, buf1);
+            group(q + 1, buf1, buf0);
         }
+      }
     }
 }
 
@@ -489,13 +508,13 @@ static void launch_index(const IndexArgs &a, hipStream_t stream) {
 
 template <bool F4>
 static void launch_index_mq(const IndexArgs &a, hipStream_t stream) {
-    constexpr int tile = kSubTiles * kBlockSlots;
+    constexpr int tile = kPrefillNS * kPrefillST * kBlockSlots;
     const dim3 grid((a.n_q + kPrefillQT - 1) / kPrefillQT, (a.max_slots + tile - 1) / tile), block(256);
     switch (a.h_idx / 16) {
-    case 1: hipLaunchKernelGGL((index_score_mq_kernel<1, F4, kPrefillQT>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((index_score_mq_kernel<2, F4, kPrefillQT>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((index_score_mq_kernel<3, F4, kPrefillQT>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((index_score_mq_kernel<4, F4, kPrefillQT>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((index_score_mq_kernel<1, F4, kPrefillQT, kPrefillST, kPrefillNS>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((index_score_mq_kernel<2, F4, kPrefillQT, kPrefillST, kPrefillNS>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((index_score_mq_kernel<3, F4, kPrefillQT, kPrefillST, kPrefillNS>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((index_score_mq_kernel<4, F4, kPrefillQT, kPrefillST, kPrefillNS>), grid, block, 0, stream, a); break;
     }
 }
 

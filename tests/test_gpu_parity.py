@@ -247,6 +247,45 @@ def test_index_scores_multi_query_tiles(S, oracle, key_fp4):
     assert np.array_equal(idx, exact_topk_of(sc, nv, lay.k))
 
 
+@pytest.mark.parametrize("key_fp4", [False, True], ids=["fp8_keys", "mxfp4_keys"])
+def test_index_scores_multi_query_spans(S, oracle, key_fp4):
+    """The prefill form of the index kernel over rows longer than one span of
+    a workgroup's blocks: 9000 and 5200 slots, so workgroups take a second
+    span (and stop early where their queries see fewer slots), with pairs of
+    one sequence (shared keys) and pairs across sequences (a pass each, in
+    every span)."""
+    rng = np.random.default_rng(8)
+    ctx = [36000, 20800]
+    queries = []
+    for i in range(520):
+        if i % 4 < 2:                                   # a pair of adjacent tokens of one sequence
+            b = (i // 4) % 2
+            p0 = int(rng.integers(ctx[b] // 2, ctx[b] - 1)) if i % 4 == 0 else queries[-1][1] + 1
+            queries.append((b, min(p0, ctx[b] - 1)))
+        else:                                           # a pair across sequences
+            b = i % 2
+            queries.append((b, int(rng.integers(0, ctx[b]))))
+    lay = I.build_layer(24, ratio=4, H=16, ctx=ctx, queries=queries, n_slots=[9000, 5200],
+                        W=16, k=128, H_I=16, key_fp4=key_fp4)
+    idx_ref, len_ref, sc_ref = oracle_index_topk(oracle, lay)
+    to_device(lay)
+    assert lay.n_q * ((lay.max_slots + 2047) // 2048) > 512    # the multi-query form
+    sc, idx, ln = gpu_index_topk(S, lay)
+    torch.cuda.synchronize()
+    sc, idx, ln = sc.cpu().numpy(), idx.cpu().numpy(), ln.cpu().numpy()
+    nv = nvis_of(lay, 4)
+    assert nv.max() > 8192                              # some workgroups reach a third 4096-slot run
+    for t in range(lay.n_q):
+        n = nv[t]
+        o = sc_ref[t, :n].astype(np.float64)
+        g = sc[t, :n].astype(np.float64)
+        assert np.all(np.abs(g - o) <= 1e-5 * np.abs(o) + 1e-7 * max(1e-30, np.max(np.abs(o), initial=0))), t
+        assert np.all(np.isnan(sc[t, n:])), t              # nothing past n_vis is written
+    assert np.array_equal(ln, len_ref)
+    check_topk_sets(idx, ln, sc_ref, nv, lay.k)
+    assert np.array_equal(idx, exact_topk_of(sc, nv, lay.k))
+
+
 @pytest.mark.parametrize("H", [16, 48])
 def test_topk_select_warm_equals_select(S, oracle, H):
     """The select with the decode's L2 warm-up (extra read-only workgroups) gives
