@@ -7,28 +7,28 @@
 // (the kernel takes SWA indices together with compressed top-k indices);
 // "DeepseekV4Attention" (devpress), _forward_decode / _forward_prefill.
 //
-// Common pieces.  Every attended entry of a query is first resolved through
-// the block tables into a physical row (SWA entries e < window are positions
-// p-window+1+e, the rest are compressed slot ids); the rows are then gathered
-// chunk by chunk into an LDS tile as bf16 (compressed rows dequantised on the
-// way: code * scale; SWA rows too when the SWA pool holds fp8 rows, as "From
-// MLA to CSA + HCA" 5.5 describes the V4 SWA cache), with the next chunk's
-// global loads in flight while the
-// current chunk is computed.  On the tile, per wave and 16 heads:
-//   S^T = K . Q^T               v_mfma_f32_16x16x32_bf16, Q^T held in registers
+// This file holds the prefill kernel, the merge of decode list splits, the
+// decode's split plan and the launchers; the decode kernel itself is in
+// decode.hip.
+//
+// Prefill.  Every attended entry of a query is first resolved through the
+// block tables into a physical row (SWA entries e < window are positions
+// p-window+1+e, the rest are compressed slot ids).  The rows are then
+// gathered chunk by chunk into an LDS tile as bf16 (compressed rows
+// dequantised on the way: code * scale; SWA rows too when the SWA pool holds
+// fp8 rows, as "From MLA to CSA + HCA" 5.5 describes the V4 SWA cache), with
+// later chunks' global loads in flight.  On a tile:
+//   S^T = K . Q^T               v_mfma_f32_16x16x32_bf16, one wave per 16
+//                               heads, its Q^T in registers
 //   online softmax per head     each lane owns one head: no cross-lane rescale
 //   O^T += V^T . P^T            the score accumulators' lane layout already is
 //                               the P^T operand layout (the MFMA k-order is a
-//                               shared permutation of the rows), and V^T comes
-//                               from the row-major tile via ds_read_tr16_b64.
-//
-// Decode (few queries, long lists): one workgroup per (query, 16-head group,
-// list split); its four waves take 16 rows each of every 64-row chunk and
-// merge their softmax states through LDS.  Head groups of one query are
-// numbered so that they land on the same XCD and share its L2 for the rows.
-// When a query's list is split across workgroups, a combine kernel merges
-// the partial (O, max, sum) states.  Prefill (many queries): one workgroup per
-// query token; its waves are the head groups and share each 32-row tile.
+//                               shared permutation of the rows); V^T comes
+//                               from the row-major tile via ds_read_tr16_b64,
+//                               each wave taking a slice of the output dims
+//                               for every head.
+// Decode splits.  When a query's list is split across workgroups (decode.hip),
+// mla_combine_kernel merges the partial (O, max, sum) states.
 
 #include "slc_internal.hpp"
 
