@@ -770,10 +770,10 @@ def main():
     torch.cuda.synchronize()
 
     graph = None
-    per_graph = len(reps) * args.graph_cycles
     if args.graph:
-        # one graph holds graph_cycles passes over the replicas (per_graph
-        # consecutive steps), so a replay's launch cost is shared by many steps
+        # the K timed steps captured once, as one graph cycling the replicas
+        # (a serving loop replays its decode step the same way); its first
+        # replay is part of the warm-up
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -783,23 +783,31 @@ def main():
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(per_graph):
+            for i in range(args.steps):
                 step(reps[i % len(reps)])
-        for _ in range(max(1, args.warmup // per_graph)):
-            graph.replay()
+        graph.replay()
         torch.cuda.synchronize()
 
     log("warm-up done")
-    # ---- headline: K whole steps launched back to back, no event in between ----
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # ---- K whole steps launched back to back, no event in between ----
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
         step(reps[i % len(reps)])
     t_end.record()
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step_eager = t_start.elapsed_time(t_end) / args.steps
+    # ---- headline: the same K steps as one replay of the captured graph ----
+    ms_step = ms_step_eager
+    if graph is not None:
+        torch.cuda.synchronize()
+        t_start.record()
+        graph.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        ms_step = t_start.elapsed_time(t_end) / args.steps
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
@@ -808,21 +816,12 @@ def main():
     torch.cuda.synchronize()
     ms_step_separate = t_start.elapsed_time(t_end) / args.steps
 
-    # ---- the same steps as replays of the captured graph (reported alongside) ----
-    graph_ms = None
-    if graph is not None:
-        n_rep = max(1, args.steps // per_graph)
-        torch.cuda.synchronize()
-        t_start.record()
-        for _ in range(n_rep):
-            graph.replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        graph_ms = t_start.elapsed_time(t_end) / (n_rep * per_graph)
 
     # ---- per-kernel: back-to-back launches of one op over the replicas, as
     # replays of a graph of that op alone (an eager loop of one short op is
     # bound by the host's launch rate, not by the GPU) ----
+    per_graph = len(reps) * args.graph_cycles
+
     def graph_timed(fn, n):
         if not args.graph:
             return timed(fn, n)
@@ -901,9 +900,9 @@ def main():
                    "block_rows": 64, "replicas": args.replicas},
         "achieved_step_GBps": STEP_BYTES / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": STEP_BYTES / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "timing": "eager_launches",
+        "timing": "graph_replay" if graph is not None else "eager_launches",
+        "eager_ms_per_step": ms_step_eager,
         "ms_per_step_three_calls": ms_step_separate,
-        "graph_ms_per_step": graph_ms,
         "kernels_us": {"index_scores": idx_ms * 1e3,
                        "sparse_mla_decode_topk": topk_decode_ms * 1e3,
                        "topk_select_separate": topk_ms * 1e3,

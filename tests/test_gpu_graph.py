@@ -56,6 +56,70 @@ def test_graph_replays_match_eager():
         assert torch.isfinite(junk)
 
 
+def test_graph_replays_of_the_fused_step_match_eager():
+    """The timed decode step (index scores, then the select and the decode in
+    one call) as one graph of several steps over two input sets, replayed with
+    eager work between replays: every replay gives the eager lists and
+    outputs bit for bit."""
+    from sparse_long_context_compressor_amd import slc
+    lays = []
+    for seed in (31, 32):
+        lay = I.build_layer(seed, ratio=4, H=64, ctx=[20000] * 8, queries=[(b, 19999) for b in range(8)],
+                            n_slots=[5000] * 8, W=128, k=512, H_I=64)
+        to_device(lay)
+        lays.append(lay)
+    dev = lays[0].q.device
+    ms = lays[0].max_slots
+    n, H = lays[0].n_q, lays[0].H
+
+    def bufs():
+        return dict(sc=torch.empty((n, ms), dtype=torch.float32, device=dev),
+                    idx=torch.empty((n, 512), dtype=torch.int32, device=dev),
+                    ln=torch.empty(n, dtype=torch.int32, device=dev),
+                    out=torch.empty((n, H, 512), dtype=torch.bfloat16, device=dev),
+                    lse=torch.empty((n, H), dtype=torch.float32, device=dev))
+    bs = [bufs(), bufs()]
+    ws = torch.empty(max(slc.sparse_mla_workspace_size(True, n, H, 128, 512), 256), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        lay, b = lays[i % 2], bs[i % 2]
+        slc.index_scores(lay.qi, lay.qi_scale, lay.qi_w, lay.q_seq, lay.q_pos, 4, lay.key_pool,
+                         lay.key_table, lay.n_slots, ms, b["sc"])
+        slc.sparse_mla_decode_topk(4, lay.q, lay.q_seq, lay.q_pos, lay.W, lay.swa_pool, lay.swa_table,
+                                   lay.cmp_pool, lay.cmp_table, lay.k, b["sc"], ms, lay.n_slots,
+                                   b["idx"], b["ln"], lay.sm_scale, b["out"], b["lse"], ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(2):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    keys = ("idx", "ln", "out", "lse")
+    ref = [[b[k].clone() for k in keys] for b in bs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(6):
+            step(i)
+    for r in range(4):
+        for b in bs:
+            for k in keys:
+                b[k].zero_()
+        junk = torch.randn(1 << 20, device=dev).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for b, rb in zip(bs, ref):
+            for k, want in zip(keys, rb):
+                got = b[k]
+                if k == "out":
+                    got, want = got.view(torch.int16), want.view(torch.int16)
+                assert torch.equal(got, want), f"replay {r}: {k} differs"
+        assert torch.isfinite(junk)
+
+
 def test_graph_of_a_serving_step_with_the_streaming_calls():
     """A decode step with the per-step writers captured too: the new tokens'
     SWA rows inserted into an fp8 pool, the streaming compressor's state save
