@@ -232,16 +232,21 @@ constexpr int kPreRows = 32;   // rows per prefill chunk
 // one 8-byte load of (m, l) per split.  SN > 0: exactly SN splits, every
 // load issued before any is used (no data-dependent branch between them);
 // SN = 0: any number, in a loop.
+// Grid: ceil(n_q / 8) * 8 * NB blocks of 256 threads, NB = n_heads / 4 per
+// query; the blocks of query t share blockIdx % 8 with the decode's
+// workgroups of t, so a query's partial states are read on the XCD (and
+// through the L2) that wrote them.
 constexpr int kCombCols = 8;
 
 template <int SN>
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
-    const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t per_q = static_cast<int64_t>(a.n_heads) * (kDN / kCombCols);
-    if (id >= per_q * a.n_q) return;
-    const int t = static_cast<int>(id / per_q);
-    const int h = static_cast<int>((id % per_q) / (kDN / kCombCols));
-    const int c8 = static_cast<int>(id % (kDN / kCombCols));
+    const int nb = a.n_heads * (kDN / kCombCols) / 256;              // blocks per query
+    const int grp = blockIdx.x / (8 * nb), rem = blockIdx.x % (8 * nb);
+    const int t = 8 * grp + (rem & 7);
+    if (t >= a.n_q) return;                                          // uniform per block
+    const int id = (rem >> 3) * 256 + threadIdx.x;                   // within the query
+    const int h = id / (kDN / kCombCols);
+    const int c8 = id % (kDN / kCombCols);
     const int S = SN > 0 ? SN : a.n_splits;
     auto slot_of = [&](int sp) { return (static_cast<int64_t>(t) * S + sp) * a.n_heads + h; };
     auto ml_of = [&](int64_t slot) { return *reinterpret_cast<const f32x2 *>(a.part_ml + 2 * slot); };
@@ -503,8 +508,9 @@ void attention_plan(int n_q, int n_heads, int window, int k, bool decode, int *n
 }
 
 hipError_t launch_combine(const AttnArgs &a, hipStream_t stream) {
-    const int64_t threads = static_cast<int64_t>(a.n_q) * a.n_heads * (kDN / kCombCols);
-    const dim3 cgrid(static_cast<unsigned>((threads + 255) / 256)), cblock(256);
+    // n_heads is a multiple of 16, so a query's threads fill whole blocks
+    const unsigned nb = static_cast<unsigned>(a.n_heads * (kDN / kCombCols) / 256);
+    const dim3 cgrid(static_cast<unsigned>((a.n_q + 7) / 8) * 8u * nb), cblock(256);
     switch (a.n_splits) {
     case 2: hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, stream, a); break;
     case 3: hipLaunchKernelGGL(mla_combine_kernel<3>, cgrid, cblock, 0, stream, a); break;
