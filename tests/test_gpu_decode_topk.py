@@ -159,6 +159,20 @@ def _rows():
     n = 1000
     v = rng.normal(size=n).astype(f32)
     rows.append(("k_n_minus_1_1000", v, 999))
+    # full rows, where every wave of the select bounds the threshold by
+    # itself: the top keys all in the first waves' slots (the other waves'
+    # bounds sit far below them), heavy ties everywhere, and a row just long
+    # enough for its last wave to hold k / 8 groups
+    n = 16384
+    v = rng.uniform(0.0, 1.0, n).astype(f32)
+    v[rng.permutation(2000)[:600]] = (2.0 + rng.uniform(0.0, 1.0, 600)).astype(f32)
+    rows.append(("wave_bound_concentrated_16384", v, 512))
+    n = 16384
+    v = rng.integers(0, 41, n).astype(f32)
+    rows.append(("wave_bound_ties_16384", v, 512))
+    n = 14592
+    v = rng.normal(size=n).astype(f32)
+    rows.append(("wave_bound_short_last_wave_14592", v, 512))
     # one query, k = 4096: 8 splits of exactly 512 list entries (the largest
     # share the one-launch form takes)
     n = 16384

@@ -376,6 +376,16 @@ def _crafted_rows():
     n = 777
     v = rng.normal(size=n).astype(f32)
     rows.append(("short_row", v, 300))
+    # full rows, where every wave of the select bounds the threshold by
+    # itself: the top keys concentrated in the first waves' slots, and heavy
+    # ties everywhere
+    n = 16384
+    v = rng.uniform(0.0, 1.0, n).astype(f32)
+    v[rng.permutation(2000)[:600]] = (2.0 + rng.uniform(0.0, 1.0, 600)).astype(f32)
+    rows.append(("wave_bound_concentrated", v, 512))
+    n = 16384
+    v = rng.integers(0, 41, n).astype(f32)
+    rows.append(("wave_bound_ties", v, 512))
     # past 65536 slots (the long-row kernel): a 1M-token context at ratio 4 is
     # 262144 slots; heavy exact ties at the threshold, -inf and signed zeros
     n = 262144
