@@ -36,7 +36,7 @@ namespace slc {
 
 namespace {
 
-constexpr int kKPitch = kD + 8;        // bf16 per LDS row: 1168 B, spreads banks
+constexpr int kKPitch = kD + 16;       // bf16 per LDS row: 1184 B (2 mod 4 16-byte units: no bank conflicts for the K and V^T reads)
 constexpr int kMaxEntries = SLC_MAX_WINDOW + SLC_MAX_TOPK;
 constexpr int kMaxCombineSplits = 8;    // splits the combine kernel merges unrolled
 

@@ -7,10 +7,16 @@
 
 namespace slc {
 
-constexpr int kB16Pitch = 2 * kD + 16;          // bytes per bf16 row in LDS (1168)
-constexpr int kF8Pitch = 688;                   // 512 codes | 64 bf16 rope | 8 fp32 scales | pad
+// Row pitches in LDS.  Measured on gfx950 (a microbenchmark of the kernels'
+// own read patterns, eight reads in flight per wave): with a pitch of 16 B
+// times 2 mod 4 units, 16-byte reads of 16 rows at one column and the
+// transposing reads of 4 rows run conflict-free (5.7 and 3.8 clocks per wave
+// instruction and CU); odd multiples of 16 B measured 8.1 and 5.6.
+constexpr int kB16Pitch = 2 * kD + 32;          // bytes per bf16 row in LDS (1184)
+constexpr int kF8Pitch = 672;                   // 512 codes | 64 bf16 rope | 8 fp32 scales
 constexpr int kF8Data = SLC_CMP_ROW_BYTES;      // 640: codes + rope, then the scales
-static_assert(kF8Pitch % 16 == 0 && (kF8Pitch / 16) % 2 == 1, "16-byte reads of 8 rows hit distinct banks");
+static_assert(kB16Pitch % 64 == 32 && kF8Pitch % 64 == 32, "row pitches of 2 mod 4 16-byte units");
+static_assert(kF8Pitch >= kF8Data + 32, "a row's scales fit behind its codes and rope");
 
 namespace {
 
