@@ -400,16 +400,6 @@ void mla_prefill_kernel(AttnArgs a) {
                 }
                 sacc[mt] = s0 + s1;
             }
-            // schedule: six operand reads issued ahead of the first product, then one
-            // read per product, so each product's operand has been in flight for
-            // several products (the loop's bound is the LDS read latency)
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // DS reads
-#pragma unroll
-            for (int i = 0; i < 2 * (kD / 32) - 6; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
             float x[8], pv[8];
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
